@@ -1,0 +1,212 @@
+#!/usr/bin/env python3
+"""Forward + backward throughput of the RAWINT4 routed-expert LoRA layer on one MI355X.
+
+A step is one forward and one backward of the layer (grouping, gate/up GEMM with
+SwiGLU, down GEMM with the route-weighted combine, down and gate/up transpose-
+free dX, LoRA side products and the six LoRA gradient reductions) over one
+synthetic batch already resident in HBM.  Prints ONE JSON line on stdout;
+progress goes to stderr.
+
+Default workload: 384 experts, top-8, hidden 7168, intermediate 2048, LoRA rank 64
+(alpha 128), 16384 tokens, SwiGLU clamp 7, uniform routing.  ``--config`` picks
+another of the five workloads of ``int4_quantized_moe_amd.workloads.CONFIGS``.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "routed-expert fwd+bwd tokens/sec per layer; % MFMA peak / % HBM BW"
+PEAK_MFMA_FP16 = 2.5e15  # dense fp16/bf16 MFMA, FLOP/s
+PEAK_HBM = 8.0e12  # bytes/s
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def phase_work(cfg, slots):
+    """Algorithmic flops and packed-weight bytes per launch of each phase.
+
+    Flops per token-slot: gate/up 4HI + 4rI, down 2IH + 2rH, down dX 2HI + 2rI,
+    gate/up dX 4IH + 4rH (each with its in-GEMM LoRA term); LoRA side products
+    4rH, 2rI, 2rH, 4rI; LoRA gradients 6rH + 6rI; in all 12HI + 18r(H+I).
+    Packed-weight bytes: codes (N*K/2) plus bf16 scales (N*K/16) of each active
+    expert's projection(s) the phase streams.
+    """
+    H, I, r = cfg.hidden, cfg.intermediate, cfg.rank
+    proj = H * I // 2 + H * I // 16  # one projection of one expert
+    return {
+        "gemm_gate_up": (slots * (4 * H * I + 4 * r * I), 2 * proj),
+        "gemm_down": (slots * (2 * I * H + 2 * r * H), proj),
+        "gemm_down_dx": (slots * (2 * H * I + 2 * r * I), proj),
+        "gemm_gate_up_dx": (slots * (4 * I * H + 4 * r * H), 2 * proj),
+        "lora_a_gate_up": (slots * 4 * r * H, 0),
+        "lora_a_down": (slots * 2 * r * I, 0),
+        "lora_b_down_bwd": (slots * 2 * r * H, 0),
+        "lora_b_gate_up_bwd": (slots * 4 * r * I, 0),
+        "lora_grads": (slots * (6 * r * H + 6 * r * I), 0),
+    }
+
+
+def cpu_baseline(cfg, weights, batch, target_s):
+    """The oracle, as it stands, on the first n tokens of the same batch."""
+    import numpy as np
+
+    import oracle as O
+
+    def run(n):
+        t0 = time.perf_counter()
+        O.moe(cfg, weights, batch.inputs[:n], batch.expert_ids[:n], batch.route_weights[:n], batch.grad_output[:n])
+        return time.perf_counter() - t0
+
+    n = min(8, cfg.qlen)
+    t = run(n)
+    log(f"cpu oracle pilot: {n} tokens in {t:.2f}s")
+    if t < target_s / 3 and n < cfg.qlen:
+        n = int(min(cfg.qlen, max(n, n * target_s / max(t, 1e-3))))
+        t = run(n)
+        log(f"cpu oracle sample: {n} tokens in {t:.2f}s")
+    active = int(np.unique(batch.expert_ids[:n]).size)
+    return {
+        "value": n / t,
+        "unit": "tokens/s",
+        "cores": O.num_threads(),
+        "kind": "oracle",
+        "sample": f"first {n} of {cfg.qlen} tokens ({n * cfg.top_k} token-slots, {active} active experts), "
+                  f"fwd+bwd, fp64 accumulation, {t:.1f} s wall",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", type=int, default=4, help="index into workloads.CONFIGS")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (expert parallelism is designed, "
+              "not built); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from int4_quantized_moe_amd import _lib, device, workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    cfg = workloads.CONFIGS[args.config]
+    seed = workloads.config_seed(args.config)
+    log(f"workload {cfg.name}: generating (seed {seed})")
+    t0 = time.perf_counter()
+    weights = workloads.make_weights(cfg, seed)
+    batch = workloads.make_batch(cfg, seed)
+    log(f"generated in {time.perf_counter() - t0:.1f}s; uploading")
+    dl = device.DeviceLayer(cfg, weights, "cuda:0")
+    db = device.DeviceBatch(batch, "cuda:0")
+    ws = dl.workspace(db.qlen)
+    grads = dl.grad_buffers(fill=0.0)
+    out = torch.empty((db.qlen, cfg.hidden), dtype=torch.bfloat16, device="cuda:0")
+    dx = torch.empty_like(out)
+    droute = torch.empty((db.qlen, cfg.top_k), dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        dl.forward(db.inputs, db.expert_ids, db.route_weights, ws, output=out, stream=stream)
+        dl.backward(db.inputs, db.expert_ids, db.route_weights, db.grad_output, ws, grads, accumulate=False,
+                    grad_scale=1.0, grad_input=dx, grad_route=droute, stream=stream)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    _lib.kt_rawint4_profile_read()  # drop anything recorded before
+    _lib.kt_rawint4_profile_enable(True)
+    log(f"timing {args.steps} steps")
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    _lib.kt_rawint4_profile_enable(False)
+    phases = _lib.kt_rawint4_profile_read()
+    gpu_ms = start.elapsed_time(stop)
+    ms_per_step = gpu_ms / args.steps
+    value = db.qlen * args.steps / (gpu_ms / 1e3)
+    log(f"{ms_per_step:.3f} ms/step (wall {1e3 * wall / args.steps:.3f}), {value:.1f} tokens/s")
+
+    slots = int(np.count_nonzero((batch.expert_ids >= 0) & (batch.expert_ids < cfg.num_experts)))
+    active = int(np.unique(batch.expert_ids).size)
+    work = phase_work(cfg, slots)
+    per_step = {}
+    for name, (ms, n) in phases.items():
+        if n:
+            per_step[name] = round(ms / args.steps, 4)
+            log(f"  {name:22s} {ms / n:9.3f} ms/launch x {n / args.steps:.0f}/step")
+    gemms = [p for p in work if p.startswith("gemm") and phases.get(p, (0, 0))[1]]
+    dom = max(gemms, key=lambda p: phases[p][0])
+    dom_ms = phases[dom][0] / phases[dom][1]
+    flops, wbytes = work[dom]
+    wbytes *= active
+    if flops / max(wbytes, 1) > PEAK_MFMA_FP16 / PEAK_HBM:
+        achieved, peak = flops / (dom_ms / 1e3) / 1e12, PEAK_MFMA_FP16 / 1e12
+        roof = {"bound": "mfma", "unit": "TFLOP/s"}
+    else:
+        achieved, peak = wbytes / (dom_ms / 1e3) / 1e9, PEAK_HBM / 1e9
+        roof = {"bound": "hbm", "unit": "GB/s"}
+    roof.update({"kernel": dom, "achieved": round(achieved, 2), "peak": peak, "frac": round(achieved / peak, 4),
+                 "traffic": None, "avg_ms": round(dom_ms, 4)})
+    total_flops = slots * (12 * cfg.hidden * cfg.intermediate + 18 * cfg.rank * (cfg.hidden + cfg.intermediate))
+    total_wbytes = 2 * 3 * active * (cfg.hidden * cfg.intermediate // 2 + cfg.hidden * cfg.intermediate // 16)
+    log(f"step: {total_flops / (ms_per_step / 1e3) / 1e12:.1f} TFLOP/s "
+        f"({100 * total_flops / (ms_per_step / 1e3) / PEAK_MFMA_FP16:.2f}% MFMA), packed weights "
+        f"{total_wbytes / (ms_per_step / 1e3) / 1e9:.1f} GB/s ({100 * total_wbytes / (ms_per_step / 1e3) / PEAK_HBM:.2f}% HBM)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, weights, batch, args.cpu_seconds)
+        log(f"cpu baseline {cpu['value']:.2f} tokens/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "experts": cfg.num_experts, "top_k": cfg.top_k, "hidden": cfg.hidden,
+                   "intermediate": cfg.intermediate, "rank": cfg.rank, "alpha": cfg.alpha, "qlen": cfg.qlen,
+                   "swiglu_limit": cfg.swiglu_limit, "routing": cfg.routing, "active_experts": active},
+        "mfma_frac_step": round(total_flops / (ms_per_step / 1e3) / PEAK_MFMA_FP16, 4),
+        "hbm_frac_step": round(total_wbytes / (ms_per_step / 1e3) / PEAK_HBM, 4),
+        "phase_ms_per_step": per_step,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

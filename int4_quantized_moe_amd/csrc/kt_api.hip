@@ -1,0 +1,523 @@
+// C ABI of the RAWINT4 routed-expert LoRA layer: argument checks, workspace map
+// and the order of kernel launches for the forward and the backward.
+#include <math.h>
+#include <stdio.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "kt_common.hpp"
+#include "kt_internal.hpp"
+
+namespace kt {
+
+static thread_local std::string g_last_error;
+
+static int fail(int code, const char* msg) {
+  g_last_error = msg;
+  return code;
+}
+
+static size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct Planner {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  }
+};
+
+static void plan_group_part(Planner& pl, WsMap& w, int64_t Ms, int64_t E) {
+  w.nb = (Ms + kGroupBlock - 1) / kGroupBlock;
+  w.max_tiles = Ms / kMT + (E < Ms ? E : Ms);
+  w.counters = pl.take(sizeof(unsigned long long) * kNumCounters);
+  w.counts = pl.take(sizeof(int32_t) * (size_t)E);
+  w.offsets = pl.take(sizeof(int32_t) * (size_t)(E + 1));
+  w.blockcnt = pl.take(sizeof(int32_t) * (size_t)(w.nb * E));
+  w.sorted_slot = pl.take(sizeof(int32_t) * (size_t)Ms);
+  w.row_of_slot = pl.take(sizeof(int32_t) * (size_t)Ms);
+  w.tile_e = pl.take(sizeof(int32_t) * (size_t)w.max_tiles);
+  w.tile_m0 = pl.take(sizeof(int32_t) * (size_t)w.max_tiles);
+  w.group_end = pl.off;
+}
+
+WsMap plan_group_workspace(int64_t qlen, int64_t top_k, int64_t E) {
+  WsMap w{};
+  Planner pl;
+  plan_group_part(pl, w, qlen * top_k, E);
+  w.total = pl.off;
+  return w;
+}
+
+WsMap plan_workspace(const Dims& d) {
+  WsMap w{};
+  Planner pl;
+  plan_group_part(pl, w, d.Ms, d.E);
+  w.h_nch = (d.I + kHChunk - 1) / kHChunk;
+  w.dr_nt = (d.I + kNT - 1) / kNT;
+  w.dg_nch = 2 * w.dr_nt;
+  const size_t Ms = (size_t)d.Ms, q = (size_t)d.qlen, H = (size_t)d.H, I = (size_t)d.I, R = (size_t)d.R;
+  w.xh = pl.take(2 * q * H);
+  w.xexp = pl.take(4 * q);
+  w.ua = pl.take(4 * Ms * R);
+  w.ub = pl.take(4 * Ms * R);
+  w.g = pl.take(4 * Ms * I);
+  w.u = pl.take(4 * Ms * I);
+  w.hh = pl.take(2 * Ms * I);
+  w.hexp = pl.take(4 * Ms * (size_t)w.h_nch);
+  w.ud = pl.take(4 * Ms * R);
+  w.stage = pl.take(4 * Ms * H);
+  w.dyh = pl.take(2 * q * H);
+  w.dyexp = pl.take(4 * q);
+  w.dyb = pl.take(4 * Ms * R);
+  w.dgu = pl.take(2 * Ms * 2 * I);
+  w.dguexp = pl.take(4 * Ms * (size_t)w.dg_nch);
+  w.dgb = pl.take(4 * Ms * R);
+  w.dub = pl.take(4 * Ms * R);
+  w.drpart = pl.take(4 * Ms * (size_t)w.dr_nt);
+  w.total = pl.off;
+  return w;
+}
+
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+static int check_layer(const kt_rawint4_moe_layer* L, int32_t qlen, Dims* d) {
+  if (!L) return fail(KT_RAWINT4_EINVAL, "layer is NULL");
+  if (L->num_experts < 1 || L->num_experts > KT_RAWINT4_MAX_EXPERTS)
+    return fail(KT_RAWINT4_EINVAL, "num_experts must be in [1, 8192]");
+  if (L->top_k < 1 || L->top_k > L->num_experts) return fail(KT_RAWINT4_EINVAL, "top_k must be in [1, num_experts]");
+  if (L->hidden <= 0 || L->hidden % KT_RAWINT4_GROUP_SIZE || L->hidden > 65536)
+    return fail(KT_RAWINT4_EINVAL, "hidden must be a positive multiple of 32 (at most 65536)");
+  if (L->intermediate <= 0 || L->intermediate % KT_RAWINT4_GROUP_SIZE || L->intermediate > 65536)
+    return fail(KT_RAWINT4_EINVAL, "intermediate must be a positive multiple of 32 (at most 65536)");
+  if (L->rank < 1 || L->rank > KT_RAWINT4_MAX_RANK) return fail(KT_RAWINT4_EINVAL, "rank must be in [1, 128]");
+  if (!isfinite(L->alpha)) return fail(KT_RAWINT4_EINVAL, "alpha must be finite");
+  if (!isfinite(L->swiglu_limit) || L->swiglu_limit < 0.f)
+    return fail(KT_RAWINT4_EINVAL, "swiglu_limit must be finite and non-negative");
+  if (qlen < 0) return fail(KT_RAWINT4_EINVAL, "qlen must be non-negative");
+  if ((int64_t)qlen * L->top_k >= ((int64_t)1 << 31)) return fail(KT_RAWINT4_EINVAL, "qlen * top_k must be below 2^31");
+  const void* ptrs[] = {L->gate_packed, L->up_packed,   L->down_packed, L->gate_scale,  L->up_scale,
+                        L->down_scale,  L->gate_lora_a, L->gate_lora_b, L->up_lora_a,   L->up_lora_b,
+                        L->down_lora_a, L->down_lora_b};
+  for (const void* p : ptrs)
+    if (!p) return fail(KT_RAWINT4_EINVAL, "a weight, scale or LoRA pointer is NULL");
+  if (!aligned(L->gate_packed, 16) || !aligned(L->up_packed, 16) || !aligned(L->down_packed, 16))
+    return fail(KT_RAWINT4_EINVAL, "packed weights must be 16-byte aligned");
+  if (!aligned(L->gate_scale, 2) || !aligned(L->up_scale, 2) || !aligned(L->down_scale, 2))
+    return fail(KT_RAWINT4_EINVAL, "scales must be 2-byte aligned");
+  const float* lora[] = {L->gate_lora_a, L->gate_lora_b, L->up_lora_a, L->up_lora_b, L->down_lora_a, L->down_lora_b};
+  for (const float* p : lora)
+    if (!aligned(p, 4)) return fail(KT_RAWINT4_EINVAL, "LoRA tensors must be 4-byte aligned");
+  d->E = L->num_experts;
+  d->K = L->top_k;
+  d->H = L->hidden;
+  d->I = L->intermediate;
+  d->R = L->rank;
+  d->qlen = qlen;
+  d->Ms = (int64_t)qlen * L->top_k;
+  d->sc = L->alpha / (float)L->rank;
+  d->limit = L->swiglu_limit;
+  return KT_RAWINT4_OK;
+}
+
+static LayerPtrs layer_ptrs(const kt_rawint4_moe_layer* L) {
+  LayerPtrs p;
+  p.wg = L->gate_packed;
+  p.wu = L->up_packed;
+  p.wd = L->down_packed;
+  p.sg = L->gate_scale;
+  p.su = L->up_scale;
+  p.sd = L->down_scale;
+  p.ag = L->gate_lora_a;
+  p.bg = L->gate_lora_b;
+  p.au = L->up_lora_a;
+  p.bu = L->up_lora_b;
+  p.ad = L->down_lora_a;
+  p.bd = L->down_lora_b;
+  return p;
+}
+
+static int check_workspace(void* ws, size_t bytes, size_t need) {
+  if (!ws) return fail(KT_RAWINT4_EINVAL, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(KT_RAWINT4_EINVAL, "workspace must be 256-byte aligned");
+  if (bytes < need) return fail(KT_RAWINT4_EWORKSPACE, "workspace is smaller than the required size");
+  return KT_RAWINT4_OK;
+}
+
+static int launched() {
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) {
+    g_last_error = std::string("HIP launch failed: ") + hipGetErrorString(err);
+    return KT_RAWINT4_EHIP;
+  }
+  g_last_error.clear();
+  return KT_RAWINT4_OK;
+}
+
+static RowView view_tok_bf16(const uint16_t* p, int64_t ld, const float* slot_scale = nullptr) {
+  RowView v{};
+  v.kind = kSrcTokBf16;
+  v.ptr = p;
+  v.ld = ld;
+  v.slot_scale = slot_scale;
+  return v;
+}
+
+static RowView view_f32(const float* p, int64_t ld, const float* slot_scale = nullptr) {
+  RowView v{};
+  v.kind = kSrcF32;
+  v.ptr = p;
+  v.ld = ld;
+  v.slot_scale = slot_scale;
+  return v;
+}
+
+static RowView view_half(const uint16_t* p, int64_t ld, int64_t col_off, const int32_t* exps, int64_t exp_ld,
+                         int64_t exp_off, int64_t chunk_w) {
+  RowView v{};
+  v.kind = kSrcHalfChunked;
+  v.ptr = p;
+  v.ld = ld;
+  v.col_off = col_off;
+  v.exps = exps;
+  v.exp_ld = exp_ld;
+  v.exp_off = exp_off;
+  v.chunk_w = chunk_w;
+  return v;
+}
+
+
+// ---------------------------------------------------------------- per-phase event timing
+
+enum Phase {
+  kPhGroup = 0,
+  kPhXHalf,
+  kPhLoraXA,
+  kPhGemmGateUp,
+  kPhLoraHA,
+  kPhGemmDown,
+  kPhCombineFwd,
+  kPhDyHalf,
+  kPhLoraDyB,
+  kPhGemmDownBwd,
+  kPhLoraDgB,
+  kPhGemmGateUpBwd,
+  kPhCombineBwd,
+  kPhDRoute,
+  kPhLoraGrads,
+  kNumPhases
+};
+
+static const char* const kPhaseNames[kNumPhases] = {
+    "group",        "x_to_half",      "lora_a_gate_up", "gemm_gate_up",     "lora_a_down",
+    "gemm_down",    "combine_fwd",    "dy_to_half",     "lora_b_down_bwd",  "gemm_down_dx",
+    "lora_b_gate_up_bwd", "gemm_gate_up_dx", "combine_bwd", "droute",       "lora_grads"};
+
+struct ProfRec {
+  int phase;
+  hipEvent_t a, b;
+};
+
+static std::mutex g_prof_mu;
+static bool g_prof_on = false;
+static std::vector<hipEvent_t> g_prof_pool;
+static std::vector<ProfRec> g_prof_recs;
+
+static hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t ev = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return ev;
+  }
+  hipEvent_t ev = nullptr;
+  if (hipEventCreate(&ev) != hipSuccess) return nullptr;
+  return ev;
+}
+
+// Records a start/stop event pair around the launches of one phase on the
+// caller's stream while profiling is enabled.
+struct PhaseScope {
+  int phase;
+  hipStream_t st;
+  hipEvent_t a = nullptr, b = nullptr;
+  PhaseScope(int ph, hipStream_t s) : phase(ph), st(s) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!g_prof_on) return;
+    a = prof_event();
+    b = prof_event();
+    if (a && b) hipEventRecord(a, st);
+  }
+  ~PhaseScope() {
+    if (!a || !b) return;
+    hipEventRecord(b, st);
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_recs.push_back({phase, a, b});
+  }
+};
+
+}  // namespace kt
+
+using namespace kt;
+
+extern "C" {
+
+size_t kt_rawint4_moe_workspace_bytes(const kt_rawint4_moe_layer* layer, int32_t qlen) {
+  Dims d;
+  if (check_layer(layer, qlen, &d) != KT_RAWINT4_OK) return 0;
+  return plan_workspace(d).total;
+}
+
+int kt_rawint4_moe_fwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const uint16_t* inputs,
+                       const int64_t* expert_ids, const float* route_weights, uint16_t* output, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  Dims d;
+  int rc = check_layer(layer, qlen, &d);
+  if (rc) return rc;
+  if (qlen == 0) {
+    g_last_error.clear();
+    return KT_RAWINT4_OK;
+  }
+  if (!inputs || !expert_ids || !route_weights || !output)
+    return fail(KT_RAWINT4_EINVAL, "inputs, expert_ids, route_weights and output must be non-NULL");
+  if (!aligned(inputs, 16) || !aligned(output, 8) || !aligned(expert_ids, 8) || !aligned(route_weights, 4))
+    return fail(KT_RAWINT4_EINVAL, "inputs must be 16-byte aligned, output and expert_ids 8-byte aligned");
+  const WsMap w = plan_workspace(d);
+  rc = check_workspace(workspace, workspace_bytes, w.total);
+  if (rc) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const LayerPtrs L = layer_ptrs(layer);
+  void* ws = workspace;
+
+  {
+    PhaseScope ph(kPhGroup, st);
+    launch_init_counters(ws, w, st);
+    launch_group(d, w, ws, expert_ids, st);
+  }
+  {
+    PhaseScope ph(kPhXHalf, st);
+    launch_rows_to_half(inputs, d.qlen, d.H, ws_ptr<uint16_t>(ws, w.xh), ws_ptr<int32_t>(ws, w.xexp), st);
+  }
+  const RowView xv = view_tok_bf16(inputs, d.H);
+  {
+    PhaseScope ph(kPhLoraXA, st);
+    launch_lora_rowproj(d, w, ws, xv, d.H, L.ag, true, ws_ptr<float>(ws, w.ua), st);
+    launch_lora_rowproj(d, w, ws, xv, d.H, L.au, true, ws_ptr<float>(ws, w.ub), st);
+  }
+  {
+    PhaseScope ph(kPhGemmGateUp, st);
+    launch_gemm(kGateUp, d, w, ws, L, route_weights, st);
+  }
+  const RowView hv = view_half(ws_ptr<uint16_t>(ws, w.hh), d.I, 0, ws_ptr<int32_t>(ws, w.hexp), w.h_nch, 0, kHChunk);
+  {
+    PhaseScope ph(kPhLoraHA, st);
+    launch_lora_rowproj(d, w, ws, hv, d.I, L.ad, true, ws_ptr<float>(ws, w.ud), st);
+  }
+  {
+    PhaseScope ph(kPhGemmDown, st);
+    launch_gemm(kDown, d, w, ws, L, route_weights, st);
+  }
+  {
+    PhaseScope ph(kPhCombineFwd, st);
+    launch_combine(d, ws_ptr<float>(ws, w.stage), expert_ids, output, st);
+  }
+  return launched();
+}
+
+int kt_rawint4_moe_bwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const uint16_t* inputs,
+                       const int64_t* expert_ids, const float* route_weights, const uint16_t* grad_output,
+                       uint16_t* grad_input, float* grad_route, float* d_gate_a, float* d_gate_b, float* d_up_a,
+                       float* d_up_b, float* d_down_a, float* d_down_b, int32_t accumulate, float grad_scale,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  Dims d;
+  int rc = check_layer(layer, qlen, &d);
+  if (rc) return rc;
+  float* grads[6] = {d_gate_a, d_gate_b, d_up_a, d_up_b, d_down_a, d_down_b};
+  for (float* g : grads) {
+    if (!g) return fail(KT_RAWINT4_EINVAL, "the six LoRA gradient buffers must be non-NULL");
+    if (!aligned(g, 4)) return fail(KT_RAWINT4_EINVAL, "LoRA gradient buffers must be 4-byte aligned");
+  }
+  if (!isfinite(grad_scale)) return fail(KT_RAWINT4_EINVAL, "grad_scale must be finite");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t gsz[6] = {d.E * d.R * d.H, d.E * d.I * d.R, d.E * d.R * d.H,
+                          d.E * d.I * d.R, d.E * d.R * d.I, d.E * d.H * d.R};
+  if (qlen == 0) {
+    if (!accumulate)
+      for (int j = 0; j < 6; ++j) launch_fill_zero_f32(grads[j], gsz[j], st);
+    return launched();
+  }
+  if (!inputs || !expert_ids || !route_weights || !grad_output || !grad_input)
+    return fail(KT_RAWINT4_EINVAL, "inputs, expert_ids, route_weights, grad_output and grad_input must be non-NULL");
+  if (!aligned(inputs, 16) || !aligned(grad_output, 16) || !aligned(grad_input, 8) || !aligned(expert_ids, 8) ||
+      !aligned(route_weights, 4) || (grad_route && !aligned(grad_route, 4)))
+    return fail(KT_RAWINT4_EINVAL, "inputs and grad_output must be 16-byte aligned, grad_input 8-byte aligned");
+  const WsMap w = plan_workspace(d);
+  rc = check_workspace(workspace, workspace_bytes, w.total);
+  if (rc) return rc;
+  const LayerPtrs L = layer_ptrs(layer);
+  void* ws = workspace;
+
+  {
+    PhaseScope ph(kPhDyHalf, st);
+    launch_rows_to_half(grad_output, d.qlen, d.H, ws_ptr<uint16_t>(ws, w.dyh), ws_ptr<int32_t>(ws, w.dyexp), st);
+  }
+  const RowView dyv = view_tok_bf16(grad_output, d.H);
+  {
+    PhaseScope ph(kPhLoraDyB, st);
+    launch_lora_rowproj(d, w, ws, dyv, d.H, L.bd, false, ws_ptr<float>(ws, w.dyb), st);
+  }
+  {
+    PhaseScope ph(kPhGemmDownBwd, st);
+    launch_gemm(kDownBwd, d, w, ws, L, route_weights, st);
+  }
+  const RowView dgv = view_half(ws_ptr<uint16_t>(ws, w.dgu), 2 * d.I, 0, ws_ptr<int32_t>(ws, w.dguexp), w.dg_nch, 0, kNT);
+  const RowView duv =
+      view_half(ws_ptr<uint16_t>(ws, w.dgu), 2 * d.I, d.I, ws_ptr<int32_t>(ws, w.dguexp), w.dg_nch, w.dg_nch / 2, kNT);
+  {
+    PhaseScope ph(kPhLoraDgB, st);
+    launch_lora_rowproj(d, w, ws, dgv, d.I, L.bg, false, ws_ptr<float>(ws, w.dgb), st);
+    launch_lora_rowproj(d, w, ws, duv, d.I, L.bu, false, ws_ptr<float>(ws, w.dub), st);
+  }
+  {
+    PhaseScope ph(kPhGemmGateUpBwd, st);
+    launch_gemm(kGateUpBwd, d, w, ws, L, route_weights, st);
+  }
+  {
+    PhaseScope ph(kPhCombineBwd, st);
+    launch_combine(d, ws_ptr<float>(ws, w.stage), expert_ids, grad_input, st);
+  }
+  if (grad_route) {
+    PhaseScope ph(kPhDRoute, st);
+    launch_droute(d, w, ws, grad_route, st);
+  }
+  PhaseScope ph_grads(kPhLoraGrads, st);
+
+  const float gs = grad_scale * d.sc;
+  const RowView xv = view_tok_bf16(inputs, d.H);
+  const RowView hv = view_half(ws_ptr<uint16_t>(ws, w.hh), d.I, 0, ws_ptr<int32_t>(ws, w.hexp), w.h_nch, 0, kHChunk);
+  // down: dB_d = sc sum (rw dY) (x) ud,  dA_d = sc sum (rw dyB) (x) h
+  launch_lora_grad(d, w, ws, view_tok_bf16(grad_output, d.H, route_weights), d.H, view_f32(ws_ptr<float>(ws, w.ud), d.R),
+                   d.R, d_down_b, accumulate, gs, st);
+  launch_lora_grad(d, w, ws, view_f32(ws_ptr<float>(ws, w.dyb), d.R, route_weights), d.R, hv, d.I, d_down_a,
+                   accumulate, gs, st);
+  // gate/up: dB = sc sum dG (x) ua,  dA = sc sum dgB (x) x
+  launch_lora_grad(d, w, ws, dgv, d.I, view_f32(ws_ptr<float>(ws, w.ua), d.R), d.R, d_gate_b, accumulate, gs, st);
+  launch_lora_grad(d, w, ws, view_f32(ws_ptr<float>(ws, w.dgb), d.R), d.R, xv, d.H, d_gate_a, accumulate, gs, st);
+  launch_lora_grad(d, w, ws, duv, d.I, view_f32(ws_ptr<float>(ws, w.ub), d.R), d.R, d_up_b, accumulate, gs, st);
+  launch_lora_grad(d, w, ws, view_f32(ws_ptr<float>(ws, w.dub), d.R), d.R, xv, d.H, d_up_a, accumulate, gs, st);
+  return launched();
+}
+
+int kt_rawint4_unpack(const uint8_t* packed, int64_t n, int64_t k, int8_t* codes, void* stream) {
+  if (n < 0 || k < 0 || k % 2) return fail(KT_RAWINT4_EINVAL, "n must be >= 0 and k a non-negative even number");
+  if (n * k > 0 && (!packed || !codes)) return fail(KT_RAWINT4_EINVAL, "packed and codes must be non-NULL");
+  launch_unpack(packed, n, k, codes, static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+int kt_rawint4_dequant(const uint8_t* packed, const uint16_t* scales, int64_t n, int64_t k, float* weights,
+                       void* stream) {
+  if (n < 0 || k < 0 || k % KT_RAWINT4_GROUP_SIZE)
+    return fail(KT_RAWINT4_EINVAL, "n must be >= 0 and k a multiple of 32");
+  if (n * k > 0 && (!packed || !scales || !weights))
+    return fail(KT_RAWINT4_EINVAL, "packed, scales and weights must be non-NULL");
+  if (!aligned(packed, 4)) return fail(KT_RAWINT4_EINVAL, "packed must be 4-byte aligned");
+  launch_dequant(packed, scales, n, k, weights, static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+size_t kt_rawint4_group_workspace_bytes(int32_t qlen, int32_t top_k, int32_t num_experts) {
+  if (qlen < 0 || top_k < 1 || num_experts < 1 || num_experts > KT_RAWINT4_MAX_EXPERTS) {
+    fail(KT_RAWINT4_EINVAL, "invalid grouping dimensions");
+    return 0;
+  }
+  return plan_group_workspace(qlen, top_k, num_experts).total;
+}
+
+int kt_rawint4_group(const int64_t* expert_ids, int32_t qlen, int32_t top_k, int32_t num_experts, int32_t* offsets,
+                     int32_t* sorted_slot, void* workspace, size_t workspace_bytes, void* stream) {
+  if (qlen < 0 || top_k < 1 || num_experts < 1 || num_experts > KT_RAWINT4_MAX_EXPERTS)
+    return fail(KT_RAWINT4_EINVAL, "invalid grouping dimensions");
+  if ((int64_t)qlen * top_k >= ((int64_t)1 << 31)) return fail(KT_RAWINT4_EINVAL, "qlen * top_k must be below 2^31");
+  if (!offsets || (qlen > 0 && (!expert_ids || !sorted_slot)))
+    return fail(KT_RAWINT4_EINVAL, "expert_ids, offsets and sorted_slot must be non-NULL");
+  const WsMap w = plan_group_workspace(qlen, top_k, num_experts);
+  int rc = check_workspace(workspace, workspace_bytes, w.total);
+  if (rc) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Dims d{};
+  d.E = num_experts;
+  d.K = top_k;
+  d.qlen = qlen;
+  d.Ms = (int64_t)qlen * top_k;
+  launch_init_counters(workspace, w, st);
+  launch_group(d, w, workspace, expert_ids, st);
+  if (hipMemcpyAsync(offsets, ws_ptr<int32_t>(workspace, w.offsets), sizeof(int32_t) * (size_t)(num_experts + 1),
+                     hipMemcpyDeviceToDevice, st) != hipSuccess)
+    return launched();
+  if (d.Ms > 0 && hipMemcpyAsync(sorted_slot, ws_ptr<int32_t>(workspace, w.sorted_slot), sizeof(int32_t) * (size_t)d.Ms,
+                                 hipMemcpyDeviceToDevice, st) != hipSuccess)
+    return launched();
+  return launched();
+}
+
+int kt_rawint4_moe_diagnostics(const void* workspace, size_t workspace_bytes, int64_t* bad_ids, int64_t* bad_scales,
+                               void* stream) {
+  if (!workspace) return fail(KT_RAWINT4_EINVAL, "workspace is NULL");
+  if (workspace_bytes < sizeof(unsigned long long) * kNumCounters)
+    return fail(KT_RAWINT4_EWORKSPACE, "workspace is smaller than the counter block");
+  unsigned long long host[kNumCounters];
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(host, workspace, sizeof(host), hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return launched();
+  if (bad_ids) *bad_ids = (int64_t)host[kBadIds];
+  if (bad_scales) *bad_scales = (int64_t)host[kBadScales];
+  g_last_error.clear();
+  return KT_RAWINT4_OK;
+}
+
+int kt_rawint4_profile_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = on != 0;
+  g_last_error.clear();
+  return KT_RAWINT4_OK;
+}
+
+int kt_rawint4_profile_read(float* ms, int32_t* launches, int32_t capacity) {
+  if (!ms || !launches || capacity < kNumPhases)
+    return fail(KT_RAWINT4_EINVAL, "ms and launches need room for every phase");
+  for (int i = 0; i < kNumPhases; ++i) {
+    ms[i] = 0.f;
+    launches[i] = 0;
+  }
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  int rc = KT_RAWINT4_OK;
+  for (const ProfRec& r : g_prof_recs) {
+    float t = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) {
+      rc = fail(KT_RAWINT4_EHIP, "event timing failed");
+    } else {
+      ms[r.phase] += t;
+      launches[r.phase] += 1;
+    }
+    g_prof_pool.push_back(r.a);
+    g_prof_pool.push_back(r.b);
+  }
+  g_prof_recs.clear();
+  if (rc == KT_RAWINT4_OK) g_last_error.clear();
+  return rc == KT_RAWINT4_OK ? kNumPhases : rc;
+}
+
+const char* kt_rawint4_profile_phase_name(int32_t phase) {
+  if (phase < 0 || phase >= kNumPhases) return "";
+  return kPhaseNames[phase];
+}
+
+const char* kt_rawint4_last_error(void) { return g_last_error.c_str(); }
+
+const char* kt_rawint4_weight_layout(void) { return "compressed-tensors-rawint4-g32-v1"; }
+
+}  // extern "C"

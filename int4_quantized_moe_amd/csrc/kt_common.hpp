@@ -1,0 +1,106 @@
+// Device helpers shared by the gfx950 kernels of the RAWINT4 routed-expert layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kt {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kGroup = 32;  // RAWINT4 group size along K
+
+// ---------------------------------------------------------------- scalar conversions
+
+__device__ __forceinline__ float bf16_to_float(uint16_t bits) { return __uint_as_float((uint32_t)bits << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet)
+__device__ __forceinline__ uint16_t float_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint16_t float_to_half_bits(float f) {
+  _Float16 h = (_Float16)f;  // round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+
+// 2^d as fp16 bits for d <= 0 (0 below the smallest subnormal)
+__device__ __forceinline__ uint16_t half_pow2_bits(int d) {
+  if (d >= -14) return (uint16_t)((d + 15) << 10);
+  if (d >= -24) return (uint16_t)(1u << (d + 24));
+  return 0;
+}
+
+// Exponent p such that maxabs * 2^p < 2^15 (fp16 holds it with headroom);
+// 0 for zero or non-finite maxima.
+__device__ __forceinline__ int pow2_exponent_for(float maxabs) {
+  if (!(maxabs > 0.f) || !(maxabs < INFINITY)) return 0;
+  int ex;
+  (void)frexpf(maxabs, &ex);  // maxabs = f * 2^ex, f in [0.5, 1)
+  return 15 - ex;
+}
+
+// Split fp32 v into bf16 hi + lo with v ~= hi + lo (relative error < 2^-16).
+__device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) {
+  hi = float_to_bf16(v);
+  lo = float_to_bf16(v - bf16_to_float(hi));
+}
+
+// ---------------------------------------------------------------- RAWINT4 decode
+
+// Nonzero scales in [2^-14, 8160] make (c - 8) * scale exact in fp16.
+__device__ __forceinline__ bool scale_in_domain(float s) {
+  float a = fabsf(s);
+  return a == 0.f || (a >= 6.103515625e-05f && a <= 8160.f);
+}
+
+// fp16 pair ((c0 - 8) * s0, (c1 - 8) * s1) from nibble codes c0, c1 in [0, 15].
+// 0x6400 | c is the fp16 value 1024 + c; subtracting 1032 leaves c - 8 exactly,
+// and the product with an in-domain scale is exact.
+__device__ __forceinline__ uint32_t decode_pair(uint32_t c0, uint32_t c1, half2_t s) {
+  uint32_t magic = c0 | (c1 << 16) | 0x64006400u;
+  half2_t v = __builtin_bit_cast(half2_t, magic);
+  const half2_t bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+  v = (v - bias) * s;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// 8 consecutive codes of one packed dword (low nibble first) -> 8 fp16 values
+// in natural k order, all with scale s.
+__device__ __forceinline__ u32x4 decode_dword(uint32_t w, half2_t s) {
+  u32x4 r;
+  r.x = decode_pair(w & 15u, (w >> 4) & 15u, s);
+  r.y = decode_pair((w >> 8) & 15u, (w >> 12) & 15u, s);
+  r.z = decode_pair((w >> 16) & 15u, (w >> 20) & 15u, s);
+  r.w = decode_pair((w >> 24) & 15u, w >> 28, s);
+  return r;
+}
+
+// ---------------------------------------------------------------- MFMA
+
+__device__ __forceinline__ floatx4 mfma_f16(u32x4 a, u32x4 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c, 0,
+                                                0, 0);
+}
+
+__device__ __forceinline__ floatx4 mfma_bf16(u32x4 a, u32x4 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- activation
+
+// Sigmoid with the exponent argument clamped so exp never overflows.
+__device__ __forceinline__ float sigmoid_f(float z) { return 1.f / (1.f + expf(fminf(-z, 88.f))); }
+
+}  // namespace kt

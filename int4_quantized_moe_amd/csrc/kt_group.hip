@@ -1,0 +1,158 @@
+// Token-slot -> expert grouping: per-block histograms, one scan that also lays
+// out the tile lists, and a stable placement of the slots.
+//
+// The grouping follows the routed loop of the page "rawint4_sft_reference.py"
+// (routed_rawint4_lora visits every (token, slot) and indexes its expert); the
+// sort-by-expert form follows the token grouping of the page
+// "test_gemma4_moe.py" (flatten, sort by expert, expert offsets).  Within one
+// expert the slots stay in flat slot order t*k+s, which makes the permutation
+// unique.  Ids outside [0, E) are dropped and counted.
+#include "kt_common.hpp"
+#include "kt_internal.hpp"
+
+namespace kt {
+
+__global__ void k_init_counters(unsigned long long* counters) {
+  if (threadIdx.x < kNumCounters) counters[threadIdx.x] = 0ull;
+}
+
+// blockcnt[b, e] = number of slots in [b*kGroupBlock, (b+1)*kGroupBlock) routed to e
+__global__ __launch_bounds__(256) void k_group_count(const int64_t* __restrict__ ids, int64_t Ms, int E,
+                                                     int32_t* __restrict__ blockcnt,
+                                                     unsigned long long* __restrict__ counters) {
+  extern __shared__ int32_t hist[];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const int64_t s0 = (int64_t)blockIdx.x * kGroupBlock;
+  int bad = 0;
+  for (int j = threadIdx.x; j < kGroupBlock; j += blockDim.x) {
+    const int64_t s = s0 + j;
+    if (s < Ms) {
+      const int64_t e = ids[s];
+      if (e >= 0 && e < E)
+        atomicAdd(&hist[e], 1);
+      else
+        ++bad;
+    }
+  }
+  if (bad) atomicAdd(&counters[kBadIds], (unsigned long long)bad);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) blockcnt[(int64_t)blockIdx.x * E + e] = hist[e];
+}
+
+// inclusive block-wide scan of one int per thread (blockDim.x <= 1024)
+__device__ int block_inclusive_scan(int v, int32_t* buf) {
+  const int t = threadIdx.x;
+  buf[t] = v;
+  __syncthreads();
+  for (int off = 1; off < (int)blockDim.x; off <<= 1) {
+    int add = t >= off ? buf[t - off] : 0;
+    __syncthreads();
+    buf[t] += add;
+    __syncthreads();
+  }
+  int r = buf[t];
+  __syncthreads();
+  return r;
+}
+
+// One block: expert totals, exclusive offsets, per-block placement bases
+// (blockcnt is rewritten in place), and the list of (expert, first row) tiles
+// of kMT rows.
+__global__ __launch_bounds__(1024) void k_group_scan(int E, int64_t nb, int32_t* __restrict__ blockcnt,
+                                                     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ tile_e, int32_t* __restrict__ tile_m0,
+                                                     unsigned long long* __restrict__ counters) {
+  __shared__ int32_t buf[1024];
+  const int T = blockDim.x;
+  const int per = (E + T - 1) / T;
+  const int e0 = min(E, (int)threadIdx.x * per), e1 = min(E, e0 + per);
+  int local = 0, ltiles = 0;
+  for (int e = e0; e < e1; ++e) {
+    int c = 0;
+    for (int64_t b = 0; b < nb; ++b) c += blockcnt[b * E + e];
+    counts[e] = c;
+    local += c;
+    ltiles += (c + kMT - 1) / kMT;
+  }
+  const int incl = block_inclusive_scan(local, buf);
+  const int tincl = block_inclusive_scan(ltiles, buf);
+  int run = incl - local, trun = tincl - ltiles;
+  for (int e = e0; e < e1; ++e) {
+    const int c = counts[e];
+    offsets[e] = run;
+    int base = run;
+    for (int64_t b = 0; b < nb; ++b) {
+      const int v = blockcnt[b * E + e];
+      blockcnt[b * E + e] = base;
+      base += v;
+    }
+    const int nt = (c + kMT - 1) / kMT;
+    for (int j = 0; j < nt; ++j) {
+      tile_e[trun + j] = e;
+      tile_m0[trun + j] = run + j * kMT;
+    }
+    trun += nt;
+    run += c;
+  }
+  if ((int)threadIdx.x == T - 1) {
+    offsets[E] = incl;
+    counters[kNumTiles] = (unsigned long long)tincl;
+  }
+}
+
+// Stable placement: a slot's rank among equal experts inside its block comes
+// from the slots before it (rounds of blockDim.x slots, earlier rounds counted
+// in cnt[]).
+__global__ __launch_bounds__(256) void k_group_place(const int64_t* __restrict__ ids, int64_t Ms, int E,
+                                                     const int32_t* __restrict__ blockbase,
+                                                     int32_t* __restrict__ sorted_slot,
+                                                     int32_t* __restrict__ row_of_slot) {
+  extern __shared__ int32_t cnt[];
+  __shared__ int32_t rid[256];
+  const int t = threadIdx.x;
+  for (int e = t; e < E; e += blockDim.x) cnt[e] = 0;
+  __syncthreads();
+  const int64_t s0 = (int64_t)blockIdx.x * kGroupBlock;
+  for (int r0 = 0; r0 < kGroupBlock; r0 += 256) {
+    const int64_t s = s0 + r0 + t;
+    int e = -1;
+    if (s < Ms) {
+      const int64_t v = ids[s];
+      if (v >= 0 && v < E) e = (int)v;
+    }
+    rid[t] = e;
+    __syncthreads();
+    if (e >= 0) {
+      int rank = 0;
+      for (int j = 0; j < t; ++j) rank += (rid[j] == e);
+      const int pos = blockbase[(int64_t)blockIdx.x * E + e] + cnt[e] + rank;
+      sorted_slot[pos] = (int32_t)s;
+      row_of_slot[s] = pos;
+    } else if (s < Ms) {
+      row_of_slot[s] = -1;
+    }
+    __syncthreads();
+    if (e >= 0) atomicAdd(&cnt[e], 1);
+    __syncthreads();
+  }
+}
+
+void launch_init_counters(void* ws, const WsMap& w, hipStream_t st) {
+  k_init_counters<<<1, 64, 0, st>>>(ws_ptr<unsigned long long>(ws, w.counters));
+}
+
+void launch_group(const Dims& d, const WsMap& w, void* ws, const int64_t* ids, hipStream_t st) {
+  const int E = (int)d.E;
+  int32_t* blockcnt = ws_ptr<int32_t>(ws, w.blockcnt);
+  unsigned long long* counters = ws_ptr<unsigned long long>(ws, w.counters);
+  const size_t lds = sizeof(int32_t) * (size_t)E;
+  if (w.nb > 0) k_group_count<<<(unsigned)w.nb, 256, lds, st>>>(ids, d.Ms, E, blockcnt, counters);
+  k_group_scan<<<1, 1024, 0, st>>>(E, w.nb, blockcnt, ws_ptr<int32_t>(ws, w.counts), ws_ptr<int32_t>(ws, w.offsets),
+                                   ws_ptr<int32_t>(ws, w.tile_e), ws_ptr<int32_t>(ws, w.tile_m0), counters);
+  if (w.nb > 0)
+    k_group_place<<<(unsigned)w.nb, 256, lds, st>>>(ids, d.Ms, E, blockcnt, ws_ptr<int32_t>(ws, w.sorted_slot),
+                                                   ws_ptr<int32_t>(ws, w.row_of_slot));
+}
+
+}  // namespace kt

@@ -1,0 +1,93 @@
+// Host-side plan of one layer call: dimensions, tile sizes and the workspace map.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/kt_rawint4.h"
+
+namespace kt {
+
+// Tile geometry shared by the grouping (tile lists) and the matrix kernels.
+constexpr int kMT = 64;          // token-slot rows per tile
+constexpr int kGroupBlock = 1024;  // slots per block of the grouping histogram
+constexpr int kHChunk = 64;      // columns of I per gate/up tile (h exponent chunk)
+constexpr int kNT = 128;         // output columns per tile of the other GEMMs
+
+// Device counters at the head of the workspace.
+enum Counter { kBadIds = 0, kBadScales = 1, kNumTiles = 2, kNumCounters = 8 };
+
+struct Dims {
+  int64_t E, K, H, I, R, qlen, Ms;
+  float sc, limit;
+};
+
+struct WsMap {
+  // grouping
+  size_t counters, counts, offsets, blockcnt, sorted_slot, row_of_slot, tile_e, tile_m0;
+  // forward state kept for the backward
+  size_t xh, xexp, ua, ub, g, u, hh, hexp, ud;
+  // transient staging of per-slot rows (forward y, backward dx)
+  size_t stage;
+  // backward
+  size_t dyh, dyexp, dyb, dgu, dguexp, dgb, dub, drpart;
+  size_t group_end;  // bytes needed by the grouping alone
+  size_t total;
+  int64_t nb, max_tiles, h_nch, dg_nch, dr_nt;
+};
+
+WsMap plan_workspace(const Dims& d);
+WsMap plan_group_workspace(int64_t qlen, int64_t top_k, int64_t E);
+
+template <typename T>
+inline T* ws_ptr(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+// ---------------------------------------------------------------- launchers (enqueue only)
+
+void launch_group(const Dims& d, const WsMap& w, void* ws, const int64_t* ids, hipStream_t st);
+void launch_rows_to_half(const uint16_t* src, int64_t rows, int64_t cols, uint16_t* dst, int32_t* exps,
+                         hipStream_t st);
+
+struct LayerPtrs {
+  const uint8_t *wg, *wu, *wd;
+  const uint16_t *sg, *su, *sd;
+  const float *ag, *bg, *au, *bu, *ad, *bd;
+};
+
+enum GemmKind { kGateUp = 0, kDown = 1, kDownBwd = 2, kGateUpBwd = 3 };
+
+void launch_gemm(GemmKind kind, const Dims& d, const WsMap& w, void* ws, const LayerPtrs& L, const float* route_weights,
+                 hipStream_t st);
+
+// fp32 LoRA products and gradient reductions
+enum RowSrc { kSrcTokBf16 = 0, kSrcF32 = 1, kSrcHalfChunked = 2 };
+struct RowView {
+  int kind;
+  const void* ptr;
+  int64_t ld;       // row stride (elements)
+  int64_t col_off;  // added to the column index
+  const int32_t* exps;
+  int64_t exp_ld, exp_off, chunk_w;
+  const float* slot_scale;  // optional per-slot multiplier (route weights)
+};
+
+// out[m, q] = sum_k src(m, k) * W(e, q, k), q < R, k < kdim; W is [E, R, kdim]
+// (rk = true) or [E, kdim, R] (rk = false).
+void launch_lora_rowproj(const Dims& d, const WsMap& w, void* ws, const RowView& src, int64_t kdim, const float* W,
+                         bool rk, float* out, hipStream_t st);
+// G[e, p, q] = (acc ? G : 0) + scale * sum_{m in e} P(m, p) Q(m, q)
+void launch_lora_grad(const Dims& d, const WsMap& w, void* ws, const RowView& P, int64_t np, const RowView& Q,
+                      int64_t nq, float* G, int accumulate, float scale, hipStream_t st);
+void launch_fill_zero_f32(float* p, int64_t n, hipStream_t st);
+
+void launch_combine(const Dims& d, const float* stage, const int64_t* ids, uint16_t* out, hipStream_t st);
+void launch_droute(const Dims& d, const WsMap& w, void* ws, float* grad_route, hipStream_t st);
+void launch_init_counters(void* ws, const WsMap& w, hipStream_t st);
+
+void launch_unpack(const uint8_t* packed, int64_t n, int64_t k, int8_t* codes, hipStream_t st);
+void launch_dequant(const uint8_t* packed, const uint16_t* scales, int64_t n, int64_t k, float* out, hipStream_t st);
+
+}  // namespace kt
