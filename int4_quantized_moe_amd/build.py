@@ -24,6 +24,7 @@ CFLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
+    "-fno-strict-aliasing",
     "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I" + os.path.join(ROOT, "include"),

@@ -17,7 +17,7 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // One block per row: p = exponent that maps the row's largest magnitude below
 // 2^15, then every element is stored as fp16(x * 2^p) (exact for bf16 values
-// within 2^-24..2^15 of the scaled range).
+// within 2^-24..2^15 of the scaled range), at its within-8 permuted position.
 __global__ __launch_bounds__(256) void k_rows_to_half(const uint16_t* __restrict__ src, int64_t cols,
                                                       uint16_t* __restrict__ dst, int32_t* __restrict__ exps) {
   __shared__ float red[4];
@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void k_rows_to_half(const uint16_t* __restrict
   mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const int p = pow2_exponent_for(mx);
   for (int64_t c = threadIdx.x; c < cols; c += blockDim.x)
-    dst[row * cols + c] = float_to_half_bits(ldexpf(bf16_to_float(s[c]), p));
+    dst[row * cols + perm_pos((int)c)] = float_to_half_bits(ldexpf(bf16_to_float(s[c]), p));
   if (threadIdx.x == 0) exps[row] = p;
 }
 
@@ -51,7 +51,7 @@ __device__ __forceinline__ float rv_value(const RowView& v, int64_t m, int64_t c
   } else if (v.kind == kSrcF32) {
     val = static_cast<const float*>(v.ptr)[m * v.ld + v.col_off + c];
   } else {
-    val = half_bits_to_float(static_cast<const uint16_t*>(v.ptr)[m * v.ld + v.col_off + c]);
+    val = half_bits_to_float(static_cast<const uint16_t*>(v.ptr)[m * v.ld + perm_pos((int)(v.col_off + c))]);
     val = ldexpf(val, -v.exps[m * v.exp_ld + v.exp_off + c / v.chunk_w]);
   }
   if (v.slot_scale) val *= v.slot_scale[sorted_slot[m]];
@@ -60,7 +60,7 @@ __device__ __forceinline__ float rv_value(const RowView& v, int64_t m, int64_t c
 
 // ---------------------------------------------------------------- LoRA side products
 
-// out[m, q] = sum_k src(m, k) W(e, q, k) for the kMT rows of one tile and 32
+// out[m, q] = sum_k src(m, k) W(e, q, k) for the kMTAux rows of one tile and 32
 // values of q; fp32 throughout, k summed in increasing order.
 __global__ __launch_bounds__(256) void k_lora_rowproj(RowView src, int64_t kdim, const float* __restrict__ W, int rk,
                                                       float* __restrict__ out, int R, int topk,
@@ -69,19 +69,19 @@ __global__ __launch_bounds__(256) void k_lora_rowproj(RowView src, int64_t kdim,
                                                       const int32_t* __restrict__ tile_e,
                                                       const int32_t* __restrict__ tile_m0,
                                                       const unsigned long long* __restrict__ counters) {
-  __shared__ float S[kMT][65];
+  __shared__ float S[kMTAux][65];
   __shared__ float Wc[32][65];
   const int tile = blockIdx.x;
-  if ((unsigned long long)tile >= counters[kNumTiles]) return;
+  if ((unsigned long long)tile >= counters[kNumTilesAux]) return;
   const int e = tile_e[tile], m0 = tile_m0[tile];
-  const int mlen = min(kMT, offsets[e + 1] - m0);
+  const int mlen = min(kMTAux, offsets[e + 1] - m0);
   const int q0 = blockIdx.y * 32;
   const int tid = threadIdx.x, row = tid >> 2, qs = (tid & 3) * 8;
   float acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.f;
   for (int64_t k0 = 0; k0 < kdim; k0 += 64) {
-    for (int it = tid; it < kMT * 64; it += 256) {
+    for (int it = tid; it < kMTAux * 64; it += 256) {
       const int r = it >> 6, kk = it & 63;
       S[r][kk] = (r < mlen && k0 + kk < kdim) ? rv_value(src, m0 + r, k0 + kk, sorted_slot, topk) : 0.f;
     }
@@ -112,11 +112,11 @@ __global__ __launch_bounds__(256) void k_lora_rowproj(RowView src, int64_t kdim,
 
 void launch_lora_rowproj(const Dims& d, const WsMap& w, void* ws, const RowView& src, int64_t kdim, const float* W,
                          bool rk, float* out, hipStream_t st) {
-  if (w.max_tiles == 0) return;
-  dim3 grid((unsigned)w.max_tiles, (unsigned)((d.R + 31) / 32));
+  if (w.max_tiles_aux == 0) return;
+  dim3 grid((unsigned)w.max_tiles_aux, (unsigned)((d.R + 31) / 32));
   k_lora_rowproj<<<grid, 256, 0, st>>>(src, kdim, W, rk ? 1 : 0, out, (int)d.R, (int)d.K,
                                        ws_ptr<int32_t>(ws, w.sorted_slot), ws_ptr<int32_t>(ws, w.offsets),
-                                       ws_ptr<int32_t>(ws, w.tile_e), ws_ptr<int32_t>(ws, w.tile_m0),
+                                       ws_ptr<int32_t>(ws, w.tile_e_aux), ws_ptr<int32_t>(ws, w.tile_m0_aux),
                                        ws_ptr<unsigned long long>(ws, w.counters));
 }
 

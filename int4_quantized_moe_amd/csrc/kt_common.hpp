@@ -75,6 +75,24 @@ __device__ __forceinline__ uint32_t decode_pair(uint32_t c0, uint32_t c1, half2_
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Activation rows in fp16 are stored with every aligned group of 8 elements in
+// the order k0 k4 k1 k5 k2 k6 k3 k7, the order in which decode_dword_perm
+// produces weights; the position of logical element k:
+__host__ __device__ __forceinline__ int perm_pos(int k) { return (k & ~7) | ((k & 3) << 1) | ((k >> 2) & 1); }
+
+// 8 codes of one packed dword (nibble i = code k_i) -> fp16 weights in the order
+// k0 k4 k1 k5 k2 k6 k3 k7.  Pair (k_i, k_{i+4}) is scaled by s[i] (low half for
+// k_i, high half for k_{i+4}).  One and-or per pair builds both magic values.
+__device__ __forceinline__ u32x4 decode_dword_perm(uint32_t w, half2_t s0, half2_t s1, half2_t s2, half2_t s3) {
+  const half2_t bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+  u32x4 r;
+  r.x = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2_t, (w & 0x000F000Fu) | 0x64006400u) - bias) * s0);
+  r.y = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2_t, ((w >> 4) & 0x000F000Fu) | 0x64006400u) - bias) * s1);
+  r.z = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2_t, ((w >> 8) & 0x000F000Fu) | 0x64006400u) - bias) * s2);
+  r.w = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2_t, ((w >> 12) & 0x000F000Fu) | 0x64006400u) - bias) * s3);
+  return r;
+}
+
 // 8 consecutive codes of one packed dword (low nibble first) -> 8 fp16 values
 // in natural k order, all with scale s.
 __device__ __forceinline__ u32x4 decode_dword(uint32_t w, half2_t s) {

@@ -7,19 +7,27 @@
 //   kDownBwd   g_h = dY W_d (+ LoRA), then dRoute = <g_h, h> partials and the
 //              SwiGLU/clamp gradient dG, dU
 //   kGateUpBwd dx = dG W_g + dU W_u (+ LoRA), into per-slot staging
-// A work tile is kMT token-slot rows of one expert (sorted by the grouping) by a
-// block of output columns.  The int4 weights are decoded on the fly into exact
-// fp16 values ((c - 8) * scale fits fp16's 11-bit significand) and multiplied
-// with fp16 activations on v_mfma_f32_16x16x32_f16, accumulating in fp32.
+//
+// A work tile is MT token-slot rows of one expert (rows sorted by the grouping)
+// by kNT = 256 output columns; the four waves of a workgroup split the columns
+// (64 each) and share the activation tile, which is staged in LDS 64 contraction
+// values at a time, double buffered.
+//
+// Weights are decoded on the fly into exact fp16 ((c - 8) * scale fits fp16's
+// 11-bit significand) and multiplied on v_mfma_f32_16x16x32_f16 with fp32
+// accumulation.  In the stored orientation (kGateUp, kDown: contraction along
+// the packed K) every lane loads its 16 nibbles straight into registers.  The
+// two gradient GEMMs contract over the weight rows: the raw packed rows are
+// copied into LDS as they are and read back with ds_read_tr4_b64, which hands
+// each lane 16 consecutive rows of one column; this is the transpose-free dX of
+// transpose_free_rawint4_dx with the transpose done by the LDS read.
+//
 // Activations carry a power-of-two exponent per row (x, dY) or per (row, column
-// chunk) (h, dG, dU) so that fp16's range never clips them; the chunk
-// exponents are brought to the row's common exponent when the tile is staged.
-// The two gradient GEMMs read W in its stored [N, K] orientation and contract
-// over N: the decode transposes 8x8 nibble blocks while staging, which is the
-// transpose-free dX of transpose_free_rawint4_dx (no transposed or dense copy).
-// The LoRA terms ride along as extra K-steps: the fp32 LoRA-A products and the
-// fp32 LoRA matrices are split into bf16 hi + lo parts and multiplied with
-// three bf16 MFMAs (hi*hi + hi*lo + lo*hi), about 16 significant bits each.
+// chunk) (h, dG, dU) so that fp16's range never clips them; chunk exponents are
+// brought to the row's smallest exponent while the tile is staged, and the
+// epilogue removes it.  LoRA terms ride along as extra K-steps: the fp32 LoRA-A
+// side products and the fp32 LoRA matrices are split into bf16 hi + lo and
+// multiplied with three bf16 MFMAs (hi*hi + hi*lo + lo*hi).
 #include <limits.h>
 
 #include "kt_common.hpp"
@@ -27,7 +35,12 @@
 
 namespace kt {
 
-constexpr int KP = 40;  // LDS row pitch in 16-bit elements: 80 bytes keeps 16-byte reads conflict free
+constexpr int kKS = 64;       // contraction values per super-step (two quant groups)
+constexpr int kAP = kKS + 8;  // activation tile pitch in 16-bit elements (144 B)
+constexpr int kWP = 144;      // raw weight tile pitch in bytes (128 B of codes for 256 columns)
+
+typedef int v2i_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i_t* lds_v2i_ptr;
 
 struct GemmParams {
   int E, topk, H, I, R;
@@ -38,7 +51,7 @@ struct GemmParams {
   const int32_t* tile_m0;
   const unsigned long long* counters;
   LayerPtrs L;
-  const uint16_t* a_src;      // fp16 activation rows
+  const uint16_t* a_src;      // fp16 activation rows (within-8 permuted order)
   const int32_t* a_rowexp;    // per token exponent (x, dY)
   const int32_t* a_chunkexp;  // per (row, chunk) exponent (h, dG|dU)
   int a_nch, a_chunkw;
@@ -61,43 +74,77 @@ struct GemmParams {
   int n_ntiles;
 };
 
+// local column (0..255 within the tile) of N-block f of wave w
 template <int KIND>
-__device__ __forceinline__ int bcol(int wn, int f) {
-  if constexpr (KIND == kGateUp) return f < 2 ? wn * 32 + f * 16 : 64 + wn * 32 + (f - 2) * 16;
-  return wn * 64 + f * 16;
+__device__ __forceinline__ int local_col(int w, int f) {
+  if constexpr (KIND == kGateUp) return f < 2 ? w * 32 + f * 16 : kHChunk + w * 32 + (f - 2) * 16;
+  return w * 64 + f * 16;
 }
 
 __device__ __forceinline__ uint32_t mul_half2(uint32_t v, half2_t s) {
   return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, v) * s);
 }
 
-template <int KIND>
+__device__ __forceinline__ u32x4 pack_bf16x8(const uint16_t* v) {
+  u32x4 r;
+  r.x = v[0] | ((uint32_t)v[1] << 16);
+  r.y = v[2] | ((uint32_t)v[3] << 16);
+  r.z = v[4] | ((uint32_t)v[5] << 16);
+  r.w = v[6] | ((uint32_t)v[7] << 16);
+  return r;
+}
+
+// SwiGLU with the boundary-inclusive clamp; masks are 1 where the gradient passes
+__device__ __forceinline__ void clamp_swiglu(float g, float u, float limit, float& gp, float& up, float& mg,
+                                             float& mu) {
+  gp = g;
+  up = u;
+  mg = 1.f;
+  mu = 1.f;
+  if (limit > 0.f) {
+    if (!(g <= limit)) {
+      gp = limit;
+      mg = 0.f;
+    }
+    if (u < -limit) {
+      up = -limit;
+      mu = 0.f;
+    } else if (u > limit) {
+      up = limit;
+      mu = 0.f;
+    }
+  }
+}
+
+template <int KIND, int MT>
 __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
-  __shared__ __align__(16) uint16_t As[2][kMT * KP];
-  __shared__ __align__(16) uint16_t Bs[2][kNT * KP];
-  __shared__ int32_t s_src[kMT], s_exp[kMT], s_slot[kMT];
-  __shared__ float s_red[3][2][kMT];
+  constexpr int MB = MT / 16;
+  constexpr bool kT = (KIND == kDownBwd || KIND == kGateUpBwd);
+  constexpr bool kChunked = (KIND == kDown || KIND == kGateUpBwd);
+  constexpr int kAChunks = (MT * 8 + 255) / 256;  // 16-byte activation pieces per thread per super-step
+  __shared__ __align__(16) uint16_t As[2][MT * kAP];
+  __shared__ __align__(16) uint8_t Wl[kT ? 2 : 1][kT ? kKS * kWP : 16];
+  __shared__ __align__(16) uint16_t Sc[kT ? 2 : 1][kT ? (kNT / 32) * kKS : 8];
+  __shared__ int32_t s_src[MT], s_exp[MT], s_slot[MT];
 
   const int tile = (int)(blockIdx.x / (unsigned)p.n_ntiles);
   const int nt = (int)(blockIdx.x % (unsigned)p.n_ntiles);
   if ((unsigned long long)tile >= p.counters[kNumTiles]) return;
   const int e = p.tile_e[tile], m0 = p.tile_m0[tile];
-  const int mlen = min(kMT, p.offsets[e + 1] - m0);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  const int mlen = min(MT, p.offsets[e + 1] - m0);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
   const int H = p.H, I = p.I, R = p.R;
-
-  constexpr bool kTransB = (KIND == kDownBwd || KIND == kGateUpBwd);
-  constexpr bool kChunkedA = (KIND == kDown || KIND == kGateUpBwd);
   const int n0 = (KIND == kGateUp) ? nt * kHChunk : nt * kNT;
   const int nout = (KIND == kGateUp || KIND == kDownBwd) ? I : H;
   const int kdim = (KIND == kGateUp || KIND == kDownBwd) ? H : (KIND == kDown ? I : 2 * I);
+  const int nss = (kdim + kKS - 1) / kKS;
 
-  if (tid < kMT) {
+  if (tid < MT) {
     int src = -1, ex = 0, slot = -1;
     if (tid < mlen) {
       const int m = m0 + tid;
       slot = p.sorted_slot[m];
-      if constexpr (kChunkedA) {
+      if constexpr (kChunked) {
         src = m;
         int mn = INT_MAX;
         for (int c = 0; c < p.a_nch; ++c) mn = min(mn, p.a_chunkexp[(size_t)m * p.a_nch + c]);
@@ -113,150 +160,238 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
   }
   __syncthreads();
 
-  floatx4 acc[2][4];
+  floatx4 acc[MB][4];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < MB; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // ------------------------------------------------------------ main K loop (fp16)
-  for (int k0 = 0; k0 < kdim; k0 += kGroup) {
-    {  // A tile: kMT rows x 32 columns, one 16-byte piece per thread
-      const int row = tid >> 2, part = tid & 3;
-      const int src = s_src[row];
+  // ---------------------------------------------------------------- staging helpers
+  u32x4 areg[kAChunks];
+  auto load_a = [&](int k0) {
+#pragma unroll
+    for (int t = 0; t < kAChunks; ++t) {
+      const int q = tid + 256 * t;
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (src >= 0) {
-        v = *reinterpret_cast<const u32x4*>(p.a_src + (size_t)src * p.lda + k0 + part * 8);
-        if constexpr (kChunkedA) {
-          int c;
-          if constexpr (KIND == kDown) {
-            c = k0 / p.a_chunkw;
-          } else {
-            c = k0 < I ? k0 / p.a_chunkw : p.a_nch / 2 + (k0 - I) / p.a_chunkw;
-          }
-          const int d = s_exp[row] - p.a_chunkexp[(size_t)src * p.a_nch + c];
-          if (d != 0) {
-            const uint16_t sb = half_pow2_bits(d);
-            const half2_t s2 = __builtin_bit_cast(half2_t, (uint32_t)sb | ((uint32_t)sb << 16));
-            v.x = mul_half2(v.x, s2);
-            v.y = mul_half2(v.y, s2);
-            v.z = mul_half2(v.z, s2);
-            v.w = mul_half2(v.w, s2);
+      if (q < MT * 8) {
+        const int row = q >> 3, k = k0 + 8 * (q & 7);
+        const int src = s_src[row];
+        if (src >= 0 && k < kdim) {
+          v = *reinterpret_cast<const u32x4*>(p.a_src + (size_t)src * p.lda + k);
+          if constexpr (kChunked) {
+            int c;
+            if constexpr (KIND == kDown)
+              c = k / p.a_chunkw;
+            else
+              c = k < I ? k / p.a_chunkw : p.a_nch / 2 + (k - I) / p.a_chunkw;
+            const int d = s_exp[row] - p.a_chunkexp[(size_t)src * p.a_nch + c];
+            if (d != 0) {
+              const uint16_t sb = half_pow2_bits(d);
+              const half2_t s2 = __builtin_bit_cast(half2_t, (uint32_t)sb | ((uint32_t)sb << 16));
+              v.x = mul_half2(v.x, s2);
+              v.y = mul_half2(v.y, s2);
+              v.z = mul_half2(v.z, s2);
+              v.w = mul_half2(v.w, s2);
+            }
           }
         }
       }
-      *reinterpret_cast<u32x4*>(&As[0][row * KP + part * 8]) = v;
+      areg[t] = v;
     }
-    if constexpr (!kTransB) {
-      // B tile, stored orientation: output column = weight row, 32 consecutive k
-      for (int it = tid; it < kNT * 4; it += 256) {
-        const int j = it >> 2, d = it & 3;
-        u32x4 r = {0u, 0u, 0u, 0u};
-        const uint8_t* W;
-        const uint16_t* S;
-        size_t row;
-        int rk;
-        bool valid;
-        if constexpr (KIND == kGateUp) {
-          const bool up = j >= kHChunk;
-          const int n = n0 + (j & (kHChunk - 1));
-          valid = n < I;
-          W = up ? p.L.wu : p.L.wg;
-          S = up ? p.L.su : p.L.sg;
-          row = (size_t)e * I + n;
-          rk = H;
-        } else {
-          const int n = n0 + j;
-          valid = n < H;
-          W = p.L.wd;
-          S = p.L.sd;
-          row = (size_t)e * H + n;
-          rk = I;
-        }
-        if (valid) {
-          const uint32_t wv = *reinterpret_cast<const uint32_t*>(W + row * (size_t)(rk / 2) + k0 / 2 + d * 4);
-          const float sf = bf16_to_float(S[row * (size_t)(rk / kGroup) + k0 / kGroup]);
-          if (d == 0 && !scale_in_domain(sf)) atomicAdd(p.bad_scales, 1ull);
-          const _Float16 sh = (_Float16)sf;
-          r = decode_dword(wv, half2_t{sh, sh});
-        }
-        *reinterpret_cast<u32x4*>(&Bs[0][j * KP + d * 8]) = r;
-      }
-    } else {
-      // B tile, contraction over the weight rows: 8 rows x 8 columns per task,
-      // decoded into column-major 16-byte pieces (8 contraction values each)
-      if (tid < 64) {
-        const int ro = tid >> 4, co = tid & 15;
-        const int c = n0 + co * 8;
-        const bool valid = c < nout;
-        uint32_t wv[8];
-        float sv[8];
+  };
+  auto store_a = [&](int buf) {
 #pragma unroll
-        for (int rr = 0; rr < 8; ++rr) {
-          const int kk = k0 + ro * 8 + rr;
-          const uint8_t* W;
-          const uint16_t* S;
-          size_t row;
-          int rk;
-          if constexpr (KIND == kDownBwd) {
-            W = p.L.wd;
-            S = p.L.sd;
-            row = (size_t)e * H + kk;
-            rk = I;
-          } else {
-            const bool up = kk >= I;
-            W = up ? p.L.wu : p.L.wg;
-            S = up ? p.L.su : p.L.sg;
-            row = (size_t)e * I + (up ? kk - I : kk);
-            rk = H;
-          }
-          wv[rr] = 0u;
-          sv[rr] = 0.f;
-          if (valid) {
-            wv[rr] = *reinterpret_cast<const uint32_t*>(W + row * (size_t)(rk / 2) + c / 2);
-            sv[rr] = bf16_to_float(S[row * (size_t)(rk / kGroup) + c / kGroup]);
-            if (!scale_in_domain(sv[rr])) atomicAdd(p.bad_scales, 1ull);
-          }
-        }
-        half2_t sp[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) sp[q] = half2_t{(_Float16)sv[2 * q], (_Float16)sv[2 * q + 1]};
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          u32x4 o;
-          o.x = decode_pair((wv[0] >> (4 * jj)) & 15u, (wv[1] >> (4 * jj)) & 15u, sp[0]);
-          o.y = decode_pair((wv[2] >> (4 * jj)) & 15u, (wv[3] >> (4 * jj)) & 15u, sp[1]);
-          o.z = decode_pair((wv[4] >> (4 * jj)) & 15u, (wv[5] >> (4 * jj)) & 15u, sp[2]);
-          o.w = decode_pair((wv[6] >> (4 * jj)) & 15u, (wv[7] >> (4 * jj)) & 15u, sp[3]);
-          if (!valid) o = u32x4{0u, 0u, 0u, 0u};
-          *reinterpret_cast<u32x4*>(&Bs[0][(co * 8 + jj) * KP + ro * 8]) = o;
-        }
-      }
+    for (int t = 0; t < kAChunks; ++t) {
+      const int q = tid + 256 * t;
+      if (q < MT * 8) *reinterpret_cast<u32x4*>(&As[buf][(q >> 3) * kAP + 8 * (q & 7)]) = areg[t];
     }
-    __syncthreads();
-    u32x4 af[2];
-#pragma unroll
-    for (int fm = 0; fm < 2; ++fm)
-      af[fm] = *reinterpret_cast<const u32x4*>(&As[0][(wm * 32 + fm * 16 + (lane & 15)) * KP + (lane >> 4) * 8]);
+  };
+
+  // stored orientation: each lane's 16 nibbles of its output column for one super-step
+  uint32_t breg[4][2];
+  uint32_t bscale[4];  // fp16 scale in both halves
+  auto load_b = [&](int k0, uint32_t (&bw)[4][2], uint32_t (&bs)[4]) {
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-      const u32x4 bf = *reinterpret_cast<const u32x4*>(&Bs[0][(bcol<KIND>(wn, f) + (lane & 15)) * KP + (lane >> 4) * 8]);
+      const uint8_t* W;
+      const uint16_t* S;
+      size_t row;
+      int rk;
+      bool valid;
+      if constexpr (KIND == kGateUp) {
+        const int col = n0 + w * 32 + (f & 1) * 16 + lr;
+        valid = col < I;
+        W = f < 2 ? p.L.wg : p.L.wu;
+        S = f < 2 ? p.L.sg : p.L.su;
+        row = (size_t)e * I + col;
+        rk = H;
+      } else {
+        const int col = n0 + w * 64 + f * 16 + lr;
+        valid = col < H;
+        W = p.L.wd;
+        S = p.L.sd;
+        row = (size_t)e * H + col;
+        rk = I;
+      }
+      const int k = k0 + 16 * lg;
+      uint2 v = make_uint2(0u, 0u);
+      uint32_t sh = 0u;
+      if (valid && k < kdim) {
+        v = *reinterpret_cast<const uint2*>(W + row * (size_t)(rk / 2) + k / 2);
+        const float sf = bf16_to_float(S[row * (size_t)(rk / kGroup) + k / kGroup]);
+        if (!scale_in_domain(sf) && (lg & 1) == 0) atomicAdd(p.bad_scales, 1ull);
+        sh = float_to_half_bits(sf);
+      }
+      bw[f][0] = v.x;
+      bw[f][1] = v.y;
+      bs[f] = sh | (sh << 16);
+    }
+  };
+
+  // contraction over weight rows: raw packed rows and their scales into LDS
+  u32x4 wreg[2];
+  uint16_t sreg[2];
+  auto load_w = [&](int k0) {
 #pragma unroll
-      for (int fm = 0; fm < 2; ++fm) acc[fm][f] = mfma_f16(af[fm], bf, acc[fm][f]);
+    for (int t = 0; t < 2; ++t) {
+      const int q = tid + 256 * t;
+      const int row = q >> 3, c16 = q & 7;
+      const int kk = k0 + row, c = n0 + 32 * c16;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      uint16_t sh = 0;
+      if (kk < kdim && c < nout) {
+        const uint8_t* W;
+        const uint16_t* S;
+        size_t wrow;
+        int rk;
+        if constexpr (KIND == kDownBwd) {
+          W = p.L.wd;
+          S = p.L.sd;
+          wrow = (size_t)e * H + kk;
+          rk = I;
+        } else {
+          const bool up = kk >= I;
+          W = up ? p.L.wu : p.L.wg;
+          S = up ? p.L.su : p.L.sg;
+          wrow = (size_t)e * I + (up ? kk - I : kk);
+          rk = H;
+        }
+        v = *reinterpret_cast<const u32x4*>(W + wrow * (size_t)(rk / 2) + c / 2);
+        const float sf = bf16_to_float(S[wrow * (size_t)(rk / kGroup) + c / kGroup]);
+        if (!scale_in_domain(sf)) atomicAdd(p.bad_scales, 1ull);
+        sh = float_to_half_bits(sf);
+      }
+      wreg[t] = v;
+      sreg[t] = sh;
+    }
+  };
+  auto store_w = [&](int buf) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int q = tid + 256 * t;
+      const int row = q >> 3, c16 = q & 7;
+      *reinterpret_cast<u32x4*>(&Wl[buf][row * kWP + 16 * c16]) = wreg[t];
+      Sc[buf][c16 * kKS + perm_pos(row)] = sreg[t];
+    }
+  };
+
+  auto compute = [&](int cur) {
+    if constexpr (kT) {
+      v2i_t tr[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const int lc = local_col<KIND>(w, f);
+        tr[f] = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_v2i_ptr)(&Wl[cur][(16 * lg + lr) * kWP + lc / 2]));
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        u32x4 af[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          af[mb] = *reinterpret_cast<const u32x4*>(&As[cur][(mb * 16 + lr) * kAP + 16 * lg + 8 * j]);
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          const int cg = local_col<KIND>(w, f) / 32;
+          u32x4 sp;  // 8 fp16 scales written as 16-bit values: copy, do not type-pun
+          __builtin_memcpy(&sp, &Sc[cur][cg * kKS + 16 * lg + 8 * j], sizeof(sp));
+          const uint32_t word = j ? (uint32_t)tr[f].y : (uint32_t)tr[f].x;
+          // bit-cast whole scalars: clang's bit_cast of an ext-vector component reads component 0
+          const uint32_t s0 = sp.x, s1 = sp.y, s2 = sp.z, s3 = sp.w;
+          const u32x4 bf = decode_dword_perm(word, __builtin_bit_cast(half2_t, s0), __builtin_bit_cast(half2_t, s1),
+                                             __builtin_bit_cast(half2_t, s2), __builtin_bit_cast(half2_t, s3));
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) acc[mb][f] = mfma_f16(af[mb], bf, acc[mb][f]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        u32x4 af[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          af[mb] = *reinterpret_cast<const u32x4*>(&As[cur][(mb * 16 + lr) * kAP + 16 * lg + 8 * j]);
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          const half2_t s2 = __builtin_bit_cast(half2_t, bscale[f]);
+          const u32x4 bf = decode_dword_perm(breg[f][j], s2, s2, s2, s2);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) acc[mb][f] = mfma_f16(af[mb], bf, acc[mb][f]);
+        }
+      }
+    }
+  };
+
+  // ---------------------------------------------------------------- main loop (fp16)
+  load_a(0);
+  if constexpr (kT) {
+    load_w(0);
+    store_w(0);
+  } else {
+    load_b(0, breg, bscale);
+  }
+  store_a(0);
+  __syncthreads();
+  for (int ss = 0; ss < nss; ++ss) {
+    const int cur = ss & 1;
+    const bool more = ss + 1 < nss;
+    uint32_t bnext[4][2];
+    uint32_t snext[4];
+    if (more) {
+      load_a((ss + 1) * kKS);
+      if constexpr (kT)
+        load_w((ss + 1) * kKS);
+      else
+        load_b((ss + 1) * kKS, bnext, snext);
+    }
+    compute(cur);
+    if (more) {
+      store_a(cur ^ 1);
+      if constexpr (kT) {
+        store_w(cur ^ 1);
+      } else {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          breg[f][0] = bnext[f][0];
+          breg[f][1] = bnext[f][1];
+          bscale[f] = snext[f];
+        }
+      }
     }
     __syncthreads();
   }
 
-  // ------------------------------------------------------------ LoRA K-steps (bf16 hi/lo)
+  // ---------------------------------------------------------------- LoRA K-steps (bf16 hi/lo)
   const int KL = (KIND == kGateUp || KIND == kGateUpBwd) ? 2 * R : R;
   for (int q0 = 0; q0 < KL; q0 += kGroup) {
-    {
-      const int row = tid >> 2, qq = (tid & 3) * 8;
+    u32x4 ah[MB], al[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int row = mb * 16 + lr;
       const float coef = ldexpf(p.sc, s_exp[row]);
       uint16_t hi[8], lo[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int q = q0 + qq + j;
+      for (int i = 0; i < 8; ++i) {
+        const int q = q0 + 8 * lg + i;
         float v = 0.f;
         if (row < mlen && q < KL) {
           const size_t m = (size_t)(m0 + row);
@@ -266,40 +401,32 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
             v = p.la0[m * R + q];
           v *= coef;
         }
-        split_bf16(v, hi[j], lo[j]);
+        split_bf16(v, hi[i], lo[i]);
       }
-      u32x4 vh, vl;
-      vh.x = hi[0] | ((uint32_t)hi[1] << 16);
-      vh.y = hi[2] | ((uint32_t)hi[3] << 16);
-      vh.z = hi[4] | ((uint32_t)hi[5] << 16);
-      vh.w = hi[6] | ((uint32_t)hi[7] << 16);
-      vl.x = lo[0] | ((uint32_t)lo[1] << 16);
-      vl.y = lo[2] | ((uint32_t)lo[3] << 16);
-      vl.z = lo[4] | ((uint32_t)lo[5] << 16);
-      vl.w = lo[6] | ((uint32_t)lo[7] << 16);
-      *reinterpret_cast<u32x4*>(&As[0][row * KP + qq]) = vh;
-      *reinterpret_cast<u32x4*>(&As[1][row * KP + qq]) = vl;
+      ah[mb] = pack_bf16x8(hi);
+      al[mb] = pack_bf16x8(lo);
     }
-    {
-      const int j = tid >> 1, qq = (tid & 1) * 16;
-      for (int jj = 0; jj < 16; ++jj) {
-        const int q = q0 + qq + jj;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      uint16_t hi[8], lo[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int q = q0 + 8 * lg + i;
         float v = 0.f;
         if constexpr (KIND == kGateUp) {
-          const bool up = j >= kHChunk;
-          const int n = n0 + (j & (kHChunk - 1));
+          const int n = n0 + w * 32 + (f & 1) * 16 + lr;
           if (n < I) {
-            if (!up && q < R) v = p.L.bg[((size_t)e * I + n) * R + q];
-            if (up && q >= R && q < 2 * R) v = p.L.bu[((size_t)e * I + n) * R + (q - R)];
+            if (f < 2 && q < R) v = p.L.bg[((size_t)e * I + n) * R + q];
+            if (f >= 2 && q >= R && q < 2 * R) v = p.L.bu[((size_t)e * I + n) * R + (q - R)];
           }
         } else if constexpr (KIND == kDown) {
-          const int n = n0 + j;
+          const int n = n0 + w * 64 + f * 16 + lr;
           if (n < H && q < R) v = p.L.bd[((size_t)e * H + n) * R + q];
         } else if constexpr (KIND == kDownBwd) {
-          const int c = n0 + j;
+          const int c = n0 + w * 64 + f * 16 + lr;
           if (c < I && q < R) v = p.L.ad[((size_t)e * R + q) * I + c];
         } else {
-          const int c = n0 + j;
+          const int c = n0 + w * 64 + f * 16 + lr;
           if (c < H) {
             if (q < R)
               v = p.L.ag[((size_t)e * R + q) * H + c];
@@ -307,190 +434,184 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
               v = p.L.au[((size_t)e * R + (q - R)) * H + c];
           }
         }
-        uint16_t hi, lo;
-        split_bf16(v, hi, lo);
-        Bs[0][j * KP + qq + jj] = hi;
-        Bs[1][j * KP + qq + jj] = lo;
+        split_bf16(v, hi[i], lo[i]);
+      }
+      const u32x4 bh = pack_bf16x8(hi), bl = pack_bf16x8(lo);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        acc[mb][f] = mfma_bf16(ah[mb], bh, acc[mb][f]);
+        acc[mb][f] = mfma_bf16(ah[mb], bl, acc[mb][f]);
+        acc[mb][f] = mfma_bf16(al[mb], bh, acc[mb][f]);
       }
     }
-    __syncthreads();
-    u32x4 ah[2], al[2];
-#pragma unroll
-    for (int fm = 0; fm < 2; ++fm) {
-      const int off = (wm * 32 + fm * 16 + (lane & 15)) * KP + (lane >> 4) * 8;
-      ah[fm] = *reinterpret_cast<const u32x4*>(&As[0][off]);
-      al[fm] = *reinterpret_cast<const u32x4*>(&As[1][off]);
-    }
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const int off = (bcol<KIND>(wn, f) + (lane & 15)) * KP + (lane >> 4) * 8;
-      const u32x4 bh = *reinterpret_cast<const u32x4*>(&Bs[0][off]);
-      const u32x4 bl = *reinterpret_cast<const u32x4*>(&Bs[1][off]);
-#pragma unroll
-      for (int fm = 0; fm < 2; ++fm) {
-        acc[fm][f] = mfma_bf16(ah[fm], bh, acc[fm][f]);
-        acc[fm][f] = mfma_bf16(ah[fm], bl, acc[fm][f]);
-        acc[fm][f] = mfma_bf16(al[fm], bh, acc[fm][f]);
-      }
-    }
-    __syncthreads();
   }
 
-  // ------------------------------------------------------------ epilogues
-  const int lc = lane & 15, lg = lane >> 4;
+  // ---------------------------------------------------------------- epilogues
+  // the activation tile is free now: reuse it for the cross-wave row reductions
+  float* red = reinterpret_cast<float*>(&As[0][0]);  // [3][4 waves][MT]
   const float limit = p.limit;
   if constexpr (KIND == kGateUp) {
-    float hv[2][2][4];
-    float rmax[2][4];
+    // pass 1: g, u saved in fp32, row maxima of h over the tile's 128 columns
 #pragma unroll
-    for (int fm = 0; fm < 2; ++fm)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = wm * 32 + fm * 16 + lg * 4 + i;
+        const int row = mb * 16 + lg * 4 + i;
         const bool vrow = row < mlen;
         const size_t m = (size_t)(m0 + row);
         const int ex = s_exp[row];
-        rmax[fm][i] = 0.f;
+        float mx = 0.f;
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
-          const int col = n0 + wn * 32 + f * 16 + lc;
+          const int col = n0 + w * 32 + f * 16 + lr;
           const bool valid = vrow && col < I;
-          const float g = ldexpf(acc[fm][f][i], -ex);
-          const float u = ldexpf(acc[fm][f + 2][i], -ex);
+          const float g = ldexpf(acc[mb][f][i], -ex);
+          const float u = ldexpf(acc[mb][f + 2][i], -ex);
           if (valid) {
             p.gsave[m * I + col] = g;
             p.usave[m * I + col] = u;
           }
-          float gp = g, up = u;
-          if (limit > 0.f) {
-            if (!(g <= limit)) gp = limit;
-            up = fminf(fmaxf(u, -limit), limit);
-          }
+          float gp, up, mg, mu;
+          clamp_swiglu(g, u, limit, gp, up, mg, mu);
           const float h = valid ? gp * sigmoid_f(gp) * up : 0.f;
-          hv[fm][f][i] = h;
-          rmax[fm][i] = fmaxf(rmax[fm][i], fabsf(h));
+          mx = fmaxf(mx, fabsf(h));
         }
-        float v = rmax[fm][i];
-        v = fmaxf(v, __shfl_xor(v, 1));
-        v = fmaxf(v, __shfl_xor(v, 2));
-        v = fmaxf(v, __shfl_xor(v, 4));
-        v = fmaxf(v, __shfl_xor(v, 8));
-        if (lc == 0) s_red[0][wn][row] = v;
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+        if (lr == 0) red[w * MT + row] = mx;
       }
     __syncthreads();
+    // pass 2: h in fp16 times 2^p, p per (row, 128-column chunk)
 #pragma unroll
-    for (int fm = 0; fm < 2; ++fm)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = wm * 32 + fm * 16 + lg * 4 + i;
+        const int row = mb * 16 + lg * 4 + i;
         if (row >= mlen) continue;
         const size_t m = (size_t)(m0 + row);
-        const int pe = pow2_exponent_for(fmaxf(s_red[0][0][row], s_red[0][1][row]));
-        if (wn == 0 && lc == 0) p.hexp[m * p.h_nch + nt] = pe;
+        const int ex = s_exp[row];
+        const float mx = fmaxf(fmaxf(red[row], red[MT + row]), fmaxf(red[2 * MT + row], red[3 * MT + row]));
+        const int pe = pow2_exponent_for(mx);
+        if (w == 0 && lr == 0) p.hexp[m * p.h_nch + nt] = pe;
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
-          const int col = n0 + wn * 32 + f * 16 + lc;
-          if (col < I) p.hh[m * I + col] = float_to_half_bits(ldexpf(hv[fm][f][i], pe));
+          const int col = n0 + w * 32 + f * 16 + lr;
+          if (col >= I) continue;
+          float gp, up, mg, mu;
+          clamp_swiglu(ldexpf(acc[mb][f][i], -ex), ldexpf(acc[mb][f + 2][i], -ex), limit, gp, up, mg, mu);
+          p.hh[m * I + perm_pos(col)] = float_to_half_bits(ldexpf(gp * sigmoid_f(gp) * up, pe));
         }
       }
   } else if constexpr (KIND == kDown || KIND == kGateUpBwd) {
 #pragma unroll
-    for (int fm = 0; fm < 2; ++fm)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = wm * 32 + fm * 16 + lg * 4 + i;
+        const int row = mb * 16 + lg * 4 + i;
         if (row >= mlen) continue;
         const int slot = s_slot[row];
-        const float w = (KIND == kDown) ? p.rw[slot] : 1.f;
+        const float wgt = (KIND == kDown) ? p.rw[slot] : 1.f;
         const int ex = s_exp[row];
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
-          const int col = n0 + wn * 64 + f * 16 + lc;
-          if (col < H) p.stage[(size_t)slot * H + col] = w * ldexpf(acc[fm][f][i], -ex);
+          const int col = n0 + w * 64 + f * 16 + lr;
+          if (col < H) p.stage[(size_t)slot * H + col] = wgt * ldexpf(acc[mb][f][i], -ex);
         }
       }
   } else {  // kDownBwd
-    float du[2][4][4];
+    // pass 1: dRoute partial sums and the row maxima of dG and dU
 #pragma unroll
-    for (int fm = 0; fm < 2; ++fm)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = wm * 32 + fm * 16 + lg * 4 + i;
+        const int row = mb * 16 + lg * 4 + i;
         const bool vrow = row < mlen;
         const size_t m = (size_t)(m0 + row);
-        const float w = vrow ? p.rw[s_slot[row]] : 0.f;
+        const float wgt = vrow ? p.rw[s_slot[row]] : 0.f;
         const int ex = s_exp[row];
-        float dr = 0.f, mg = 0.f, mu = 0.f;
+        float dr = 0.f, mxg = 0.f, mxu = 0.f;
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
-          const int col = n0 + wn * 64 + f * 16 + lc;
-          const bool valid = vrow && col < I;
-          const float gh = ldexpf(acc[fm][f][i], -ex);
-          const float g = valid ? p.gsave[m * I + col] : 0.f;
-          const float u = valid ? p.usave[m * I + col] : 0.f;
-          float gp = g, up = u, mgate = 1.f, mup = 1.f;
-          if (limit > 0.f) {
-            if (!(g <= limit)) {
-              gp = limit;
-              mgate = 0.f;
-            }
-            if (u < -limit) {
-              up = -limit;
-              mup = 0.f;
-            } else if (u > limit) {
-              up = limit;
-              mup = 0.f;
-            }
-          }
+          const int col = n0 + w * 64 + f * 16 + lr;
+          if (!(vrow && col < I)) continue;
+          const float gh = ldexpf(acc[mb][f][i], -ex);
+          float gp, up, mg, mu;
+          clamp_swiglu(p.gsave[m * I + col], p.usave[m * I + col], limit, gp, up, mg, mu);
           const float sg = sigmoid_f(gp);
           const float si = gp * sg;
           const float dsi = sg * (1.f + gp * (1.f - sg));
-          dr += valid ? gh * si * up : 0.f;
-          const float dh = w * gh;
-          const float dgv = valid ? dh * up * dsi * mgate : 0.f;
-          const float duv = valid ? dh * si * mup : 0.f;
-          acc[fm][f][i] = dgv;
-          du[fm][f][i] = duv;
-          mg = fmaxf(mg, fabsf(dgv));
-          mu = fmaxf(mu, fabsf(duv));
+          dr += gh * si * up;
+          const float dh = wgt * gh;
+          mxg = fmaxf(mxg, fabsf(dh * up * dsi * mg));
+          mxu = fmaxf(mxu, fabsf(dh * si * mu));
         }
 #pragma unroll
         for (int off = 1; off < 16; off <<= 1) {
           dr += __shfl_xor(dr, off);
-          mg = fmaxf(mg, __shfl_xor(mg, off));
-          mu = fmaxf(mu, __shfl_xor(mu, off));
+          mxg = fmaxf(mxg, __shfl_xor(mxg, off));
+          mxu = fmaxf(mxu, __shfl_xor(mxu, off));
         }
-        if (lc == 0) {
-          s_red[0][wn][row] = dr;
-          s_red[1][wn][row] = mg;
-          s_red[2][wn][row] = mu;
+        if (lr == 0) {
+          red[w * MT + row] = dr;
+          red[(4 + w) * MT + row] = mxg;
+          red[(8 + w) * MT + row] = mxu;
         }
       }
     __syncthreads();
     const int half_nch = p.dg_nch / 2;
+    // pass 2: dG, dU in fp16 times 2^p, p per (row, 256-column chunk)
 #pragma unroll
-    for (int fm = 0; fm < 2; ++fm)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = wm * 32 + fm * 16 + lg * 4 + i;
+        const int row = mb * 16 + lg * 4 + i;
         if (row >= mlen) continue;
         const size_t m = (size_t)(m0 + row);
-        const int pg = pow2_exponent_for(fmaxf(s_red[1][0][row], s_red[1][1][row]));
-        const int pu = pow2_exponent_for(fmaxf(s_red[2][0][row], s_red[2][1][row]));
-        if (wn == 0 && lc == 0) {
-          p.drpart[m * p.dr_nt + nt] = s_red[0][0][row] + s_red[0][1][row];
+        const float wgt = p.rw[s_slot[row]];
+        const int ex = s_exp[row];
+        const int pg = pow2_exponent_for(fmaxf(fmaxf(red[4 * MT + row], red[5 * MT + row]),
+                                               fmaxf(red[6 * MT + row], red[7 * MT + row])));
+        const int pu = pow2_exponent_for(fmaxf(fmaxf(red[8 * MT + row], red[9 * MT + row]),
+                                               fmaxf(red[10 * MT + row], red[11 * MT + row])));
+        if (w == 0 && lr == 0) {
+          p.drpart[m * p.dr_nt + nt] = (red[row] + red[MT + row]) + (red[2 * MT + row] + red[3 * MT + row]);
           p.dguexp[m * p.dg_nch + nt] = pg;
           p.dguexp[m * p.dg_nch + half_nch + nt] = pu;
         }
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
-          const int col = n0 + wn * 64 + f * 16 + lc;
-          if (col < I) {
-            p.dgu[m * (size_t)(2 * I) + col] = float_to_half_bits(ldexpf(acc[fm][f][i], pg));
-            p.dgu[m * (size_t)(2 * I) + I + col] = float_to_half_bits(ldexpf(du[fm][f][i], pu));
-          }
+          const int col = n0 + w * 64 + f * 16 + lr;
+          if (col >= I) continue;
+          const float gh = ldexpf(acc[mb][f][i], -ex);
+          float gp, up, mg, mu;
+          clamp_swiglu(p.gsave[m * I + col], p.usave[m * I + col], limit, gp, up, mg, mu);
+          const float sg = sigmoid_f(gp);
+          const float si = gp * sg;
+          const float dsi = sg * (1.f + gp * (1.f - sg));
+          const float dh = wgt * gh;
+          const int pc = perm_pos(col);
+          p.dgu[m * (size_t)(2 * I) + pc] = float_to_half_bits(ldexpf(dh * up * dsi * mg, pg));
+          p.dgu[m * (size_t)(2 * I) + I + pc] = float_to_half_bits(ldexpf(dh * si * mu, pu));
         }
       }
+  }
+}
+
+template <int KIND>
+static void launch_kind(int mt, unsigned grid, const GemmParams& p, hipStream_t st) {
+  switch (mt) {
+    case 16:
+      k_gemm<KIND, 16><<<grid, 256, 0, st>>>(p);
+      break;
+    case 32:
+      k_gemm<KIND, 32><<<grid, 256, 0, st>>>(p);
+      break;
+    case 64:
+      k_gemm<KIND, 64><<<grid, 256, 0, st>>>(p);
+      break;
+    default:
+      k_gemm<KIND, 128><<<grid, 256, 0, st>>>(p);
+      break;
   }
 }
 
@@ -563,16 +684,16 @@ void launch_gemm(GemmKind kind, const Dims& d, const WsMap& w, void* ws, const L
   if (grid == 0) return;
   switch (kind) {
     case kGateUp:
-      k_gemm<kGateUp><<<grid, 256, 0, st>>>(p);
+      launch_kind<kGateUp>((int)w.mt, grid, p, st);
       break;
     case kDown:
-      k_gemm<kDown><<<grid, 256, 0, st>>>(p);
+      launch_kind<kDown>((int)w.mt, grid, p, st);
       break;
     case kDownBwd:
-      k_gemm<kDownBwd><<<grid, 256, 0, st>>>(p);
+      launch_kind<kDownBwd>((int)w.mt, grid, p, st);
       break;
     case kGateUpBwd:
-      k_gemm<kGateUpBwd><<<grid, 256, 0, st>>>(p);
+      launch_kind<kGateUpBwd>((int)w.mt, grid, p, st);
       break;
   }
 }

@@ -57,27 +57,31 @@ __device__ int block_inclusive_scan(int v, int32_t* buf) {
 }
 
 // One block: expert totals, exclusive offsets, per-block placement bases
-// (blockcnt is rewritten in place), and the list of (expert, first row) tiles
-// of kMT rows.
-__global__ __launch_bounds__(1024) void k_group_scan(int E, int64_t nb, int32_t* __restrict__ blockcnt,
+// (blockcnt is rewritten in place), and two lists of (expert, first row) tiles:
+// `mt` rows for the matrix kernels, kMTAux rows for the LoRA kernels.
+__global__ __launch_bounds__(1024) void k_group_scan(int E, int64_t nb, int mt, int32_t* __restrict__ blockcnt,
                                                      int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                      int32_t* __restrict__ tile_e, int32_t* __restrict__ tile_m0,
+                                                     int32_t* __restrict__ tile_e_aux,
+                                                     int32_t* __restrict__ tile_m0_aux,
                                                      unsigned long long* __restrict__ counters) {
   __shared__ int32_t buf[1024];
   const int T = blockDim.x;
   const int per = (E + T - 1) / T;
   const int e0 = min(E, (int)threadIdx.x * per), e1 = min(E, e0 + per);
-  int local = 0, ltiles = 0;
+  int local = 0, ltiles = 0, latiles = 0;
   for (int e = e0; e < e1; ++e) {
     int c = 0;
     for (int64_t b = 0; b < nb; ++b) c += blockcnt[b * E + e];
     counts[e] = c;
     local += c;
-    ltiles += (c + kMT - 1) / kMT;
+    ltiles += (c + mt - 1) / mt;
+    latiles += (c + kMTAux - 1) / kMTAux;
   }
   const int incl = block_inclusive_scan(local, buf);
   const int tincl = block_inclusive_scan(ltiles, buf);
-  int run = incl - local, trun = tincl - ltiles;
+  const int taincl = block_inclusive_scan(latiles, buf);
+  int run = incl - local, trun = tincl - ltiles, tarun = taincl - latiles;
   for (int e = e0; e < e1; ++e) {
     const int c = counts[e];
     offsets[e] = run;
@@ -87,17 +91,24 @@ __global__ __launch_bounds__(1024) void k_group_scan(int E, int64_t nb, int32_t*
       blockcnt[b * E + e] = base;
       base += v;
     }
-    const int nt = (c + kMT - 1) / kMT;
+    const int nt = (c + mt - 1) / mt;
     for (int j = 0; j < nt; ++j) {
       tile_e[trun + j] = e;
-      tile_m0[trun + j] = run + j * kMT;
+      tile_m0[trun + j] = run + j * mt;
     }
     trun += nt;
+    const int nta = (c + kMTAux - 1) / kMTAux;
+    for (int j = 0; j < nta; ++j) {
+      tile_e_aux[tarun + j] = e;
+      tile_m0_aux[tarun + j] = run + j * kMTAux;
+    }
+    tarun += nta;
     run += c;
   }
   if ((int)threadIdx.x == T - 1) {
     offsets[E] = incl;
     counters[kNumTiles] = (unsigned long long)tincl;
+    counters[kNumTilesAux] = (unsigned long long)taincl;
   }
 }
 
@@ -148,8 +159,10 @@ void launch_group(const Dims& d, const WsMap& w, void* ws, const int64_t* ids, h
   unsigned long long* counters = ws_ptr<unsigned long long>(ws, w.counters);
   const size_t lds = sizeof(int32_t) * (size_t)E;
   if (w.nb > 0) k_group_count<<<(unsigned)w.nb, 256, lds, st>>>(ids, d.Ms, E, blockcnt, counters);
-  k_group_scan<<<1, 1024, 0, st>>>(E, w.nb, blockcnt, ws_ptr<int32_t>(ws, w.counts), ws_ptr<int32_t>(ws, w.offsets),
-                                   ws_ptr<int32_t>(ws, w.tile_e), ws_ptr<int32_t>(ws, w.tile_m0), counters);
+  k_group_scan<<<1, 1024, 0, st>>>(E, w.nb, (int)w.mt, blockcnt, ws_ptr<int32_t>(ws, w.counts),
+                                   ws_ptr<int32_t>(ws, w.offsets), ws_ptr<int32_t>(ws, w.tile_e),
+                                   ws_ptr<int32_t>(ws, w.tile_m0), ws_ptr<int32_t>(ws, w.tile_e_aux),
+                                   ws_ptr<int32_t>(ws, w.tile_m0_aux), counters);
   if (w.nb > 0)
     k_group_place<<<(unsigned)w.nb, 256, lds, st>>>(ids, d.Ms, E, blockcnt, ws_ptr<int32_t>(ws, w.sorted_slot),
                                                    ws_ptr<int32_t>(ws, w.row_of_slot));

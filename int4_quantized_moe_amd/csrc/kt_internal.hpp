@@ -4,19 +4,36 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "../../include/kt_rawint4.h"
 
 namespace kt {
 
 // Tile geometry shared by the grouping (tile lists) and the matrix kernels.
-constexpr int kMT = 64;          // token-slot rows per tile
+constexpr int kMTAux = 64;         // token-slot rows per tile of the fp32 LoRA kernels
 constexpr int kGroupBlock = 1024;  // slots per block of the grouping histogram
-constexpr int kHChunk = 64;      // columns of I per gate/up tile (h exponent chunk)
-constexpr int kNT = 128;         // output columns per tile of the other GEMMs
+constexpr int kHChunk = 128;       // columns of I per gate/up tile (h exponent chunk)
+constexpr int kNT = 256;           // output columns per tile of the other GEMMs (dG/dU exponent chunk)
+
+// Rows per GEMM tile for a call: the smallest of 16/32/64/128 that covers the
+// mean number of token-slots per expert (heavier experts take several tiles).
+// KT_RAWINT4_GEMM_ROWS=16|32|64|128 overrides the choice (tuning and tests).
+inline int choose_gemm_rows(int64_t Ms, int64_t E) {
+  if (const char* env = getenv("KT_RAWINT4_GEMM_ROWS")) {
+    const int v = atoi(env);
+    if (v == 16 || v == 32 || v == 64 || v == 128) return v;
+  }
+  const int64_t active = E < Ms ? E : Ms;
+  const int64_t mean = active > 0 ? (Ms + active - 1) / active : 0;
+  if (mean <= 16) return 16;
+  if (mean <= 32) return 32;
+  if (mean <= 64) return 64;
+  return 128;
+}
 
 // Device counters at the head of the workspace.
-enum Counter { kBadIds = 0, kBadScales = 1, kNumTiles = 2, kNumCounters = 8 };
+enum Counter { kBadIds = 0, kBadScales = 1, kNumTiles = 2, kNumTilesAux = 3, kNumCounters = 8 };
 
 struct Dims {
   int64_t E, K, H, I, R, qlen, Ms;
@@ -25,7 +42,7 @@ struct Dims {
 
 struct WsMap {
   // grouping
-  size_t counters, counts, offsets, blockcnt, sorted_slot, row_of_slot, tile_e, tile_m0;
+  size_t counters, counts, offsets, blockcnt, sorted_slot, row_of_slot, tile_e, tile_m0, tile_e_aux, tile_m0_aux;
   // forward state kept for the backward
   size_t xh, xexp, ua, ub, g, u, hh, hexp, ud;
   // transient staging of per-slot rows (forward y, backward dx)
@@ -34,7 +51,7 @@ struct WsMap {
   size_t dyh, dyexp, dyb, dgu, dguexp, dgb, dub, drpart;
   size_t group_end;  // bytes needed by the grouping alone
   size_t total;
-  int64_t nb, max_tiles, h_nch, dg_nch, dr_nt;
+  int64_t nb, mt, max_tiles, max_tiles_aux, h_nch, dg_nch, dr_nt;
 };
 
 WsMap plan_workspace(const Dims& d);

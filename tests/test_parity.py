@@ -135,13 +135,18 @@ def _run_gpu(dev, cfg, weights, batch, grads_fill=7.0, accumulate=False, grad_sc
 
 
 def _check_all(tag, gpu, ref, active, grad_scale=1.0):
-    _close(f"{tag}.forward", gpu["out"], ref["out"])
-    _close(f"{tag}.dX", gpu["dx"], ref["dx"])
-    _close(f"{tag}.dRoute", gpu["droute"], ref["droute"], rel=DROUTE_REL_L2, cos=0.995)
+    checks = [("forward", gpu["out"], ref["out"], REL_L2, COSINE), ("dX", gpu["dx"], ref["dx"], REL_L2, COSINE),
+              ("dRoute", gpu["droute"], ref["droute"], DROUTE_REL_L2, 0.995)]
+    checks += [(n, gpu["grads"][n], grad_scale * ref["grads"][n], REL_L2, COSINE) for n in O.LORA_NAMES]
+    failures = []
+    for name, a, e, rel, cos in checks:  # report every metric before failing
+        try:
+            _close(f"{tag}.{name}", a, e, rel=rel, cos=cos)
+        except AssertionError as err:
+            failures.append(str(err))
+    assert not failures, "; ".join(failures)
     for n in O.LORA_NAMES:
-        expected = grad_scale * ref["grads"][n]
-        _close(f"{tag}.{n}", gpu["grads"][n], expected)
-        for e in range(expected.shape[0]):
+        for e in range(gpu["grads"][n].shape[0]):
             if e not in active:
                 assert np.count_nonzero(gpu["grads"][n][e]) == 0, f"{tag}.{n}: stale rows for expert {e}"
 
@@ -174,6 +179,21 @@ def test_layer_ragged_shapes(dev):
     _, _, _, gpu = _run_gpu(dev, cfg, weights, batch)
     ref = O.moe(cfg, weights, batch.inputs, batch.expert_ids, batch.route_weights, batch.grad_output)
     _check_all("ragged", gpu, ref, set(batch.expert_ids.ravel().tolist()))
+
+
+@pytest.mark.parametrize("rows", [16, 32, 64, 128])
+def test_layer_every_tile_height(dev, rows, monkeypatch):
+    # one expert with 300 slots (several tiles of every height) plus light experts
+    cfg = W.LayerConfig("heights", 5, 2, 160, 224, 6, 12.0, 180, 2.5, x_std=2.0)
+    _say("layer tile height", rows)
+    weights = W.make_weights(cfg, 91)
+    batch = W.make_batch(cfg, 91)
+    batch.expert_ids[:150, 0] = 1
+    batch.expert_ids[:150, 1] = np.where(batch.expert_ids[:150, 1] == 1, 3, batch.expert_ids[:150, 1])
+    monkeypatch.setenv("KT_RAWINT4_GEMM_ROWS", str(rows))
+    _, _, _, gpu = _run_gpu(dev, cfg, weights, batch)
+    ref = O.moe(cfg, weights, batch.inputs, batch.expert_ids, batch.route_weights, batch.grad_output)
+    _check_all(f"rows{rows}", gpu, ref, set(batch.expert_ids.ravel().tolist()))
 
 
 def test_layer_dropped_ids_and_window(dev):
