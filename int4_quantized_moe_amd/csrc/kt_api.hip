@@ -252,13 +252,22 @@ struct PhaseScope {
     if (!g_prof_on) return;
     a = prof_event();
     b = prof_event();
-    if (a && b) hipEventRecord(a, st);
+    if (!a || !b || hipEventRecord(a, st) != hipSuccess) release();
   }
   ~PhaseScope() {
     if (!a || !b) return;
-    hipEventRecord(b, st);
     std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (hipEventRecord(b, st) != hipSuccess) {
+      release();
+      return;
+    }
     g_prof_recs.push_back({phase, a, b});
+  }
+  // called with g_prof_mu held: give the events back unrecorded
+  void release() {
+    if (a) g_prof_pool.push_back(a);
+    if (b) g_prof_pool.push_back(b);
+    a = b = nullptr;
   }
 };
 
@@ -307,8 +316,7 @@ int kt_rawint4_moe_fwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const ui
   const RowView xv = view_tok_bf16(inputs, d.H);
   {
     PhaseScope ph(kPhLoraXA, st);
-    launch_lora_rowproj(d, w, ws, xv, d.H, L.ag, true, ws_ptr<float>(ws, w.ua), st);
-    launch_lora_rowproj(d, w, ws, xv, d.H, L.au, true, ws_ptr<float>(ws, w.ub), st);
+    launch_lora_rowproj(d, w, ws, xv, d.H, L.ag, L.au, true, ws_ptr<float>(ws, w.ua), ws_ptr<float>(ws, w.ub), st);
   }
   {
     PhaseScope ph(kPhGemmGateUp, st);
@@ -317,7 +325,7 @@ int kt_rawint4_moe_fwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const ui
   const RowView hv = view_half(ws_ptr<uint16_t>(ws, w.hh), d.I, 0, ws_ptr<int32_t>(ws, w.hexp), w.h_nch, 0, kHChunk);
   {
     PhaseScope ph(kPhLoraHA, st);
-    launch_lora_rowproj(d, w, ws, hv, d.I, L.ad, true, ws_ptr<float>(ws, w.ud), st);
+    launch_lora_rowproj(d, w, ws, hv, d.I, L.ad, nullptr, true, ws_ptr<float>(ws, w.ud), nullptr, st);
   }
   {
     PhaseScope ph(kPhGemmDown, st);
@@ -370,7 +378,7 @@ int kt_rawint4_moe_bwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const ui
   const RowView dyv = view_tok_bf16(grad_output, d.H);
   {
     PhaseScope ph(kPhLoraDyB, st);
-    launch_lora_rowproj(d, w, ws, dyv, d.H, L.bd, false, ws_ptr<float>(ws, w.dyb), st);
+    launch_lora_rowproj(d, w, ws, dyv, d.H, L.bd, nullptr, false, ws_ptr<float>(ws, w.dyb), nullptr, st);
   }
   {
     PhaseScope ph(kPhGemmDownBwd, st);
@@ -381,8 +389,8 @@ int kt_rawint4_moe_bwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const ui
       view_half(ws_ptr<uint16_t>(ws, w.dgu), 2 * d.I, d.I, ws_ptr<int32_t>(ws, w.dguexp), w.dg_nch, w.dg_nch / 2, kNT);
   {
     PhaseScope ph(kPhLoraDgB, st);
-    launch_lora_rowproj(d, w, ws, dgv, d.I, L.bg, false, ws_ptr<float>(ws, w.dgb), st);
-    launch_lora_rowproj(d, w, ws, duv, d.I, L.bu, false, ws_ptr<float>(ws, w.dub), st);
+    launch_lora_rowproj(d, w, ws, dgv, d.I, L.bg, nullptr, false, ws_ptr<float>(ws, w.dgb), nullptr, st);
+    launch_lora_rowproj(d, w, ws, duv, d.I, L.bu, nullptr, false, ws_ptr<float>(ws, w.dub), nullptr, st);
   }
   {
     PhaseScope ph(kPhGemmGateUpBwd, st);

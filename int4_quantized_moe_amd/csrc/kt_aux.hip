@@ -1,7 +1,6 @@
 // Auxiliary kernels of the routed layer: activation rows to fp16 with a
-// power-of-two exponent, LoRA side products and LoRA gradient reductions in
-// fp32, the per-token slot combine, the route-weight gradient, and the codec
-// test hooks.
+// power-of-two exponent, zero fill, the per-token slot combine, the
+// route-weight gradient, and the codec test hooks.
 #include "kt_common.hpp"
 #include "kt_internal.hpp"
 
@@ -38,145 +37,6 @@ __global__ __launch_bounds__(256) void k_rows_to_half(const uint16_t* __restrict
 void launch_rows_to_half(const uint16_t* src, int64_t rows, int64_t cols, uint16_t* dst, int32_t* exps,
                          hipStream_t st) {
   if (rows > 0) k_rows_to_half<<<(unsigned)rows, 256, 0, st>>>(src, cols, dst, exps);
-}
-
-// ---------------------------------------------------------------- row views
-
-__device__ __forceinline__ float rv_value(const RowView& v, int64_t m, int64_t c, const int32_t* sorted_slot,
-                                          int topk) {
-  float val;
-  if (v.kind == kSrcTokBf16) {
-    const int64_t tok = sorted_slot[m] / topk;
-    val = bf16_to_float(static_cast<const uint16_t*>(v.ptr)[tok * v.ld + v.col_off + c]);
-  } else if (v.kind == kSrcF32) {
-    val = static_cast<const float*>(v.ptr)[m * v.ld + v.col_off + c];
-  } else {
-    val = half_bits_to_float(static_cast<const uint16_t*>(v.ptr)[m * v.ld + perm_pos((int)(v.col_off + c))]);
-    val = ldexpf(val, -v.exps[m * v.exp_ld + v.exp_off + c / v.chunk_w]);
-  }
-  if (v.slot_scale) val *= v.slot_scale[sorted_slot[m]];
-  return val;
-}
-
-// ---------------------------------------------------------------- LoRA side products
-
-// out[m, q] = sum_k src(m, k) W(e, q, k) for the kMTAux rows of one tile and 32
-// values of q; fp32 throughout, k summed in increasing order.
-__global__ __launch_bounds__(256) void k_lora_rowproj(RowView src, int64_t kdim, const float* __restrict__ W, int rk,
-                                                      float* __restrict__ out, int R, int topk,
-                                                      const int32_t* __restrict__ sorted_slot,
-                                                      const int32_t* __restrict__ offsets,
-                                                      const int32_t* __restrict__ tile_e,
-                                                      const int32_t* __restrict__ tile_m0,
-                                                      const unsigned long long* __restrict__ counters) {
-  __shared__ float S[kMTAux][65];
-  __shared__ float Wc[32][65];
-  const int tile = blockIdx.x;
-  if ((unsigned long long)tile >= counters[kNumTilesAux]) return;
-  const int e = tile_e[tile], m0 = tile_m0[tile];
-  const int mlen = min(kMTAux, offsets[e + 1] - m0);
-  const int q0 = blockIdx.y * 32;
-  const int tid = threadIdx.x, row = tid >> 2, qs = (tid & 3) * 8;
-  float acc[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
-  for (int64_t k0 = 0; k0 < kdim; k0 += 64) {
-    for (int it = tid; it < kMTAux * 64; it += 256) {
-      const int r = it >> 6, kk = it & 63;
-      S[r][kk] = (r < mlen && k0 + kk < kdim) ? rv_value(src, m0 + r, k0 + kk, sorted_slot, topk) : 0.f;
-    }
-    for (int it = tid; it < 32 * 64; it += 256) {
-      const int qi = it >> 6, kk = it & 63;
-      const int q = q0 + qi;
-      const int64_t k = k0 + kk;
-      float v = 0.f;
-      if (q < R && k < kdim) v = rk ? W[((int64_t)e * R + q) * kdim + k] : W[((int64_t)e * kdim + k) * R + q];
-      Wc[qi][kk] = v;
-    }
-    __syncthreads();
-    for (int kk = 0; kk < 64; ++kk) {
-      const float s = S[row][kk];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] += s * Wc[qs + j][kk];
-    }
-    __syncthreads();
-  }
-  if (row < mlen) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int q = q0 + qs + j;
-      if (q < R) out[(int64_t)(m0 + row) * R + q] = acc[j];
-    }
-  }
-}
-
-void launch_lora_rowproj(const Dims& d, const WsMap& w, void* ws, const RowView& src, int64_t kdim, const float* W,
-                         bool rk, float* out, hipStream_t st) {
-  if (w.max_tiles_aux == 0) return;
-  dim3 grid((unsigned)w.max_tiles_aux, (unsigned)((d.R + 31) / 32));
-  k_lora_rowproj<<<grid, 256, 0, st>>>(src, kdim, W, rk ? 1 : 0, out, (int)d.R, (int)d.K,
-                                       ws_ptr<int32_t>(ws, w.sorted_slot), ws_ptr<int32_t>(ws, w.offsets),
-                                       ws_ptr<int32_t>(ws, w.tile_e_aux), ws_ptr<int32_t>(ws, w.tile_m0_aux),
-                                       ws_ptr<unsigned long long>(ws, w.counters));
-}
-
-// ---------------------------------------------------------------- LoRA gradient reductions
-
-// G[e, p, q] = (accumulate ? G : 0) + scale * sum_{rows m of e} P(m, p) Q(m, q);
-// one block per (expert, 64x64 tile); rows summed in sorted (= slot) order.
-__global__ __launch_bounds__(256) void k_lora_grad(RowView P, int64_t np, RowView Q, int64_t nq,
-                                                   float* __restrict__ G, int accumulate, float scale, int topk,
-                                                   const int32_t* __restrict__ sorted_slot,
-                                                   const int32_t* __restrict__ offsets) {
-  __shared__ float Pc[32][65];
-  __shared__ float Qc[32][65];
-  const int e = blockIdx.x;
-  const int64_t p0 = (int64_t)blockIdx.y * 64, q0 = (int64_t)blockIdx.z * 64;
-  const int start = offsets[e], cnt = offsets[e + 1] - start;
-  if (cnt == 0 && accumulate) return;
-  const int tid = threadIdx.x, pi = (tid >> 4) * 4, qi = (tid & 15) * 4;
-  float acc[4][4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = 0.f;
-  for (int mm = 0; mm < cnt; mm += 32) {
-    for (int it = tid; it < 32 * 64; it += 256) {
-      const int r = it >> 6, c = it & 63;
-      const int64_t m = start + mm + r;
-      const bool vr = mm + r < cnt;
-      Pc[r][c] = (vr && p0 + c < np) ? rv_value(P, m, p0 + c, sorted_slot, topk) : 0.f;
-      Qc[r][c] = (vr && q0 + c < nq) ? rv_value(Q, m, q0 + c, sorted_slot, topk) : 0.f;
-    }
-    __syncthreads();
-    for (int r = 0; r < 32; ++r) {
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const float pv = Pc[r][pi + a];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] += pv * Qc[r][qi + b];
-      }
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int64_t p = p0 + pi + a, q = q0 + qi + b;
-      if (p < np && q < nq) {
-        const int64_t idx = ((int64_t)e * np + p) * nq + q;
-        const float prev = accumulate ? G[idx] : 0.f;
-        G[idx] = prev + scale * acc[a][b];
-      }
-    }
-}
-
-void launch_lora_grad(const Dims& d, const WsMap& w, void* ws, const RowView& P, int64_t np, const RowView& Q,
-                      int64_t nq, float* G, int accumulate, float scale, hipStream_t st) {
-  dim3 grid((unsigned)d.E, (unsigned)((np + 63) / 64), (unsigned)((nq + 63) / 64));
-  k_lora_grad<<<grid, 256, 0, st>>>(P, np, Q, nq, G, accumulate, scale, (int)d.K, ws_ptr<int32_t>(ws, w.sorted_slot),
-                                    ws_ptr<int32_t>(ws, w.offsets));
 }
 
 __global__ void k_fill_zero(float* p, int64_t n) {

@@ -16,8 +16,10 @@ constexpr int kGroupBlock = 1024;  // slots per block of the grouping histogram
 constexpr int kHChunk = 128;       // columns of I per gate/up tile (h exponent chunk)
 constexpr int kNT = 256;           // output columns per tile of the other GEMMs (dG/dU exponent chunk)
 
-// Rows per GEMM tile for a call: the smallest of 16/32/64/128 that covers the
-// mean number of token-slots per expert (heavier experts take several tiles).
+// Rows per GEMM tile for a call: the smallest of 16/32/64 that covers the mean
+// number of token-slots per expert (heavier experts take several tiles).  The
+// 128-row tiles run one wave per SIMD and measured slower than 64-row tiles at
+// 16384 tokens, so they are used only on request.
 // KT_RAWINT4_GEMM_ROWS=16|32|64|128 overrides the choice (tuning and tests).
 inline int choose_gemm_rows(int64_t Ms, int64_t E) {
   if (const char* env = getenv("KT_RAWINT4_GEMM_ROWS")) {
@@ -28,8 +30,7 @@ inline int choose_gemm_rows(int64_t Ms, int64_t E) {
   const int64_t mean = active > 0 ? (Ms + active - 1) / active : 0;
   if (mean <= 16) return 16;
   if (mean <= 32) return 32;
-  if (mean <= 64) return 64;
-  return 128;
+  return 64;
 }
 
 // Device counters at the head of the workspace.
@@ -79,7 +80,7 @@ enum GemmKind { kGateUp = 0, kDown = 1, kDownBwd = 2, kGateUpBwd = 3 };
 void launch_gemm(GemmKind kind, const Dims& d, const WsMap& w, void* ws, const LayerPtrs& L, const float* route_weights,
                  hipStream_t st);
 
-// fp32 LoRA products and gradient reductions
+// LoRA side products and gradient reductions (bf16 hi/lo MFMA)
 enum RowSrc { kSrcTokBf16 = 0, kSrcF32 = 1, kSrcHalfChunked = 2 };
 struct RowView {
   int kind;
@@ -92,9 +93,10 @@ struct RowView {
 };
 
 // out[m, q] = sum_k src(m, k) * W(e, q, k), q < R, k < kdim; W is [E, R, kdim]
-// (rk = true) or [E, kdim, R] (rk = false).
+// (rk = true) or [E, kdim, R] (rk = false).  With W2 set, a second product with
+// the same rows goes to out2.
 void launch_lora_rowproj(const Dims& d, const WsMap& w, void* ws, const RowView& src, int64_t kdim, const float* W,
-                         bool rk, float* out, hipStream_t st);
+                         const float* W2, bool rk, float* out, float* out2, hipStream_t st);
 // G[e, p, q] = (acc ? G : 0) + scale * sum_{m in e} P(m, p) Q(m, q)
 void launch_lora_grad(const Dims& d, const WsMap& w, void* ws, const RowView& P, int64_t np, const RowView& Q,
                       int64_t nq, float* G, int accumulate, float scale, hipStream_t st);
