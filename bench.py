@@ -93,6 +93,9 @@ def main():
     ap.add_argument("--config", type=int, default=4, help="index into workloads.CONFIGS")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after timing, run one plain elementwise copy (torch.neg, fp32) of this many MiB: "
+                         "the calibration kernel for hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (expert parallelism is designed, "
@@ -177,6 +180,16 @@ def main():
     log(f"step: {total_flops / (ms_per_step / 1e3) / 1e12:.1f} TFLOP/s "
         f"({100 * total_flops / (ms_per_step / 1e3) / PEAK_MFMA_FP16:.2f}% MFMA), packed weights "
         f"{total_wbytes / (ms_per_step / 1e3) / 1e9:.1f} GB/s ({100 * total_wbytes / (ms_per_step / 1e3) / PEAK_HBM:.2f}% HBM)")
+
+    if args.copy_mib:
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {args.copy_mib} MiB read, {args.copy_mib} MiB written")
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:

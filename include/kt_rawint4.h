@@ -67,7 +67,7 @@ extern "C" {
  * LoRA tensors (fp32): gate_lora_a [E, r, H], gate_lora_b [E, I, r],
  * up_lora_a [E, r, H], up_lora_b [E, I, r], down_lora_a [E, r, I],
  * down_lora_b [E, H, r] (names and order of the page
- * "test_rawint4_sft_numerical.py", GRAD_SHAPES).
+ * "test_rawint4_sft_numerical.py", GRAD_SHAPES), each 16-byte aligned.
  */
 typedef struct kt_rawint4_moe_layer {
   int32_t num_experts;
@@ -111,7 +111,9 @@ size_t kt_rawint4_moe_workspace_bytes(const kt_rawint4_moe_layer* layer, int32_t
  * [0, E) are dropped (the slot contributes nothing) and counted.
  * The workspace keeps what the backward needs (grouping, fp32 gate/up
  * pre-activations from which the clamp masks are decided, h, LoRA-A
- * products); a later forward into the same workspace replaces it.
+ * products, and the three scale tensors converted once to fp16 and
+ * transposed to [E, K/32, N]: 1/8 the size of the packed codes); a later
+ * forward into the same workspace replaces it.
  * qlen == 0 is a valid no-op.
  */
 int kt_rawint4_moe_fwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const uint16_t* inputs,
@@ -173,8 +175,9 @@ int kt_rawint4_group(const int64_t* expert_ids, int32_t qlen, int32_t top_k, int
 /*
  * Synchronising read of the device-side counters of the latest forward in
  * `workspace` (written by kt_rawint4_moe_fwd or kt_rawint4_group): expert ids
- * outside [0, E) and scale reads outside the numeric domain.  Host pointers
- * out; either may be NULL.
+ * outside [0, E) and scales outside the numeric domain (each scale of the
+ * three projections is checked once per forward).  Host pointers out; either
+ * may be NULL.
  */
 int kt_rawint4_moe_diagnostics(const void* workspace, size_t workspace_bytes, int64_t* bad_ids, int64_t* bad_scales,
                                void* stream);
@@ -183,12 +186,13 @@ int kt_rawint4_moe_diagnostics(const void* workspace, size_t workspace_bytes, in
  * Per-phase timing of the layer's launches, for measurement.  While enabled,
  * every forward/backward records a hipEvent pair around each phase (grouping,
  * activation conversion, LoRA side products, each grouped GEMM, combine,
- * route-weight gradient, LoRA gradient reductions) on the caller's stream.
+ * route-weight gradient, LoRA gradient reductions, and the forward's one
+ * conversion of the scales to fp16) on the caller's stream.
  * kt_rawint4_profile_read waits for the recorded events, writes the summed
  * milliseconds and the number of recorded launches of each phase into
  * ms[capacity] / launches[capacity] (host arrays), clears the records and
  * returns the number of phases (or a negative error code; capacity must cover
- * every phase, 15 at present).  Phase names: kt_rawint4_profile_phase_name.
+ * every phase, 16 at present).  Phase names: kt_rawint4_profile_phase_name.
  */
 int kt_rawint4_profile_enable(int32_t on);
 int kt_rawint4_profile_read(float* ms, int32_t* launches, int32_t capacity);

@@ -60,6 +60,9 @@ WsMap plan_workspace(const Dims& d) {
   WsMap w{};
   Planner pl;
   plan_group_part(pl, w, d.Ms, d.E);
+  w.sct_g = pl.take(2 * (size_t)d.E * (size_t)d.I * (size_t)(d.H / 32));
+  w.sct_u = pl.take(2 * (size_t)d.E * (size_t)d.I * (size_t)(d.H / 32));
+  w.sct_d = pl.take(2 * (size_t)d.E * (size_t)d.H * (size_t)(d.I / 32));
   w.h_nch = (d.I + kHChunk - 1) / kHChunk;
   w.dr_nt = (d.I + kNT - 1) / kNT;
   w.dg_nch = 2 * w.dr_nt;
@@ -73,6 +76,7 @@ WsMap plan_workspace(const Dims& d) {
   w.hh = pl.take(2 * Ms * I);
   w.hexp = pl.take(4 * Ms * (size_t)w.h_nch);
   w.ud = pl.take(4 * Ms * R);
+  w.lsplit = pl.take(2 * 2 * Ms * 2 * (size_t)lora_half_width((int64_t)R));
   w.stage = pl.take(4 * Ms * H);
   w.dyh = pl.take(2 * q * H);
   w.dyexp = pl.take(4 * q);
@@ -114,7 +118,7 @@ static int check_layer(const kt_rawint4_moe_layer* L, int32_t qlen, Dims* d) {
     return fail(KT_RAWINT4_EINVAL, "scales must be 2-byte aligned");
   const float* lora[] = {L->gate_lora_a, L->gate_lora_b, L->up_lora_a, L->up_lora_b, L->down_lora_a, L->down_lora_b};
   for (const float* p : lora)
-    if (!aligned(p, 4)) return fail(KT_RAWINT4_EINVAL, "LoRA tensors must be 4-byte aligned");
+    if (!aligned(p, 16)) return fail(KT_RAWINT4_EINVAL, "LoRA tensors must be 16-byte aligned");
   d->E = L->num_experts;
   d->K = L->top_k;
   d->H = L->hidden;
@@ -198,6 +202,7 @@ static RowView view_half(const uint16_t* p, int64_t ld, int64_t col_off, const i
 
 enum Phase {
   kPhGroup = 0,
+  kPhScales,
   kPhXHalf,
   kPhLoraXA,
   kPhGemmGateUp,
@@ -216,7 +221,7 @@ enum Phase {
 };
 
 static const char* const kPhaseNames[kNumPhases] = {
-    "group",        "x_to_half",      "lora_a_gate_up", "gemm_gate_up",     "lora_a_down",
+    "group",        "scales_fp16",    "x_to_half",      "lora_a_gate_up", "gemm_gate_up",     "lora_a_down",
     "gemm_down",    "combine_fwd",    "dy_to_half",     "lora_b_down_bwd",  "gemm_down_dx",
     "lora_b_gate_up_bwd", "gemm_gate_up_dx", "combine_bwd", "droute",       "lora_grads"};
 
@@ -310,22 +315,33 @@ int kt_rawint4_moe_fwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const ui
     launch_group(d, w, ws, expert_ids, st);
   }
   {
+    PhaseScope ph(kPhScales, st);
+    unsigned long long* bad = ws_ptr<unsigned long long>(ws, w.counters) + kBadScales;
+    launch_scales_t(layer->gate_scale, d.E, d.I, d.H / 32, ws_ptr<uint16_t>(ws, w.sct_g), bad, st);
+    launch_scales_t(layer->up_scale, d.E, d.I, d.H / 32, ws_ptr<uint16_t>(ws, w.sct_u), bad, st);
+    launch_scales_t(layer->down_scale, d.E, d.H, d.I / 32, ws_ptr<uint16_t>(ws, w.sct_d), bad, st);
+  }
+  {
     PhaseScope ph(kPhXHalf, st);
     launch_rows_to_half(inputs, d.qlen, d.H, ws_ptr<uint16_t>(ws, w.xh), ws_ptr<int32_t>(ws, w.xexp), st);
   }
   const RowView xv = view_tok_bf16(inputs, d.H);
   {
     PhaseScope ph(kPhLoraXA, st);
-    launch_lora_rowproj(d, w, ws, xv, d.H, L.ag, L.au, true, ws_ptr<float>(ws, w.ua), ws_ptr<float>(ws, w.ub), st);
+    launch_lora_rowproj(d, w, ws, xv, d.H, L.ag, L.au, true, ws_ptr<float>(ws, w.ua), ws_ptr<float>(ws, w.ub),
+                        2 * lora_half_width(d.R), 0, lora_half_width(d.R), st);
   }
   {
     PhaseScope ph(kPhGemmGateUp, st);
     launch_gemm(kGateUp, d, w, ws, L, route_weights, st);
+    launch_normalize_chunks(ws_ptr<uint16_t>(ws, w.hh), ws_ptr<int32_t>(ws, w.hexp),
+                            ws_ptr<int32_t>(ws, w.offsets) + d.E, d.Ms, d.I, d.I, (int)w.h_nch, kHChunk, st);
   }
   const RowView hv = view_half(ws_ptr<uint16_t>(ws, w.hh), d.I, 0, ws_ptr<int32_t>(ws, w.hexp), w.h_nch, 0, kHChunk);
   {
     PhaseScope ph(kPhLoraHA, st);
-    launch_lora_rowproj(d, w, ws, hv, d.I, L.ad, nullptr, true, ws_ptr<float>(ws, w.ud), nullptr, st);
+    launch_lora_rowproj(d, w, ws, hv, d.I, L.ad, nullptr, true, ws_ptr<float>(ws, w.ud), nullptr,
+                        lora_half_width(d.R), 0, 0, st);
   }
   {
     PhaseScope ph(kPhGemmDown, st);
@@ -378,19 +394,24 @@ int kt_rawint4_moe_bwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const ui
   const RowView dyv = view_tok_bf16(grad_output, d.H);
   {
     PhaseScope ph(kPhLoraDyB, st);
-    launch_lora_rowproj(d, w, ws, dyv, d.H, L.bd, nullptr, false, ws_ptr<float>(ws, w.dyb), nullptr, st);
+    launch_lora_rowproj(d, w, ws, dyv, d.H, L.bd, nullptr, false, ws_ptr<float>(ws, w.dyb), nullptr,
+                        lora_half_width(d.R), 0, 0, st);
   }
   {
     PhaseScope ph(kPhGemmDownBwd, st);
     launch_gemm(kDownBwd, d, w, ws, L, route_weights, st);
+    launch_normalize_chunks(ws_ptr<uint16_t>(ws, w.dgu), ws_ptr<int32_t>(ws, w.dguexp),
+                            ws_ptr<int32_t>(ws, w.offsets) + d.E, d.Ms, 2 * d.I, d.I, (int)w.dg_nch, kNT, st);
   }
   const RowView dgv = view_half(ws_ptr<uint16_t>(ws, w.dgu), 2 * d.I, 0, ws_ptr<int32_t>(ws, w.dguexp), w.dg_nch, 0, kNT);
   const RowView duv =
       view_half(ws_ptr<uint16_t>(ws, w.dgu), 2 * d.I, d.I, ws_ptr<int32_t>(ws, w.dguexp), w.dg_nch, w.dg_nch / 2, kNT);
   {
     PhaseScope ph(kPhLoraDgB, st);
-    launch_lora_rowproj(d, w, ws, dgv, d.I, L.bg, nullptr, false, ws_ptr<float>(ws, w.dgb), nullptr, st);
-    launch_lora_rowproj(d, w, ws, duv, d.I, L.bu, nullptr, false, ws_ptr<float>(ws, w.dub), nullptr, st);
+    launch_lora_rowproj(d, w, ws, dgv, d.I, L.bg, nullptr, false, ws_ptr<float>(ws, w.dgb), nullptr,
+                        2 * lora_half_width(d.R), 0, 0, st);
+    launch_lora_rowproj(d, w, ws, duv, d.I, L.bu, nullptr, false, ws_ptr<float>(ws, w.dub), nullptr,
+                        2 * lora_half_width(d.R), lora_half_width(d.R), 0, st);
   }
   {
     PhaseScope ph(kPhGemmGateUpBwd, st);

@@ -1,6 +1,8 @@
 // Auxiliary kernels of the routed layer: activation rows to fp16 with a
 // power-of-two exponent, zero fill, the per-token slot combine, the
 // route-weight gradient, and the codec test hooks.
+#include <limits.h>
+
 #include "kt_common.hpp"
 #include "kt_internal.hpp"
 
@@ -37,6 +39,103 @@ __global__ __launch_bounds__(256) void k_rows_to_half(const uint16_t* __restrict
 void launch_rows_to_half(const uint16_t* src, int64_t rows, int64_t cols, uint16_t* dst, int32_t* exps,
                          hipStream_t st) {
   if (rows > 0) k_rows_to_half<<<(unsigned)rows, 256, 0, st>>>(src, cols, dst, exps);
+}
+
+// ---------------------------------------------------------------- scales for the expert GEMMs
+
+// One scale tensor [E][rows][G] (bf16, G = K / 32) to [E][G][rows] in fp16,
+// rows of every aligned group of 8 in the within-8 permuted order, so that a
+// GEMM stage reads the scales of its column (or contraction-row) block as one
+// contiguous run in both orientations.  Scales outside the numeric domain are
+// counted (once each).  64 x 64 tiles pass through LDS so that the reads (along
+// G) and the writes (along rows) are both coalesced.
+__global__ __launch_bounds__(256) void k_scales_t(const uint16_t* __restrict__ s, int64_t rows, int64_t G,
+                                                   uint16_t* __restrict__ out, unsigned long long* bad) {
+  __shared__ uint16_t t[64][66];
+  __shared__ int nbad_w[4];
+  const int64_t e = blockIdx.z;
+  const int64_t r0 = (int64_t)blockIdx.x * 64, g0 = (int64_t)blockIdx.y * 64;
+  const uint16_t* se = s + e * rows * G;
+  uint16_t* oe = out + e * G * rows;
+  int nbad = 0;
+  for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) {
+    const int i = idx >> 6, j = idx & 63;  // row r0 + i, group g0 + j
+    const int64_t r = r0 + i, g = g0 + j;
+    uint16_t h = 0;
+    if (r < rows && g < G) {
+      const float f = bf16_to_float(se[r * G + g]);
+      nbad += scale_in_domain(f) ? 0 : 1;
+      h = float_to_half_bits(f);
+    }
+    t[i][j] = h;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) {
+    const int j = idx >> 6, i = idx & 63;  // group g0 + j, position r0 + i
+    const int64_t g = g0 + j, r = r0 + i;
+    // position i of an aligned group of 8 holds logical row (i & ~7) | ((i & 7) >> 1) | ((i & 1) << 2)
+    const int src = (i & ~7) | ((i & 7) >> 1) | ((i & 1) << 2);
+    if (r < rows && g < G) oe[g * rows + r] = t[src][j];
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) nbad += __shfl_xor(nbad, off);
+  if ((threadIdx.x & 63) == 0) nbad_w[threadIdx.x >> 6] = nbad;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int n = nbad_w[0] + nbad_w[1] + nbad_w[2] + nbad_w[3];
+    if (n) atomicAdd(bad, (unsigned long long)n);
+  }
+}
+
+void launch_scales_t(const uint16_t* s, int64_t E, int64_t rows, int64_t G, uint16_t* out, unsigned long long* bad,
+                     hipStream_t st) {
+  if (E <= 0 || rows <= 0 || G <= 0) return;
+  dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((G + 63) / 64), (unsigned)E);
+  k_scales_t<<<grid, 256, 0, st>>>(s, rows, G, out, bad);
+}
+
+// ---------------------------------------------------------------- one exponent per row
+
+// h and dG|dU leave their producing GEMM with one exponent per (row, column
+// chunk), since no tile sees a whole row.  One wave per row brings every chunk
+// to the row's smallest exponent (fp16 times 2^d, d <= 0, rounded to nearest
+// even) and records that exponent for every chunk.  Columns at or above `split`
+// belong to the second operand, whose chunks start again at `split` and are
+// numbered from nch / 2 (dG|dU); split = cols for a single operand (h).
+__global__ __launch_bounds__(256) void k_normalize_chunks(uint16_t* __restrict__ buf, int32_t* __restrict__ exps,
+                                                          const int32_t* __restrict__ nrows, int64_t cols,
+                                                          int64_t split, int nch, int chunkw) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= *nrows) return;
+  int32_t* ex = exps + row * nch;
+  int mn = INT_MAX;
+  for (int c = lane; c < nch; c += 64) mn = min(mn, ex[c]);
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) mn = min(mn, __shfl_xor(mn, off));
+  uint16_t* b = buf + row * cols;
+  for (int64_t c8 = (int64_t)lane * 8; c8 < cols; c8 += 512) {
+    const int c = c8 < split ? (int)(c8 / chunkw) : nch / 2 + (int)((c8 - split) / chunkw);
+    const int d = mn - ex[c];
+    if (d == 0) continue;
+    const uint16_t sb = half_pow2_bits(d);
+    const half2_t s2 = __builtin_bit_cast(half2_t, (uint32_t)sb | ((uint32_t)sb << 16));
+    u32x4 v = *reinterpret_cast<const u32x4*>(b + c8);
+    v.x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, (uint32_t)v.x) * s2);
+    v.y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, (uint32_t)v.y) * s2);
+    v.z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, (uint32_t)v.z) * s2);
+    v.w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, (uint32_t)v.w) * s2);
+    *reinterpret_cast<u32x4*>(b + c8) = v;
+  }
+  // every lane has read the exponents it needs before any is overwritten
+  __builtin_amdgcn_wave_barrier();
+  for (int c = lane; c < nch; c += 64) ex[c] = mn;
+}
+
+void launch_normalize_chunks(uint16_t* buf, int32_t* exps, const int32_t* nrows, int64_t max_rows, int64_t cols,
+                             int64_t split, int nch, int chunkw, hipStream_t st) {
+  if (max_rows > 0)
+    k_normalize_chunks<<<(unsigned)((max_rows + 3) / 4), 256, 0, st>>>(buf, exps, nrows, cols, split, nch, chunkw);
 }
 
 __global__ void k_fill_zero(float* p, int64_t n) {

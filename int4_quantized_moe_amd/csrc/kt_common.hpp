@@ -56,6 +56,17 @@ __device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) 
   lo = float_to_bf16(v - bf16_to_float(hi));
 }
 
+__device__ __forceinline__ uint32_t pack2(uint16_t a, uint16_t b) { return (uint32_t)a | ((uint32_t)b << 16); }
+
+// 8 fp32 values -> bf16 hi and lo planes (16 bytes each)
+__device__ __forceinline__ void split8(const float* v, u32x4& hi, u32x4& lo) {
+  uint16_t h[8], l[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) split_bf16(v[i], h[i], l[i]);
+  hi = u32x4{pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7])};
+  lo = u32x4{pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7])};
+}
+
 // ---------------------------------------------------------------- RAWINT4 decode
 
 // Nonzero scales in [2^-14, 8160] make (c - 8) * scale exact in fp16.

@@ -10,24 +10,40 @@
 //
 // A work tile is MT token-slot rows of one expert (rows sorted by the grouping)
 // by kNT = 256 output columns; the four waves of a workgroup split the columns
-// (64 each) and share the activation tile, which is staged in LDS 64 contraction
-// values at a time, double buffered.
+// (64 each) and share the activation tile.  Operands move through a three-stage
+// LDS ring of 64 contraction values per stage, filled by direct global-to-LDS
+// 16-byte loads (no register staging): while one stage is multiplied the next
+// two are in flight.  The ring waits are explicit (vmcnt) around a bare
+// s_barrier, so the compiler's conservative drain at __syncthreads does not
+// serialise the ring.  Blocks are mapped to tiles so that each XCD (blocks are
+// dealt to the eight XCDs in turn) works through a contiguous range of tiles:
+// the column tiles of one row tile, and the row tiles of one expert, then share
+// that XCD's L2.
 //
 // Weights are decoded on the fly into exact fp16 ((c - 8) * scale fits fp16's
 // 11-bit significand) and multiplied on v_mfma_f32_16x16x32_f16 with fp32
 // accumulation.  In the stored orientation (kGateUp, kDown: contraction along
-// the packed K) every lane loads its 16 nibbles straight into registers.  The
-// two gradient GEMMs contract over the weight rows: the raw packed rows are
-// copied into LDS as they are and read back with ds_read_tr4_b64, which hands
-// each lane 16 consecutive rows of one column; this is the transpose-free dX of
-// transpose_free_rawint4_dx with the transpose done by the LDS read.
+// the packed K) each column's 32 packed bytes of a stage sit in LDS and a lane
+// reads its 16 nibbles with one 8-byte read.  The two gradient GEMMs contract
+// over the weight rows: the raw packed rows are copied into LDS as they are and
+// read back with ds_read_tr4_b64, which hands each lane 16 consecutive rows of
+// one column; this is the transpose-free dX of transpose_free_rawint4_dx with
+// the transpose done by the LDS read.  Scales pass through registers into LDS
+// one stage ahead, converted to fp16 on the way (the transposed orientation
+// stores them transposed, in the activation's permuted order).
 //
-// Activations carry a power-of-two exponent per row (x, dY) or per (row, column
-// chunk) (h, dG, dU) so that fp16's range never clips them; chunk exponents are
-// brought to the row's smallest exponent while the tile is staged, and the
-// epilogue removes it.  LoRA terms ride along as extra K-steps: the fp32 LoRA-A
-// side products and the fp32 LoRA matrices are split into bf16 hi + lo and
-// multiplied with three bf16 MFMAs (hi*hi + hi*lo + lo*hi).
+// LDS tiles are XOR-swizzled in 16-byte units so that the fragment reads of a
+// wave spread over the banks: activation row r keeps chunk c in slot
+// c ^ ((r & 7) ^ ((r >> 3) & 1)); stored-orientation weight column n keeps its
+// half h in slot h ^ ((n >> 3) & 1); transposed weight row k keeps its chunk c
+// in slot c ^ ((k >> 1) & 7).
+//
+// Activations carry one power-of-two exponent per row so that fp16's range never
+// clips them (x, dY per token; h and dG|dU per sorted row after their chunk
+// exponents are brought to the row's smallest); the epilogue removes it.  LoRA
+// terms ride along as extra K-steps: the fp32 LoRA-A side products and the fp32
+// LoRA matrices are split into bf16 hi + lo and multiplied with three bf16 MFMAs
+// (hi*hi + hi*lo + lo*hi); they run while the ring's first stages are in flight.
 #include <limits.h>
 
 #include "kt_common.hpp"
@@ -35,12 +51,22 @@
 
 namespace kt {
 
-constexpr int kKS = 64;       // contraction values per super-step (two quant groups)
-constexpr int kAP = kKS + 8;  // activation tile pitch in 16-bit elements (144 B)
-constexpr int kWP = 144;      // raw weight tile pitch in bytes (128 B of codes for 256 columns)
+constexpr int kKS = 64;         // contraction values per stage (two quant groups)
+constexpr int kStages = 3;      // LDS ring depth
+constexpr int kWBytes = 8192;   // packed weight bytes per stage (256 columns x 64 values)
+constexpr int kScBytes = 1024;  // fp16 scales per stage (256 columns x 2 groups, or 64 rows x 8 groups)
+constexpr int kLBP = 544;       // row pitch in bytes of a transposed LoRA matrix group (256 bf16 + 32 B)
 
 typedef int v2i_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v2i_t* lds_v2i_ptr;
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s_t* lds_v4s_ptr;
+typedef const void __attribute__((address_space(1)))* global_ptr;
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
+typedef void __attribute__((address_space(3)))* lds_ptr;
 
 struct GemmParams {
   int E, topk, H, I, R;
@@ -53,11 +79,12 @@ struct GemmParams {
   LayerPtrs L;
   const uint16_t* a_src;      // fp16 activation rows (within-8 permuted order)
   const int32_t* a_rowexp;    // per token exponent (x, dY)
-  const int32_t* a_chunkexp;  // per (row, chunk) exponent (h, dG|dU)
-  int a_nch, a_chunkw;
+  const int32_t* a_chunkexp;  // per (row, chunk) exponent (h, dG|dU), all chunks of a row equal
+  int a_nch;
   int64_t lda;
-  const float* la0;  // LoRA-A side products per sorted row, [Ms, R]
-  const float* la1;
+  const uint16_t* lsplit;  // side product times the LoRA scale, bf16 hi/lo planes [Ms][2][KLP]
+  const uint16_t* sct0;    // fp16 scales [E][K/32][rows], rows within-8 permuted: gate (or down)
+  const uint16_t* sct1;    // up
   const float* rw;  // route weights per flat slot
   float* gsave;
   float* usave;
@@ -70,7 +97,6 @@ struct GemmParams {
   int dg_nch;
   float* drpart;
   int dr_nt;
-  unsigned long long* bad_scales;
   int n_ntiles;
 };
 
@@ -79,10 +105,6 @@ template <int KIND>
 __device__ __forceinline__ int local_col(int w, int f) {
   if constexpr (KIND == kGateUp) return f < 2 ? w * 32 + f * 16 : kHChunk + w * 32 + (f - 2) * 16;
   return w * 64 + f * 16;
-}
-
-__device__ __forceinline__ uint32_t mul_half2(uint32_t v, half2_t s) {
-  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, v) * s);
 }
 
 __device__ __forceinline__ u32x4 pack_bf16x8(const uint16_t* v) {
@@ -116,49 +138,167 @@ __device__ __forceinline__ void clamp_swiglu(float g, float u, float limit, floa
   }
 }
 
+// LDS byte address of a pointer into a __shared__ array
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
+// 16 bytes from global memory to LDS: lane l's bytes land at lds_base + 16 * l
+// (lds_base wave-uniform, through M0).  Counted by vmcnt like any vector load.
+// Issued from asm so that the compiler, which cannot tell which ring slot a
+// later LDS read touches, does not drain every outstanding copy before it; the
+// ring's explicit vmcnt waits order the copies and the reads instead.  M0 is
+// not used by anything else in these kernels.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
+  // one wait state between the M0 write and the load that reads it
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(base) : "memory");
+}
+
+// s_waitcnt with vmcnt <= N and lgkmcnt == 0 (gfx9 encoding: vmcnt in bits 3:0
+// and 15:14, expcnt in 6:4 left at its maximum, lgkmcnt in 11:8)
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// 128-row tiles hold 128 accumulators per lane and run one wave per SIMD (all 512
+// registers); smaller tiles run two or more.
 template <int KIND, int MT>
-__global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT == 128 ? 1 : 2))) void k_gemm(GemmParams p) {
   constexpr int MB = MT / 16;
   constexpr bool kT = (KIND == kDownBwd || KIND == kGateUpBwd);
   constexpr bool kChunked = (KIND == kDown || KIND == kGateUpBwd);
-  constexpr int kAChunks = (MT * 8 + 255) / 256;  // 16-byte activation pieces per thread per super-step
-  __shared__ __align__(16) uint16_t As[2][MT * kAP];
-  __shared__ __align__(16) uint8_t Wl[kT ? 2 : 1][kT ? kKS * kWP : 16];
-  __shared__ __align__(16) uint16_t Sc[kT ? 2 : 1][kT ? (kNT / 32) * kKS : 8];
+  constexpr int kABytes = MT * 128;                 // activation tile of one stage
+  constexpr int kStage = kABytes + kWBytes + kScBytes;
+  constexpr int kRowsPerInst = MT == 16 ? 4 : 8;     // activation rows per DMA instruction
+  constexpr int kAInst = MT == 16 ? 1 : MT / 32;     // activation DMA instructions per wave per stage
+  constexpr int kDmaPerStage = kAInst + 3;           // plus two weight and one scale DMA instructions
+  constexpr int kRing = kStages * kStage > kABytes + 64 * kLBP ? kStages * kStage : kABytes + 64 * kLBP;
+  __shared__ __align__(16) uint8_t ring[kRing];
   __shared__ int32_t s_src[MT], s_exp[MT], s_slot[MT];
 
-  const int tile = (int)(blockIdx.x / (unsigned)p.n_ntiles);
-  const int nt = (int)(blockIdx.x % (unsigned)p.n_ntiles);
-  if ((unsigned long long)tile >= p.counters[kNumTiles]) return;
+  // ---------------------------------------------------------------- work item
+  const unsigned total = (unsigned)p.counters[kNumTiles] * (unsigned)p.n_ntiles;
+  if (blockIdx.x >= total) return;
+  const unsigned xq = total / 8u, xr = total % 8u, xcd = blockIdx.x % 8u;
+  const unsigned item = xcd * xq + min(xcd, xr) + blockIdx.x / 8u;
+  const int tile = (int)(item / (unsigned)p.n_ntiles);
+  const int nt = (int)(item % (unsigned)p.n_ntiles);
   const int e = p.tile_e[tile], m0 = p.tile_m0[tile];
   const int mlen = min(MT, p.offsets[e + 1] - m0);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
   const int H = p.H, I = p.I, R = p.R;
   const int n0 = (KIND == kGateUp) ? nt * kHChunk : nt * kNT;
   const int nout = (KIND == kGateUp || KIND == kDownBwd) ? I : H;
   const int kdim = (KIND == kGateUp || KIND == kDownBwd) ? H : (KIND == kDown ? I : 2 * I);
+  const int ngroups = kdim / kGroup;
   const int nss = (kdim + kKS - 1) / kKS;
 
   if (tid < MT) {
-    int src = -1, ex = 0, slot = -1;
-    if (tid < mlen) {
-      const int m = m0 + tid;
-      slot = p.sorted_slot[m];
-      if constexpr (kChunked) {
-        src = m;
-        int mn = INT_MAX;
-        for (int c = 0; c < p.a_nch; ++c) mn = min(mn, p.a_chunkexp[(size_t)m * p.a_nch + c]);
-        ex = mn;
-      } else {
-        src = slot / p.topk;
-        ex = p.a_rowexp[src];
-      }
+    // rows past the tile's end read the last row again; their results are dropped
+    const int m = m0 + min(tid, mlen - 1);
+    int src, ex;
+    if constexpr (kChunked) {
+      src = m;
+      ex = p.a_chunkexp[(size_t)m * p.a_nch];
+    } else {
+      src = p.sorted_slot[m] / p.topk;
+      ex = p.a_rowexp[src];
     }
     s_src[tid] = src;
     s_exp[tid] = ex;
-    s_slot[tid] = slot;
+    s_slot[tid] = tid < mlen ? p.sorted_slot[m] : -1;
   }
   __syncthreads();
+
+  // ---------------------------------------------------------------- ring fill
+  // weight row (stored orientation: output column lc of the tile, clamped)
+  auto wrow_stored = [&](int lc) -> const uint8_t* {
+    if constexpr (KIND == kGateUp) {
+      const int col = min(n0 + (lc & (kHChunk - 1)), I - 1);
+      return (lc < kHChunk ? p.L.wg : p.L.wu) + ((size_t)e * I + col) * (size_t)(H / 2);
+    } else {
+      const int col = min(n0 + lc, H - 1);
+      return p.L.wd + ((size_t)e * H + col) * (size_t)(I / 2);
+    }
+  };
+  // weight row (transposed orientation: contraction index kk, clamped)
+  auto wrow_t = [&](int kk) -> const uint8_t* {
+    if constexpr (KIND == kDownBwd) {
+      return p.L.wd + ((size_t)e * H + kk) * (size_t)(I / 2);
+    } else {
+      const bool up = kk >= I;
+      const size_t r = (size_t)e * I + (up ? kk - I : kk);
+      return (up ? p.L.wu : p.L.wg) + r * (size_t)(H / 2);
+    }
+  };
+
+  // Issue one stage: activation, weight and scale DMAs, always kDmaPerStage of
+  // them per wave (the ring waits count on it).
+  auto issue = [&](int ss) {
+    const int k0 = ss * kKS;
+    const uint32_t st = lds_addr(ring) + (ss % kStages) * kStage;
+#pragma unroll
+    for (int i = 0; i < kAInst; ++i) {
+      const int u = w * kAInst + i;
+      const int row = kRowsPerInst * u + ((lane >> 3) & (kRowsPerInst - 1));
+      const int c = (lane & 7) ^ ((row & 7) ^ ((row >> 3) & 1));
+      int k = k0 + 8 * c;
+      if (k >= kdim) k = k0;
+      const uint16_t* g = p.a_src + (size_t)s_src[row] * p.lda + k;
+      if (MT != 16 || lane < 32) dma16(g, st + 128 * kRowsPerInst * u);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int u = w * 2 + i;
+      const uint8_t* g;
+      if constexpr (kT) {
+        const int row = 8 * u + (lane >> 3);
+        const int c16 = (lane & 7) ^ ((row >> 1) & 7);
+        const int kk = min(k0 + row, kdim - 1);
+        int c = n0 + 32 * c16;
+        if (c >= nout) c = n0;
+        g = wrow_t(kk) + c / 2;
+      } else {
+        const int lc = 32 * u + (lane >> 1);
+        int h = (lane & 1) ^ ((lc >> 3) & 1);
+        if (k0 + 32 * h >= kdim) h = 0;
+        g = wrow_stored(lc) + k0 / 2 + 16 * h;
+      }
+      dma16(g, st + kABytes + 1024 * u);
+    }
+    // scales: 1 KB per stage, a quarter per wave (16 lanes x 16 B = 8 fp16 each)
+    {
+      const int q = w * 16 + (lane & 15);
+      const uint16_t* g;
+      if constexpr (kT) {
+        // column group q >> 3 of the tile, contraction rows 8 (q & 7) .. + 7 of the stage
+        const int cg = min(n0 / kGroup + (q >> 3), nout / kGroup - 1);
+        const int kk = min(k0 + 8 * (q & 7), kdim - 8);
+        if constexpr (KIND == kDownBwd) {
+          g = p.sct0 + ((size_t)e * (I / kGroup) + cg) * H + kk;
+        } else {
+          const bool up = kk >= I;
+          g = (up ? p.sct1 : p.sct0) + ((size_t)e * (H / kGroup) + cg) * I + (up ? kk - I : kk);
+        }
+      } else {
+        // group (q >> 5) of the stage, output columns 8 (q & 31) .. + 7 of the tile
+        const int gi = min(k0 / kGroup + (q >> 5), ngroups - 1);
+        const int lc = 8 * (q & 31);
+        if constexpr (KIND == kGateUp) {
+          const int n = min(n0 + (lc & (kHChunk - 1)), I - 8);
+          g = (lc < kHChunk ? p.sct0 : p.sct1) + ((size_t)e * ngroups + gi) * I + n;
+        } else {
+          const int n = min(n0 + lc, H - 8);
+          g = p.sct0 + ((size_t)e * ngroups + gi) * H + n;
+        }
+      }
+      if (lane < 16) dma16(g, st + kABytes + kWBytes + 256 * w);
+    }
+  };
 
   floatx4 acc[MB][4];
 #pragma unroll
@@ -166,289 +306,237 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // ---------------------------------------------------------------- staging helpers
-  u32x4 areg[kAChunks];
-  auto load_a = [&](int k0) {
-#pragma unroll
-    for (int t = 0; t < kAChunks; ++t) {
-      const int q = tid + 256 * t;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (q < MT * 8) {
-        const int row = q >> 3, k = k0 + 8 * (q & 7);
-        const int src = s_src[row];
-        if (src >= 0 && k < kdim) {
-          v = *reinterpret_cast<const u32x4*>(p.a_src + (size_t)src * p.lda + k);
-          if constexpr (kChunked) {
-            int c;
-            if constexpr (KIND == kDown)
-              c = k / p.a_chunkw;
-            else
-              c = k < I ? k / p.a_chunkw : p.a_nch / 2 + (k - I) / p.a_chunkw;
-            const int d = s_exp[row] - p.a_chunkexp[(size_t)src * p.a_nch + c];
-            if (d != 0) {
-              const uint16_t sb = half_pow2_bits(d);
-              const half2_t s2 = __builtin_bit_cast(half2_t, (uint32_t)sb | ((uint32_t)sb << 16));
-              v.x = mul_half2(v.x, s2);
-              v.y = mul_half2(v.y, s2);
-              v.z = mul_half2(v.z, s2);
-              v.w = mul_half2(v.w, s2);
-            }
-          }
-        }
-      }
-      areg[t] = v;
-    }
-  };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int t = 0; t < kAChunks; ++t) {
-      const int q = tid + 256 * t;
-      if (q < MT * 8) *reinterpret_cast<u32x4*>(&As[buf][(q >> 3) * kAP + 8 * (q & 7)]) = areg[t];
-    }
-  };
+  issue(0);
+  if (nss > 1) issue(1);
 
-  // stored orientation: each lane's 16 nibbles of its output column for one super-step
-  uint32_t breg[4][2];
-  uint32_t bscale[4];  // fp16 scale in both halves
-  auto load_b = [&](int k0, uint32_t (&bw)[4][2], uint32_t (&bs)[4]) {
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const uint8_t* W;
-      const uint16_t* S;
-      size_t row;
-      int rk;
-      bool valid;
-      if constexpr (KIND == kGateUp) {
-        const int col = n0 + w * 32 + (f & 1) * 16 + lr;
-        valid = col < I;
-        W = f < 2 ? p.L.wg : p.L.wu;
-        S = f < 2 ? p.L.sg : p.L.su;
-        row = (size_t)e * I + col;
-        rk = H;
-      } else {
-        const int col = n0 + w * 64 + f * 16 + lr;
-        valid = col < H;
-        W = p.L.wd;
-        S = p.L.sd;
-        row = (size_t)e * H + col;
-        rk = I;
-      }
-      const int k = k0 + 16 * lg;
-      uint2 v = make_uint2(0u, 0u);
-      uint32_t sh = 0u;
-      if (valid && k < kdim) {
-        v = *reinterpret_cast<const uint2*>(W + row * (size_t)(rk / 2) + k / 2);
-        const float sf = bf16_to_float(S[row * (size_t)(rk / kGroup) + k / kGroup]);
-        if (!scale_in_domain(sf) && (lg & 1) == 0) atomicAdd(p.bad_scales, 1ull);
-        sh = float_to_half_bits(sf);
-      }
-      bw[f][0] = v.x;
-      bw[f][1] = v.y;
-      bs[f] = sh | (sh << 16);
-    }
-  };
-
-  // contraction over weight rows: raw packed rows and their scales into LDS
-  u32x4 wreg[2];
-  uint16_t sreg[2];
-  auto load_w = [&](int k0) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int q = tid + 256 * t;
-      const int row = q >> 3, c16 = q & 7;
-      const int kk = k0 + row, c = n0 + 32 * c16;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      uint16_t sh = 0;
-      if (kk < kdim && c < nout) {
-        const uint8_t* W;
-        const uint16_t* S;
-        size_t wrow;
-        int rk;
-        if constexpr (KIND == kDownBwd) {
-          W = p.L.wd;
-          S = p.L.sd;
-          wrow = (size_t)e * H + kk;
-          rk = I;
-        } else {
-          const bool up = kk >= I;
-          W = up ? p.L.wu : p.L.wg;
-          S = up ? p.L.su : p.L.sg;
-          wrow = (size_t)e * I + (up ? kk - I : kk);
-          rk = H;
-        }
-        v = *reinterpret_cast<const u32x4*>(W + wrow * (size_t)(rk / 2) + c / 2);
-        const float sf = bf16_to_float(S[wrow * (size_t)(rk / kGroup) + c / kGroup]);
-        if (!scale_in_domain(sf)) atomicAdd(p.bad_scales, 1ull);
-        sh = float_to_half_bits(sf);
-      }
-      wreg[t] = v;
-      sreg[t] = sh;
-    }
-  };
-  auto store_w = [&](int buf) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int q = tid + 256 * t;
-      const int row = q >> 3, c16 = q & 7;
-      *reinterpret_cast<u32x4*>(&Wl[buf][row * kWP + 16 * c16]) = wreg[t];
-      Sc[buf][c16 * kKS + perm_pos(row)] = sreg[t];
-    }
-  };
-
-  auto compute = [&](int cur) {
+  // ---------------------------------------------------------------- main loop (fp16)
+  const int aswz = (lr & 7) ^ ((lr >> 3) & 1);  // activation swizzle of rows 16 * mb + lr
+  const int a_off0 = lr * 128 + 16 * ((2 * lg) ^ aswz);
+  const int a_off1 = lr * 128 + 16 * ((2 * lg + 1) ^ aswz);
+  // One stage from the ring.  In a final half stage (contraction length an odd
+  // multiple of 32) lanes 32..63 hold values past the end: their weights are zeroed.
+  auto compute = [&](const uint8_t* st, auto tail_tag) {
+    constexpr bool kTail = decltype(tail_tag)::value;
+    const uint32_t km = (kTail && lg >= 2) ? 0u : 0xffffffffu;
+    const uint8_t* As = st;
+    const uint8_t* Bs = st + kABytes;
+    const uint16_t* Sc = reinterpret_cast<const uint16_t*>(st + kABytes + kWBytes);
     if constexpr (kT) {
       v2i_t tr[4];
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
         const int lc = local_col<KIND>(w, f);
-        tr[f] = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_v2i_ptr)(&Wl[cur][(16 * lg + lr) * kWP + lc / 2]));
+        const int slot = (lc >> 5) ^ ((lr >> 1) & 7);
+        tr[f] = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
+            (lds_v2i_ptr)(Bs + (16 * lg + lr) * 128 + 16 * slot + 8 * ((lc >> 4) & 1)));
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        u32x4 af[MB];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          af[mb] = *reinterpret_cast<const u32x4*>(&As[cur][(mb * 16 + lr) * kAP + 16 * lg + 8 * j]);
+        u32x4 bf[4];
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
-          const int cg = local_col<KIND>(w, f) / 32;
+          const int cg = local_col<KIND>(w, f) >> 5;
           u32x4 sp;  // 8 fp16 scales written as 16-bit values: copy, do not type-pun
-          __builtin_memcpy(&sp, &Sc[cur][cg * kKS + 16 * lg + 8 * j], sizeof(sp));
+          __builtin_memcpy(&sp, &Sc[cg * kKS + 16 * lg + 8 * j], sizeof(sp));
           const uint32_t word = j ? (uint32_t)tr[f].y : (uint32_t)tr[f].x;
           // bit-cast whole scalars: clang's bit_cast of an ext-vector component reads component 0
           const uint32_t s0 = sp.x, s1 = sp.y, s2 = sp.z, s3 = sp.w;
-          const u32x4 bf = decode_dword_perm(word, __builtin_bit_cast(half2_t, s0), __builtin_bit_cast(half2_t, s1),
-                                             __builtin_bit_cast(half2_t, s2), __builtin_bit_cast(half2_t, s3));
+          bf[f] = decode_dword_perm(word, __builtin_bit_cast(half2_t, s0), __builtin_bit_cast(half2_t, s1),
+                                    __builtin_bit_cast(half2_t, s2), __builtin_bit_cast(half2_t, s3)) &
+                  km;
+        }
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb) acc[mb][f] = mfma_f16(af[mb], bf, acc[mb][f]);
+        for (int mb = 0; mb < MB; ++mb) {
+          const u32x4 af = *reinterpret_cast<const u32x4*>(As + mb * 2048 + (j ? a_off1 : a_off0));
+#pragma unroll
+          for (int f = 0; f < 4; ++f) acc[mb][f] = mfma_f16(af, bf[f], acc[mb][f]);
         }
       }
     } else {
+      uint32_t raw[4][2];
+      uint32_t bs[4];
+      const int bsw = 16 * ((lg >> 1) ^ ((lr >> 3) & 1)) + 8 * (lg & 1);
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const int lc = local_col<KIND>(w, f) + lr;
+        const uint2 v = *reinterpret_cast<const uint2*>(Bs + lc * 32 + bsw);
+        raw[f][0] = v.x;
+        raw[f][1] = v.y;
+        const uint32_t sh = Sc[(lg >> 1) * kNT + local_col<KIND>(w, f) + perm_pos(lr)];
+        bs[f] = sh | (sh << 16);
+      }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        u32x4 af[MB];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          af[mb] = *reinterpret_cast<const u32x4*>(&As[cur][(mb * 16 + lr) * kAP + 16 * lg + 8 * j]);
+        u32x4 bf[4];
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
-          const half2_t s2 = __builtin_bit_cast(half2_t, bscale[f]);
-          const u32x4 bf = decode_dword_perm(breg[f][j], s2, s2, s2, s2);
+          const half2_t s2 = __builtin_bit_cast(half2_t, bs[f]);
+          bf[f] = decode_dword_perm(raw[f][j], s2, s2, s2, s2) & km;
+        }
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb) acc[mb][f] = mfma_f16(af[mb], bf, acc[mb][f]);
+        for (int mb = 0; mb < MB; ++mb) {
+          const u32x4 af = *reinterpret_cast<const u32x4*>(As + mb * 2048 + (j ? a_off1 : a_off0));
+#pragma unroll
+          for (int f = 0; f < 4; ++f) acc[mb][f] = mfma_f16(af, bf[f], acc[mb][f]);
         }
       }
     }
   };
 
-  // ---------------------------------------------------------------- main loop (fp16)
-  load_a(0);
-  if constexpr (kT) {
-    load_w(0);
-    store_w(0);
-  } else {
-    load_b(0, breg, bscale);
-  }
-  store_a(0);
-  __syncthreads();
   for (int ss = 0; ss < nss; ++ss) {
-    const int cur = ss & 1;
-    const bool more = ss + 1 < nss;
-    uint32_t bnext[4][2];
-    uint32_t snext[4];
-    if (more) {
-      load_a((ss + 1) * kKS);
-      if constexpr (kT)
-        load_w((ss + 1) * kKS);
-      else
-        load_b((ss + 1) * kKS, bnext, snext);
-    }
-    compute(cur);
-    if (more) {
-      store_a(cur ^ 1);
-      if constexpr (kT) {
-        store_w(cur ^ 1);
-      } else {
-#pragma unroll
-        for (int f = 0; f < 4; ++f) {
-          breg[f][0] = bnext[f][0];
-          breg[f][1] = bnext[f][1];
-          bscale[f] = snext[f];
-        }
-      }
-    }
-    __syncthreads();
+    // this wave's loads of stage ss have landed once at most the next stage's
+    // DMAs are outstanding; the barrier makes every wave's loads visible and
+    // frees the slot that stage ss + 2 refills
+    if (ss + 1 < nss)
+      wait_vm_lgkm<kDmaPerStage>();
+    else
+      wait_vm_lgkm<0>();
+    __builtin_amdgcn_s_barrier();
+    if (ss + 2 < nss) issue(ss + 2);
+
+    const uint8_t* st = ring + (ss % kStages) * kStage;
+    if ((kdim & (kKS - 1)) != 0 && ss == nss - 1)
+      compute(st, BoolTag<true>{});
+    else
+      compute(st, BoolTag<false>{});
   }
+  __syncthreads();  // every wave is done with the ring before it is reused
+
+  // out of the row's power-of-two scaled domain
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ex = s_exp[mb * 16 + lg * 4 + i];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) acc[mb][f][i] = ldexpf(acc[mb][f][i], -ex);
+    }
 
   // ---------------------------------------------------------------- LoRA K-steps (bf16 hi/lo)
-  const int KL = (KIND == kGateUp || KIND == kGateUpBwd) ? 2 * R : R;
-  for (int q0 = 0; q0 < KL; q0 += kGroup) {
-    u32x4 ah[MB], al[MB];
+  // One 32-value group of the LoRA contraction at a time, both operands staged
+  // in the (now idle) ring: the side product arrives as bf16 hi/lo planes
+  // already times the LoRA scale and is copied by DMA into the activation
+  // layout (hi chunks 0..3, lo chunks 4..7); the fp32 LoRA matrix entries are
+  // split into bf16 hi/lo on the way in.  For gate/up the two halves of the
+  // contraction (x A_g^T | x A_u^T) meet only their own half of the columns.
+  {
+    constexpr bool kTwoHalves = (KIND == kGateUp || KIND == kGateUpBwd);
+    const int RP = (R + kGroup - 1) / kGroup * kGroup;  // one padded half
+    const int KLP = kTwoHalves ? 2 * RP : RP;
+    uint8_t* la = ring;            // [MT][8 chunks of 16 B], activation swizzle
+    uint8_t* lb = ring + kABytes;  // stored: [256 columns][8 chunks]; transposed: hi, lo planes [32][kLBP]
+    for (int q0 = 0; q0 < KLP; q0 += kGroup) {
+      const int half = q0 >= RP ? 1 : 0;
+      const int qh = q0 - half * RP;  // first contraction index of the group within its half
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int row = mb * 16 + lr;
-      const float coef = ldexpf(p.sc, s_exp[row]);
-      uint16_t hi[8], lo[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int q = q0 + 8 * lg + i;
-        float v = 0.f;
-        if (row < mlen && q < KL) {
-          const size_t m = (size_t)(m0 + row);
-          if constexpr (KIND == kGateUp || KIND == kGateUpBwd)
-            v = q < R ? p.la0[m * R + q] : p.la1[m * R + (q - R)];
-          else
-            v = p.la0[m * R + q];
-          v *= coef;
-        }
-        split_bf16(v, hi[i], lo[i]);
+      for (int i = 0; i < kAInst; ++i) {
+        const int u = w * kAInst + i;
+        const int row = kRowsPerInst * u + ((lane >> 3) & (kRowsPerInst - 1));
+        const int c = (lane & 7) ^ ((row & 7) ^ ((row >> 3) & 1));
+        const size_t m = (size_t)(m0 + min(row, mlen - 1));
+        const uint16_t* g = p.lsplit + m * (size_t)(2 * KLP) + (c >> 2) * KLP + q0 + 8 * (c & 3);
+        if (MT != 16 || lane < 32) dma16(g, lds_addr(la) + 128 * kRowsPerInst * u);
       }
-      ah[mb] = pack_bf16x8(hi);
-      al[mb] = pack_bf16x8(lo);
-    }
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      uint16_t hi[8], lo[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int q = q0 + 8 * lg + i;
-        float v = 0.f;
+      if constexpr (!kT) {
+        // thread -> output column lc = tid, the group's 32 entries of its row
+        const int lc = tid;
+        const float* brow;
+        bool ok = true;
         if constexpr (KIND == kGateUp) {
-          const int n = n0 + w * 32 + (f & 1) * 16 + lr;
-          if (n < I) {
-            if (f < 2 && q < R) v = p.L.bg[((size_t)e * I + n) * R + q];
-            if (f >= 2 && q >= R && q < 2 * R) v = p.L.bu[((size_t)e * I + n) * R + (q - R)];
-          }
-        } else if constexpr (KIND == kDown) {
-          const int n = n0 + w * 64 + f * 16 + lr;
-          if (n < H && q < R) v = p.L.bd[((size_t)e * H + n) * R + q];
-        } else if constexpr (KIND == kDownBwd) {
-          const int c = n0 + w * 64 + f * 16 + lr;
-          if (c < I && q < R) v = p.L.ad[((size_t)e * R + q) * I + c];
+          const int n = min(n0 + (lc & (kHChunk - 1)), I - 1);
+          brow = (lc < kHChunk ? p.L.bg : p.L.bu) + ((size_t)e * I + n) * R;
+          ok = (lc < kHChunk) == (half == 0);
         } else {
-          const int c = n0 + w * 64 + f * 16 + lr;
-          if (c < H) {
-            if (q < R)
-              v = p.L.ag[((size_t)e * R + q) * H + c];
-            else if (q < 2 * R)
-              v = p.L.au[((size_t)e * R + (q - R)) * H + c];
-          }
+          const int n = min(n0 + lc, H - 1);
+          brow = p.L.bd + ((size_t)e * H + n) * R;
         }
-        split_bf16(v, hi[i], lo[i]);
+        const int sw = (lc & 7) ^ ((lc >> 3) & 1);
+#pragma unroll 1
+        for (int c8 = 0; c8 < 4; ++c8) {
+          float v[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int q = qh + 8 * c8 + i;
+            const float x = brow[min(q, R - 1)];
+            v[i] = (ok && q < R) ? x : 0.f;
+          }
+          u32x4 hi, lo;
+          split8(v, hi, lo);
+          *reinterpret_cast<u32x4*>(lb + lc * 128 + 16 * (c8 ^ sw)) = hi;
+          *reinterpret_cast<u32x4*>(lb + lc * 128 + 16 * ((4 + c8) ^ sw)) = lo;
+        }
+      } else {
+        // thread -> contraction row qi of the group, 32 consecutive output columns
+        const int qi = tid >> 3, c32 = 32 * (tid & 7);
+        const int q = qh + qi;
+        const int c = n0 + c32 < nout ? n0 + c32 : n0;
+        const float* src;
+        if constexpr (KIND == kDownBwd)
+          src = p.L.ad + ((size_t)e * R + min(q, R - 1)) * I + c;
+        else
+          src = (half ? p.L.au : p.L.ag) + ((size_t)e * R + min(q, R - 1)) * H + c;
+#pragma unroll 1
+        for (int c8 = 0; c8 < 4; ++c8) {
+          const float4 x0 = *reinterpret_cast<const float4*>(src + 8 * c8);
+          const float4 x1 = *reinterpret_cast<const float4*>(src + 8 * c8 + 4);
+          const bool ok = q < R;
+          const float v[8] = {ok ? x0.x : 0.f, ok ? x0.y : 0.f, ok ? x0.z : 0.f, ok ? x0.w : 0.f,
+                              ok ? x1.x : 0.f, ok ? x1.y : 0.f, ok ? x1.z : 0.f, ok ? x1.w : 0.f};
+          u32x4 hi, lo;
+          split8(v, hi, lo);
+          *reinterpret_cast<u32x4*>(lb + qi * kLBP + 2 * (c32 + 8 * c8)) = hi;
+          *reinterpret_cast<u32x4*>(lb + 32 * kLBP + qi * kLBP + 2 * (c32 + 8 * c8)) = lo;
+        }
       }
-      const u32x4 bh = pack_bf16x8(hi), bl = pack_bf16x8(lo);
+      wait_vm_lgkm<0>();
+      __builtin_amdgcn_s_barrier();
+
+      // plane columns at or past R within the half hold no product: mask them (they may be stale)
+      const int nval = min(max(R - (qh + 8 * lg), 0), 8);
+      u32x4 keep;
+      keep.x = (nval > 0 ? 0xffffu : 0u) | (nval > 1 ? 0xffff0000u : 0u);
+      keep.y = (nval > 2 ? 0xffffu : 0u) | (nval > 3 ? 0xffff0000u : 0u);
+      keep.z = (nval > 4 ? 0xffffu : 0u) | (nval > 5 ? 0xffff0000u : 0u);
+      keep.w = (nval > 6 ? 0xffffu : 0u) | (nval > 7 ? 0xffff0000u : 0u);
+      u32x4 bh[4], bl[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const int lc = local_col<KIND>(w, f);
+        if constexpr (!kT) {
+          bh[f] = *reinterpret_cast<const u32x4*>(lb + (lc + lr) * 128 + 16 * (lg ^ aswz));
+          bl[f] = *reinterpret_cast<const u32x4*>(lb + (lc + lr) * 128 + 16 * ((4 + lg) ^ aswz));
+        } else {
+          // lanes 4r..4r+3 address contraction row 8 lg + r (then + 4), columns 4 (lr & 3)..;
+          // each lane receives 4 consecutive rows of its column per read
+          const uint8_t* base = lb + (8 * lg + (lr >> 2)) * kLBP + 2 * (lc + 4 * (lr & 3));
+          const v4s_t h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(base));
+          const v4s_t h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(base + 4 * kLBP));
+          const v4s_t l0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(base + 32 * kLBP));
+          const v4s_t l1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(base + 36 * kLBP));
+          bh[f] = u32x4{pack2(h0.x, h0.y), pack2(h0.z, h0.w), pack2(h1.x, h1.y), pack2(h1.z, h1.w)};
+          bl[f] = u32x4{pack2(l0.x, l0.y), pack2(l0.z, l0.w), pack2(l1.x, l1.y), pack2(l1.z, l1.w)};
+        }
+      }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        acc[mb][f] = mfma_bf16(ah[mb], bh, acc[mb][f]);
-        acc[mb][f] = mfma_bf16(ah[mb], bl, acc[mb][f]);
-        acc[mb][f] = mfma_bf16(al[mb], bh, acc[mb][f]);
+        const u32x4 ah = *reinterpret_cast<const u32x4*>(la + mb * 2048 + lr * 128 + 16 * (lg ^ aswz)) & keep;
+        const u32x4 al = *reinterpret_cast<const u32x4*>(la + mb * 2048 + lr * 128 + 16 * ((4 + lg) ^ aswz)) & keep;
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          if (KIND == kGateUp && (f >> 1) != half) continue;
+          acc[mb][f] = mfma_bf16(ah, bh[f], acc[mb][f]);
+          acc[mb][f] = mfma_bf16(ah, bl[f], acc[mb][f]);
+          acc[mb][f] = mfma_bf16(al, bh[f], acc[mb][f]);
+        }
       }
+      __syncthreads();  // the group is consumed before the next one (or the epilogue) reuses the ring
     }
   }
 
   // ---------------------------------------------------------------- epilogues
-  // the activation tile is free now: reuse it for the cross-wave row reductions
-  float* red = reinterpret_cast<float*>(&As[0][0]);  // [3][4 waves][MT]
+  // the ring is free now: reuse it for the cross-wave row reductions; acc holds
+  // the plain sums
+  float* red = reinterpret_cast<float*>(ring);  // [12][MT]
   const float limit = p.limit;
   if constexpr (KIND == kGateUp) {
     // pass 1: g, u saved in fp32, row maxima of h over the tile's 128 columns
@@ -459,14 +547,13 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
         const int row = mb * 16 + lg * 4 + i;
         const bool vrow = row < mlen;
         const size_t m = (size_t)(m0 + row);
-        const int ex = s_exp[row];
         float mx = 0.f;
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
           const int col = n0 + w * 32 + f * 16 + lr;
           const bool valid = vrow && col < I;
-          const float g = ldexpf(acc[mb][f][i], -ex);
-          const float u = ldexpf(acc[mb][f + 2][i], -ex);
+          const float g = acc[mb][f][i];
+          const float u = acc[mb][f + 2][i];
           if (valid) {
             p.gsave[m * I + col] = g;
             p.usave[m * I + col] = u;
@@ -489,7 +576,6 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
         const int row = mb * 16 + lg * 4 + i;
         if (row >= mlen) continue;
         const size_t m = (size_t)(m0 + row);
-        const int ex = s_exp[row];
         const float mx = fmaxf(fmaxf(red[row], red[MT + row]), fmaxf(red[2 * MT + row], red[3 * MT + row]));
         const int pe = pow2_exponent_for(mx);
         if (w == 0 && lr == 0) p.hexp[m * p.h_nch + nt] = pe;
@@ -498,7 +584,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
           const int col = n0 + w * 32 + f * 16 + lr;
           if (col >= I) continue;
           float gp, up, mg, mu;
-          clamp_swiglu(ldexpf(acc[mb][f][i], -ex), ldexpf(acc[mb][f + 2][i], -ex), limit, gp, up, mg, mu);
+          clamp_swiglu(acc[mb][f][i], acc[mb][f + 2][i], limit, gp, up, mg, mu);
           p.hh[m * I + perm_pos(col)] = float_to_half_bits(ldexpf(gp * sigmoid_f(gp) * up, pe));
         }
       }
@@ -511,11 +597,10 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
         if (row >= mlen) continue;
         const int slot = s_slot[row];
         const float wgt = (KIND == kDown) ? p.rw[slot] : 1.f;
-        const int ex = s_exp[row];
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
           const int col = n0 + w * 64 + f * 16 + lr;
-          if (col < H) p.stage[(size_t)slot * H + col] = wgt * ldexpf(acc[mb][f][i], -ex);
+          if (col < H) p.stage[(size_t)slot * H + col] = wgt * acc[mb][f][i];
         }
       }
   } else {  // kDownBwd
@@ -528,13 +613,12 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
         const bool vrow = row < mlen;
         const size_t m = (size_t)(m0 + row);
         const float wgt = vrow ? p.rw[s_slot[row]] : 0.f;
-        const int ex = s_exp[row];
         float dr = 0.f, mxg = 0.f, mxu = 0.f;
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
           const int col = n0 + w * 64 + f * 16 + lr;
           if (!(vrow && col < I)) continue;
-          const float gh = ldexpf(acc[mb][f][i], -ex);
+          const float gh = acc[mb][f][i];
           float gp, up, mg, mu;
           clamp_swiglu(p.gsave[m * I + col], p.usave[m * I + col], limit, gp, up, mg, mu);
           const float sg = sigmoid_f(gp);
@@ -568,7 +652,6 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
         if (row >= mlen) continue;
         const size_t m = (size_t)(m0 + row);
         const float wgt = p.rw[s_slot[row]];
-        const int ex = s_exp[row];
         const int pg = pow2_exponent_for(fmaxf(fmaxf(red[4 * MT + row], red[5 * MT + row]),
                                                fmaxf(red[6 * MT + row], red[7 * MT + row])));
         const int pu = pow2_exponent_for(fmaxf(fmaxf(red[8 * MT + row], red[9 * MT + row]),
@@ -582,7 +665,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
         for (int f = 0; f < 4; ++f) {
           const int col = n0 + w * 64 + f * 16 + lr;
           if (col >= I) continue;
-          const float gh = ldexpf(acc[mb][f][i], -ex);
+          const float gh = acc[mb][f][i];
           float gp, up, mg, mu;
           clamp_swiglu(p.gsave[m * I + col], p.usave[m * I + col], limit, gp, up, mg, mu);
           const float sg = sigmoid_f(gp);
@@ -630,7 +713,6 @@ void launch_gemm(GemmKind kind, const Dims& d, const WsMap& w, void* ws, const L
   p.tile_e = ws_ptr<int32_t>(ws, w.tile_e);
   p.tile_m0 = ws_ptr<int32_t>(ws, w.tile_m0);
   p.counters = ws_ptr<unsigned long long>(ws, w.counters);
-  p.bad_scales = ws_ptr<unsigned long long>(ws, w.counters) + kBadScales;
   p.L = L;
   p.rw = route_weights;
   p.gsave = ws_ptr<float>(ws, w.g);
@@ -643,6 +725,10 @@ void launch_gemm(GemmKind kind, const Dims& d, const WsMap& w, void* ws, const L
   p.dguexp = ws_ptr<int32_t>(ws, w.dguexp);
   p.dg_nch = (int)w.dg_nch;
   p.drpart = ws_ptr<float>(ws, w.drpart);
+  p.lsplit = ws_ptr<uint16_t>(ws, w.lsplit);
+  const bool gu = (kind == kGateUp || kind == kGateUpBwd);
+  p.sct0 = ws_ptr<uint16_t>(ws, gu ? w.sct_g : w.sct_d);
+  p.sct1 = ws_ptr<uint16_t>(ws, w.sct_u);
   p.dr_nt = (int)w.dr_nt;
   switch (kind) {
     case kGateUp:
@@ -650,34 +736,26 @@ void launch_gemm(GemmKind kind, const Dims& d, const WsMap& w, void* ws, const L
       p.a_src = ws_ptr<uint16_t>(ws, w.xh);
       p.a_rowexp = ws_ptr<int32_t>(ws, w.xexp);
       p.lda = d.H;
-      p.la0 = ws_ptr<float>(ws, w.ua);
-      p.la1 = ws_ptr<float>(ws, w.ub);
       break;
     case kDown:
       p.n_ntiles = (int)((d.H + kNT - 1) / kNT);
       p.a_src = ws_ptr<uint16_t>(ws, w.hh);
       p.a_chunkexp = ws_ptr<int32_t>(ws, w.hexp);
       p.a_nch = (int)w.h_nch;
-      p.a_chunkw = kHChunk;
       p.lda = d.I;
-      p.la0 = ws_ptr<float>(ws, w.ud);
       break;
     case kDownBwd:
       p.n_ntiles = (int)((d.I + kNT - 1) / kNT);
       p.a_src = ws_ptr<uint16_t>(ws, w.dyh);
       p.a_rowexp = ws_ptr<int32_t>(ws, w.dyexp);
       p.lda = d.H;
-      p.la0 = ws_ptr<float>(ws, w.dyb);
       break;
     case kGateUpBwd:
       p.n_ntiles = (int)((d.H + kNT - 1) / kNT);
       p.a_src = ws_ptr<uint16_t>(ws, w.dgu);
       p.a_chunkexp = ws_ptr<int32_t>(ws, w.dguexp);
       p.a_nch = (int)w.dg_nch;
-      p.a_chunkw = kNT;
       p.lda = 2 * d.I;
-      p.la0 = ws_ptr<float>(ws, w.dgb);
-      p.la1 = ws_ptr<float>(ws, w.dub);
       break;
   }
   const unsigned grid = (unsigned)(w.max_tiles * p.n_ntiles);

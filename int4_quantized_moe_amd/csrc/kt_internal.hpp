@@ -16,10 +16,8 @@ constexpr int kGroupBlock = 1024;  // slots per block of the grouping histogram
 constexpr int kHChunk = 128;       // columns of I per gate/up tile (h exponent chunk)
 constexpr int kNT = 256;           // output columns per tile of the other GEMMs (dG/dU exponent chunk)
 
-// Rows per GEMM tile for a call: the smallest of 16/32/64 that covers the mean
-// number of token-slots per expert (heavier experts take several tiles).  The
-// 128-row tiles run one wave per SIMD and measured slower than 64-row tiles at
-// 16384 tokens, so they are used only on request.
+// Rows per GEMM tile for a call: the smallest of 16/32/64/128 that covers the
+// mean number of token-slots per expert (heavier experts take several tiles).
 // KT_RAWINT4_GEMM_ROWS=16|32|64|128 overrides the choice (tuning and tests).
 inline int choose_gemm_rows(int64_t Ms, int64_t E) {
   if (const char* env = getenv("KT_RAWINT4_GEMM_ROWS")) {
@@ -30,8 +28,14 @@ inline int choose_gemm_rows(int64_t Ms, int64_t E) {
   const int64_t mean = active > 0 ? (Ms + active - 1) / active : 0;
   if (mean <= 16) return 16;
   if (mean <= 32) return 32;
-  return 64;
+  if (mean <= 64) return 64;
+  return 128;
 }
+
+// The LoRA side product that an expert GEMM contracts with (the x A^T of
+// gate/up, h A_d^T, dY B_d, or dG B_g | dU B_u) is handed over as bf16 hi/lo
+// planes with each rank-R half padded to whole 32-value steps: width of one half.
+inline int64_t lora_half_width(int64_t R) { return (R + 31) / 32 * 32; }
 
 // Device counters at the head of the workspace.
 enum Counter { kBadIds = 0, kBadScales = 1, kNumTiles = 2, kNumTilesAux = 3, kNumCounters = 8 };
@@ -42,10 +46,14 @@ struct Dims {
 };
 
 struct WsMap {
+  // fp16 transposed scales of the three projections ([E][K/32][rows]), made by the forward
+  size_t sct_g, sct_u, sct_d;
   // grouping
   size_t counters, counts, offsets, blockcnt, sorted_slot, row_of_slot, tile_e, tile_m0, tile_e_aux, tile_m0_aux;
   // forward state kept for the backward
   size_t xh, xexp, ua, ub, g, u, hh, hexp, ud;
+  // the side product feeding the next expert GEMM, as bf16 hi/lo planes (reused by all four)
+  size_t lsplit;
   // transient staging of per-slot rows (forward y, backward dx)
   size_t stage;
   // backward
@@ -94,13 +102,22 @@ struct RowView {
 
 // out[m, q] = sum_k src(m, k) * W(e, q, k), q < R, k < kdim; W is [E, R, kdim]
 // (rk = true) or [E, kdim, R] (rk = false).  With W2 set, a second product with
-// the same rows goes to out2.
+// the same rows goes to out2.  Also writes the product (both halves side by
+// side) times the LoRA scale into the workspace's bf16 hi/lo planes that the
+// next expert GEMM reads.
 void launch_lora_rowproj(const Dims& d, const WsMap& w, void* ws, const RowView& src, int64_t kdim, const float* W,
-                         const float* W2, bool rk, float* out, float* out2, hipStream_t st);
+                         const float* W2, bool rk, float* out, float* out2, int64_t split_ld, int64_t split_off,
+                         int64_t split_off2, hipStream_t st);
 // G[e, p, q] = (acc ? G : 0) + scale * sum_{m in e} P(m, p) Q(m, q)
 void launch_lora_grad(const Dims& d, const WsMap& w, void* ws, const RowView& P, int64_t np, const RowView& Q,
                       int64_t nq, float* G, int accumulate, float scale, hipStream_t st);
 void launch_fill_zero_f32(float* p, int64_t n, hipStream_t st);
+// scales [E][rows][G] bf16 -> [E][G][rows] fp16, rows within-8 permuted; counts out-of-domain scales
+void launch_scales_t(const uint16_t* s, int64_t E, int64_t rows, int64_t G, uint16_t* out, unsigned long long* bad,
+                     hipStream_t st);
+// one exponent per row for h ([Ms, I], chunks of kHChunk) and dG|dU ([Ms, 2I], chunks of kNT per half)
+void launch_normalize_chunks(uint16_t* buf, int32_t* exps, const int32_t* nrows, int64_t max_rows, int64_t cols,
+                             int64_t split, int nch, int chunkw, hipStream_t st);
 
 void launch_combine(const Dims& d, const float* stage, const int64_t* ids, uint16_t* out, hipStream_t st);
 void launch_droute(const Dims& d, const WsMap& w, void* ws, float* grad_route, hipStream_t st);

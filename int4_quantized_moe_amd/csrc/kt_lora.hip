@@ -45,6 +45,12 @@ struct LoraArgs {
   int64_t kdim, nq;
   float* out;
   float* out2;
+  // the product times split_scale as bf16 hi and lo planes, [rows][2][split_ld]
+  // (column j < nq: hi at split_off + j, lo at split_ld + split_off + j; the W2
+  // half's column j at split_off2 + j)
+  uint16_t* split;
+  int64_t split_ld, split_off, split_off2;
+  float split_scale;
   // gradient: P(m, p), Q(m, q) over the expert's rows; G[e, p, q]
   RowView P, Q;
   int64_t np_, nq_;
@@ -52,17 +58,6 @@ struct LoraArgs {
   int accumulate;
   float scale;
 };
-
-__device__ __forceinline__ uint32_t pack2(uint16_t a, uint16_t b) { return (uint32_t)a | ((uint32_t)b << 16); }
-
-// 8 fp32 values -> bf16 hi and lo planes (16 bytes each)
-__device__ __forceinline__ void split8(const float* v, u32x4& hi, u32x4& lo) {
-  uint16_t h[8], l[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) split_bf16(v[i], h[i], l[i]);
-  hi = u32x4{pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7])};
-  lo = u32x4{pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7])};
-}
 
 // Up to 8 consecutive values of a row view starting at column c (c % 8 == 0), in
 // stored order (for fp16 rows the within-8 permuted order); `nvalid` columns are
@@ -179,6 +174,11 @@ __global__ __launch_bounds__(256) void k_lora_mfma(LoraArgs a) {
         const int64_t j = j0 + f * 16 + lr;
         if (i >= rows || j >= ncols) continue;
         const int64_t m = m0 + i;
+        uint16_t hi, lo;
+        split_bf16(acc[f][t] * a.split_scale, hi, lo);
+        const int64_t sc = j < a.nq ? a.split_off + j : a.split_off2 + (j - a.nq);
+        a.split[m * 2 * a.split_ld + sc] = hi;
+        a.split[m * 2 * a.split_ld + a.split_ld + sc] = lo;
         if (j < a.nq)
           a.out[m * a.nq + j] = acc[f][t];
         else
@@ -290,9 +290,15 @@ static LoraArgs base_args(const Dims& d, const WsMap& w, void* ws) {
 }
 
 void launch_lora_rowproj(const Dims& d, const WsMap& w, void* ws, const RowView& src, int64_t kdim, const float* W,
-                         const float* W2, bool rk, float* out, float* out2, hipStream_t st) {
+                         const float* W2, bool rk, float* out, float* out2, int64_t split_ld, int64_t split_off,
+                         int64_t split_off2, hipStream_t st) {
   if (w.max_tiles_aux == 0) return;
   LoraArgs a = base_args(d, w, ws);
+  a.split = ws_ptr<uint16_t>(ws, w.lsplit);
+  a.split_ld = split_ld;
+  a.split_off = split_off;
+  a.split_off2 = split_off2;
+  a.split_scale = d.sc;
   a.mode = 0;
   a.src = src;
   a.W = W;
