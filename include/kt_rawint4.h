@@ -111,9 +111,9 @@ size_t kt_rawint4_moe_workspace_bytes(const kt_rawint4_moe_layer* layer, int32_t
  * [0, E) are dropped (the slot contributes nothing) and counted.
  * The workspace keeps what the backward needs (grouping, fp32 gate/up
  * pre-activations from which the clamp masks are decided, h, LoRA-A
- * products, and the three scale tensors converted once to fp16 and
- * transposed to [E, K/32, N]: 1/8 the size of the packed codes); a later
- * forward into the same workspace replaces it.
+ * products, and the scale tensors of the experts in use converted once to
+ * fp16 and transposed to [E, K/32, N]: 1/8 the size of the packed codes); a
+ * later forward into the same workspace replaces it.
  * qlen == 0 is a valid no-op.
  */
 int kt_rawint4_moe_fwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const uint16_t* inputs,
@@ -176,8 +176,8 @@ int kt_rawint4_group(const int64_t* expert_ids, int32_t qlen, int32_t top_k, int
  * Synchronising read of the device-side counters of the latest forward in
  * `workspace` (written by kt_rawint4_moe_fwd or kt_rawint4_group): expert ids
  * outside [0, E) and scales outside the numeric domain (each scale of the
- * three projections is checked once per forward).  Host pointers out; either
- * may be NULL.
+ * three projections of every expert the forward routes to is checked once).
+ * Host pointers out; either may be NULL.
  */
 int kt_rawint4_moe_diagnostics(const void* workspace, size_t workspace_bytes, int64_t* bad_ids, int64_t* bad_scales,
                                void* stream);

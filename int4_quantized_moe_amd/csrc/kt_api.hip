@@ -317,9 +317,10 @@ int kt_rawint4_moe_fwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const ui
   {
     PhaseScope ph(kPhScales, st);
     unsigned long long* bad = ws_ptr<unsigned long long>(ws, w.counters) + kBadScales;
-    launch_scales_t(layer->gate_scale, d.E, d.I, d.H / 32, ws_ptr<uint16_t>(ws, w.sct_g), bad, st);
-    launch_scales_t(layer->up_scale, d.E, d.I, d.H / 32, ws_ptr<uint16_t>(ws, w.sct_u), bad, st);
-    launch_scales_t(layer->down_scale, d.E, d.H, d.I / 32, ws_ptr<uint16_t>(ws, w.sct_d), bad, st);
+    const int32_t* offs = ws_ptr<int32_t>(ws, w.offsets);
+    launch_scales_t(layer->gate_scale, d.E, d.I, d.H / 32, offs, ws_ptr<uint16_t>(ws, w.sct_g), bad, st);
+    launch_scales_t(layer->up_scale, d.E, d.I, d.H / 32, offs, ws_ptr<uint16_t>(ws, w.sct_u), bad, st);
+    launch_scales_t(layer->down_scale, d.E, d.H, d.I / 32, offs, ws_ptr<uint16_t>(ws, w.sct_d), bad, st);
   }
   {
     PhaseScope ph(kPhXHalf, st);

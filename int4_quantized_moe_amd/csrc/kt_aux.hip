@@ -46,36 +46,70 @@ void launch_rows_to_half(const uint16_t* src, int64_t rows, int64_t cols, uint16
 // One scale tensor [E][rows][G] (bf16, G = K / 32) to [E][G][rows] in fp16,
 // rows of every aligned group of 8 in the within-8 permuted order, so that a
 // GEMM stage reads the scales of its column (or contraction-row) block as one
-// contiguous run in both orientations.  Scales outside the numeric domain are
-// counted (once each).  64 x 64 tiles pass through LDS so that the reads (along
-// G) and the writes (along rows) are both coalesced.
+// contiguous run in both orientations.  Experts that received no token-slot
+// are skipped.  Scales outside the numeric domain are counted (once each, over
+// the experts in use).  64 x 64 tiles pass through LDS so that the reads
+// (along G, 16 bytes per lane where G allows) and the writes (along rows, 16
+// bytes per lane) are both coalesced.
 __global__ __launch_bounds__(256) void k_scales_t(const uint16_t* __restrict__ s, int64_t rows, int64_t G,
-                                                   uint16_t* __restrict__ out, unsigned long long* bad) {
-  __shared__ uint16_t t[64][66];
+                                                   const int32_t* __restrict__ offsets, uint16_t* __restrict__ out,
+                                                   unsigned long long* bad) {
+  __shared__ uint16_t t[64][72];  // [row][group], 144-byte pitch
   __shared__ int nbad_w[4];
   const int64_t e = blockIdx.z;
+  if (offsets[e + 1] == offsets[e]) return;
   const int64_t r0 = (int64_t)blockIdx.x * 64, g0 = (int64_t)blockIdx.y * 64;
   const uint16_t* se = s + e * rows * G;
   uint16_t* oe = out + e * G * rows;
   int nbad = 0;
-  for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) {
-    const int i = idx >> 6, j = idx & 63;  // row r0 + i, group g0 + j
-    const int64_t r = r0 + i, g = g0 + j;
-    uint16_t h = 0;
-    if (r < rows && g < G) {
-      const float f = bf16_to_float(se[r * G + g]);
-      nbad += scale_in_domain(f) ? 0 : 1;
-      h = float_to_half_bits(f);
+  {
+    const int i = threadIdx.x >> 2, j0 = 16 * (threadIdx.x & 3);  // row r0 + i, groups g0 + j0 .. + 15
+    const int64_t r = r0 + i;
+    uint16_t v[16];
+    if (r < rows && (G & 7) == 0 && g0 + j0 + 16 <= G) {
+      const uint4 a = *reinterpret_cast<const uint4*>(se + r * G + g0 + j0);
+      const uint4 b = *reinterpret_cast<const uint4*>(se + r * G + g0 + j0 + 8);
+      const uint32_t wds[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        v[2 * q] = (uint16_t)(wds[q] & 0xffffu);
+        v[2 * q + 1] = (uint16_t)(wds[q] >> 16);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) v[q] = (r < rows && g0 + j0 + q < G) ? se[r * G + g0 + j0 + q] : 0;
     }
-    t[i][j] = h;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const float f = bf16_to_float(v[q]);
+      nbad += (r < rows && g0 + j0 + q < G && !scale_in_domain(f)) ? 1 : 0;
+      t[i][j0 + q] = float_to_half_bits(f);
+    }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) {
-    const int j = idx >> 6, i = idx & 63;  // group g0 + j, position r0 + i
-    const int64_t g = g0 + j, r = r0 + i;
-    // position i of an aligned group of 8 holds logical row (i & ~7) | ((i & 7) >> 1) | ((i & 1) << 2)
-    const int src = (i & ~7) | ((i & 7) >> 1) | ((i & 1) << 2);
-    if (r < rows && g < G) oe[g * rows + r] = t[src][j];
+  {
+    const int j = threadIdx.x >> 2, i0 = 16 * (threadIdx.x & 3);  // group g0 + j, positions r0 + i0 .. + 15
+    const int64_t g = g0 + j;
+    if (g < G) {
+      uint16_t v[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        // position p of an aligned group of 8 holds logical row (p & ~7) | ((p & 7) >> 1) | ((p & 1) << 2)
+        const int pp = i0 + q;
+        v[q] = t[(pp & ~7) | ((pp & 7) >> 1) | ((pp & 1) << 2)][j];
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (r0 + i0 + 8 * h < rows) {  // rows is a multiple of 8
+          uint4 o;
+          o.x = v[8 * h + 0] | ((uint32_t)v[8 * h + 1] << 16);
+          o.y = v[8 * h + 2] | ((uint32_t)v[8 * h + 3] << 16);
+          o.z = v[8 * h + 4] | ((uint32_t)v[8 * h + 5] << 16);
+          o.w = v[8 * h + 6] | ((uint32_t)v[8 * h + 7] << 16);
+          *reinterpret_cast<uint4*>(oe + g * rows + r0 + i0 + 8 * h) = o;
+        }
+      }
+    }
   }
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) nbad += __shfl_xor(nbad, off);
@@ -87,11 +121,11 @@ __global__ __launch_bounds__(256) void k_scales_t(const uint16_t* __restrict__ s
   }
 }
 
-void launch_scales_t(const uint16_t* s, int64_t E, int64_t rows, int64_t G, uint16_t* out, unsigned long long* bad,
-                     hipStream_t st) {
+void launch_scales_t(const uint16_t* s, int64_t E, int64_t rows, int64_t G, const int32_t* offsets, uint16_t* out,
+                     unsigned long long* bad, hipStream_t st) {
   if (E <= 0 || rows <= 0 || G <= 0) return;
   dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((G + 63) / 64), (unsigned)E);
-  k_scales_t<<<grid, 256, 0, st>>>(s, rows, G, out, bad);
+  k_scales_t<<<grid, 256, 0, st>>>(s, rows, G, offsets, out, bad);
 }
 
 // ---------------------------------------------------------------- one exponent per row

@@ -238,7 +238,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT == 128 ?
 
   // Issue one stage: activation, weight and scale DMAs, always kDmaPerStage of
   // them per wave (the ring waits count on it).
-  auto issue = [&](int ss) {
+  auto issue_any = [&](int ss) {
     const int k0 = ss * kKS;
     const uint32_t st = lds_addr(ring) + (ss % kStages) * kStage;
 #pragma unroll
@@ -295,6 +295,104 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT == 128 ?
           const int n = min(n0 + lc, H - 8);
           g = p.sct0 + ((size_t)e * ngroups + gi) * H + n;
         }
+      }
+      if (lane < 16) dma16(g, st + kABytes + kWBytes + 256 * w);
+    }
+  };
+
+  // Per-lane source addresses of the stage-0 DMAs, advanced by a wave-uniform
+  // offset per stage (whole stages only; a final half stage takes issue_any).
+  const uint16_t* pa[kAInst];
+#pragma unroll
+  for (int i = 0; i < kAInst; ++i) {
+    const int u = w * kAInst + i;
+    const int row = kRowsPerInst * u + ((lane >> 3) & (kRowsPerInst - 1));
+    const int c = (lane & 7) ^ ((row & 7) ^ ((row >> 3) & 1));
+    pa[i] = p.a_src + (size_t)s_src[row] * p.lda + 8 * c;
+  }
+  const uint8_t* pb[2];
+  const uint8_t* pb_up[2];  // gate/up transposed: the up rows (contraction index >= I)
+  int brow[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int u = w * 2 + i;
+    if constexpr (kT) {
+      const int row = 8 * u + (lane >> 3);
+      const int c16 = (lane & 7) ^ ((row >> 1) & 7);
+      int c = n0 + 32 * c16;
+      if (c >= nout) c = n0;
+      brow[i] = row;
+      if constexpr (KIND == kDownBwd) {
+        pb[i] = p.L.wd + ((size_t)e * H + row) * (size_t)(I / 2) + c / 2;
+        pb_up[i] = pb[i];
+      } else {
+        pb[i] = p.L.wg + ((size_t)e * I + row) * (size_t)(H / 2) + c / 2;
+        // up row (kk - I), addressed from kk: offset by -I rows, used only once kk >= I
+        pb_up[i] = p.L.wu + ((int64_t)e * I + row - I) * (int64_t)(H / 2) + c / 2;
+      }
+    } else {
+      const int lc = 32 * u + (lane >> 1);
+      const int h = (lane & 1) ^ ((lc >> 3) & 1);
+      brow[i] = 0;
+      pb[i] = wrow_stored(lc) + 16 * h;
+      pb_up[i] = pb[i];
+    }
+  }
+  const uint16_t* ps;
+  const uint16_t* ps_up;
+  {
+    const int q = w * 16 + (lane & 15);
+    if constexpr (kT) {
+      const int cg = min(n0 / kGroup + (q >> 3), nout / kGroup - 1);
+      if constexpr (KIND == kDownBwd) {
+        ps = p.sct0 + ((size_t)e * (I / kGroup) + cg) * H + 8 * (q & 7);
+        ps_up = ps;
+      } else {
+        ps = p.sct0 + ((size_t)e * (H / kGroup) + cg) * I + 8 * (q & 7);
+        ps_up = p.sct1 + ((int64_t)e * (H / kGroup) + cg) * (int64_t)I + 8 * (q & 7) - I;
+      }
+    } else {
+      const int lc = 8 * (q & 31);
+      if constexpr (KIND == kGateUp) {
+        const int n = min(n0 + (lc & (kHChunk - 1)), I - 8);
+        ps = (lc < kHChunk ? p.sct0 : p.sct1) + ((size_t)e * ngroups + (q >> 5)) * I + n;
+      } else {
+        const int n = min(n0 + lc, H - 8);
+        ps = p.sct0 + ((size_t)e * ngroups + (q >> 5)) * H + n;
+      }
+      ps_up = ps;
+    }
+  }
+  auto issue = [&](int ss) {
+    const int k0 = ss * kKS;
+    if (k0 + kKS > kdim) {
+      issue_any(ss);
+      return;
+    }
+    const uint32_t st = lds_addr(ring) + (ss % kStages) * kStage;
+#pragma unroll
+    for (int i = 0; i < kAInst; ++i)
+      if (MT != 16 || lane < 32) dma16(pa[i] + k0, st + 128 * kRowsPerInst * (w * kAInst + i));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint8_t* g;
+      if constexpr (KIND == kDownBwd) {
+        g = pb[i] + (size_t)k0 * (I / 2);
+      } else if constexpr (KIND == kGateUpBwd) {
+        g = (k0 + brow[i] < I ? pb[i] : pb_up[i]) + (size_t)k0 * (H / 2);
+      } else {
+        g = pb[i] + k0 / 2;
+      }
+      dma16(g, st + kABytes + 1024 * (w * 2 + i));
+    }
+    {
+      const uint16_t* g;
+      if constexpr (KIND == kDownBwd) {
+        g = ps + k0;
+      } else if constexpr (KIND == kGateUpBwd) {
+        g = (k0 + 8 * (lane & 7) < I ? ps : ps_up) + k0;
+      } else {
+        g = ps + (size_t)(k0 / kGroup) * (KIND == kGateUp ? I : H);
       }
       if (lane < 16) dma16(g, st + kABytes + kWBytes + 256 * w);
     }
@@ -383,7 +481,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT == 128 ?
     }
   };
 
-  for (int ss = 0; ss < nss; ++ss) {
+  // whole stages in the loop (one code path, so the accumulators stay put), a
+  // final half stage after it
+  const bool half_tail = (kdim & (kKS - 1)) != 0;
+  const int nfull = half_tail ? nss - 1 : nss;
+  for (int ss = 0; ss < nfull; ++ss) {
     // this wave's loads of stage ss have landed once at most the next stage's
     // DMAs are outstanding; the barrier makes every wave's loads visible and
     // frees the slot that stage ss + 2 refills
@@ -393,12 +495,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT == 128 ?
       wait_vm_lgkm<0>();
     __builtin_amdgcn_s_barrier();
     if (ss + 2 < nss) issue(ss + 2);
-
-    const uint8_t* st = ring + (ss % kStages) * kStage;
-    if ((kdim & (kKS - 1)) != 0 && ss == nss - 1)
-      compute(st, BoolTag<true>{});
-    else
-      compute(st, BoolTag<false>{});
+    compute(ring + (ss % kStages) * kStage, BoolTag<false>{});
+  }
+  if (half_tail) {
+    wait_vm_lgkm<0>();
+    __builtin_amdgcn_s_barrier();
+    compute(ring + ((nss - 1) % kStages) * kStage, BoolTag<true>{});
   }
   __syncthreads();  // every wave is done with the ring before it is reused
 
@@ -522,8 +624,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT == 128 ?
         const u32x4 ah = *reinterpret_cast<const u32x4*>(la + mb * 2048 + lr * 128 + 16 * (lg ^ aswz)) & keep;
         const u32x4 al = *reinterpret_cast<const u32x4*>(la + mb * 2048 + lr * 128 + 16 * ((4 + lg) ^ aswz)) & keep;
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
-          if (KIND == kGateUp && (f >> 1) != half) continue;
+        for (int f = 0; f < 4; ++f) {  // (gate/up: B is zero in the other half's columns)
           acc[mb][f] = mfma_bf16(ah, bh[f], acc[mb][f]);
           acc[mb][f] = mfma_bf16(ah, bl[f], acc[mb][f]);
           acc[mb][f] = mfma_bf16(al, bh[f], acc[mb][f]);

@@ -112,9 +112,10 @@ void launch_lora_rowproj(const Dims& d, const WsMap& w, void* ws, const RowView&
 void launch_lora_grad(const Dims& d, const WsMap& w, void* ws, const RowView& P, int64_t np, const RowView& Q,
                       int64_t nq, float* G, int accumulate, float scale, hipStream_t st);
 void launch_fill_zero_f32(float* p, int64_t n, hipStream_t st);
-// scales [E][rows][G] bf16 -> [E][G][rows] fp16, rows within-8 permuted; counts out-of-domain scales
-void launch_scales_t(const uint16_t* s, int64_t E, int64_t rows, int64_t G, uint16_t* out, unsigned long long* bad,
-                     hipStream_t st);
+// scales [E][rows][G] bf16 -> [E][G][rows] fp16, rows within-8 permuted, experts in use only
+// (offsets from the grouping); counts out-of-domain scales
+void launch_scales_t(const uint16_t* s, int64_t E, int64_t rows, int64_t G, const int32_t* offsets, uint16_t* out,
+                     unsigned long long* bad, hipStream_t st);
 // one exponent per row for h ([Ms, I], chunks of kHChunk) and dG|dU ([Ms, 2I], chunks of kNT per half)
 void launch_normalize_chunks(uint16_t* buf, int32_t* exps, const int32_t* nrows, int64_t max_rows, int64_t cols,
                              int64_t split, int nch, int chunkw, hipStream_t st);

@@ -1,0 +1,105 @@
+"""GPU parity at the full benchmark sizes, in the launch configuration bench.py times.
+
+The two large workloads (384 experts, top-8, hidden 7168, intermediate 2048;
+4096 Zipf-routed tokens at rank 16 and 16384 uniformly routed tokens at rank
+64) run once through the C ABI with the default tile choice.  The oracle cannot
+redo them whole, so it checks what it can compute piece by piece:
+
+* forward output, grad_input and grad_route of sampled tokens: every token's
+  rows depend only on that token's input, routing and output gradient, so the
+  oracle runs on the sampled tokens alone;
+* the six LoRA gradients of sampled experts: an expert's gradients sum over
+  exactly the slots routed to it, so the oracle runs on the tokens that reach
+  it with every other slot dropped (id -1) -- for the Zipf workload this
+  includes the most loaded expert, whose rows span many tiles;
+* at any size: experts no slot reaches get exactly zero gradients.
+
+Bars as in test_parity: relative L2 <= 5e-3 and cosine >= 0.9999 (dRoute
+3e-2).  Each step prints what it does first.
+"""
+
+import numpy as np
+import pytest
+
+import oracle as O
+from int4_quantized_moe_amd import workloads as W
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 5e-3
+COSINE = 0.9999
+DROUTE_REL_L2 = 3e-2
+N_TOKENS = 8
+
+
+def _say(*a):
+    print("[parity-full]", *a, flush=True)
+
+
+def _close(name, actual, expected, rel=REL_L2, cos=COSINE):
+    a = np.asarray(actual, dtype=np.float64)
+    e = np.asarray(expected, dtype=np.float64)
+    assert np.isfinite(a).all(), f"{name}: non-finite values"
+    assert np.count_nonzero(e), f"{name}: reference has no signal"
+    r, c = O.relative_l2_and_cosine(a, e)
+    _say(f"{name}: rel_l2={r:.3e} cos={c:.7f}")
+    assert r <= rel and c >= cos, f"{name}: rel_l2 {r:.3e} cos {c:.7f}"
+
+
+@pytest.mark.parametrize("index", [3, 4])
+def test_full_size_sampled(index):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from int4_quantized_moe_amd import device
+
+    cfg = W.CONFIGS[index]
+    _say(f"{cfg.name}: generating")
+    cfg, weights, batch = W.make_workload(index)
+    _say(f"{cfg.name}: forward + backward on the GPU")
+    dl = device.DeviceLayer(cfg, weights)
+    db = device.DeviceBatch(batch)
+    ws = dl.workspace(db.qlen)
+    out = dl.forward(db.inputs, db.expert_ids, db.route_weights, ws)
+    grads = dl.grad_buffers(fill=7.0)
+    droute = torch.empty(batch.expert_ids.shape, dtype=torch.float32, device="cuda")
+    dx, _ = dl.backward(db.inputs, db.expert_ids, db.route_weights, db.grad_output, ws, grads, accumulate=False,
+                        grad_scale=1.0, grad_route=droute)
+    torch.cuda.synchronize()
+    bad_ids, bad_scales = __import__("int4_quantized_moe_amd")._lib.kt_rawint4_moe_diagnostics(ws)
+    assert bad_ids == 0 and bad_scales == 0
+
+    rng = np.random.default_rng(4242 + index)
+    toks = np.unique(np.concatenate([[0, cfg.qlen - 1], rng.choice(cfg.qlen, N_TOKENS, replace=False)]))
+    _say(f"{cfg.name}: oracle on tokens {toks.tolist()}")
+    ref = O.moe(cfg, weights, batch.inputs[toks], batch.expert_ids[toks], batch.route_weights[toks],
+                batch.grad_output[toks])
+    failures = []
+    for name, a, e, rel, cos in (
+            ("forward", out.float().cpu().numpy()[toks], ref["out"], REL_L2, COSINE),
+            ("dX", dx.float().cpu().numpy()[toks], ref["dx"], REL_L2, COSINE),
+            ("dRoute", droute.cpu().numpy()[toks], ref["droute"], DROUTE_REL_L2, 0.995)):
+        try:
+            _close(f"{cfg.name}.{name}", a, e, rel=rel, cos=cos)
+        except AssertionError as err:
+            failures.append(str(err))
+
+    g = {n: t.cpu().numpy() for n, t in grads.items()}
+    counts = np.bincount(batch.expert_ids.ravel(), minlength=cfg.num_experts)
+    used = np.flatnonzero(counts)
+    experts = {int(used[np.argmax(counts[used])]), int(used[np.argmin(counts[used])]), int(rng.choice(used))}
+    for e in sorted(experts):
+        rows = np.flatnonzero((batch.expert_ids == e).any(axis=1))
+        ids = np.where(batch.expert_ids[rows] == e, e, -1).astype(np.int64)
+        _say(f"{cfg.name}: oracle LoRA gradients of expert {e} ({counts[e]} slots)")
+        ref_e = O.moe(cfg, weights, batch.inputs[rows], ids, batch.route_weights[rows], batch.grad_output[rows])
+        for n in O.LORA_NAMES:
+            try:
+                _close(f"{cfg.name}.expert{e}.{n}", g[n][e], ref_e["grads"][n][e])
+            except AssertionError as err:
+                failures.append(str(err))
+    for e in np.flatnonzero(counts == 0):
+        for n in O.LORA_NAMES:
+            assert np.count_nonzero(g[n][e]) == 0, f"{cfg.name}.{n}: expert {e} has no slot but a gradient"
+    assert not failures, "; ".join(failures)
