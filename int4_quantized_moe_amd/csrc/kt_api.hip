@@ -34,7 +34,6 @@ static void plan_group_part(Planner& pl, WsMap& w, int64_t Ms, int64_t E) {
   w.nb = (Ms + kGroupBlock - 1) / kGroupBlock;
   w.mt = choose_gemm_rows(Ms, E);
   w.max_tiles = Ms / w.mt + (E < Ms ? E : Ms);
-  w.max_tiles_aux = Ms / kMTAux + (E < Ms ? E : Ms);
   w.counters = pl.take(sizeof(unsigned long long) * kNumCounters);
   w.counts = pl.take(sizeof(int32_t) * (size_t)E);
   w.offsets = pl.take(sizeof(int32_t) * (size_t)(E + 1));
@@ -43,8 +42,6 @@ static void plan_group_part(Planner& pl, WsMap& w, int64_t Ms, int64_t E) {
   w.row_of_slot = pl.take(sizeof(int32_t) * (size_t)Ms);
   w.tile_e = pl.take(sizeof(int32_t) * (size_t)w.max_tiles);
   w.tile_m0 = pl.take(sizeof(int32_t) * (size_t)w.max_tiles);
-  w.tile_e_aux = pl.take(sizeof(int32_t) * (size_t)w.max_tiles_aux);
-  w.tile_m0_aux = pl.take(sizeof(int32_t) * (size_t)w.max_tiles_aux);
   w.group_end = pl.off;
 }
 

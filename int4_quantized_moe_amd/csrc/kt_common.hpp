@@ -138,7 +138,11 @@ __device__ __forceinline__ floatx4 mfma_bf16(u32x4 a, u32x4 b, floatx4 c) {
 
 // ---------------------------------------------------------------- activation
 
-// Sigmoid with the exponent argument clamped so exp never overflows.
-__device__ __forceinline__ float sigmoid_f(float z) { return 1.f / (1.f + expf(fminf(-z, 88.f))); }
+// Sigmoid from the hardware exp2 and reciprocal (about 1 ulp each), with the
+// exponent argument clamped so that exp never overflows.
+__device__ __forceinline__ float sigmoid_f(float z) {
+  const float e = __builtin_amdgcn_exp2f(fminf(-z, 88.f) * 1.4426950408889634f);
+  return __builtin_amdgcn_rcpf(1.f + e);
+}
 
 }  // namespace kt

@@ -662,6 +662,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT == 128 ?
           float gp, up, mg, mu;
           clamp_swiglu(g, u, limit, gp, up, mg, mu);
           const float h = valid ? gp * sigmoid_f(gp) * up : 0.f;
+          acc[mb][f][i] = h;  // g and u are saved; keep h for pass 2
           mx = fmaxf(mx, fabsf(h));
         }
 #pragma unroll
@@ -684,9 +685,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT == 128 ?
         for (int f = 0; f < 2; ++f) {
           const int col = n0 + w * 32 + f * 16 + lr;
           if (col >= I) continue;
-          float gp, up, mg, mu;
-          clamp_swiglu(acc[mb][f][i], acc[mb][f + 2][i], limit, gp, up, mg, mu);
-          p.hh[m * I + perm_pos(col)] = float_to_half_bits(ldexpf(gp * sigmoid_f(gp) * up, pe));
+          p.hh[m * I + perm_pos(col)] = float_to_half_bits(ldexpf(acc[mb][f][i], pe));
         }
       }
   } else if constexpr (KIND == kDown || KIND == kGateUpBwd) {

@@ -57,31 +57,27 @@ __device__ int block_inclusive_scan(int v, int32_t* buf) {
 }
 
 // One block: expert totals, exclusive offsets, per-block placement bases
-// (blockcnt is rewritten in place), and two lists of (expert, first row) tiles:
-// `mt` rows for the matrix kernels, kMTAux rows for the LoRA kernels.
+// (blockcnt is rewritten in place), and the list of (expert, first row) tiles
+// of `mt` rows for the expert GEMMs and the LoRA side products.
 __global__ __launch_bounds__(1024) void k_group_scan(int E, int64_t nb, int mt, int32_t* __restrict__ blockcnt,
                                                      int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                      int32_t* __restrict__ tile_e, int32_t* __restrict__ tile_m0,
-                                                     int32_t* __restrict__ tile_e_aux,
-                                                     int32_t* __restrict__ tile_m0_aux,
                                                      unsigned long long* __restrict__ counters) {
   __shared__ int32_t buf[1024];
   const int T = blockDim.x;
   const int per = (E + T - 1) / T;
   const int e0 = min(E, (int)threadIdx.x * per), e1 = min(E, e0 + per);
-  int local = 0, ltiles = 0, latiles = 0;
+  int local = 0, ltiles = 0;
   for (int e = e0; e < e1; ++e) {
     int c = 0;
     for (int64_t b = 0; b < nb; ++b) c += blockcnt[b * E + e];
     counts[e] = c;
     local += c;
     ltiles += (c + mt - 1) / mt;
-    latiles += (c + kMTAux - 1) / kMTAux;
   }
   const int incl = block_inclusive_scan(local, buf);
   const int tincl = block_inclusive_scan(ltiles, buf);
-  const int taincl = block_inclusive_scan(latiles, buf);
-  int run = incl - local, trun = tincl - ltiles, tarun = taincl - latiles;
+  int run = incl - local, trun = tincl - ltiles;
   for (int e = e0; e < e1; ++e) {
     const int c = counts[e];
     offsets[e] = run;
@@ -97,18 +93,11 @@ __global__ __launch_bounds__(1024) void k_group_scan(int E, int64_t nb, int mt, 
       tile_m0[trun + j] = run + j * mt;
     }
     trun += nt;
-    const int nta = (c + kMTAux - 1) / kMTAux;
-    for (int j = 0; j < nta; ++j) {
-      tile_e_aux[tarun + j] = e;
-      tile_m0_aux[tarun + j] = run + j * kMTAux;
-    }
-    tarun += nta;
     run += c;
   }
   if ((int)threadIdx.x == T - 1) {
     offsets[E] = incl;
     counters[kNumTiles] = (unsigned long long)tincl;
-    counters[kNumTilesAux] = (unsigned long long)taincl;
   }
 }
 
@@ -161,8 +150,7 @@ void launch_group(const Dims& d, const WsMap& w, void* ws, const int64_t* ids, h
   if (w.nb > 0) k_group_count<<<(unsigned)w.nb, 256, lds, st>>>(ids, d.Ms, E, blockcnt, counters);
   k_group_scan<<<1, 1024, 0, st>>>(E, w.nb, (int)w.mt, blockcnt, ws_ptr<int32_t>(ws, w.counts),
                                    ws_ptr<int32_t>(ws, w.offsets), ws_ptr<int32_t>(ws, w.tile_e),
-                                   ws_ptr<int32_t>(ws, w.tile_m0), ws_ptr<int32_t>(ws, w.tile_e_aux),
-                                   ws_ptr<int32_t>(ws, w.tile_m0_aux), counters);
+                                   ws_ptr<int32_t>(ws, w.tile_m0), counters);
   if (w.nb > 0)
     k_group_place<<<(unsigned)w.nb, 256, lds, st>>>(ids, d.Ms, E, blockcnt, ws_ptr<int32_t>(ws, w.sorted_slot),
                                                    ws_ptr<int32_t>(ws, w.row_of_slot));

@@ -11,7 +11,6 @@
 namespace kt {
 
 // Tile geometry shared by the grouping (tile lists) and the matrix kernels.
-constexpr int kMTAux = 64;         // token-slot rows per tile of the fp32 LoRA kernels
 constexpr int kGroupBlock = 1024;  // slots per block of the grouping histogram
 constexpr int kHChunk = 128;       // columns of I per gate/up tile (h exponent chunk)
 constexpr int kNT = 256;           // output columns per tile of the other GEMMs (dG/dU exponent chunk)
@@ -38,7 +37,7 @@ inline int choose_gemm_rows(int64_t Ms, int64_t E) {
 inline int64_t lora_half_width(int64_t R) { return (R + 31) / 32 * 32; }
 
 // Device counters at the head of the workspace.
-enum Counter { kBadIds = 0, kBadScales = 1, kNumTiles = 2, kNumTilesAux = 3, kNumCounters = 8 };
+enum Counter { kBadIds = 0, kBadScales = 1, kNumTiles = 2, kNumCounters = 8 };
 
 struct Dims {
   int64_t E, K, H, I, R, qlen, Ms;
@@ -49,7 +48,7 @@ struct WsMap {
   // fp16 transposed scales of the three projections ([E][K/32][rows]), made by the forward
   size_t sct_g, sct_u, sct_d;
   // grouping
-  size_t counters, counts, offsets, blockcnt, sorted_slot, row_of_slot, tile_e, tile_m0, tile_e_aux, tile_m0_aux;
+  size_t counters, counts, offsets, blockcnt, sorted_slot, row_of_slot, tile_e, tile_m0;
   // forward state kept for the backward
   size_t xh, xexp, ua, ub, g, u, hh, hexp, ud;
   // the side product feeding the next expert GEMM, as bf16 hi/lo planes (reused by all four)
@@ -60,7 +59,7 @@ struct WsMap {
   size_t dyh, dyexp, dyb, dgu, dguexp, dgb, dub, drpart;
   size_t group_end;  // bytes needed by the grouping alone
   size_t total;
-  int64_t nb, mt, max_tiles, max_tiles_aux, h_nch, dg_nch, dr_nt;
+  int64_t nb, mt, max_tiles, h_nch, dg_nch, dr_nt;
 };
 
 WsMap plan_workspace(const Dims& d);
