@@ -52,7 +52,6 @@
 namespace kt {
 
 constexpr int kKS = 64;         // contraction values per stage (two quant groups)
-constexpr int kStages = 3;      // LDS ring depth
 constexpr int kWBytes = 8192;   // packed weight bytes per stage (256 columns x 64 values)
 constexpr int kScBytes = 1024;  // fp16 scales per stage (256 columns x 2 groups, or 64 rows x 8 groups)
 constexpr int kLBP = 544;       // row pitch in bytes of a transposed LoRA matrix group (256 bf16 + 32 B)
@@ -163,10 +162,11 @@ __device__ __forceinline__ void wait_vm_lgkm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
 
-// 128-row tiles hold 128 accumulators per lane and run one wave per SIMD (all 512
-// registers); smaller tiles run two or more.
+// Every tile height runs at least two waves per SIMD: a single wave issues VALU
+// at half the SIMD's rate, and the weight decode needs the full rate to stay
+// under the MFMA time.
 template <int KIND, int MT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT == 128 ? 1 : 2))) void k_gemm(GemmParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm(GemmParams p) {
   constexpr int MB = MT / 16;
   constexpr bool kT = (KIND == kDownBwd || KIND == kGateUpBwd);
   constexpr bool kChunked = (KIND == kDown || KIND == kGateUpBwd);
@@ -175,6 +175,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT == 128 ?
   constexpr int kRowsPerInst = MT == 16 ? 4 : 8;     // activation rows per DMA instruction
   constexpr int kAInst = MT == 16 ? 1 : MT / 32;     // activation DMA instructions per wave per stage
   constexpr int kDmaPerStage = kAInst + 3;           // plus two weight and one scale DMA instructions
+  // Up to 32 rows the fragments of the next stage are read and decoded while
+  // the current one is multiplied (kPipe; stages s + 2 .. s + 3 in flight).
+  // Taller tiles need the registers for accumulators: each stage is decoded
+  // and multiplied in turn, two workgroups per CU overlap each other, and
+  // stages s + 1 .. s + 2 are in flight.
+  constexpr bool kPipe = MT <= 32;
+  constexpr int kStages = kPipe ? 4 : 3;
   constexpr int kRing = kStages * kStage > kABytes + 64 * kLBP ? kStages * kStage : kABytes + 64 * kLBP;
   __shared__ __align__(16) uint8_t ring[kRing];
   __shared__ int32_t s_src[MT], s_exp[MT], s_slot[MT];
@@ -404,8 +411,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT == 128 ?
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  issue(0);
-  if (nss > 1) issue(1);
+#pragma unroll
+  for (int i = 0; i < kStages - 1; ++i)
+    if (i < nss) issue(i);
 
   // ---------------------------------------------------------------- main loop (fp16)
   const int aswz = (lr & 7) ^ ((lr >> 3) & 1);  // activation swizzle of rows 16 * mb + lr
@@ -413,43 +421,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT == 128 ?
   const int a_off1 = lr * 128 + 16 * ((2 * lg + 1) ^ aswz);
   // One stage from the ring.  In a final half stage (contraction length an odd
   // multiple of 32) lanes 32..63 hold values past the end: their weights are zeroed.
-  auto compute = [&](const uint8_t* st, auto tail_tag) {
-    constexpr bool kTail = decltype(tail_tag)::value;
-    const uint32_t km = (kTail && lg >= 2) ? 0u : 0xffffffffu;
-    const uint8_t* As = st;
+  // Weight fragments of one stage: codes and scales read from its slot and
+  // decoded to fp16 (in a final half stage -- contraction length an odd multiple
+  // of 32 -- lanes 32..63 hold values past the end: their weights are zeroed).
+  auto decode = [&](const uint8_t* st, bool tail, u32x4 (&bf)[2][4]) {
+    const uint32_t km = (tail && lg >= 2) ? 0u : 0xffffffffu;
     const uint8_t* Bs = st + kABytes;
     const uint16_t* Sc = reinterpret_cast<const uint16_t*>(st + kABytes + kWBytes);
     if constexpr (kT) {
       v2i_t tr[4];
+      u32x4 sp[2][4];
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
         const int lc = local_col<KIND>(w, f);
         const int slot = (lc >> 5) ^ ((lr >> 1) & 7);
         tr[f] = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
             (lds_v2i_ptr)(Bs + (16 * lg + lr) * 128 + 16 * slot + 8 * ((lc >> 4) & 1)));
+#pragma unroll
+        for (int j = 0; j < 2; ++j)  // 8 fp16 scales written as 16-bit values: copy, do not type-pun
+          __builtin_memcpy(&sp[j][f], &Sc[(lc >> 5) * kKS + 16 * lg + 8 * j], sizeof(u32x4));
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        u32x4 bf[4];
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
-          const int cg = local_col<KIND>(w, f) >> 5;
-          u32x4 sp;  // 8 fp16 scales written as 16-bit values: copy, do not type-pun
-          __builtin_memcpy(&sp, &Sc[cg * kKS + 16 * lg + 8 * j], sizeof(sp));
           const uint32_t word = j ? (uint32_t)tr[f].y : (uint32_t)tr[f].x;
           // bit-cast whole scalars: clang's bit_cast of an ext-vector component reads component 0
-          const uint32_t s0 = sp.x, s1 = sp.y, s2 = sp.z, s3 = sp.w;
-          bf[f] = decode_dword_perm(word, __builtin_bit_cast(half2_t, s0), __builtin_bit_cast(half2_t, s1),
-                                    __builtin_bit_cast(half2_t, s2), __builtin_bit_cast(half2_t, s3)) &
-                  km;
+          const uint32_t s0 = sp[j][f].x, s1 = sp[j][f].y, s2 = sp[j][f].z, s3 = sp[j][f].w;
+          bf[j][f] = decode_dword_perm(word, __builtin_bit_cast(half2_t, s0), __builtin_bit_cast(half2_t, s1),
+                                       __builtin_bit_cast(half2_t, s2), __builtin_bit_cast(half2_t, s3)) &
+                     km;
         }
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const u32x4 af = *reinterpret_cast<const u32x4*>(As + mb * 2048 + (j ? a_off1 : a_off0));
-#pragma unroll
-          for (int f = 0; f < 4; ++f) acc[mb][f] = mfma_f16(af, bf[f], acc[mb][f]);
-        }
-      }
     } else {
       uint32_t raw[4][2];
       uint32_t bs[4];
@@ -464,43 +466,110 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT == 128 ?
         bs[f] = sh | (sh << 16);
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        u32x4 bf[4];
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
           const half2_t s2 = __builtin_bit_cast(half2_t, bs[f]);
-          bf[f] = decode_dword_perm(raw[f][j], s2, s2, s2, s2) & km;
+          bf[j][f] = decode_dword_perm(raw[f][j], s2, s2, s2, s2) & km;
         }
+    }
+  };
+  // activation fragments of one stage from its slot
+  auto read_a = [&](const uint8_t* st, u32x4 (&af)[2][MB]) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const u32x4 af = *reinterpret_cast<const u32x4*>(As + mb * 2048 + (j ? a_off1 : a_off0));
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int f = 0; f < 4; ++f) acc[mb][f] = mfma_f16(af, bf[f], acc[mb][f]);
-        }
-      }
+      for (int mb = 0; mb < MB; ++mb)
+        af[j][mb] = *reinterpret_cast<const u32x4*>(st + mb * 2048 + (j ? a_off1 : a_off0));
+  };
+  // MFMAs of one stage, both operands already in registers
+  auto mma = [&](const u32x4 (&af)[2][MB], const u32x4 (&bf)[2][4]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int f = 0; f < 4; ++f) acc[mb][f] = mfma_f16(af[j][mb], bf[j][f], acc[mb][f]);
+  };
+  const bool half_tail = (kdim & (kKS - 1)) != 0;
+  auto slot = [&](int ss) { return ring + (ss % kStages) * kStage; };
+  // Stage ss: wait until stage ss + 1 has landed (each wave waits for its own
+  // DMAs, the barrier for everyone's; it also frees the slot of stage ss - 1),
+  // refill that slot with stage ss + kStages - 1, then run stage ss's MFMAs from
+  // registers while stage ss + 1's activation fragments and weight codes are
+  // read and its weights decoded.
+  auto step = [&](int ss, const u32x4 (&acur)[2][MB], const u32x4 (&bcur)[2][4], u32x4 (&anxt)[2][MB],
+                  u32x4 (&bnxt)[2][4]) {
+    static_assert(!kPipe || kStages == 4, "ring depth");
+    if (ss + 1 < nss) {
+      const int later = min(kStages - 3, nss - 2 - ss);  // stages issued after stage ss + 1
+      if (later >= 2)
+        wait_vm_lgkm<2 * kDmaPerStage>();
+      else if (later == 1)
+        wait_vm_lgkm<kDmaPerStage>();
+      else
+        wait_vm_lgkm<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    if (ss + kStages - 1 < nss) issue(ss + kStages - 1);
+    const int sn = min(ss + 1, nss - 1);  // (re-reads the last stage at the end; unused)
+    read_a(slot(sn), anxt);
+    decode(slot(sn), half_tail && sn == nss - 1, bnxt);
+    mma(acur, bcur);
+    // keep the next stage's reads and decode in this block, next to these
+    // MFMAs, rather than letting them sink into the block that consumes them
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int f = 0; f < 4; ++f) asm volatile("" : "+v"(bnxt[j][f]));
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) asm volatile("" : "+v"(anxt[j][mb]));
     }
   };
 
-  // whole stages in the loop (one code path, so the accumulators stay put), a
-  // final half stage after it
-  const bool half_tail = (kdim & (kKS - 1)) != 0;
-  const int nfull = half_tail ? nss - 1 : nss;
-  for (int ss = 0; ss < nfull; ++ss) {
-    // this wave's loads of stage ss have landed once at most the next stage's
-    // DMAs are outstanding; the barrier makes every wave's loads visible and
-    // frees the slot that stage ss + 2 refills
-    if (ss + 1 < nss)
-      wait_vm_lgkm<kDmaPerStage>();
-    else
-      wait_vm_lgkm<0>();
-    __builtin_amdgcn_s_barrier();
-    if (ss + 2 < nss) issue(ss + 2);
-    compute(ring + (ss % kStages) * kStage, BoolTag<false>{});
-  }
-  if (half_tail) {
-    wait_vm_lgkm<0>();
-    __builtin_amdgcn_s_barrier();
-    compute(ring + ((nss - 1) % kStages) * kStage, BoolTag<true>{});
+  if constexpr (kPipe) {
+    u32x4 afa[2][MB], afb[2][MB], bfa[2][4], bfb[2][4];
+    {
+      // stage 0 landed: the stages issued after it may still be in flight
+      const int later = min(kStages - 2, nss - 1);
+      if (later >= 2)
+        wait_vm_lgkm<2 * kDmaPerStage>();
+      else if (later == 1)
+        wait_vm_lgkm<kDmaPerStage>();
+      else
+        wait_vm_lgkm<0>();
+      __builtin_amdgcn_s_barrier();
+      read_a(slot(0), afa);
+      decode(slot(0), half_tail && nss == 1, bfa);
+    }
+    int ss = 0;
+    for (; ss + 1 < nss; ss += 2) {
+      step(ss, afa, bfa, afb, bfb);
+      step(ss + 1, afb, bfb, afa, bfa);
+    }
+    if (ss < nss) step(ss, afa, bfa, afb, bfb);
+  } else {
+    for (int ss = 0; ss < nss; ++ss) {
+      // this wave's loads of stage ss have landed once at most the later
+      // stages' DMAs are outstanding; the barrier makes every wave's loads
+      // visible and frees the slot that stage ss + kStages - 1 refills
+      if (ss + 1 < nss)
+        wait_vm_lgkm<kDmaPerStage>();
+      else
+        wait_vm_lgkm<0>();
+      __builtin_amdgcn_s_barrier();
+      if (ss + kStages - 1 < nss) issue(ss + kStages - 1);
+      u32x4 bf[2][4];
+      decode(slot(ss), half_tail && ss == nss - 1, bf);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const u32x4 af = *reinterpret_cast<const u32x4*>(slot(ss) + mb * 2048 + (j ? a_off1 : a_off0));
+#pragma unroll
+          for (int f = 0; f < 4; ++f) acc[mb][f] = mfma_f16(af, bf[j][f], acc[mb][f]);
+        }
+    }
   }
   __syncthreads();  // every wave is done with the ring before it is reused
 

@@ -25,12 +25,22 @@
 
 namespace kt {
 
-constexpr int kLT = 64;       // output tile edge
-constexpr int kLK = 32;       // contraction step
-constexpr int kLQ = kLT + 8;  // [k][column] pitch in 16-bit elements (144 B)
-
 typedef short v4s_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s_t* lds_v4s_ptr;
+
+// 8 fp32 -> bf16 hi (top 16 bits) and lo (top 16 bits of the exact remainder)
+__device__ __forceinline__ void split8_trunc(const float* v, u32x4& hi, u32x4& lo) {
+  uint32_t h[8], l[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t u = __float_as_uint(v[i]);
+    h[i] = u & 0xffff0000u;
+    l[i] = __float_as_uint(v[i] - __uint_as_float(h[i]));
+  }
+  hi = u32x4{(h[0] >> 16) | h[1], (h[2] >> 16) | h[3], (h[4] >> 16) | h[5], (h[6] >> 16) | h[7]};
+  lo = u32x4{(l[0] >> 16) | (l[1] & 0xffff0000u), (l[2] >> 16) | (l[3] & 0xffff0000u),
+             (l[4] >> 16) | (l[5] & 0xffff0000u), (l[6] >> 16) | (l[7] & 0xffff0000u)};
+}
 
 struct LoraArgs {
   int topk;
@@ -78,100 +88,145 @@ __device__ __forceinline__ void load8(const RowView& v, int64_t m, int64_t c, in
   }
 }
 
-__global__ __launch_bounds__(256) void k_lora_grad(LoraArgs a) {
-  __shared__ __align__(16) uint16_t Ah[kLK * kLQ], Al[kLK * kLQ], Bh[kLK * kLQ], Bl[kLK * kLQ];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
-  floatx4 acc[4];
-#pragma unroll
-  for (int f = 0; f < 4; ++f) acc[f] = floatx4{0.f, 0.f, 0.f, 0.f};
+// Gradient tile: 64 columns of the rank-wide operand (LoRA-A/B side product,
+// fp32) by 256 columns of the wide one (x, dY, h, dG, dU); both staged
+// row-major in LDS ([token row][column], hi and lo planes).
+constexpr int kGU = 64;            // narrow-operand columns per tile
+constexpr int kGV = 256;           // wide-operand columns per tile
+constexpr int kGK = 32;            // token rows per step
+constexpr int kUP = 2 * kGU + 16;  // LDS row pitch in bytes, narrow operand
+constexpr int kVP = 2 * kGV + 32;  // LDS row pitch in bytes, wide operand
 
+// 8 values of a view at row m from column c, in logical column order, times the
+// slot scale; zeros for an invalid row or past the last column
+__device__ __forceinline__ void load_logical8(const RowView& v, int64_t m, int64_t c, int32_t slot, int topk,
+                                              bool valid, int64_t ncols, float* out) {
+  float t[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (valid && c < ncols) {
+    load8(v, m, c, v.kind == kSrcTokBf16 ? slot / topk : (int32_t)m, (int)min<int64_t>(8, ncols - c), t);
+    if (v.slot_scale) {
+      const float sv = v.slot_scale[slot];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) t[i] *= sv;
+    }
+  }
+  // fp16 views keep the within-8 permuted column order: logical offset i sits at perm_pos(i)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) out[i] = v.kind == kSrcHalfChunked ? t[(i & 4) ? 2 * (i & 3) + 1 : 2 * i] : t[i];
+}
+
+// G[e, p, q] = (accumulate ? G : 0) + scale * sum_m P(m, p) Q(m, q).  The narrow
+// operand U is P (TRANS = false) or Q (TRANS = true); with TRANS the MFMA
+// operands are swapped so that the tile comes out transposed and the stores
+// run along q either way.
+template <bool TRANS>
+__global__ __launch_bounds__(256) void k_lora_grad(LoraArgs a) {
+  __shared__ __align__(16) uint8_t Uh[kGK * kUP], Ul[kGK * kUP], Vh[kGK * kVP], Vl[kGK * kVP];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
+  const RowView& U = TRANS ? a.Q : a.P;
+  const RowView& V = TRANS ? a.P : a.Q;
+  const int64_t nu = TRANS ? a.nq_ : a.np_, nv = TRANS ? a.np_ : a.nq_;
   const int e = blockIdx.x;
   const int m0 = a.offsets[e];
   const int rows = a.offsets[e + 1] - m0;
   if (rows == 0 && a.accumulate) return;
-  const int64_t i0 = (int64_t)blockIdx.y * kLT, j0 = (int64_t)blockIdx.z * kLT;
-  for (int k0 = 0; k0 < rows; k0 += kLK) {
-    // thread -> (token row k, 8 consecutive output columns), stored row-major [k][column]
-    const int k = tid >> 3, c = 8 * (tid & 7);
-    const bool vk = k0 + k < rows;
-    const int64_t m = m0 + k0 + k;
-    float pv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float qv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (vk) {
-      const int32_t slot = a.sorted_slot[m];
-      const int32_t tok = slot / a.topk;
-      if (i0 + c < a.np_) {
-        load8(a.P, m, i0 + c, a.P.kind == kSrcTokBf16 ? tok : (int32_t)m, (int)min<int64_t>(8, a.np_ - (i0 + c)), pv);
-        if (a.P.slot_scale) {
-          const float sv = a.P.slot_scale[slot];
+  const int64_t u0 = (int64_t)blockIdx.y * kGU, v0 = (int64_t)blockIdx.z * kGV;
+
+  floatx4 acc[4][4];
 #pragma unroll
-          for (int t = 0; t < 8; ++t) pv[t] *= sv;
-        }
-      }
-      if (j0 + c < a.nq_) {
-        load8(a.Q, m, j0 + c, a.Q.kind == kSrcTokBf16 ? tok : (int32_t)m, (int)min<int64_t>(8, a.nq_ - (j0 + c)), qv);
-        if (a.Q.slot_scale) {
-          const float sv = a.Q.slot_scale[slot];
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int t = 0; t < 8; ++t) qv[t] *= sv;
-        }
-      }
-    }
-    // fp16 views keep the within-8 permuted column order: put each value at its logical column
-    float pl[8], ql[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int src = (t & 4) ? 2 * (t & 3) + 1 : 2 * t;  // stored slot of logical offset t
-      pl[t] = a.P.kind == kSrcHalfChunked ? pv[src] : pv[t];
-      ql[t] = a.Q.kind == kSrcHalfChunked ? qv[src] : qv[t];
-    }
-    u32x4 hi, lo;
-    split8(pl, hi, lo);
-    __builtin_memcpy(&Ah[k * kLQ + c], &hi, 16);
-    __builtin_memcpy(&Al[k * kLQ + c], &lo, 16);
-    split8(ql, hi, lo);
-    __builtin_memcpy(&Bh[k * kLQ + c], &hi, 16);
-    __builtin_memcpy(&Bl[k * kLQ + c], &lo, 16);
-    __syncthreads();
-    // lanes 4r..4r+3 of a 16-lane group address token row (8 lg + r) (+4), columns 4 (lr & 3).. of the block:
-    // each lane receives 4 consecutive token rows of its column
-    const int rr = lr >> 2, cc = 4 * (lr & 3);
-    u32x4 ah, al;
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  float ureg[8], vreg[4][8];
+  auto load = [&](int k0) {
     {
-      const int base = (8 * lg + rr) * kLQ + w * 16 + cc;
-      const v4s_t h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(&Ah[base]));
-      const v4s_t h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(&Ah[base + 4 * kLQ]));
-      const v4s_t l0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(&Al[base]));
-      const v4s_t l1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(&Al[base + 4 * kLQ]));
-      ah = u32x4{pack2(h0.x, h0.y), pack2(h0.z, h0.w), pack2(h1.x, h1.y), pack2(h1.z, h1.w)};
-      al = u32x4{pack2(l0.x, l0.y), pack2(l0.z, l0.w), pack2(l1.x, l1.y), pack2(l1.z, l1.w)};
+      const int r = tid >> 3, c = 8 * (tid & 7);
+      const int64_t m = m0 + min(k0 + r, rows - 1);
+      load_logical8(U, m, u0 + c, a.sorted_slot[m], a.topk, k0 + r < rows, nu, ureg);
     }
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const int base = (8 * lg + rr) * kLQ + f * 16 + cc;
-      const v4s_t h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(&Bh[base]));
-      const v4s_t h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(&Bh[base + 4 * kLQ]));
-      const v4s_t l0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(&Bl[base]));
-      const v4s_t l1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(&Bl[base + 4 * kLQ]));
-      const u32x4 bh = {pack2(h0.x, h0.y), pack2(h0.z, h0.w), pack2(h1.x, h1.y), pack2(h1.z, h1.w)};
-      const u32x4 bl = {pack2(l0.x, l0.y), pack2(l0.z, l0.w), pack2(l1.x, l1.y), pack2(l1.z, l1.w)};
-      acc[f] = mfma_bf16(ah, bh, acc[f]);
-      acc[f] = mfma_bf16(ah, bl, acc[f]);
-      acc[f] = mfma_bf16(al, bh, acc[f]);
+    for (int i = 0; i < 4; ++i) {
+      const int q = tid + 256 * i, r = q >> 5, c = 8 * (q & 31);
+      const int64_t m = m0 + min(k0 + r, rows - 1);
+      load_logical8(V, m, v0 + c, a.sorted_slot[m], a.topk, k0 + r < rows, nv, vreg[i]);
     }
+  };
+  auto store = [&]() {
+    u32x4 hi, lo;
+    {
+      const int r = tid >> 3, c = 8 * (tid & 7);
+      split8_trunc(ureg, hi, lo);
+      *reinterpret_cast<u32x4*>(&Uh[r * kUP + 2 * c]) = hi;
+      *reinterpret_cast<u32x4*>(&Ul[r * kUP + 2 * c]) = lo;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = tid + 256 * i, r = q >> 5, c = 8 * (q & 31);
+      split8_trunc(vreg[i], hi, lo);
+      *reinterpret_cast<u32x4*>(&Vh[r * kVP + 2 * c]) = hi;
+      *reinterpret_cast<u32x4*>(&Vl[r * kVP + 2 * c]) = lo;
+    }
+  };
+  // lanes 4r..4r+3 of a 16-lane group address token row 8 lg + r (then + 4), columns 4 (lr & 3)..:
+  // each lane receives 4 consecutive token rows of its column per read
+  auto frag = [&](const uint8_t* plane, int pitch, int col) -> u32x4 {
+    const int base = (8 * lg + (lr >> 2)) * pitch + 2 * (col + 4 * (lr & 3));
+    const v4s_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(plane + base));
+    const v4s_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(plane + base + 4 * pitch));
+    return u32x4{pack2(x0.x, x0.y), pack2(x0.z, x0.w), pack2(x1.x, x1.y), pack2(x1.z, x1.w)};
+  };
+
+  if (rows > 0) load(0);
+  for (int k0 = 0; k0 < rows; k0 += kGK) {
+    store();
     __syncthreads();
-  }
+    if (k0 + kGK < rows) load(k0 + kGK);  // in flight while this step is multiplied
+    u32x4 uh[4], ul[4];
 #pragma unroll
-  for (int f = 0; f < 4; ++f)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int64_t i = i0 + w * 16 + lg * 4 + t;  // output row (p)
-      const int64_t j = j0 + f * 16 + lr;          // output column (q)
-      if (i >= a.np_ || j >= a.nq_) continue;
-      const int64_t idx = ((int64_t)e * a.np_ + i) * a.nq_ + j;
-      const float prev = a.accumulate ? a.G[idx] : 0.f;
-      a.G[idx] = prev + a.scale * acc[f][t];
+    for (int ub = 0; ub < 4; ++ub) {
+      uh[ub] = frag(Uh, kUP, 16 * ub);
+      ul[ub] = frag(Ul, kUP, 16 * ub);
     }
+#pragma unroll
+    for (int vb = 0; vb < 4; ++vb) {
+      const u32x4 vh = frag(Vh, kVP, 64 * w + 16 * vb);
+      const u32x4 vl = frag(Vl, kVP, 64 * w + 16 * vb);
+#pragma unroll
+      for (int ub = 0; ub < 4; ++ub) {
+        if constexpr (TRANS) {
+          acc[ub][vb] = mfma_bf16(vh, uh[ub], acc[ub][vb]);
+          acc[ub][vb] = mfma_bf16(vh, ul[ub], acc[ub][vb]);
+          acc[ub][vb] = mfma_bf16(vl, uh[ub], acc[ub][vb]);
+        } else {
+          acc[ub][vb] = mfma_bf16(uh[ub], vh, acc[ub][vb]);
+          acc[ub][vb] = mfma_bf16(uh[ub], vl, acc[ub][vb]);
+          acc[ub][vb] = mfma_bf16(ul[ub], vh, acc[ub][vb]);
+        }
+      }
+    }
+    __syncthreads();  // every wave is done with this step before the next store
+  }
+
+#pragma unroll
+  for (int ub = 0; ub < 4; ++ub)
+#pragma unroll
+    for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int64_t p, q;
+        if constexpr (TRANS) {  // tile rows run along the wide operand (p), columns along q
+          p = v0 + 64 * w + 16 * vb + 4 * lg + i;
+          q = u0 + 16 * ub + lr;
+        } else {
+          p = u0 + 16 * ub + 4 * lg + i;
+          q = v0 + 64 * w + 16 * vb + lr;
+        }
+        if (p >= a.np_ || q >= a.nq_) continue;
+        const int64_t idx = ((int64_t)e * a.np_ + p) * a.nq_ + q;
+        const float prev = a.accumulate ? a.G[idx] : 0.f;
+        a.G[idx] = prev + a.scale * acc[ub][vb][i];
+      }
 }
 
 // ================================================================ side products
@@ -198,20 +253,6 @@ struct SideArgs {
   int64_t split_ld, split_off, split_off2;
   float split_scale;
 };
-
-// 8 fp32 -> bf16 hi (top 16 bits) and lo (top 16 bits of the exact remainder)
-__device__ __forceinline__ void split8_trunc(const float* v, u32x4& hi, u32x4& lo) {
-  uint32_t h[8], l[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t u = __float_as_uint(v[i]);
-    h[i] = u & 0xffff0000u;
-    l[i] = __float_as_uint(v[i] - __uint_as_float(h[i]));
-  }
-  hi = u32x4{(h[0] >> 16) | h[1], (h[2] >> 16) | h[3], (h[4] >> 16) | h[5], (h[6] >> 16) | h[7]};
-  lo = u32x4{(l[0] >> 16) | (l[1] & 0xffff0000u), (l[2] >> 16) | (l[3] & 0xffff0000u),
-             (l[4] >> 16) | (l[5] & 0xffff0000u), (l[6] >> 16) | (l[7] & 0xffff0000u)};
-}
 
 // slot t of an aligned group of 8 in the within-8 permuted order holds logical offset:
 __device__ __forceinline__ int perm_src(int t) { return (t & 1) ? 4 + (t >> 1) : (t >> 1); }
@@ -266,13 +307,23 @@ __global__ __launch_bounds__(256) void k_lora_side(SideArgs a) {
         const int kr = q / (NQ / 8), c8 = q % (NQ / 8);
         const float* row = a.W + ((int64_t)e * kdim + k0 + kr) * R;
         const float* row2 = a.W2 ? a.W2 + ((int64_t)e * kdim + k0 + kr) * R : row;
+        const int col0 = 8 * c8;
+        const bool second0 = col0 >= R;
+        const int cc = second0 ? col0 - R : col0;
+        if ((R & 3) == 0 && cc + 8 <= R && col0 + 8 <= a.nq) {  // 8 columns inside one matrix, 16-byte aligned
+          const float* p = (second0 ? row2 : row) + cc;
+          const float4 x0 = *reinterpret_cast<const float4*>(p), x1 = *reinterpret_cast<const float4*>(p + 4);
+          breg[i][0] = x0.x, breg[i][1] = x0.y, breg[i][2] = x0.z, breg[i][3] = x0.w;
+          breg[i][4] = x1.x, breg[i][5] = x1.y, breg[i][6] = x1.z, breg[i][7] = x1.w;
+        } else {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int col = 8 * c8 + t;
-          const bool second = col >= R;
-          const int qq = min(second ? col - R : col, R - 1);
-          const float x = (second ? row2 : row)[qq];
-          breg[i][t] = col < a.nq ? x : 0.f;
+          for (int t = 0; t < 8; ++t) {
+            const int col = col0 + t;
+            const bool second = col >= R;
+            const int qq = min(second ? col - R : col, R - 1);
+            const float x = (second ? row2 : row)[qq];
+            breg[i][t] = col < a.nq ? x : 0.f;
+          }
         }
       }
     }
@@ -484,8 +535,14 @@ void launch_lora_grad(const Dims& d, const WsMap& w, void* ws, const RowView& P,
   a.G = G;
   a.accumulate = accumulate;
   a.scale = scale;
-  dim3 grid((unsigned)d.E, (unsigned)((np + kLT - 1) / kLT), (unsigned)((nq + kLT - 1) / kLT));
-  k_lora_grad<<<grid, 256, 0, st>>>(a);
+  // the rank-wide operand is the narrow one
+  const bool trans = nq < np;
+  const int64_t nu = trans ? nq : np, nv = trans ? np : nq;
+  dim3 grid((unsigned)d.E, (unsigned)((nu + kGU - 1) / kGU), (unsigned)((nv + kGV - 1) / kGV));
+  if (trans)
+    k_lora_grad<true><<<grid, 256, 0, st>>>(a);
+  else
+    k_lora_grad<false><<<grid, 256, 0, st>>>(a);
 }
 
 }  // namespace kt
