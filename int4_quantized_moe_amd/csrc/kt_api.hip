@@ -60,8 +60,8 @@ WsMap plan_workspace(const Dims& d) {
   w.sct_g = pl.take(2 * (size_t)d.E * (size_t)d.I * (size_t)(d.H / 32));
   w.sct_u = pl.take(2 * (size_t)d.E * (size_t)d.I * (size_t)(d.H / 32));
   w.sct_d = pl.take(2 * (size_t)d.E * (size_t)d.H * (size_t)(d.I / 32));
-  w.h_nch = (d.I + kHChunk - 1) / kHChunk;
-  w.dr_nt = (d.I + kNT - 1) / kNT;
+  w.h_nch = (d.I + kHExp - 1) / kHExp;
+  w.dr_nt = (d.I + kDgExp - 1) / kDgExp;
   w.dg_nch = 2 * w.dr_nt;
   const size_t Ms = (size_t)d.Ms, q = (size_t)d.qlen, H = (size_t)d.H, I = (size_t)d.I, R = (size_t)d.R;
   w.xh = pl.take(2 * q * H);
@@ -333,9 +333,9 @@ int kt_rawint4_moe_fwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const ui
     PhaseScope ph(kPhGemmGateUp, st);
     launch_gemm(kGateUp, d, w, ws, L, route_weights, st);
     launch_normalize_chunks(ws_ptr<uint16_t>(ws, w.hh), ws_ptr<int32_t>(ws, w.hexp),
-                            ws_ptr<int32_t>(ws, w.offsets) + d.E, d.Ms, d.I, d.I, (int)w.h_nch, kHChunk, st);
+                            ws_ptr<int32_t>(ws, w.offsets) + d.E, d.Ms, d.I, d.I, (int)w.h_nch, kHExp, st);
   }
-  const RowView hv = view_half(ws_ptr<uint16_t>(ws, w.hh), d.I, 0, ws_ptr<int32_t>(ws, w.hexp), w.h_nch, 0, kHChunk);
+  const RowView hv = view_half(ws_ptr<uint16_t>(ws, w.hh), d.I, 0, ws_ptr<int32_t>(ws, w.hexp), w.h_nch, 0, kHExp);
   {
     PhaseScope ph(kPhLoraHA, st);
     launch_lora_rowproj(d, w, ws, hv, d.I, L.ad, nullptr, true, ws_ptr<float>(ws, w.ud), nullptr,
@@ -399,11 +399,11 @@ int kt_rawint4_moe_bwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const ui
     PhaseScope ph(kPhGemmDownBwd, st);
     launch_gemm(kDownBwd, d, w, ws, L, route_weights, st);
     launch_normalize_chunks(ws_ptr<uint16_t>(ws, w.dgu), ws_ptr<int32_t>(ws, w.dguexp),
-                            ws_ptr<int32_t>(ws, w.offsets) + d.E, d.Ms, 2 * d.I, d.I, (int)w.dg_nch, kNT, st);
+                            ws_ptr<int32_t>(ws, w.offsets) + d.E, d.Ms, 2 * d.I, d.I, (int)w.dg_nch, kDgExp, st);
   }
-  const RowView dgv = view_half(ws_ptr<uint16_t>(ws, w.dgu), 2 * d.I, 0, ws_ptr<int32_t>(ws, w.dguexp), w.dg_nch, 0, kNT);
+  const RowView dgv = view_half(ws_ptr<uint16_t>(ws, w.dgu), 2 * d.I, 0, ws_ptr<int32_t>(ws, w.dguexp), w.dg_nch, 0, kDgExp);
   const RowView duv =
-      view_half(ws_ptr<uint16_t>(ws, w.dgu), 2 * d.I, d.I, ws_ptr<int32_t>(ws, w.dguexp), w.dg_nch, w.dg_nch / 2, kNT);
+      view_half(ws_ptr<uint16_t>(ws, w.dgu), 2 * d.I, d.I, ws_ptr<int32_t>(ws, w.dguexp), w.dg_nch, w.dg_nch / 2, kDgExp);
   {
     PhaseScope ph(kPhLoraDgB, st);
     launch_lora_rowproj(d, w, ws, dgv, d.I, L.bg, nullptr, false, ws_ptr<float>(ws, w.dgb), nullptr,
@@ -427,7 +427,7 @@ int kt_rawint4_moe_bwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const ui
 
   const float gs = grad_scale * d.sc;
   const RowView xv = view_tok_bf16(inputs, d.H);
-  const RowView hv = view_half(ws_ptr<uint16_t>(ws, w.hh), d.I, 0, ws_ptr<int32_t>(ws, w.hexp), w.h_nch, 0, kHChunk);
+  const RowView hv = view_half(ws_ptr<uint16_t>(ws, w.hh), d.I, 0, ws_ptr<int32_t>(ws, w.hexp), w.h_nch, 0, kHExp);
   // down: dB_d = sc sum (rw dY) (x) ud,  dA_d = sc sum (rw dyB) (x) h
   launch_lora_grad(d, w, ws, view_tok_bf16(grad_output, d.H, route_weights), d.H, view_f32(ws_ptr<float>(ws, w.ud), d.R),
                    d.R, d_down_b, accumulate, gs, st);

@@ -136,6 +136,29 @@ __device__ __forceinline__ floatx4 mfma_bf16(u32x4 a, u32x4 b, floatx4 c) {
                                                  0, 0, 0);
 }
 
+// ---------------------------------------------------------------- 16-lane reductions (DPP)
+
+// The 16 lanes of each DPP row (lanes 16r .. 16r + 15) end with the same result:
+// swap neighbours, swap pairs, mirror within 8, mirror within 16.  Every lane
+// combines the same operands in a commutative order, so the results are equal
+// bit for bit.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1, 0, 3, 2]
+  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2, 3, 0, 1]
+  v = fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror
+  return fmaxf(v, dpp_f<0x140>(v));  // row_mirror
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v = v + dpp_f<0xB1>(v);
+  v = v + dpp_f<0x4E>(v);
+  v = v + dpp_f<0x141>(v);
+  return v + dpp_f<0x140>(v);
+}
+
 // ---------------------------------------------------------------- activation
 
 // Sigmoid from the hardware exp2 and reciprocal (about 1 ulp each), with the

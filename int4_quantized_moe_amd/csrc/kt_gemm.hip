@@ -704,19 +704,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   }
 
   // ---------------------------------------------------------------- epilogues
-  // the ring is free now: reuse it for the cross-wave row reductions; acc holds
-  // the plain sums
-  float* red = reinterpret_cast<float*>(ring);  // [12][MT]
+  // acc holds the plain sums.  One pass: every exponent belongs to one wave's
+  // columns of one row, so a 16-lane reduction finds it.
   const float limit = p.limit;
   if constexpr (KIND == kGateUp) {
-    // pass 1: g, u saved in fp32, row maxima of h over the tile's 128 columns
+    // g, u saved in fp32; h in fp16 times 2^p, p per (row, this wave's 32 columns)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = mb * 16 + lg * 4 + i;
         const bool vrow = row < mlen;
-        const size_t m = (size_t)(m0 + row);
+        const size_t m = (size_t)(m0 + min(row, mlen - 1));
+        float h[2];
         float mx = 0.f;
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
@@ -730,31 +730,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
           }
           float gp, up, mg, mu;
           clamp_swiglu(g, u, limit, gp, up, mg, mu);
-          const float h = valid ? gp * sigmoid_f(gp) * up : 0.f;
-          acc[mb][f][i] = h;  // g and u are saved; keep h for pass 2
-          mx = fmaxf(mx, fabsf(h));
+          h[f] = valid ? gp * sigmoid_f(gp) * up : 0.f;
+          mx = fmaxf(mx, fabsf(h[f]));
         }
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-        if (lr == 0) red[w * MT + row] = mx;
-      }
-    __syncthreads();
-    // pass 2: h in fp16 times 2^p, p per (row, 128-column chunk)
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = mb * 16 + lg * 4 + i;
-        if (row >= mlen) continue;
-        const size_t m = (size_t)(m0 + row);
-        const float mx = fmaxf(fmaxf(red[row], red[MT + row]), fmaxf(red[2 * MT + row], red[3 * MT + row]));
-        const int pe = pow2_exponent_for(mx);
-        if (w == 0 && lr == 0) p.hexp[m * p.h_nch + nt] = pe;
+        const int pe = pow2_exponent_for(row16_max(mx));
+        if (vrow && lr == 0 && n0 + w * 32 < I) p.hexp[m * p.h_nch + (n0 + w * 32) / kHExp] = pe;
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
           const int col = n0 + w * 32 + f * 16 + lr;
-          if (col >= I) continue;
-          p.hh[m * I + perm_pos(col)] = float_to_half_bits(ldexpf(acc[mb][f][i], pe));
+          if (vrow && col < I) p.hh[m * I + perm_pos(col)] = float_to_half_bits(ldexpf(h[f], pe));
         }
       }
   } else if constexpr (KIND == kDown || KIND == kGateUpBwd) {
@@ -773,77 +757,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         }
       }
   } else {  // kDownBwd
-    // pass 1: dRoute partial sums and the row maxima of dG and dU
+    // dRoute partial sums per (row, this wave's 64 columns); dG and dU in fp16
+    // times 2^p, p per (row, this wave's 64 columns) for each
+    const int half_nch = p.dg_nch / 2;
+    const int chunk = (n0 + w * 64) / kDgExp;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = mb * 16 + lg * 4 + i;
         const bool vrow = row < mlen;
-        const size_t m = (size_t)(m0 + row);
+        const size_t m = (size_t)(m0 + min(row, mlen - 1));
         const float wgt = vrow ? p.rw[s_slot[row]] : 0.f;
+        float dg[4], du[4];
         float dr = 0.f, mxg = 0.f, mxu = 0.f;
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
           const int col = n0 + w * 64 + f * 16 + lr;
-          if (!(vrow && col < I)) continue;
+          const bool valid = vrow && col < I;
+          const int cc = min(col, I - 1);
           const float gh = acc[mb][f][i];
           float gp, up, mg, mu;
-          clamp_swiglu(p.gsave[m * I + col], p.usave[m * I + col], limit, gp, up, mg, mu);
+          clamp_swiglu(p.gsave[m * I + cc], p.usave[m * I + cc], limit, gp, up, mg, mu);
           const float sg = sigmoid_f(gp);
           const float si = gp * sg;
           const float dsi = sg * (1.f + gp * (1.f - sg));
-          dr += gh * si * up;
           const float dh = wgt * gh;
-          mxg = fmaxf(mxg, fabsf(dh * up * dsi * mg));
-          mxu = fmaxf(mxu, fabsf(dh * si * mu));
+          dr += valid ? gh * si * up : 0.f;
+          dg[f] = valid ? dh * up * dsi * mg : 0.f;
+          du[f] = valid ? dh * si * mu : 0.f;
+          mxg = fmaxf(mxg, fabsf(dg[f]));
+          mxu = fmaxf(mxu, fabsf(du[f]));
         }
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-          dr += __shfl_xor(dr, off);
-          mxg = fmaxf(mxg, __shfl_xor(mxg, off));
-          mxu = fmaxf(mxu, __shfl_xor(mxu, off));
-        }
-        if (lr == 0) {
-          red[w * MT + row] = dr;
-          red[(4 + w) * MT + row] = mxg;
-          red[(8 + w) * MT + row] = mxu;
-        }
-      }
-    __syncthreads();
-    const int half_nch = p.dg_nch / 2;
-    // pass 2: dG, dU in fp16 times 2^p, p per (row, 256-column chunk)
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = mb * 16 + lg * 4 + i;
-        if (row >= mlen) continue;
-        const size_t m = (size_t)(m0 + row);
-        const float wgt = p.rw[s_slot[row]];
-        const int pg = pow2_exponent_for(fmaxf(fmaxf(red[4 * MT + row], red[5 * MT + row]),
-                                               fmaxf(red[6 * MT + row], red[7 * MT + row])));
-        const int pu = pow2_exponent_for(fmaxf(fmaxf(red[8 * MT + row], red[9 * MT + row]),
-                                               fmaxf(red[10 * MT + row], red[11 * MT + row])));
-        if (w == 0 && lr == 0) {
-          p.drpart[m * p.dr_nt + nt] = (red[row] + red[MT + row]) + (red[2 * MT + row] + red[3 * MT + row]);
-          p.dguexp[m * p.dg_nch + nt] = pg;
-          p.dguexp[m * p.dg_nch + half_nch + nt] = pu;
+        dr = row16_sum(dr);
+        const int pg = pow2_exponent_for(row16_max(mxg));
+        const int pu = pow2_exponent_for(row16_max(mxu));
+        if (vrow && lr == 0 && n0 + w * 64 < I) {
+          p.drpart[m * p.dr_nt + chunk] = dr;
+          p.dguexp[m * p.dg_nch + chunk] = pg;
+          p.dguexp[m * p.dg_nch + half_nch + chunk] = pu;
         }
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
           const int col = n0 + w * 64 + f * 16 + lr;
-          if (col >= I) continue;
-          const float gh = acc[mb][f][i];
-          float gp, up, mg, mu;
-          clamp_swiglu(p.gsave[m * I + col], p.usave[m * I + col], limit, gp, up, mg, mu);
-          const float sg = sigmoid_f(gp);
-          const float si = gp * sg;
-          const float dsi = sg * (1.f + gp * (1.f - sg));
-          const float dh = wgt * gh;
+          if (!(vrow && col < I)) continue;
           const int pc = perm_pos(col);
-          p.dgu[m * (size_t)(2 * I) + pc] = float_to_half_bits(ldexpf(dh * up * dsi * mg, pg));
-          p.dgu[m * (size_t)(2 * I) + I + pc] = float_to_half_bits(ldexpf(dh * si * mu, pu));
+          p.dgu[m * (size_t)(2 * I) + pc] = float_to_half_bits(ldexpf(dg[f], pg));
+          p.dgu[m * (size_t)(2 * I) + I + pc] = float_to_half_bits(ldexpf(du[f], pu));
         }
       }
   }

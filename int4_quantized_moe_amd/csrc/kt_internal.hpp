@@ -12,8 +12,10 @@ namespace kt {
 
 // Tile geometry shared by the grouping (tile lists) and the matrix kernels.
 constexpr int kGroupBlock = 1024;  // slots per block of the grouping histogram
-constexpr int kHChunk = 128;       // columns of I per gate/up tile (h exponent chunk)
-constexpr int kNT = 256;           // output columns per tile of the other GEMMs (dG/dU exponent chunk)
+constexpr int kHChunk = 128;       // columns of I per gate/up tile
+constexpr int kNT = 256;           // output columns per tile of the other GEMMs
+constexpr int kHExp = 32;          // columns of h per exponent (one wave's share of a gate/up tile)
+constexpr int kDgExp = 64;         // columns of dG (or dU) per exponent (one wave's share of a down-dX tile)
 
 // Rows per GEMM tile for a call: the smallest of 16/32/64/128 that covers the
 // mean number of token-slots per expert (heavier experts take several tiles).
