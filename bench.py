@@ -173,8 +173,14 @@ def main():
     else:
         achieved, peak = wbytes / (dom_ms / 1e3) / 1e9, PEAK_HBM / 1e9
         roof = {"bound": "hbm", "unit": "GB/s"}
+    # HBM bytes per launch of the dominant kernel, from the committed counter summary
+    # (profiles/hbm_traffic_<phase>_<workload>.txt), only while it was taken from these sources
+    from int4_quantized_moe_amd import profsum
+
+    measured = profsum.read_traffic(os.path.join(ROOT, "profiles", f"hbm_traffic_{dom}_{cfg.name}.txt"))
+    traffic = None if measured is None else int(round(measured["read"] + measured["write"]))
     roof.update({"kernel": dom, "achieved": round(achieved, 2), "peak": peak, "frac": round(achieved / peak, 4),
-                 "traffic": None, "avg_ms": round(dom_ms, 4)})
+                 "traffic": traffic, "avg_ms": round(dom_ms, 4)})
     total_flops = slots * (12 * cfg.hidden * cfg.intermediate + 18 * cfg.rank * (cfg.hidden + cfg.intermediate))
     total_wbytes = 2 * 3 * active * (cfg.hidden * cfg.intermediate // 2 + cfg.hidden * cfg.intermediate // 16)
     log(f"step: {total_flops / (ms_per_step / 1e3) / 1e12:.1f} TFLOP/s "

@@ -186,13 +186,14 @@ int kt_rawint4_moe_diagnostics(const void* workspace, size_t workspace_bytes, in
  * Per-phase timing of the layer's launches, for measurement.  While enabled,
  * every forward/backward records a hipEvent pair around each phase (grouping,
  * activation conversion, LoRA side products, each grouped GEMM, combine,
- * route-weight gradient, LoRA gradient reductions, and the forward's one
- * conversion of the scales to fp16) on the caller's stream.
+ * route-weight gradient, LoRA gradient reductions, the forward's one
+ * conversion of the scales to fp16, and the passes that give h and dG|dU one
+ * exponent per row) on the caller's stream.
  * kt_rawint4_profile_read waits for the recorded events, writes the summed
  * milliseconds and the number of recorded launches of each phase into
  * ms[capacity] / launches[capacity] (host arrays), clears the records and
  * returns the number of phases (or a negative error code; capacity must cover
- * every phase, 16 at present).  Phase names: kt_rawint4_profile_phase_name.
+ * every phase, 18 at present).  Phase names: kt_rawint4_profile_phase_name.
  */
 int kt_rawint4_profile_enable(int32_t on);
 int kt_rawint4_profile_read(float* ms, int32_t* launches, int32_t capacity);

@@ -203,12 +203,14 @@ enum Phase {
   kPhXHalf,
   kPhLoraXA,
   kPhGemmGateUp,
+  kPhHRows,
   kPhLoraHA,
   kPhGemmDown,
   kPhCombineFwd,
   kPhDyHalf,
   kPhLoraDyB,
   kPhGemmDownBwd,
+  kPhDguRows,
   kPhLoraDgB,
   kPhGemmGateUpBwd,
   kPhCombineBwd,
@@ -218,9 +220,10 @@ enum Phase {
 };
 
 static const char* const kPhaseNames[kNumPhases] = {
-    "group",        "scales_fp16",    "x_to_half",      "lora_a_gate_up", "gemm_gate_up",     "lora_a_down",
-    "gemm_down",    "combine_fwd",    "dy_to_half",     "lora_b_down_bwd",  "gemm_down_dx",
-    "lora_b_gate_up_bwd", "gemm_gate_up_dx", "combine_bwd", "droute",       "lora_grads"};
+    "group",           "scales_fp16",     "x_to_half",          "lora_a_gate_up",  "gemm_gate_up",
+    "h_rows",          "lora_a_down",     "gemm_down",          "combine_fwd",     "dy_to_half",
+    "lora_b_down_bwd", "gemm_down_dx",    "dgu_rows",           "lora_b_gate_up_bwd", "gemm_gate_up_dx",
+    "combine_bwd",     "droute",          "lora_grads"};
 
 struct ProfRec {
   int phase;
@@ -332,6 +335,9 @@ int kt_rawint4_moe_fwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const ui
   {
     PhaseScope ph(kPhGemmGateUp, st);
     launch_gemm(kGateUp, d, w, ws, L, route_weights, st);
+  }
+  {
+    PhaseScope ph(kPhHRows, st);
     launch_normalize_chunks(ws_ptr<uint16_t>(ws, w.hh), ws_ptr<int32_t>(ws, w.hexp),
                             ws_ptr<int32_t>(ws, w.offsets) + d.E, d.Ms, d.I, d.I, (int)w.h_nch, kHExp, st);
   }
@@ -398,6 +404,9 @@ int kt_rawint4_moe_bwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const ui
   {
     PhaseScope ph(kPhGemmDownBwd, st);
     launch_gemm(kDownBwd, d, w, ws, L, route_weights, st);
+  }
+  {
+    PhaseScope ph(kPhDguRows, st);
     launch_normalize_chunks(ws_ptr<uint16_t>(ws, w.dgu), ws_ptr<int32_t>(ws, w.dguexp),
                             ws_ptr<int32_t>(ws, w.offsets) + d.E, d.Ms, 2 * d.I, d.I, (int)w.dg_nch, kDgExp, st);
   }

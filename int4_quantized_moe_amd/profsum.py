@@ -1,0 +1,152 @@
+"""Short text summaries of rocprofv3 output for this library's kernels.
+
+    python -m int4_quantized_moe_amd.profsum trace DIR OUT --command "..."
+        kernel table (calls, average and total time) from DIR/run_kernel_stats.csv
+
+    python -m int4_quantized_moe_amd.profsum traffic FETCH_DIR WRITE_DIR OUT --kernel NAME
+            --phase PHASE --workload NAME --copy-mib N --command "..."
+        HBM bytes per dispatch of one kernel from a FETCH_SIZE run and a
+        WRITE_SIZE run, each scaled by what the same counter reads for the
+        plain elementwise copy bench.py --copy-mib N runs (N MiB read, N MiB
+        written), tagged with the hash of the library sources so that a stale
+        figure is recognised.
+
+bench.py reads the traffic summary of its dominant kernel and reports it only
+while the sources hash the same.
+"""
+
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+
+
+def source_hash() -> str:
+    """sha256 over the library's kernel sources, public header and build settings."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(HERE, "csrc", "*"))) + sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
+    files.append(os.path.join(HERE, "build.py"))
+    for path in files:
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _find(directory: str, suffix: str) -> str:
+    hits = sorted(glob.glob(os.path.join(directory, "**", "*" + suffix), recursive=True))
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {directory}")
+    return hits[0]
+
+
+def _counter_per_dispatch(path: str):
+    """{kernel name: {counter: [value summed over the dispatch's rows, per dispatch]}}"""
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    names = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            key = r["Dispatch_Id"]
+            names[key] = r["Kernel_Name"]
+            per[key][r["Counter_Name"]] += float(r["Counter_Value"])
+    out = collections.defaultdict(lambda: collections.defaultdict(list))
+    for key, counters in per.items():
+        for c, v in counters.items():
+            out[names[key]][c].append(v)
+    return out
+
+
+def trace(directory: str, out: str, command: str) -> None:
+    rows = list(csv.DictReader(open(_find(directory, "kernel_stats.csv"))))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = ["# rocprofv3 kernel summary (--kernel-trace --stats)", f"# command: {command}",
+             f"# library sources sha256: {source_hash()}", "",
+             f"{'kernel':64s} {'calls':>6s} {'avg_us':>11s} {'total_ms':>10s} {'pct':>6s}"]
+    for r in rows:
+        lines.append(f"{r['Name'][:64]:64s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:11.1f} "
+                     f"{float(r['TotalDurationNs']) / 1e6:10.3f} {float(r['Percentage']):6.2f}")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def traffic(fetch_dir: str, write_dir: str, out: str, kernel: str, phase: str, workload: str, copy_mib: int,
+            command: str) -> None:
+    fetch = _counter_per_dispatch(_find(fetch_dir, "counter_collection.csv"))
+    write = _counter_per_dispatch(_find(write_dir, "counter_collection.csv"))
+
+    def pick(table, counter, needle):
+        vals = [v for name, cs in table.items() if needle in name for v in cs.get(counter, [])]
+        if not vals:
+            raise KeyError(f"{counter}: no dispatch of a kernel matching {needle!r}")
+        return sum(vals) / len(vals), len(vals)
+
+    copy_bytes = copy_mib * (1 << 20)
+    f_copy, _ = pick(fetch, "FETCH_SIZE", "neg_kernel")
+    w_copy, _ = pick(write, "WRITE_SIZE", "neg_kernel")
+    f_kib, nf = pick(fetch, "FETCH_SIZE", kernel)
+    w_kib, nw = pick(write, "WRITE_SIZE", kernel)
+    f_scale = copy_bytes / (f_copy * 1024.0)
+    w_scale = copy_bytes / (w_copy * 1024.0)
+    read_b = f_kib * 1024.0 * f_scale
+    write_b = w_kib * 1024.0 * w_scale
+    lines = [f"# HBM traffic of {kernel} ({phase}) at workload {workload}",
+             "# two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE), KiB per dispatch, each scaled by",
+             f"# what the same counter reads for a plain elementwise copy of {copy_mib} MiB (bench.py --copy-mib)",
+             f"# command: {command}",
+             f"kernel: {kernel}", f"phase: {phase}", f"workload: {workload}", f"source_sha256: {source_hash()}",
+             f"dispatches: {nf} {nw}", f"fetch_kib_per_dispatch: {f_kib:.1f}", f"write_kib_per_dispatch: {w_kib:.1f}",
+             f"copy_fetch_kib: {f_copy:.1f}", f"copy_write_kib: {w_copy:.1f}",
+             f"fetch_scale: {f_scale:.4f}", f"write_scale: {w_scale:.4f}",
+             f"hbm_read_bytes_per_launch: {read_b:.0f}", f"hbm_write_bytes_per_launch: {write_b:.0f}",
+             f"hbm_bytes_per_launch: {read_b + write_b:.0f}"]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def read_traffic(path: str):
+    """Bytes per launch from a traffic summary, or None if absent or taken from other sources."""
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != source_hash():
+        return None
+    return {"read": float(kv["hbm_read_bytes_per_launch"]), "write": float(kv["hbm_write_bytes_per_launch"])}
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    sub = ap.add_subparsers(dest="mode", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("dir")
+    t.add_argument("out")
+    t.add_argument("--command", required=True)
+    c = sub.add_parser("traffic")
+    c.add_argument("fetch_dir")
+    c.add_argument("write_dir")
+    c.add_argument("out")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--phase", required=True)
+    c.add_argument("--workload", required=True)
+    c.add_argument("--copy-mib", type=int, required=True)
+    c.add_argument("--command", required=True)
+    a = ap.parse_args()
+    if a.mode == "trace":
+        trace(a.dir, a.out, a.command)
+    else:
+        traffic(a.fetch_dir, a.write_dir, a.out, a.kernel, a.phase, a.workload, a.copy_mib, a.command)
+
+
+if __name__ == "__main__":
+    main()

@@ -29,10 +29,10 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_profile_phase_names():
-    names = [kt.kt_rawint4_profile_phase_name(i) for i in range(16)]
-    assert names[0] == "group" and "scales_fp16" in names and "gemm_gate_up" in names
-    assert names[-1] == "lora_grads" and len(set(names)) == 16
-    assert kt.kt_rawint4_profile_phase_name(16) == ""
+    names = [kt.kt_rawint4_profile_phase_name(i) for i in range(18)]
+    assert names[0] == "group" and "scales_fp16" in names and "gemm_gate_up" in names and "h_rows" in names
+    assert names[-1] == "lora_grads" and len(set(names)) == 18
+    assert kt.kt_rawint4_profile_phase_name(18) == ""
     kt.kt_rawint4_profile_enable(False)
     assert sum(n for _, n in kt.kt_rawint4_profile_read().values()) == 0
 
