@@ -34,12 +34,13 @@ static void plan_group_part(Planner& pl, WsMap& w, int64_t Ms, int64_t E) {
   w.nb = (Ms + kGroupBlock - 1) / kGroupBlock;
   w.mt = choose_gemm_rows(Ms, E);
   w.max_tiles = Ms / w.mt + (E < Ms ? E : Ms);
-  w.counters = pl.take(sizeof(unsigned long long) * kNumCounters);
+  w.counters = pl.take(sizeof(unsigned long long) * kCounterWords);
   w.counts = pl.take(sizeof(int32_t) * (size_t)E);
   w.offsets = pl.take(sizeof(int32_t) * (size_t)(E + 1));
   w.blockcnt = pl.take(sizeof(int32_t) * (size_t)(w.nb * E));
   w.sorted_slot = pl.take(sizeof(int32_t) * (size_t)Ms);
   w.row_of_slot = pl.take(sizeof(int32_t) * (size_t)Ms);
+  w.tok_of_row = pl.take(sizeof(int32_t) * (size_t)Ms);
   w.tile_e = pl.take(sizeof(int32_t) * (size_t)w.max_tiles);
   w.tile_m0 = pl.take(sizeof(int32_t) * (size_t)w.max_tiles);
   w.group_end = pl.off;
@@ -83,6 +84,8 @@ WsMap plan_workspace(const Dims& d) {
   w.dgb = pl.take(4 * Ms * R);
   w.dub = pl.take(4 * Ms * R);
   w.drpart = pl.take(4 * Ms * (size_t)w.dr_nt);
+  w.gplanes = pl.take(2 * Ms * (size_t)grad_geom(d.R).row);
+  w.gexp = pl.take(4 * 2 * (size_t)d.E);
   w.total = pl.off;
   return w;
 }
@@ -434,19 +437,8 @@ int kt_rawint4_moe_bwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const ui
   }
   PhaseScope ph_grads(kPhLoraGrads, st);
 
-  const float gs = grad_scale * d.sc;
-  const RowView xv = view_tok_bf16(inputs, d.H);
-  const RowView hv = view_half(ws_ptr<uint16_t>(ws, w.hh), d.I, 0, ws_ptr<int32_t>(ws, w.hexp), w.h_nch, 0, kHExp);
-  // down: dB_d = sc sum (rw dY) (x) ud,  dA_d = sc sum (rw dyB) (x) h
-  launch_lora_grad(d, w, ws, view_tok_bf16(grad_output, d.H, route_weights), d.H, view_f32(ws_ptr<float>(ws, w.ud), d.R),
-                   d.R, d_down_b, accumulate, gs, st);
-  launch_lora_grad(d, w, ws, view_f32(ws_ptr<float>(ws, w.dyb), d.R, route_weights), d.R, hv, d.I, d_down_a,
-                   accumulate, gs, st);
-  // gate/up: dB = sc sum dG (x) ua,  dA = sc sum dgB (x) x
-  launch_lora_grad(d, w, ws, dgv, d.I, view_f32(ws_ptr<float>(ws, w.ua), d.R), d.R, d_gate_b, accumulate, gs, st);
-  launch_lora_grad(d, w, ws, view_f32(ws_ptr<float>(ws, w.dgb), d.R), d.R, xv, d.H, d_gate_a, accumulate, gs, st);
-  launch_lora_grad(d, w, ws, duv, d.I, view_f32(ws_ptr<float>(ws, w.ub), d.R), d.R, d_up_b, accumulate, gs, st);
-  launch_lora_grad(d, w, ws, view_f32(ws_ptr<float>(ws, w.dub), d.R), d.R, xv, d.H, d_up_a, accumulate, gs, st);
+  LoraGradOut go{d_gate_a, d_gate_b, d_up_a, d_up_b, d_down_a, d_down_b};
+  launch_lora_grads(d, w, ws, inputs, grad_output, route_weights, go, accumulate, grad_scale * d.sc, st);
   return launched();
 }
 

@@ -168,4 +168,37 @@ __device__ __forceinline__ float sigmoid_f(float z) {
   return __builtin_amdgcn_rcpf(1.f + e);
 }
 
+// ---------------------------------------------------------------- global -> LDS copies
+
+// LDS byte address of a pointer into a __shared__ array
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
+// 16 bytes from global memory to LDS: lane l's bytes land at lds_base + 16 * l
+// (lds_base wave-uniform, through M0).  Counted by vmcnt like any vector load.
+// Issued from asm so that the compiler, which cannot tell which ring slot a
+// later LDS read touches, does not drain every outstanding copy before it; the
+// ring's explicit vmcnt waits order the copies and the reads instead.  M0 is
+// not used by anything else in these kernels.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
+  // one wait state between the M0 write and the load that reads it
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(base) : "memory");
+}
+
+// 4 bytes from global memory to LDS: lane l's bytes land at lds_base + 4 * l.
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(g), "s"(base) : "memory");
+}
+
+// s_waitcnt with vmcnt <= N and lgkmcnt == 0 (gfx9 encoding: vmcnt in bits 3:0
+// and 15:14, expcnt in 6:4 left at its maximum, lgkmcnt in 11:8)
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
 }  // namespace kt

@@ -137,31 +137,6 @@ __device__ __forceinline__ void clamp_swiglu(float g, float u, float limit, floa
   }
 }
 
-// LDS byte address of a pointer into a __shared__ array
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
-}
-
-// 16 bytes from global memory to LDS: lane l's bytes land at lds_base + 16 * l
-// (lds_base wave-uniform, through M0).  Counted by vmcnt like any vector load.
-// Issued from asm so that the compiler, which cannot tell which ring slot a
-// later LDS read touches, does not drain every outstanding copy before it; the
-// ring's explicit vmcnt waits order the copies and the reads instead.  M0 is
-// not used by anything else in these kernels.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
-  // one wait state between the M0 write and the load that reads it
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(base) : "memory");
-}
-
-// s_waitcnt with vmcnt <= N and lgkmcnt == 0 (gfx9 encoding: vmcnt in bits 3:0
-// and 15:14, expcnt in 6:4 left at its maximum, lgkmcnt in 11:8)
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
-}
-
 // Every tile height runs at least two waves per SIMD: a single wave issues VALU
 // at half the SIMD's rate, and the weight decode needs the full rate to stay
 // under the MFMA time.

@@ -13,7 +13,7 @@
 namespace kt {
 
 __global__ void k_init_counters(unsigned long long* counters) {
-  if (threadIdx.x < kNumCounters) counters[threadIdx.x] = 0ull;
+  if (threadIdx.x < kCounterWords) counters[threadIdx.x] = 0ull;
 }
 
 // blockcnt[b, e] = number of slots in [b*kGroupBlock, (b+1)*kGroupBlock) routed to e
@@ -104,10 +104,11 @@ __global__ __launch_bounds__(1024) void k_group_scan(int E, int64_t nb, int mt, 
 // Stable placement: a slot's rank among equal experts inside its block comes
 // from the slots before it (rounds of blockDim.x slots, earlier rounds counted
 // in cnt[]).
-__global__ __launch_bounds__(256) void k_group_place(const int64_t* __restrict__ ids, int64_t Ms, int E,
+__global__ __launch_bounds__(256) void k_group_place(const int64_t* __restrict__ ids, int64_t Ms, int E, int topk,
                                                      const int32_t* __restrict__ blockbase,
                                                      int32_t* __restrict__ sorted_slot,
-                                                     int32_t* __restrict__ row_of_slot) {
+                                                     int32_t* __restrict__ row_of_slot,
+                                                     int32_t* __restrict__ tok_of_row) {
   extern __shared__ int32_t cnt[];
   __shared__ int32_t rid[256];
   const int t = threadIdx.x;
@@ -128,6 +129,7 @@ __global__ __launch_bounds__(256) void k_group_place(const int64_t* __restrict__
       for (int j = 0; j < t; ++j) rank += (rid[j] == e);
       const int pos = blockbase[(int64_t)blockIdx.x * E + e] + cnt[e] + rank;
       sorted_slot[pos] = (int32_t)s;
+      tok_of_row[pos] = (int32_t)(s / topk);
       row_of_slot[s] = pos;
     } else if (s < Ms) {
       row_of_slot[s] = -1;
@@ -152,8 +154,10 @@ void launch_group(const Dims& d, const WsMap& w, void* ws, const int64_t* ids, h
                                    ws_ptr<int32_t>(ws, w.offsets), ws_ptr<int32_t>(ws, w.tile_e),
                                    ws_ptr<int32_t>(ws, w.tile_m0), counters);
   if (w.nb > 0)
-    k_group_place<<<(unsigned)w.nb, 256, lds, st>>>(ids, d.Ms, E, blockcnt, ws_ptr<int32_t>(ws, w.sorted_slot),
-                                                   ws_ptr<int32_t>(ws, w.row_of_slot));
+    k_group_place<<<(unsigned)w.nb, 256, lds, st>>>(ids, d.Ms, E, (int)d.K, blockcnt,
+                                                   ws_ptr<int32_t>(ws, w.sorted_slot),
+                                                   ws_ptr<int32_t>(ws, w.row_of_slot),
+                                                   ws_ptr<int32_t>(ws, w.tok_of_row));
 }
 
 }  // namespace kt

@@ -38,8 +38,47 @@ inline int choose_gemm_rows(int64_t Ms, int64_t E) {
 // planes with each rank-R half padded to whole 32-value steps: width of one half.
 inline int64_t lora_half_width(int64_t R) { return (R + 31) / 32 * 32; }
 
-// Device counters at the head of the workspace.
-enum Counter { kBadIds = 0, kBadScales = 1, kNumTiles = 2, kNumCounters = 8 };
+// Device counters at the head of the workspace (kCounterWords words, all cleared
+// by the forward); words kZeroWord.. hold 16 zero bytes that copies of rows past
+// the end of an operand read instead.
+enum Counter { kBadIds = 0, kBadScales = 1, kNumTiles = 2, kNumCounters = 8, kZeroWord = 16, kCounterWords = 32 };
+
+// LoRA gradient reductions: the rank-wide operand of each of the four families
+// (x: [dG B_g | dU B_u], dY: rw ud, h: rw dyB, dG|dU: ua | ub) is laid out as
+// 16-bit hi/lo planes [Ms][2][np] with np a whole number of narrow tiles.
+inline int64_t grad_rank16(int64_t R) { return (R + 15) / 16 * 16; }
+struct GradFam {
+  int nut;     // narrow columns per tile: 16, 32, 64 or 128
+  int nu;      // narrow tiles
+  int64_t np;  // plane width (nu * nut)
+};
+inline GradFam grad_family(int64_t width) {
+  GradFam f;
+  f.nut = width <= 16 ? 16 : width <= 32 ? 32 : width <= 64 ? 64 : 128;
+  f.nu = (int)((width + f.nut - 1) / f.nut);
+  f.np = (int64_t)f.nu * f.nut;
+  return f;
+}
+struct GradGeom {
+  int64_t r16;
+  GradFam x, dy, h, g;          // g: one half (dG or dU); its planes hold both halves
+  int64_t off_x, off_dy, off_h, off_g, row;  // plane offsets within a row (elements) and row width
+};
+inline GradGeom grad_geom(int64_t R) {
+  GradGeom G;
+  G.r16 = grad_rank16(R);
+  G.x = grad_family(2 * G.r16);
+  G.dy = grad_family(G.r16);
+  G.h = grad_family(G.r16);
+  G.g = grad_family(G.r16);
+  // each family's row is [hi np | lo np]; the families sit side by side in one row
+  G.off_x = 0;
+  G.off_dy = G.off_x + 2 * G.x.np;
+  G.off_h = G.off_dy + 2 * G.dy.np;
+  G.off_g = G.off_h + 2 * G.h.np;
+  G.row = G.off_g + 2 * (2 * G.g.np);
+  return G;
+}
 
 struct Dims {
   int64_t E, K, H, I, R, qlen, Ms;
@@ -50,7 +89,7 @@ struct WsMap {
   // fp16 transposed scales of the three projections ([E][K/32][rows]), made by the forward
   size_t sct_g, sct_u, sct_d;
   // grouping
-  size_t counters, counts, offsets, blockcnt, sorted_slot, row_of_slot, tile_e, tile_m0;
+  size_t counters, counts, offsets, blockcnt, sorted_slot, row_of_slot, tok_of_row, tile_e, tile_m0;
   // forward state kept for the backward
   size_t xh, xexp, ua, ub, g, u, hh, hexp, ud;
   // the side product feeding the next expert GEMM, as bf16 hi/lo planes (reused by all four)
@@ -59,6 +98,8 @@ struct WsMap {
   size_t stage;
   // backward
   size_t dyh, dyexp, dyb, dgu, dguexp, dgb, dub, drpart;
+  // LoRA gradients: narrow-operand planes ([Ms][GradGeom::row] 16-bit) and per-expert exponents [E][2]
+  size_t gplanes, gexp;
   size_t group_end;  // bytes needed by the grouping alone
   size_t total;
   int64_t nb, mt, max_tiles, h_nch, dg_nch, dr_nt;
@@ -109,9 +150,14 @@ struct RowView {
 void launch_lora_rowproj(const Dims& d, const WsMap& w, void* ws, const RowView& src, int64_t kdim, const float* W,
                          const float* W2, bool rk, float* out, float* out2, int64_t split_ld, int64_t split_off,
                          int64_t split_off2, hipStream_t st);
-// G[e, p, q] = (acc ? G : 0) + scale * sum_{m in e} P(m, p) Q(m, q)
-void launch_lora_grad(const Dims& d, const WsMap& w, void* ws, const RowView& P, int64_t np, const RowView& Q,
-                      int64_t nq, float* G, int accumulate, float scale, hipStream_t st);
+// The six LoRA gradients, G = (accumulate ? G : 0) + scale * dL/dG / sc, from the
+// saved side products, h, dG|dU and the caller's inputs and grad_output.
+struct LoraGradOut {
+  float *ag, *bg, *au, *bu, *ad, *bd;
+};
+void launch_lora_grads(const Dims& d, const WsMap& w, void* ws, const uint16_t* inputs, const uint16_t* grad_output,
+                       const float* route_weights, const LoraGradOut& out, int accumulate, float scale,
+                       hipStream_t st);
 void launch_fill_zero_f32(float* p, int64_t n, hipStream_t st);
 // scales [E][rows][G] bf16 -> [E][G][rows] fp16, rows within-8 permuted, experts in use only
 // (offsets from the grouping); counts out-of-domain scales

@@ -20,6 +20,8 @@
 // 32 at a time in a fixed order, so results do not depend on scheduling; both
 // operands are staged row-major ([k][column]) and read back with
 // ds_read_tr16_b64, which hands each lane 4 consecutive rows of one column.
+#include <limits.h>
+
 #include "kt_common.hpp"
 #include "kt_internal.hpp"
 
@@ -40,193 +42,6 @@ __device__ __forceinline__ void split8_trunc(const float* v, u32x4& hi, u32x4& l
   hi = u32x4{(h[0] >> 16) | h[1], (h[2] >> 16) | h[3], (h[4] >> 16) | h[5], (h[6] >> 16) | h[7]};
   lo = u32x4{(l[0] >> 16) | (l[1] & 0xffff0000u), (l[2] >> 16) | (l[3] & 0xffff0000u),
              (l[4] >> 16) | (l[5] & 0xffff0000u), (l[6] >> 16) | (l[7] & 0xffff0000u)};
-}
-
-struct LoraArgs {
-  int topk;
-  const int32_t* sorted_slot;
-  const int32_t* offsets;
-  // P(m, p), Q(m, q) over the expert's rows; G[e, p, q]
-  RowView P, Q;
-  int64_t np_, nq_;
-  float* G;
-  int accumulate;
-  float scale;
-};
-
-// Up to 8 consecutive values of a row view starting at column c (c % 8 == 0), in
-// stored order (for fp16 rows the within-8 permuted order); `nvalid` columns are
-// read, the rest are 0.  bf16 and fp16 rows are H or I wide (multiples of 32),
-// so for them nvalid is always 8.
-__device__ __forceinline__ void load8(const RowView& v, int64_t m, int64_t c, int32_t tok_or_m, int nvalid,
-                                      float* out) {
-  if (v.kind == kSrcTokBf16) {
-    const uint16_t* p = static_cast<const uint16_t*>(v.ptr) + (int64_t)tok_or_m * v.ld + v.col_off + c;
-    u32x4 r;
-    __builtin_memcpy(&r, p, 16);
-    const uint32_t wds[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      out[2 * i] = __uint_as_float(wds[i] << 16);
-      out[2 * i + 1] = __uint_as_float(wds[i] & 0xffff0000u);
-    }
-  } else if (v.kind == kSrcF32) {
-    const float* p = static_cast<const float*>(v.ptr) + m * v.ld + v.col_off + c;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) out[i] = i < nvalid ? p[i] : 0.f;
-  } else {
-    const uint16_t* p = static_cast<const uint16_t*>(v.ptr) + m * v.ld + v.col_off + c;
-    u32x4 r;
-    __builtin_memcpy(&r, p, 16);
-    const int ex = v.exps[m * v.exp_ld + v.exp_off + c / v.chunk_w];
-    const uint32_t wds[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      out[2 * i] = ldexpf(half_bits_to_float((uint16_t)(wds[i] & 0xffffu)), -ex);
-      out[2 * i + 1] = ldexpf(half_bits_to_float((uint16_t)(wds[i] >> 16)), -ex);
-    }
-  }
-}
-
-// Gradient tile: 64 columns of the rank-wide operand (LoRA-A/B side product,
-// fp32) by 256 columns of the wide one (x, dY, h, dG, dU); both staged
-// row-major in LDS ([token row][column], hi and lo planes).
-constexpr int kGU = 64;            // narrow-operand columns per tile
-constexpr int kGV = 256;           // wide-operand columns per tile
-constexpr int kGK = 32;            // token rows per step
-constexpr int kUP = 2 * kGU + 16;  // LDS row pitch in bytes, narrow operand
-constexpr int kVP = 2 * kGV + 32;  // LDS row pitch in bytes, wide operand
-
-// 8 values of a view at row m from column c, in logical column order, times the
-// slot scale; zeros for an invalid row or past the last column
-__device__ __forceinline__ void load_logical8(const RowView& v, int64_t m, int64_t c, int32_t slot, int topk,
-                                              bool valid, int64_t ncols, float* out) {
-  float t[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (valid && c < ncols) {
-    load8(v, m, c, v.kind == kSrcTokBf16 ? slot / topk : (int32_t)m, (int)min<int64_t>(8, ncols - c), t);
-    if (v.slot_scale) {
-      const float sv = v.slot_scale[slot];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) t[i] *= sv;
-    }
-  }
-  // fp16 views keep the within-8 permuted column order: logical offset i sits at perm_pos(i)
-#pragma unroll
-  for (int i = 0; i < 8; ++i) out[i] = v.kind == kSrcHalfChunked ? t[(i & 4) ? 2 * (i & 3) + 1 : 2 * i] : t[i];
-}
-
-// G[e, p, q] = (accumulate ? G : 0) + scale * sum_m P(m, p) Q(m, q).  The narrow
-// operand U is P (TRANS = false) or Q (TRANS = true); with TRANS the MFMA
-// operands are swapped so that the tile comes out transposed and the stores
-// run along q either way.
-template <bool TRANS>
-__global__ __launch_bounds__(256) void k_lora_grad(LoraArgs a) {
-  __shared__ __align__(16) uint8_t Uh[kGK * kUP], Ul[kGK * kUP], Vh[kGK * kVP], Vl[kGK * kVP];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
-  const RowView& U = TRANS ? a.Q : a.P;
-  const RowView& V = TRANS ? a.P : a.Q;
-  const int64_t nu = TRANS ? a.nq_ : a.np_, nv = TRANS ? a.np_ : a.nq_;
-  const int e = blockIdx.x;
-  const int m0 = a.offsets[e];
-  const int rows = a.offsets[e + 1] - m0;
-  if (rows == 0 && a.accumulate) return;
-  const int64_t u0 = (int64_t)blockIdx.y * kGU, v0 = (int64_t)blockIdx.z * kGV;
-
-  floatx4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  float ureg[8], vreg[4][8];
-  auto load = [&](int k0) {
-    {
-      const int r = tid >> 3, c = 8 * (tid & 7);
-      const int64_t m = m0 + min(k0 + r, rows - 1);
-      load_logical8(U, m, u0 + c, a.sorted_slot[m], a.topk, k0 + r < rows, nu, ureg);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = tid + 256 * i, r = q >> 5, c = 8 * (q & 31);
-      const int64_t m = m0 + min(k0 + r, rows - 1);
-      load_logical8(V, m, v0 + c, a.sorted_slot[m], a.topk, k0 + r < rows, nv, vreg[i]);
-    }
-  };
-  auto store = [&]() {
-    u32x4 hi, lo;
-    {
-      const int r = tid >> 3, c = 8 * (tid & 7);
-      split8_trunc(ureg, hi, lo);
-      *reinterpret_cast<u32x4*>(&Uh[r * kUP + 2 * c]) = hi;
-      *reinterpret_cast<u32x4*>(&Ul[r * kUP + 2 * c]) = lo;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = tid + 256 * i, r = q >> 5, c = 8 * (q & 31);
-      split8_trunc(vreg[i], hi, lo);
-      *reinterpret_cast<u32x4*>(&Vh[r * kVP + 2 * c]) = hi;
-      *reinterpret_cast<u32x4*>(&Vl[r * kVP + 2 * c]) = lo;
-    }
-  };
-  // lanes 4r..4r+3 of a 16-lane group address token row 8 lg + r (then + 4), columns 4 (lr & 3)..:
-  // each lane receives 4 consecutive token rows of its column per read
-  auto frag = [&](const uint8_t* plane, int pitch, int col) -> u32x4 {
-    const int base = (8 * lg + (lr >> 2)) * pitch + 2 * (col + 4 * (lr & 3));
-    const v4s_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(plane + base));
-    const v4s_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(plane + base + 4 * pitch));
-    return u32x4{pack2(x0.x, x0.y), pack2(x0.z, x0.w), pack2(x1.x, x1.y), pack2(x1.z, x1.w)};
-  };
-
-  if (rows > 0) load(0);
-  for (int k0 = 0; k0 < rows; k0 += kGK) {
-    store();
-    __syncthreads();
-    if (k0 + kGK < rows) load(k0 + kGK);  // in flight while this step is multiplied
-    u32x4 uh[4], ul[4];
-#pragma unroll
-    for (int ub = 0; ub < 4; ++ub) {
-      uh[ub] = frag(Uh, kUP, 16 * ub);
-      ul[ub] = frag(Ul, kUP, 16 * ub);
-    }
-#pragma unroll
-    for (int vb = 0; vb < 4; ++vb) {
-      const u32x4 vh = frag(Vh, kVP, 64 * w + 16 * vb);
-      const u32x4 vl = frag(Vl, kVP, 64 * w + 16 * vb);
-#pragma unroll
-      for (int ub = 0; ub < 4; ++ub) {
-        if constexpr (TRANS) {
-          acc[ub][vb] = mfma_bf16(vh, uh[ub], acc[ub][vb]);
-          acc[ub][vb] = mfma_bf16(vh, ul[ub], acc[ub][vb]);
-          acc[ub][vb] = mfma_bf16(vl, uh[ub], acc[ub][vb]);
-        } else {
-          acc[ub][vb] = mfma_bf16(uh[ub], vh, acc[ub][vb]);
-          acc[ub][vb] = mfma_bf16(uh[ub], vl, acc[ub][vb]);
-          acc[ub][vb] = mfma_bf16(ul[ub], vh, acc[ub][vb]);
-        }
-      }
-    }
-    __syncthreads();  // every wave is done with this step before the next store
-  }
-
-#pragma unroll
-  for (int ub = 0; ub < 4; ++ub)
-#pragma unroll
-    for (int vb = 0; vb < 4; ++vb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int64_t p, q;
-        if constexpr (TRANS) {  // tile rows run along the wide operand (p), columns along q
-          p = v0 + 64 * w + 16 * vb + 4 * lg + i;
-          q = u0 + 16 * ub + lr;
-        } else {
-          p = u0 + 16 * ub + 4 * lg + i;
-          q = v0 + 64 * w + 16 * vb + lr;
-        }
-        if (p >= a.np_ || q >= a.nq_) continue;
-        const int64_t idx = ((int64_t)e * a.np_ + p) * a.nq_ + q;
-        const float prev = a.accumulate ? a.G[idx] : 0.f;
-        a.G[idx] = prev + a.scale * acc[ub][vb][i];
-      }
 }
 
 // ================================================================ side products
@@ -522,27 +337,482 @@ void launch_lora_rowproj(const Dims& d, const WsMap& w, void* ws, const RowView&
   }
 }
 
-void launch_lora_grad(const Dims& d, const WsMap& w, void* ws, const RowView& P, int64_t np, const RowView& Q,
-                      int64_t nq, float* G, int accumulate, float scale, hipStream_t st) {
-  LoraArgs a{};
-  a.topk = (int)d.K;
-  a.sorted_slot = ws_ptr<int32_t>(ws, w.sorted_slot);
-  a.offsets = ws_ptr<int32_t>(ws, w.offsets);
-  a.P = P;
-  a.Q = Q;
-  a.np_ = np;
-  a.nq_ = nq;
-  a.G = G;
+// ================================================================ gradients
+
+struct GradPrepArgs {
+  const int32_t* offsets;
+  const int32_t* sorted_slot;
+  const int32_t* tile_e;
+  const int32_t* tile_m0;
+  const unsigned long long* counters;
+  int mt, R;
+  const float* rw;  // route weight per flat slot
+  const int32_t* hexp;
+  int64_t h_nch;
+  const int32_t* dgexp;
+  int64_t dg_nch;
+  const float *ua, *ub, *ud, *dyb, *dgb, *dub;  // side products [Ms][R]
+  uint16_t* planes;                             // [Ms][row]
+  int64_t row, r16;
+  int64_t off_x, np_x, off_dy, np_dy, off_h, np_h, off_g, np_g;  // np_g: one half
+  int32_t* gexp;                                                 // [E][2]: h family, dG|dU family
+};
+
+// Per expert, the power-of-two exponent S of each fp16 narrow family that puts
+// its largest magnitude into [2^14, 2^15): h family rw * dyB * 2^-hexp, dG|dU
+// family ua | ub * 2^-dgexp (hexp, dgexp: the wide row's own exponent, so the
+// wide fp16 values can be used as they are).  One block per expert.
+__global__ __launch_bounds__(256) void k_grad_exps(GradPrepArgs a) {
+  __shared__ int s_max[2];
+  const int e = blockIdx.x;
+  const int m0 = a.offsets[e], m1 = a.offsets[e + 1];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (threadIdx.x < 2) s_max[threadIdx.x] = INT_MIN;
+  __syncthreads();
+  int mh = INT_MIN, mg = INT_MIN;
+  for (int m = m0 + w; m < m1; m += 4) {
+    const float rw = a.rw[a.sorted_slot[m]];
+    const int he = a.hexp[(int64_t)m * a.h_nch], ge = a.dgexp[(int64_t)m * a.dg_nch];
+    for (int p = lane; p < a.R; p += 64) {
+      const int64_t i = (int64_t)m * a.R + p;
+      int ex;
+      const float vh = fabsf(a.dyb[i] * rw);
+      if (vh > 0.f && vh < INFINITY) {
+        (void)frexpf(vh, &ex);
+        mh = max(mh, ex - he);
+      }
+      const float vg = fmaxf(fabsf(a.ua[i]), fabsf(a.ub[i]));
+      if (vg > 0.f && vg < INFINITY) {
+        (void)frexpf(vg, &ex);
+        mg = max(mg, ex - ge);
+      }
+    }
+  }
+  atomicMax(&s_max[0], mh);
+  atomicMax(&s_max[1], mg);
+  __syncthreads();
+  if (threadIdx.x < 2) {
+    const int mx = s_max[threadIdx.x];
+    a.gexp[2 * e + threadIdx.x] = mx == INT_MIN ? 0 : 15 - mx;
+  }
+}
+
+// The narrow planes of one row tile: every row's four families as 16-bit hi/lo
+// pairs (bf16 by truncation for the x and dY families, fp16 rounded to nearest
+// for the h and dG|dU families after the expert's exponent), zero past the rank.
+__global__ __launch_bounds__(256) void k_grad_planes(GradPrepArgs a) {
+  const int tile = blockIdx.x;
+  if ((unsigned long long)tile >= a.counters[kNumTiles]) return;
+  const int e = a.tile_e[tile], m0 = a.tile_m0[tile];
+  const int mlen = min(a.mt, a.offsets[e + 1] - m0);
+  const int sh = a.gexp[2 * e], sg = a.gexp[2 * e + 1];
+  const int R = a.R;
+  const int ux = (int)(a.np_x / 8), ud = (int)(a.np_dy / 8), uh = (int)(a.np_h / 8), ug = (int)(a.np_g / 4);
+  const int units = ux + ud + uh + ug;
+  for (int idx = threadIdx.x; idx < mlen * units; idx += blockDim.x) {
+    const int r = idx / units;
+    int j = idx % units;
+    const int64_t m = m0 + r;
+    float v[8];
+    int64_t off, pw;
+    bool f16;
+    if (j < ux) {  // [dG B_g | dU B_u], each padded to r16
+      const int64_t u = 8 * j;
+      const bool second = u >= a.r16;
+      const float* src = second ? a.dub : a.dgb;
+      const int64_t c = second ? u - a.r16 : u;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) v[t] = c + t < R ? src[m * R + c + t] : 0.f;
+      off = a.off_x + u;
+      pw = a.np_x;
+      f16 = false;
+    } else if ((j -= ux) < ud) {  // rw ud
+      const int64_t u = 8 * j;
+      const float rw = a.rw[a.sorted_slot[m]];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) v[t] = u + t < R ? a.ud[m * R + u + t] * rw : 0.f;
+      off = a.off_dy + u;
+      pw = a.np_dy;
+      f16 = false;
+    } else if ((j -= ud) < uh) {  // rw dyB 2^(S - hexp)
+      const int64_t u = 8 * j;
+      const float rw = a.rw[a.sorted_slot[m]];
+      const int k = sh - a.hexp[m * a.h_nch];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) v[t] = u + t < R ? ldexpf(a.dyb[m * R + u + t] * rw, k) : 0.f;
+      off = a.off_h + u;
+      pw = a.np_h;
+      f16 = true;
+    } else {  // ua | ub 2^(S - dgexp), halves np_g apart
+      j -= uh;
+      const int64_t u = 8 * j;
+      const bool second = u >= a.np_g;
+      const float* src = second ? a.ub : a.ua;
+      const int64_t c = second ? u - a.np_g : u;
+      const int k = sg - a.dgexp[m * a.dg_nch];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) v[t] = c + t < R ? ldexpf(src[m * R + c + t], k) : 0.f;
+      off = a.off_g + u;
+      pw = 2 * a.np_g;
+      f16 = true;
+    }
+    u32x4 hi, lo;
+    if (f16) {
+      uint16_t h[8], l[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        h[t] = float_to_half_bits(v[t]);
+        l[t] = float_to_half_bits(v[t] - half_bits_to_float(h[t]));
+      }
+      hi = u32x4{pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7])};
+      lo = u32x4{pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7])};
+    } else {
+      split8_trunc(v, hi, lo);
+    }
+    uint16_t* dst = a.planes + m * a.row + off;
+    *reinterpret_cast<u32x4*>(dst) = hi;
+    *reinterpret_cast<u32x4*>(dst + pw) = lo;
+  }
+}
+
+struct GradArgs {
+  int E, R;
+  const int32_t* offsets;
+  const int32_t* tok_of_row;
+  const uint16_t* wide;  // row-major 16-bit rows (token rows, or sorted rows)
+  int64_t wld;           // row stride (elements)
+  int64_t wcols;         // columns of one half
+  int64_t whalf;         // column offset of the second half in a row
+  int nhalves, nvh;      // halves, 256-column tiles per half
+  const uint16_t* planes;  // this family's first plane column
+  int64_t prow, pw;        // plane row stride; hi at 0, lo at pw
+  int64_t uhalf;           // narrow plane offset for the second wide half
+  int nu;                  // narrow tiles
+  int64_t usplit;          // narrow index where the second output starts
+  const int32_t* gexp;
+  int gexp_sel;  // -1: no exponent
+  float* out0;
+  float* out1;
+  int accumulate;
+  float scale;
+  const void* zero;  // 16 zero bytes
+};
+
+// Families: 0 = x (bf16 token rows, narrow x wide), 1 = dY (bf16 token rows,
+// wide x narrow), 2 = h (fp16 sorted rows, narrow x wide), 3 = dG|dU (fp16
+// sorted rows in two halves, wide x narrow).  fp16 rows keep the within-8
+// permuted column order of the matrix kernels.
+template <int NUT, int FAM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_lora_grad(GradArgs a) {
+  constexpr bool kF16 = FAM >= 2, kGather = FAM <= 1, kTrans = (FAM & 1) != 0, kPerm = FAM >= 2;
+  constexpr int kGK = 32;                // expert rows per step (one MFMA contraction)
+  constexpr int kWRow = 512;             // LDS bytes of one wide row (256 columns)
+  constexpr int kWBytes = kGK * kWRow;
+  constexpr int kNRow = 4 * NUT;         // LDS bytes of one narrow row: NUT hi then NUT lo values
+  constexpr int kNC = NUT / 4;           // 16-byte chunks per narrow row
+  constexpr int kStage = kWBytes + kGK * kNRow;
+  constexpr int kStages = NUT == 128 ? 2 : 3;
+  constexpr int L = kStages - 1;         // steps in flight ahead of the one multiplied
+  constexpr int kNI = NUT >= 32 ? NUT / 32 : 1;       // narrow copies per wave per step
+  constexpr int kOps = 4 + kNI + (kGather ? 1 : 0);  // copies per wave per step
+  constexpr int WN = NUT < 64 ? NUT : 64;             // narrow columns per wave
+  constexpr int WAVES_N = NUT / WN;
+  constexpr int WV = 64 * WAVES_N;                    // wide columns per wave
+  constexpr int NB = WN / 16, VB = WV / 16;
+  static_assert(L == 1 || L == 2, "ring depth");
+  __shared__ __align__(16) uint8_t ring[kStages * kStage];
+  __shared__ __align__(16) int32_t ridx[kGather ? 4 * kGK : 4];
+
+  // work item (expert, narrow tile, half, wide tile), wide tiles fastest; each
+  // XCD (blocks are dealt to the eight in turn) takes a contiguous range
+  const unsigned per_e = (unsigned)(a.nu * a.nhalves * a.nvh);
+  const unsigned total = (unsigned)a.E * per_e;
+  if (blockIdx.x >= total) return;
+  const unsigned xq = total / 8u, xr = total % 8u, xcd = blockIdx.x % 8u;
+  const unsigned item = xcd * xq + min(xcd, xr) + blockIdx.x / 8u;
+  const int e = (int)(item / per_e);
+  const unsigned rem = item % per_e;
+  const int ut = (int)(rem / (unsigned)(a.nhalves * a.nvh));
+  const int half = (int)((rem / (unsigned)a.nvh) % (unsigned)a.nhalves);
+  const int vt = (int)(rem % (unsigned)a.nvh);
+  const int m0 = a.offsets[e], rows = a.offsets[e + 1] - m0;
+  if (rows == 0 && a.accumulate) return;
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t v0 = (int64_t)vt * 256;
+  const int vend = (int)min<int64_t>(256, a.wcols - v0);
+  const int64_t wcol0 = half * a.whalf + v0;
+  const int64_t ncol0 = half * a.uhalf + (int64_t)ut * NUT;
+  const int nsteps = (rows + kGK - 1) / kGK;
+  const uint32_t ring0 = lds_addr(ring);
+
+  // 16-byte chunk c of LDS row r sits at c ^ swz(r): the 4 rows x 32 bytes that
+  // a 16-lane transposed read touches fall on distinct banks
+  auto swz_w = [](int r) { return 2 * ((r & 3) | (((r >> 3) & 1) << 2)); };
+  auto swz_n = [](int r) {
+    return kNC >= 16 ? 2 * ((r & 3) | (((r >> 3) & 1) << 2)) : kNC == 8 ? 2 * (r & 3) : 2 * ((r >> 1) & 1);
+  };
+
+  // token ids of step t's rows (clamped to the expert's last row) into ridx slot t % 4
+  auto issue_idx = [&](int t) {
+    if constexpr (kGather) {
+      if (lane < kGK) dma4(a.tok_of_row + m0 + min(t * kGK + lane, rows - 1), lds_addr(&ridx[(t & 3) * kGK]));
+    }
+  };
+  // Step t's copies, kOps per wave: the token ids of step t + L first, then the
+  // wide rows (rows past the expert's end repeat its last row) and the narrow
+  // rows (zero past the end), so a wait for step t also covers ids of t + L.
+  auto issue = [&](int t) {
+    issue_idx(t + L);
+    const uint32_t st = ring0 + (t % kStages) * kStage;
+    const int k0 = t * kGK;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 2 * (4 * w + j) + (lane >> 5);
+      const int c = (lane & 31) ^ swz_w(r);
+      const int col = 8 * c < vend ? 8 * c : 0;
+      int64_t rowid;
+      if constexpr (kGather)
+        rowid = ridx[(t & 3) * kGK + r];
+      else
+        rowid = m0 + min(k0 + r, rows - 1);
+      dma16(a.wide + rowid * a.wld + wcol0 + col, st + 1024 * (4 * w + j));
+    }
+#pragma unroll
+    for (int i = 0; i < kNI; ++i) {
+      if (NUT >= 32 || lane < 2 * NUT) {
+        const int g = w * 2 * NUT + 64 * i + lane;
+        const int r = g / kNC;
+        const int c = (g % kNC) ^ swz_n(r);
+        const int plane = c / (kNC / 2), cc = c % (kNC / 2);
+        const void* src = k0 + r < rows
+                              ? (const void*)(a.planes + (int64_t)(m0 + k0 + r) * a.prow + plane * a.pw + ncol0 + 8 * cc)
+                              : a.zero;
+        dma16(src, st + kWBytes + 16 * (w * 2 * NUT + 64 * i));
+      }
+    }
+  };
+
+  // 8 consecutive rows (8 lg ..) of column col of a row-major LDS block, as the
+  // MFMA operand of lane (lr, lg): two transposed reads of 4 rows each
+  auto frag = [&](const uint8_t* base, int pitch, int chunk0, int col, bool wide) -> u32x4 {
+    const int r0 = 8 * lg + (lr >> 2), cc = col + 4 * (lr & 3);
+    const int c = chunk0 + (cc >> 3);
+    const int s0 = wide ? swz_w(r0) : swz_n(r0), s1 = wide ? swz_w(r0 + 4) : swz_n(r0 + 4);
+    const v4s_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4s_ptr)(base + r0 * pitch + 16 * (c ^ s0) + 2 * (cc & 7)));
+    const v4s_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4s_ptr)(base + (r0 + 4) * pitch + 16 * (c ^ s1) + 2 * (cc & 7)));
+    return u32x4{pack2(x0.x, x0.y), pack2(x0.z, x0.w), pack2(x1.x, x1.y), pack2(x1.z, x1.w)};
+  };
+  auto mma = [](u32x4 x, u32x4 y, floatx4 c) { return kF16 ? mfma_f16(x, y, c) : mfma_bf16(x, y, c); };
+
+  constexpr int A0 = kTrans ? VB : NB, A1 = kTrans ? NB : VB;
+  floatx4 acc[A0][A1];
+#pragma unroll
+  for (int i = 0; i < A0; ++i)
+#pragma unroll
+    for (int j = 0; j < A1; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int wn0 = (w % WAVES_N) * WN, wv0 = (w / WAVES_N) * WV;
+
+  if (nsteps > 0) {
+    if constexpr (kGather) {
+#pragma unroll
+      for (int t = 0; t < L; ++t) issue_idx(t);
+      wait_vm_lgkm<0>();
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
+#pragma unroll
+    for (int t = 0; t < L; ++t)
+      if (t < nsteps) issue(t);
+    for (int s = 0; s < nsteps; ++s) {
+      // step s has landed once at most the later step's copies are outstanding;
+      // the barrier shows every wave's copies and frees the slot refilled next
+      if (L == 2 && s + 1 < nsteps)
+        wait_vm_lgkm<kOps>();
+      else
+        wait_vm_lgkm<0>();
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (s + L < nsteps) issue(s + L);
+      if (wv0 < vend) {
+        const uint8_t* sw = ring + (s % kStages) * kStage;
+        const uint8_t* sn = sw + kWBytes;
+        u32x4 nh[NB], nl[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          nh[nb] = frag(sn, kNRow, 0, wn0 + 16 * nb, false);
+          nl[nb] = frag(sn, kNRow, kNC / 2, wn0 + 16 * nb, false);
+        }
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb) {
+          const u32x4 wf = frag(sw, kWRow, 0, wv0 + 16 * vb, true);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            if constexpr (kTrans) {
+              acc[vb][nb] = mma(wf, nh[nb], acc[vb][nb]);
+              acc[vb][nb] = mma(wf, nl[nb], acc[vb][nb]);
+            } else {
+              acc[nb][vb] = mma(nh[nb], wf, acc[nb][vb]);
+              acc[nb][vb] = mma(nl[nb], wf, acc[nb][vb]);
+            }
+          }
+        }
+      }
+    }
+  }
+
+  // G = (accumulate ? G : 0) + scale * 2^-S * acc
+  const int S = a.gexp_sel >= 0 ? a.gexp[2 * e + a.gexp_sel] : 0;
+  auto logical = [](int j) { return kPerm ? (j & ~7) | perm_src(j & 7) : j; };
+#pragma unroll
+  for (int i0 = 0; i0 < A0; ++i0)
+#pragma unroll
+    for (int i1 = 0; i1 < A1; ++i1)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v = a.scale * ldexpf(acc[i0][i1][i], -S);
+        float* out;
+        int64_t idx;
+        if constexpr (kTrans) {  // rows along the wide operand, columns along the rank
+          const int j = wv0 + 16 * i0 + 4 * lg + i;
+          const int64_t q = (int64_t)ut * NUT + wn0 + 16 * i1 + lr;
+          if (j >= vend || q >= a.R) continue;
+          out = half ? a.out1 : a.out0;
+          idx = ((int64_t)e * a.wcols + v0 + logical(j)) * a.R + q;
+        } else {  // rows along the rank, columns along the wide operand
+          const int64_t ug = (int64_t)ut * NUT + wn0 + 16 * i0 + 4 * lg + i;
+          const int j = wv0 + 16 * i1 + lr;
+          const bool second = ug >= a.usplit;
+          const int64_t p = second ? ug - a.usplit : ug;
+          if (j >= vend || p >= a.R) continue;
+          out = second ? a.out1 : a.out0;
+          idx = ((int64_t)e * a.R + p) * a.wcols + v0 + logical(j);
+        }
+        out[idx] = (a.accumulate ? out[idx] : 0.f) + v;
+      }
+}
+
+template <int FAM>
+static void launch_grad_family(int nut, unsigned grid, const GradArgs& a, hipStream_t st) {
+  switch (nut) {
+    case 16:
+      k_lora_grad<16, FAM><<<grid, 256, 0, st>>>(a);
+      break;
+    case 32:
+      k_lora_grad<32, FAM><<<grid, 256, 0, st>>>(a);
+      break;
+    case 64:
+      k_lora_grad<64, FAM><<<grid, 256, 0, st>>>(a);
+      break;
+    default:
+      k_lora_grad<128, FAM><<<grid, 256, 0, st>>>(a);
+      break;
+  }
+}
+
+void launch_lora_grads(const Dims& d, const WsMap& w, void* ws, const uint16_t* inputs, const uint16_t* grad_output,
+                       const float* route_weights, const LoraGradOut& out, int accumulate, float scale,
+                       hipStream_t st) {
+  const GradGeom G = grad_geom(d.R);
+  GradPrepArgs p{};
+  p.offsets = ws_ptr<int32_t>(ws, w.offsets);
+  p.sorted_slot = ws_ptr<int32_t>(ws, w.sorted_slot);
+  p.tile_e = ws_ptr<int32_t>(ws, w.tile_e);
+  p.tile_m0 = ws_ptr<int32_t>(ws, w.tile_m0);
+  p.counters = ws_ptr<unsigned long long>(ws, w.counters);
+  p.mt = (int)w.mt;
+  p.R = (int)d.R;
+  p.rw = route_weights;
+  p.hexp = ws_ptr<int32_t>(ws, w.hexp);
+  p.h_nch = w.h_nch;
+  p.dgexp = ws_ptr<int32_t>(ws, w.dguexp);
+  p.dg_nch = w.dg_nch;
+  p.ua = ws_ptr<float>(ws, w.ua);
+  p.ub = ws_ptr<float>(ws, w.ub);
+  p.ud = ws_ptr<float>(ws, w.ud);
+  p.dyb = ws_ptr<float>(ws, w.dyb);
+  p.dgb = ws_ptr<float>(ws, w.dgb);
+  p.dub = ws_ptr<float>(ws, w.dub);
+  p.planes = ws_ptr<uint16_t>(ws, w.gplanes);
+  p.row = G.row;
+  p.r16 = G.r16;
+  p.off_x = G.off_x;
+  p.np_x = G.x.np;
+  p.off_dy = G.off_dy;
+  p.np_dy = G.dy.np;
+  p.off_h = G.off_h;
+  p.np_h = G.h.np;
+  p.off_g = G.off_g;
+  p.np_g = G.g.np;
+  p.gexp = ws_ptr<int32_t>(ws, w.gexp);
+  k_grad_exps<<<(unsigned)d.E, 256, 0, st>>>(p);
+  if (w.max_tiles > 0) k_grad_planes<<<(unsigned)w.max_tiles, 256, 0, st>>>(p);
+
+  GradArgs a{};
+  a.E = (int)d.E;
+  a.R = (int)d.R;
+  a.offsets = p.offsets;
+  a.tok_of_row = ws_ptr<int32_t>(ws, w.tok_of_row);
+  a.prow = G.row;
+  a.gexp = p.gexp;
   a.accumulate = accumulate;
   a.scale = scale;
-  // the rank-wide operand is the narrow one
-  const bool trans = nq < np;
-  const int64_t nu = trans ? nq : np, nv = trans ? np : nq;
-  dim3 grid((unsigned)d.E, (unsigned)((nu + kGU - 1) / kGU), (unsigned)((nv + kGV - 1) / kGV));
-  if (trans)
-    k_lora_grad<true><<<grid, 256, 0, st>>>(a);
-  else
-    k_lora_grad<false><<<grid, 256, 0, st>>>(a);
+  a.zero = ws_ptr<unsigned long long>(ws, w.counters) + kZeroWord;
+  const uint16_t* planes = p.planes;
+  auto tiles = [](int64_t n) { return (int)((n + 255) / 256); };
+  auto grid = [&](const GradFam& f) { return (unsigned)(a.E * f.nu * a.nhalves * a.nvh); };
+  // dA_g, dA_u = sc sum [dG B_g | dU B_u] (x) x
+  a.wide = inputs;
+  a.wld = d.H;
+  a.wcols = d.H;
+  a.whalf = 0;
+  a.nhalves = 1;
+  a.nvh = tiles(d.H);
+  a.planes = planes + G.off_x;
+  a.pw = G.x.np;
+  a.uhalf = 0;
+  a.nu = G.x.nu;
+  a.usplit = G.r16;
+  a.gexp_sel = -1;
+  a.out0 = out.ag;
+  a.out1 = out.au;
+  launch_grad_family<0>(G.x.nut, grid(G.x), a, st);
+  // dB_d = sc sum dY (x) rw ud
+  a.wide = grad_output;
+  a.planes = planes + G.off_dy;
+  a.pw = G.dy.np;
+  a.nu = G.dy.nu;
+  a.usplit = INT64_MAX;
+  a.out0 = out.bd;
+  a.out1 = out.bd;
+  launch_grad_family<1>(G.dy.nut, grid(G.dy), a, st);
+  // dA_d = sc sum rw dyB (x) h
+  a.wide = ws_ptr<uint16_t>(ws, w.hh);
+  a.wld = d.I;
+  a.wcols = d.I;
+  a.nvh = tiles(d.I);
+  a.planes = planes + G.off_h;
+  a.pw = G.h.np;
+  a.nu = G.h.nu;
+  a.gexp_sel = 0;
+  a.out0 = out.ad;
+  a.out1 = out.ad;
+  launch_grad_family<2>(G.h.nut, grid(G.h), a, st);
+  // dB_g, dB_u = sc sum dG (x) ua, dU (x) ub
+  a.wide = ws_ptr<uint16_t>(ws, w.dgu);
+  a.wld = 2 * d.I;
+  a.whalf = d.I;
+  a.nhalves = 2;
+  a.planes = planes + G.off_g;
+  a.pw = 2 * G.g.np;
+  a.uhalf = G.g.np;
+  a.nu = G.g.nu;
+  a.gexp_sel = 1;
+  a.out0 = out.bg;
+  a.out1 = out.bu;
+  launch_grad_family<3>(G.g.nut, grid(G.g), a, st);
 }
 
 }  // namespace kt
