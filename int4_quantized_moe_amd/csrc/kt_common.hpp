@@ -91,25 +91,31 @@ __device__ __forceinline__ uint32_t decode_pair(uint32_t c0, uint32_t c1, half2_
 // produces weights; the position of logical element k:
 __host__ __device__ __forceinline__ int perm_pos(int k) { return (k & ~7) | ((k & 3) << 1) | ((k >> 2) & 1); }
 
-// (a & m) | o in one instruction (the compiler splits it into two when the
-// constants are literals)
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(o));
-  return r;
+// The decode's nibble mask and fp16 magic as values the compiler cannot see
+// through: with them (w & m) | o becomes one v_and_or_b32 (literal operands
+// would make it split the and-or in two).  Made once per kernel.
+struct DecodeConsts {
+  uint32_t m, o;
+};
+__device__ __forceinline__ DecodeConsts decode_consts() {
+  uint32_t m = 0x000F000Fu, o = 0x64006400u;
+  asm volatile("" : "+s"(m));
+  asm volatile("" : "+v"(o));
+  return DecodeConsts{m, o};
 }
 
 // 8 codes of one packed dword (nibble i = code k_i) -> fp16 weights in the order
 // k0 k4 k1 k5 k2 k6 k3 k7.  Pair (k_i, k_{i+4}) is scaled by s[i] (low half for
-// k_i, high half for k_{i+4}).  One and-or per pair builds both magic values.
-__device__ __forceinline__ u32x4 decode_dword_perm(uint32_t w, half2_t s0, half2_t s1, half2_t s2, half2_t s3) {
+// k_i, high half for k_{i+4}).  One and-or per pair builds both magic values
+// 1024 + c; subtracting 1032 leaves c - 8 exactly.
+__device__ __forceinline__ u32x4 decode_dword_perm(uint32_t w, half2_t s0, half2_t s1, half2_t s2, half2_t s3,
+                                                   DecodeConsts dc) {
   const half2_t bias = {(_Float16)1032.0f, (_Float16)1032.0f};
-  const uint32_t m = 0x000F000Fu, o = 0x64006400u;
   u32x4 r;
-  r.x = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2_t, and_or(w, m, o)) - bias) * s0);
-  r.y = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2_t, and_or(w >> 4, m, o)) - bias) * s1);
-  r.z = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2_t, and_or(w >> 8, m, o)) - bias) * s2);
-  r.w = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2_t, and_or(w >> 12, m, o)) - bias) * s3);
+  r.x = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2_t, (w & dc.m) | dc.o) - bias) * s0);
+  r.y = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2_t, ((w >> 4) & dc.m) | dc.o) - bias) * s1);
+  r.z = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2_t, ((w >> 8) & dc.m) | dc.o) - bias) * s2);
+  r.w = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2_t, ((w >> 12) & dc.m) | dc.o) - bias) * s3);
   return r;
 }
 

@@ -85,6 +85,7 @@ struct GemmParams {
   const uint16_t* sct0;    // fp16 scales [E][K/32][rows], rows within-8 permuted: gate (or down)
   const uint16_t* sct1;    // up
   const float* rw;  // route weights per flat slot
+  const void* zero;  // 16 zero bytes
   float* gsave;
   float* usave;
   uint16_t* hh;
@@ -158,6 +159,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   constexpr bool kPipe = MT <= 32;
   constexpr int kStages = kPipe ? 4 : 3;
   constexpr int kRing = kStages * kStage > kABytes + 64 * kLBP ? kStages * kStage : kABytes + 64 * kLBP;
+  // the ring holds the activation tiles of all slots, then their weight tiles,
+  // then their scales, so that a slot known at compile time is an immediate offset
+  constexpr int kWReg = kStages * kABytes, kSReg = kStages * (kABytes + kWBytes);
   __shared__ __align__(16) uint8_t ring[kRing];
   __shared__ int32_t s_src[MT], s_exp[MT], s_slot[MT];
 
@@ -222,16 +226,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   // them per wave (the ring waits count on it).
   auto issue_any = [&](int ss) {
     const int k0 = ss * kKS;
-    const uint32_t st = lds_addr(ring) + (ss % kStages) * kStage;
+    const int sl = ss % kStages;
+    const uint32_t sa = lds_addr(ring) + sl * kABytes, sw = lds_addr(ring) + kWReg + sl * kWBytes,
+                   ssc = lds_addr(ring) + kSReg + sl * kScBytes;
 #pragma unroll
     for (int i = 0; i < kAInst; ++i) {
       const int u = w * kAInst + i;
       const int row = kRowsPerInst * u + ((lane >> 3) & (kRowsPerInst - 1));
       const int c = (lane & 7) ^ ((row & 7) ^ ((row >> 3) & 1));
-      int k = k0 + 8 * c;
-      if (k >= kdim) k = k0;
-      const uint16_t* g = p.a_src + (size_t)s_src[row] * p.lda + k;
-      if (MT != 16 || lane < 32) dma16(g, st + 128 * kRowsPerInst * u);
+      // activation values past the contraction's end come from the zero chunk,
+      // which cancels whatever the clamped weights of the final half stage hold
+      const int k = k0 + 8 * c;
+      const void* g = k < kdim ? (const void*)(p.a_src + (size_t)s_src[row] * p.lda + k) : p.zero;
+      if (MT != 16 || lane < 32) dma16(g, sa + 128 * kRowsPerInst * u);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -250,7 +257,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         if (k0 + 32 * h >= kdim) h = 0;
         g = wrow_stored(lc) + k0 / 2 + 16 * h;
       }
-      dma16(g, st + kABytes + 1024 * u);
+      dma16(g, sw + 1024 * u);
     }
     // scales: 1 KB per stage, a quarter per wave (16 lanes x 16 B = 8 fp16 each)
     {
@@ -278,7 +285,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
           g = p.sct0 + ((size_t)e * ngroups + gi) * H + n;
         }
       }
-      if (lane < 16) dma16(g, st + kABytes + kWBytes + 256 * w);
+      if (lane < 16) dma16(g, ssc + 256 * w);
     }
   };
 
@@ -351,10 +358,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       issue_any(ss);
       return;
     }
-    const uint32_t st = lds_addr(ring) + (ss % kStages) * kStage;
+    const int sl = ss % kStages;
+    const uint32_t sa = lds_addr(ring) + sl * kABytes, sw = lds_addr(ring) + kWReg + sl * kWBytes,
+                   ssc = lds_addr(ring) + kSReg + sl * kScBytes;
 #pragma unroll
     for (int i = 0; i < kAInst; ++i)
-      if (MT != 16 || lane < 32) dma16(pa[i] + k0, st + 128 * kRowsPerInst * (w * kAInst + i));
+      if (MT != 16 || lane < 32) dma16(pa[i] + k0, sa + 128 * kRowsPerInst * (w * kAInst + i));
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const uint8_t* g;
@@ -365,7 +374,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       } else {
         g = pb[i] + k0 / 2;
       }
-      dma16(g, st + kABytes + 1024 * (w * 2 + i));
+      dma16(g, sw + 1024 * (w * 2 + i));
     }
     {
       const uint16_t* g;
@@ -376,7 +385,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       } else {
         g = ps + (size_t)(k0 / kGroup) * (KIND == kGateUp ? I : H);
       }
-      if (lane < 16) dma16(g, st + kABytes + kWBytes + 256 * w);
+      if (lane < 16) dma16(g, ssc + 256 * w);
     }
   };
 
@@ -394,15 +403,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int aswz = (lr & 7) ^ ((lr >> 3) & 1);  // activation swizzle of rows 16 * mb + lr
   const int a_off0 = lr * 128 + 16 * ((2 * lg) ^ aswz);
   const int a_off1 = lr * 128 + 16 * ((2 * lg + 1) ^ aswz);
-  // One stage from the ring.  In a final half stage (contraction length an odd
-  // multiple of 32) lanes 32..63 hold values past the end: their weights are zeroed.
   // Weight fragments of one stage: codes and scales read from its slot and
-  // decoded to fp16 (in a final half stage -- contraction length an odd multiple
-  // of 32 -- lanes 32..63 hold values past the end: their weights are zeroed).
-  auto decode = [&](const uint8_t* st, bool tail, u32x4 (&bf)[2][4]) {
-    const uint32_t km = (tail && lg >= 2) ? 0u : 0xffffffffu;
-    const uint8_t* Bs = st + kABytes;
-    const uint16_t* Sc = reinterpret_cast<const uint16_t*>(st + kABytes + kWBytes);
+  // decoded to fp16.  (In a final half stage the values past the contraction's
+  // end are clamped copies; the zero activations there cancel them.)
+  const DecodeConsts dc = decode_consts();
+  auto decode = [&](int sl, u32x4 (&bf)[2][4]) {
+    const uint8_t* Bs = ring + kWReg + sl * kWBytes;
+    const uint16_t* Sc = reinterpret_cast<const uint16_t*>(ring + kSReg + sl * kScBytes);
     if constexpr (kT) {
       v2i_t tr[4];
       u32x4 sp[2][4];
@@ -424,8 +431,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
           // bit-cast whole scalars: clang's bit_cast of an ext-vector component reads component 0
           const uint32_t s0 = sp[j][f].x, s1 = sp[j][f].y, s2 = sp[j][f].z, s3 = sp[j][f].w;
           bf[j][f] = decode_dword_perm(word, __builtin_bit_cast(half2_t, s0), __builtin_bit_cast(half2_t, s1),
-                                       __builtin_bit_cast(half2_t, s2), __builtin_bit_cast(half2_t, s3)) &
-                     km;
+                                       __builtin_bit_cast(half2_t, s2), __builtin_bit_cast(half2_t, s3), dc);
         }
     } else {
       uint32_t raw[4][2];
@@ -445,12 +451,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
           const half2_t s2 = __builtin_bit_cast(half2_t, bs[f]);
-          bf[j][f] = decode_dword_perm(raw[f][j], s2, s2, s2, s2) & km;
+          bf[j][f] = decode_dword_perm(raw[f][j], s2, s2, s2, s2, dc);
         }
     }
   };
   // activation fragments of one stage from its slot
-  auto read_a = [&](const uint8_t* st, u32x4 (&af)[2][MB]) {
+  auto read_a = [&](int sl, u32x4 (&af)[2][MB]) {
+    const uint8_t* st = ring + sl * kABytes;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -466,8 +473,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
         for (int f = 0; f < 4; ++f) acc[mb][f] = mfma_f16(af[j][mb], bf[j][f], acc[mb][f]);
   };
-  const bool half_tail = (kdim & (kKS - 1)) != 0;
-  auto slot = [&](int ss) { return ring + (ss % kStages) * kStage; };
   // Stage ss: wait until stage ss + 1 has landed (each wave waits for its own
   // DMAs, the barrier for everyone's; it also frees the slot of stage ss - 1),
   // refill that slot with stage ss + kStages - 1, then run stage ss's MFMAs from
@@ -488,8 +493,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     __builtin_amdgcn_s_barrier();
     if (ss + kStages - 1 < nss) issue(ss + kStages - 1);
     const int sn = min(ss + 1, nss - 1);  // (re-reads the last stage at the end; unused)
-    read_a(slot(sn), anxt);
-    decode(slot(sn), half_tail && sn == nss - 1, bnxt);
+    read_a(sn % kStages, anxt);
+    decode(sn % kStages, bnxt);
     mma(acur, bcur);
     // keep the next stage's reads and decode in this block, next to these
     // MFMAs, rather than letting them sink into the block that consumes them
@@ -514,8 +519,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       else
         wait_vm_lgkm<0>();
       __builtin_amdgcn_s_barrier();
-      read_a(slot(0), afa);
-      decode(slot(0), half_tail && nss == 1, bfa);
+      read_a(0, afa);
+      decode(0, bfa);
     }
     int ss = 0;
     for (; ss + 1 < nss; ss += 2) {
@@ -524,26 +529,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
     if (ss < nss) step(ss, afa, bfa, afb, bfb);
   } else {
-    for (int ss = 0; ss < nss; ++ss) {
-      // this wave's loads of stage ss have landed once at most the later
-      // stages' DMAs are outstanding; the barrier makes every wave's loads
-      // visible and frees the slot that stage ss + kStages - 1 refills
-      if (ss + 1 < nss)
-        wait_vm_lgkm<kDmaPerStage>();
-      else
-        wait_vm_lgkm<0>();
-      __builtin_amdgcn_s_barrier();
-      if (ss + kStages - 1 < nss) issue(ss + kStages - 1);
-      u32x4 bf[2][4];
-      decode(slot(ss), half_tail && ss == nss - 1, bf);
+    // unrolled by the ring depth, so that each stage's slot is a constant
+    for (int s0 = 0; s0 < nss; s0 += kStages) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int sl = 0; sl < kStages; ++sl) {
+        const int ss = s0 + sl;
+        if (ss >= nss) break;
+        // this wave's loads of stage ss have landed once at most the later
+        // stages' DMAs are outstanding; the barrier makes every wave's loads
+        // visible and frees the slot that stage ss + kStages - 1 refills
+        if (ss + 1 < nss)
+          wait_vm_lgkm<kDmaPerStage>();
+        else
+          wait_vm_lgkm<0>();
+        __builtin_amdgcn_s_barrier();
+        if (ss + kStages - 1 < nss) issue(ss + kStages - 1);
+        u32x4 bf[2][4];
+        decode(sl, bf);
+        const uint8_t* st = ring + sl * kABytes;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const u32x4 af = *reinterpret_cast<const u32x4*>(slot(ss) + mb * 2048 + (j ? a_off1 : a_off0));
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int f = 0; f < 4; ++f) acc[mb][f] = mfma_f16(af, bf[j][f], acc[mb][f]);
-        }
+          for (int mb = 0; mb < MB; ++mb) {
+            const u32x4 af = *reinterpret_cast<const u32x4*>(st + mb * 2048 + (j ? a_off1 : a_off0));
+#pragma unroll
+            for (int f = 0; f < 4; ++f) acc[mb][f] = mfma_f16(af, bf[j][f], acc[mb][f]);
+          }
+      }
     }
   }
   __syncthreads();  // every wave is done with the ring before it is reused
@@ -830,6 +842,7 @@ void launch_gemm(GemmKind kind, const Dims& d, const WsMap& w, void* ws, const L
   p.dg_nch = (int)w.dg_nch;
   p.drpart = ws_ptr<float>(ws, w.drpart);
   p.lsplit = ws_ptr<uint16_t>(ws, w.lsplit);
+  p.zero = ws_ptr<unsigned long long>(ws, w.counters) + kZeroWord;
   const bool gu = (kind == kGateUp || kind == kGateUpBwd);
   p.sct0 = ws_ptr<uint16_t>(ws, gu ? w.sct_g : w.sct_d);
   p.sct1 = ws_ptr<uint16_t>(ws, w.sct_u);

@@ -502,8 +502,8 @@ struct GradArgs {
 // wide x narrow), 2 = h (fp16 sorted rows, narrow x wide), 3 = dG|dU (fp16
 // sorted rows in two halves, wide x narrow).  fp16 rows keep the within-8
 // permuted column order of the matrix kernels.
-template <int NUT, int FAM>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_lora_grad(GradArgs a) {
+template <int NUT, int FAM, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void k_lora_grad(GradArgs a) {
   constexpr bool kF16 = FAM >= 2, kGather = FAM <= 1, kTrans = (FAM & 1) != 0, kPerm = FAM >= 2;
   constexpr int kGK = 32;                // expert rows per step (one MFMA contraction)
   constexpr int kWRow = 512;             // LDS bytes of one wide row (256 columns)
@@ -511,15 +511,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   constexpr int kNRow = 4 * NUT;         // LDS bytes of one narrow row: NUT hi then NUT lo values
   constexpr int kNC = NUT / 4;           // 16-byte chunks per narrow row
   constexpr int kStage = kWBytes + kGK * kNRow;
-  constexpr int kStages = NUT == 128 ? 2 : 3;
-  constexpr int L = kStages - 1;         // steps in flight ahead of the one multiplied
-  constexpr int kNI = NUT >= 32 ? NUT / 32 : 1;       // narrow copies per wave per step
-  constexpr int kOps = 4 + kNI + (kGather ? 1 : 0);  // copies per wave per step
-  constexpr int WN = NUT < 64 ? NUT : 64;             // narrow columns per wave
+  constexpr int kStages = 3;
+  constexpr int L = kStages - 1;                    // steps in flight ahead of the one multiplied
+  constexpr int kWI = 16 / NW;                      // wide copies (1 KB each) per wave per step
+  constexpr int kNCW = 8 * NUT / NW;                // narrow 16-byte chunks per wave per step
+  constexpr int kNI = kNCW >= 64 ? kNCW / 64 : 1;   // narrow copies per wave per step
+  constexpr int kOps = kWI + kNI + (kGather ? 1 : 0);
+  constexpr int WN = NUT < 64 ? NUT : 64;           // narrow columns per wave
   constexpr int WAVES_N = NUT / WN;
-  constexpr int WV = 64 * WAVES_N;                    // wide columns per wave
+  constexpr int WV = 256 * WAVES_N / NW;            // wide columns per wave
   constexpr int NB = WN / 16, VB = WV / 16;
-  static_assert(L == 1 || L == 2, "ring depth");
+  static_assert(NW == 4 || NW == 8, "waves");
+  static_assert(kNCW % 64 == 0 || kNCW == 32, "narrow copy shape");
   __shared__ __align__(16) uint8_t ring[kStages * kStage];
   __shared__ __align__(16) int32_t ridx[kGather ? 4 * kGK : 4];
 
@@ -567,8 +570,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     const uint32_t st = ring0 + (t % kStages) * kStage;
     const int k0 = t * kGK;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 2 * (4 * w + j) + (lane >> 5);
+    for (int j = 0; j < kWI; ++j) {
+      const int q = kWI * w + j;
+      const int r = 2 * q + (lane >> 5);
       const int c = (lane & 31) ^ swz_w(r);
       const int col = 8 * c < vend ? 8 * c : 0;
       int64_t rowid;
@@ -576,19 +580,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         rowid = ridx[(t & 3) * kGK + r];
       else
         rowid = m0 + min(k0 + r, rows - 1);
-      dma16(a.wide + rowid * a.wld + wcol0 + col, st + 1024 * (4 * w + j));
+      dma16(a.wide + rowid * a.wld + wcol0 + col, st + 1024 * q);
     }
 #pragma unroll
     for (int i = 0; i < kNI; ++i) {
-      if (NUT >= 32 || lane < 2 * NUT) {
-        const int g = w * 2 * NUT + 64 * i + lane;
+      if (kNCW >= 64 || lane < kNCW) {
+        const int g = w * kNCW + 64 * i + lane;
         const int r = g / kNC;
         const int c = (g % kNC) ^ swz_n(r);
         const int plane = c / (kNC / 2), cc = c % (kNC / 2);
         const void* src = k0 + r < rows
                               ? (const void*)(a.planes + (int64_t)(m0 + k0 + r) * a.prow + plane * a.pw + ncol0 + 8 * cc)
                               : a.zero;
-        dma16(src, st + kWBytes + 16 * (w * 2 * NUT + 64 * i));
+        dma16(src, st + kWBytes + 16 * (w * kNCW + 64 * i));
       }
     }
   };
@@ -629,7 +633,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     for (int s = 0; s < nsteps; ++s) {
       // step s has landed once at most the later step's copies are outstanding;
       // the barrier shows every wave's copies and frees the slot refilled next
-      if (L == 2 && s + 1 < nsteps)
+      if (s + 1 < nsteps)
         wait_vm_lgkm<kOps>();
       else
         wait_vm_lgkm<0>();
@@ -698,16 +702,16 @@ template <int FAM>
 static void launch_grad_family(int nut, unsigned grid, const GradArgs& a, hipStream_t st) {
   switch (nut) {
     case 16:
-      k_lora_grad<16, FAM><<<grid, 256, 0, st>>>(a);
+      k_lora_grad<16, FAM, 4><<<grid, 256, 0, st>>>(a);
       break;
     case 32:
-      k_lora_grad<32, FAM><<<grid, 256, 0, st>>>(a);
+      k_lora_grad<32, FAM, 4><<<grid, 256, 0, st>>>(a);
       break;
     case 64:
-      k_lora_grad<64, FAM><<<grid, 256, 0, st>>>(a);
+      k_lora_grad<64, FAM, 4><<<grid, 256, 0, st>>>(a);
       break;
-    default:
-      k_lora_grad<128, FAM><<<grid, 256, 0, st>>>(a);
+    default:  // 8 waves: the 128-column narrow block and a three-step ring take one CU's LDS
+      k_lora_grad<128, FAM, 8><<<grid, 512, 0, st>>>(a);
       break;
   }
 }
