@@ -43,6 +43,13 @@ static void plan_group_part(Planner& pl, WsMap& w, int64_t Ms, int64_t E) {
   w.tok_of_row = pl.take(sizeof(int32_t) * (size_t)Ms);
   w.tile_e = pl.take(sizeof(int32_t) * (size_t)w.max_tiles);
   w.tile_m0 = pl.take(sizeof(int32_t) * (size_t)w.max_tiles);
+  const int forced = forced_gemm_rows();
+  w.gbulk = forced ? forced : 128;
+  w.gmixed = forced == 0;
+  w.max_gtiles = Ms / w.gbulk + (E < Ms ? E : Ms);
+  w.gtile_e = pl.take(sizeof(int32_t) * (size_t)w.max_gtiles);
+  w.gtile_m0 = pl.take(sizeof(int32_t) * (size_t)w.max_gtiles);
+  w.gtile_mt = pl.take(sizeof(int32_t) * (size_t)w.max_gtiles);
   w.group_end = pl.off;
 }
 

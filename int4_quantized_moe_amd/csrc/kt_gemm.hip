@@ -74,6 +74,7 @@ struct GemmParams {
   const int32_t* offsets;
   const int32_t* tile_e;
   const int32_t* tile_m0;
+  const int32_t* tile_mt;
   const unsigned long long* counters;
   LayerPtrs L;
   const uint16_t* a_src;      // fp16 activation rows (within-8 permuted order)
@@ -138,16 +139,21 @@ __device__ __forceinline__ void clamp_swiglu(float g, float u, float limit, floa
   }
 }
 
-// Every tile height runs at least two waves per SIMD: a single wave issues VALU
-// at half the SIMD's rate, and the weight decode needs the full rate to stay
-// under the MFMA time.
+// LDS bytes of the ring of a tile height (the LoRA K-steps reuse it).
+__host__ __device__ constexpr int gemm_ring_bytes(int MT) {
+  const int a = MT * 128, st = (MT <= 32 ? 4 : 3) * (a + kWBytes + kScBytes), lora = a + 64 * kLBP;
+  return st > lora ? st : lora;
+}
+constexpr int kRingMax = gemm_ring_bytes(128) > gemm_ring_bytes(32) ? gemm_ring_bytes(128) : gemm_ring_bytes(32);
+
+// One work tile of height MT; the LDS belongs to the calling kernel.
 template <int KIND, int MT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm(GemmParams p) {
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt, uint8_t* ring, int32_t* s_src,
+                                          int32_t* s_exp, int32_t* s_slot) {
   constexpr int MB = MT / 16;
   constexpr bool kT = (KIND == kDownBwd || KIND == kGateUpBwd);
   constexpr bool kChunked = (KIND == kDown || KIND == kGateUpBwd);
   constexpr int kABytes = MT * 128;                 // activation tile of one stage
-  constexpr int kStage = kABytes + kWBytes + kScBytes;
   constexpr int kRowsPerInst = MT == 16 ? 4 : 8;     // activation rows per DMA instruction
   constexpr int kAInst = MT == 16 ? 1 : MT / 32;     // activation DMA instructions per wave per stage
   constexpr int kDmaPerStage = kAInst + 3;           // plus two weight and one scale DMA instructions
@@ -158,20 +164,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   // stages s + 1 .. s + 2 are in flight.
   constexpr bool kPipe = MT <= 32;
   constexpr int kStages = kPipe ? 4 : 3;
-  constexpr int kRing = kStages * kStage > kABytes + 64 * kLBP ? kStages * kStage : kABytes + 64 * kLBP;
+  static_assert(gemm_ring_bytes(MT) <= kRingMax, "ring");
   // the ring holds the activation tiles of all slots, then their weight tiles,
   // then their scales, so that a slot known at compile time is an immediate offset
   constexpr int kWReg = kStages * kABytes, kSReg = kStages * (kABytes + kWBytes);
-  __shared__ __align__(16) uint8_t ring[kRing];
-  __shared__ int32_t s_src[MT], s_exp[MT], s_slot[MT];
 
-  // ---------------------------------------------------------------- work item
-  const unsigned total = (unsigned)p.counters[kNumTiles] * (unsigned)p.n_ntiles;
-  if (blockIdx.x >= total) return;
-  const unsigned xq = total / 8u, xr = total % 8u, xcd = blockIdx.x % 8u;
-  const unsigned item = xcd * xq + min(xcd, xr) + blockIdx.x / 8u;
-  const int tile = (int)(item / (unsigned)p.n_ntiles);
-  const int nt = (int)(item % (unsigned)p.n_ntiles);
   const int e = p.tile_e[tile], m0 = p.tile_m0[tile];
   const int mlen = min(MT, p.offsets[e + 1] - m0);
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
@@ -796,20 +793,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   }
 }
 
+// Every tile height runs at least two waves per SIMD: a single wave issues VALU
+// at half the SIMD's rate, and the weight decode needs the full rate to stay
+// under the MFMA time.  One launch covers tiles of every height (each expert's
+// rows: full tiles of the largest height, then one tile of the smallest height
+// that holds the rest); a tile's height selects its code path.
 template <int KIND>
-static void launch_kind(int mt, unsigned grid, const GemmParams& p, hipStream_t st) {
-  switch (mt) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm(GemmParams p) {
+  __shared__ __align__(16) uint8_t ring[kRingMax];
+  __shared__ int32_t s_src[128], s_exp[128], s_slot[128];
+  // work item: (tile, column tile), column tiles fastest; each XCD (blocks are
+  // dealt to the eight in turn) takes a contiguous range
+  const unsigned total = (unsigned)p.counters[kNumGemmTiles] * (unsigned)p.n_ntiles;
+  if (blockIdx.x >= total) return;
+  const unsigned xq = total / 8u, xr = total % 8u, xcd = blockIdx.x % 8u;
+  const unsigned item = xcd * xq + min(xcd, xr) + blockIdx.x / 8u;
+  const int tile = (int)(item / (unsigned)p.n_ntiles);
+  const int nt = (int)(item % (unsigned)p.n_ntiles);
+  switch (p.tile_mt[tile]) {
     case 16:
-      k_gemm<KIND, 16><<<grid, 256, 0, st>>>(p);
+      gemm_tile<KIND, 16>(p, tile, nt, ring, s_src, s_exp, s_slot);
       break;
     case 32:
-      k_gemm<KIND, 32><<<grid, 256, 0, st>>>(p);
+      gemm_tile<KIND, 32>(p, tile, nt, ring, s_src, s_exp, s_slot);
       break;
     case 64:
-      k_gemm<KIND, 64><<<grid, 256, 0, st>>>(p);
+      gemm_tile<KIND, 64>(p, tile, nt, ring, s_src, s_exp, s_slot);
       break;
     default:
-      k_gemm<KIND, 128><<<grid, 256, 0, st>>>(p);
+      gemm_tile<KIND, 128>(p, tile, nt, ring, s_src, s_exp, s_slot);
       break;
   }
 }
@@ -826,8 +838,9 @@ void launch_gemm(GemmKind kind, const Dims& d, const WsMap& w, void* ws, const L
   p.limit = d.limit;
   p.sorted_slot = ws_ptr<int32_t>(ws, w.sorted_slot);
   p.offsets = ws_ptr<int32_t>(ws, w.offsets);
-  p.tile_e = ws_ptr<int32_t>(ws, w.tile_e);
-  p.tile_m0 = ws_ptr<int32_t>(ws, w.tile_m0);
+  p.tile_e = ws_ptr<int32_t>(ws, w.gtile_e);
+  p.tile_m0 = ws_ptr<int32_t>(ws, w.gtile_m0);
+  p.tile_mt = ws_ptr<int32_t>(ws, w.gtile_mt);
   p.counters = ws_ptr<unsigned long long>(ws, w.counters);
   p.L = L;
   p.rw = route_weights;
@@ -875,20 +888,20 @@ void launch_gemm(GemmKind kind, const Dims& d, const WsMap& w, void* ws, const L
       p.lda = 2 * d.I;
       break;
   }
-  const unsigned grid = (unsigned)(w.max_tiles * p.n_ntiles);
+  const unsigned grid = (unsigned)(w.max_gtiles * p.n_ntiles);
   if (grid == 0) return;
   switch (kind) {
     case kGateUp:
-      launch_kind<kGateUp>((int)w.mt, grid, p, st);
+      k_gemm<kGateUp><<<grid, 256, 0, st>>>(p);
       break;
     case kDown:
-      launch_kind<kDown>((int)w.mt, grid, p, st);
+      k_gemm<kDown><<<grid, 256, 0, st>>>(p);
       break;
     case kDownBwd:
-      launch_kind<kDownBwd>((int)w.mt, grid, p, st);
+      k_gemm<kDownBwd><<<grid, 256, 0, st>>>(p);
       break;
     case kGateUpBwd:
-      launch_kind<kGateUpBwd>((int)w.mt, grid, p, st);
+      k_gemm<kGateUpBwd><<<grid, 256, 0, st>>>(p);
       break;
   }
 }

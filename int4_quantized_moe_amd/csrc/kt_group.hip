@@ -56,28 +56,41 @@ __device__ int block_inclusive_scan(int v, int32_t* buf) {
   return r;
 }
 
+// Height of the tile that holds the last r rows of an expert (r <= bulk): the
+// smallest of 16, 32, 64, 128 that covers them.
+__device__ __forceinline__ int rest_tile_rows(int r, int bulk) {
+  const int h = r <= 16 ? 16 : r <= 32 ? 32 : r <= 64 ? 64 : 128;
+  return h < bulk ? h : bulk;
+}
+
 // One block: expert totals, exclusive offsets, per-block placement bases
-// (blockcnt is rewritten in place), and the list of (expert, first row) tiles
-// of `mt` rows for the expert GEMMs and the LoRA side products.
-__global__ __launch_bounds__(1024) void k_group_scan(int E, int64_t nb, int mt, int32_t* __restrict__ blockcnt,
-                                                     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                                                     int32_t* __restrict__ tile_e, int32_t* __restrict__ tile_m0,
+// (blockcnt is rewritten in place), and two lists of (expert, first row) tiles:
+// tiles of `mt` rows for the LoRA side products, and tiles for the expert GEMMs
+// -- full tiles of `gbulk` rows, then (if `gmixed`) one tile of the smallest
+// height that holds the rest of the expert's rows.
+__global__ __launch_bounds__(1024) void k_group_scan(int E, int64_t nb, int mt, int gbulk, int gmixed,
+                                                     int32_t* __restrict__ blockcnt, int32_t* __restrict__ counts,
+                                                     int32_t* __restrict__ offsets, int32_t* __restrict__ tile_e,
+                                                     int32_t* __restrict__ tile_m0, int32_t* __restrict__ gtile_e,
+                                                     int32_t* __restrict__ gtile_m0, int32_t* __restrict__ gtile_mt,
                                                      unsigned long long* __restrict__ counters) {
   __shared__ int32_t buf[1024];
   const int T = blockDim.x;
   const int per = (E + T - 1) / T;
   const int e0 = min(E, (int)threadIdx.x * per), e1 = min(E, e0 + per);
-  int local = 0, ltiles = 0;
+  int local = 0, ltiles = 0, lgt = 0;
   for (int e = e0; e < e1; ++e) {
     int c = 0;
     for (int64_t b = 0; b < nb; ++b) c += blockcnt[b * E + e];
     counts[e] = c;
     local += c;
     ltiles += (c + mt - 1) / mt;
+    lgt += (c + gbulk - 1) / gbulk;
   }
   const int incl = block_inclusive_scan(local, buf);
   const int tincl = block_inclusive_scan(ltiles, buf);
-  int run = incl - local, trun = tincl - ltiles;
+  const int gincl = block_inclusive_scan(lgt, buf);
+  int run = incl - local, trun = tincl - ltiles, grun = gincl - lgt;
   for (int e = e0; e < e1; ++e) {
     const int c = counts[e];
     offsets[e] = run;
@@ -93,11 +106,20 @@ __global__ __launch_bounds__(1024) void k_group_scan(int E, int64_t nb, int mt, 
       tile_m0[trun + j] = run + j * mt;
     }
     trun += nt;
+    const int ng = (c + gbulk - 1) / gbulk;
+    for (int j = 0; j < ng; ++j) {
+      const int rest = c - j * gbulk;
+      gtile_e[grun + j] = e;
+      gtile_m0[grun + j] = run + j * gbulk;
+      gtile_mt[grun + j] = (gmixed && rest < gbulk) ? rest_tile_rows(rest, gbulk) : gbulk;
+    }
+    grun += ng;
     run += c;
   }
   if ((int)threadIdx.x == T - 1) {
     offsets[E] = incl;
     counters[kNumTiles] = (unsigned long long)tincl;
+    counters[kNumGemmTiles] = (unsigned long long)gincl;
   }
 }
 
@@ -150,9 +172,11 @@ void launch_group(const Dims& d, const WsMap& w, void* ws, const int64_t* ids, h
   unsigned long long* counters = ws_ptr<unsigned long long>(ws, w.counters);
   const size_t lds = sizeof(int32_t) * (size_t)E;
   if (w.nb > 0) k_group_count<<<(unsigned)w.nb, 256, lds, st>>>(ids, d.Ms, E, blockcnt, counters);
-  k_group_scan<<<1, 1024, 0, st>>>(E, w.nb, (int)w.mt, blockcnt, ws_ptr<int32_t>(ws, w.counts),
-                                   ws_ptr<int32_t>(ws, w.offsets), ws_ptr<int32_t>(ws, w.tile_e),
-                                   ws_ptr<int32_t>(ws, w.tile_m0), counters);
+  k_group_scan<<<1, 1024, 0, st>>>(E, w.nb, (int)w.mt, (int)w.gbulk, w.gmixed ? 1 : 0, blockcnt,
+                                   ws_ptr<int32_t>(ws, w.counts), ws_ptr<int32_t>(ws, w.offsets),
+                                   ws_ptr<int32_t>(ws, w.tile_e), ws_ptr<int32_t>(ws, w.tile_m0),
+                                   ws_ptr<int32_t>(ws, w.gtile_e), ws_ptr<int32_t>(ws, w.gtile_m0),
+                                   ws_ptr<int32_t>(ws, w.gtile_mt), counters);
   if (w.nb > 0)
     k_group_place<<<(unsigned)w.nb, 256, lds, st>>>(ids, d.Ms, E, (int)d.K, blockcnt,
                                                    ws_ptr<int32_t>(ws, w.sorted_slot),

@@ -17,14 +17,21 @@ constexpr int kNT = 256;           // output columns per tile of the other GEMMs
 constexpr int kHExp = 32;          // columns of h per exponent (one wave's share of a gate/up tile)
 constexpr int kDgExp = 64;         // columns of dG (or dU) per exponent (one wave's share of a down-dX tile)
 
-// Rows per GEMM tile for a call: the smallest of 16/32/64/128 that covers the
-// mean number of token-slots per expert (heavier experts take several tiles).
-// KT_RAWINT4_GEMM_ROWS=16|32|64|128 overrides the choice (tuning and tests).
-inline int choose_gemm_rows(int64_t Ms, int64_t E) {
+// Rows per tile of the LoRA side products for a call: the smallest of
+// 16/32/64/128 that covers the mean number of token-slots per expert (heavier
+// experts take several tiles).  The expert GEMMs instead take full 128-row
+// tiles of each expert and one tile of the smallest height that holds the rest.
+// KT_RAWINT4_GEMM_ROWS=16|32|64|128 makes every tile of both lists that tall
+// (tuning and tests).
+inline int forced_gemm_rows() {
   if (const char* env = getenv("KT_RAWINT4_GEMM_ROWS")) {
     const int v = atoi(env);
     if (v == 16 || v == 32 || v == 64 || v == 128) return v;
   }
+  return 0;
+}
+inline int choose_gemm_rows(int64_t Ms, int64_t E) {
+  if (const int v = forced_gemm_rows()) return v;
   const int64_t active = E < Ms ? E : Ms;
   const int64_t mean = active > 0 ? (Ms + active - 1) / active : 0;
   if (mean <= 16) return 16;
@@ -41,7 +48,15 @@ inline int64_t lora_half_width(int64_t R) { return (R + 31) / 32 * 32; }
 // Device counters at the head of the workspace (kCounterWords words, all cleared
 // by the forward); words kZeroWord.. hold 16 zero bytes that copies of rows past
 // the end of an operand read instead.
-enum Counter { kBadIds = 0, kBadScales = 1, kNumTiles = 2, kNumCounters = 8, kZeroWord = 16, kCounterWords = 32 };
+enum Counter {
+  kBadIds = 0,
+  kBadScales = 1,
+  kNumTiles = 2,      // side-product tiles
+  kNumGemmTiles = 3,  // expert GEMM tiles
+  kNumCounters = 8,
+  kZeroWord = 16,
+  kCounterWords = 32
+};
 
 // LoRA gradient reductions: the rank-wide operand of each of the four families
 // (x: [dG B_g | dU B_u], dY: rw ud, h: rw dyB, dG|dU: ua | ub) is laid out as
@@ -90,6 +105,7 @@ struct WsMap {
   size_t sct_g, sct_u, sct_d;
   // grouping
   size_t counters, counts, offsets, blockcnt, sorted_slot, row_of_slot, tok_of_row, tile_e, tile_m0;
+  size_t gtile_e, gtile_m0, gtile_mt;  // expert GEMM tiles (mixed heights)
   // forward state kept for the backward
   size_t xh, xexp, ua, ub, g, u, hh, hexp, ud;
   // the side product feeding the next expert GEMM, as bf16 hi/lo planes (reused by all four)
@@ -103,6 +119,8 @@ struct WsMap {
   size_t group_end;  // bytes needed by the grouping alone
   size_t total;
   int64_t nb, mt, max_tiles, h_nch, dg_nch, dr_nt;
+  int64_t gbulk, max_gtiles;  // GEMM tiles: full height and bound on their number
+  bool gmixed;
 };
 
 WsMap plan_workspace(const Dims& d);

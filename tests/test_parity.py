@@ -181,19 +181,27 @@ def test_layer_ragged_shapes(dev):
     _check_all("ragged", gpu, ref, set(batch.expert_ids.ravel().tolist()))
 
 
-@pytest.mark.parametrize("rows", [16, 32, 64, 128])
+@pytest.mark.parametrize("rows", [16, 32, 64, 128, 0])
 def test_layer_every_tile_height(dev, rows, monkeypatch):
-    # one expert with 300 slots (several tiles of every height) plus light experts
+    # one expert with 157 slots (several tiles of every forced height) plus
+    # lighter experts; rows = 0 keeps the default, where the GEMM tiles of one
+    # launch have different heights (128 + a 32-row rest for the heavy expert,
+    # 64- and 128-row tiles for the others)
     cfg = W.LayerConfig("heights", 5, 2, 160, 224, 6, 12.0, 180, 2.5, x_std=2.0)
-    _say("layer tile height", rows)
+    _say("layer tile height", rows or "mixed")
     weights = W.make_weights(cfg, 91)
     batch = W.make_batch(cfg, 91)
     batch.expert_ids[:150, 0] = 1
     batch.expert_ids[:150, 1] = np.where(batch.expert_ids[:150, 1] == 1, 3, batch.expert_ids[:150, 1])
-    monkeypatch.setenv("KT_RAWINT4_GEMM_ROWS", str(rows))
+    if rows:
+        monkeypatch.setenv("KT_RAWINT4_GEMM_ROWS", str(rows))
+    else:
+        monkeypatch.delenv("KT_RAWINT4_GEMM_ROWS", raising=False)
+        counts = np.bincount(batch.expert_ids.ravel(), minlength=cfg.num_experts)
+        assert counts.max() > 128 and 0 < counts[counts > 0].min() <= 64
     _, _, _, gpu = _run_gpu(dev, cfg, weights, batch)
     ref = O.moe(cfg, weights, batch.inputs, batch.expert_ids, batch.route_weights, batch.grad_output)
-    _check_all(f"rows{rows}", gpu, ref, set(batch.expert_ids.ravel().tolist()))
+    _check_all(f"rows{rows or 'mixed'}", gpu, ref, set(batch.expert_ids.ravel().tolist()))
 
 
 def test_layer_dropped_ids_and_window(dev):
