@@ -82,7 +82,9 @@ WsMap plan_workspace(const Dims& d) {
   w.hexp = pl.take(4 * Ms * (size_t)w.h_nch);
   w.ud = pl.take(4 * Ms * R);
   w.lsplit = pl.take(2 * 2 * Ms * 2 * (size_t)lora_half_width((int64_t)R));
-  w.stage = pl.take(4 * Ms * H);
+  w.st_nch = (d.H + kStageExp - 1) / kStageExp;
+  w.stage = pl.take(2 * Ms * H);
+  w.stexp = pl.take(4 * Ms * (size_t)w.st_nch);
   w.dyh = pl.take(2 * q * H);
   w.dyexp = pl.take(4 * q);
   w.dyb = pl.take(4 * Ms * R);
@@ -363,7 +365,8 @@ int kt_rawint4_moe_fwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const ui
   }
   {
     PhaseScope ph(kPhCombineFwd, st);
-    launch_combine(d, ws_ptr<float>(ws, w.stage), expert_ids, output, st);
+    launch_combine(d, ws_ptr<uint16_t>(ws, w.stage), ws_ptr<int32_t>(ws, w.stexp), w.st_nch, expert_ids, output,
+                   st);
   }
   return launched();
 }
@@ -436,7 +439,8 @@ int kt_rawint4_moe_bwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const ui
   }
   {
     PhaseScope ph(kPhCombineBwd, st);
-    launch_combine(d, ws_ptr<float>(ws, w.stage), expert_ids, grad_input, st);
+    launch_combine(d, ws_ptr<uint16_t>(ws, w.stage), ws_ptr<int32_t>(ws, w.stexp), w.st_nch, expert_ids,
+                   grad_input, st);
   }
   if (grad_route) {
     PhaseScope ph(kPhDRoute, st);

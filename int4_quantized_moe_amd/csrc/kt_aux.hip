@@ -183,9 +183,11 @@ void launch_fill_zero_f32(float* p, int64_t n, hipStream_t st) {
 
 // ---------------------------------------------------------------- combine and dRoute
 
-// out[t, c] = sum over valid slots s of stage[t*k + s, c], in slot order, to bf16
-__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ stage, const int64_t* __restrict__ ids,
-                                                 int topk, int E, int64_t H, uint16_t* __restrict__ out) {
+// out[t, c] = sum over valid slots s of stage[t*k + s, c] * 2^-p(t*k + s, c / 64), in slot
+// order, in fp32, then to bf16 (round to nearest even); staged values are fp16
+__global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ stage, const int32_t* __restrict__ stexp,
+                                                 int64_t st_nch, const int64_t* __restrict__ ids, int topk, int E,
+                                                 int64_t H, uint16_t* __restrict__ out) {
   const int64_t t = blockIdx.x;
   const int64_t c = ((int64_t)blockIdx.y * blockDim.x + threadIdx.x) * 4;
   if (c >= H) return;
@@ -194,11 +196,12 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ stage
     const int64_t slot = t * topk + s;
     const int64_t e = ids[slot];
     if (e < 0 || e >= E) continue;
-    const float4 v = *reinterpret_cast<const float4*>(stage + slot * H + c);
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
+    const uint2 v = *reinterpret_cast<const uint2*>(stage + slot * H + c);
+    const int ex = -stexp[slot * st_nch + c / kStageExp];
+    acc.x += ldexpf(half_bits_to_float((uint16_t)(v.x & 0xffffu)), ex);
+    acc.y += ldexpf(half_bits_to_float((uint16_t)(v.x >> 16)), ex);
+    acc.z += ldexpf(half_bits_to_float((uint16_t)(v.y & 0xffffu)), ex);
+    acc.w += ldexpf(half_bits_to_float((uint16_t)(v.y >> 16)), ex);
   }
   uint2 o;
   o.x = float_to_bf16(acc.x) | ((uint32_t)float_to_bf16(acc.y) << 16);
@@ -206,10 +209,11 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ stage
   *reinterpret_cast<uint2*>(out + t * H + c) = o;
 }
 
-void launch_combine(const Dims& d, const float* stage, const int64_t* ids, uint16_t* out, hipStream_t st) {
+void launch_combine(const Dims& d, const uint16_t* stage, const int32_t* stexp, int64_t st_nch, const int64_t* ids,
+                    uint16_t* out, hipStream_t st) {
   if (d.qlen == 0) return;
   dim3 grid((unsigned)d.qlen, (unsigned)((d.H / 4 + 255) / 256));
-  k_combine<<<grid, 256, 0, st>>>(stage, ids, (int)d.K, (int)d.E, d.H, out);
+  k_combine<<<grid, 256, 0, st>>>(stage, stexp, st_nch, ids, (int)d.K, (int)d.E, d.H, out);
 }
 
 __global__ void k_droute(const int32_t* __restrict__ row_of_slot, const float* __restrict__ drpart, int64_t Ms,

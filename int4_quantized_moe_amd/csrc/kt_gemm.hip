@@ -92,7 +92,9 @@ struct GemmParams {
   uint16_t* hh;
   int32_t* hexp;
   int h_nch;
-  float* stage;
+  uint16_t* stage;  // per-slot rows in fp16 times 2^p
+  int32_t* stexp;   // p per (slot row, kStageExp columns)
+  int st_nch;
   uint16_t* dgu;
   int32_t* dguexp;
   int dg_nch;
@@ -726,18 +728,31 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
         }
       }
   } else if constexpr (KIND == kDown || KIND == kGateUpBwd) {
+    // per-slot rows (forward y * rw, backward dx) in fp16 times 2^p, p per
+    // (row, this wave's 64 columns); the combine sums them per token
+    const int chunk = (n0 + w * 64) / kStageExp;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = mb * 16 + lg * 4 + i;
-        if (row >= mlen) continue;
-        const int slot = s_slot[row];
-        const float wgt = (KIND == kDown) ? p.rw[slot] : 1.f;
+        const bool vrow = row < mlen;
+        const int slot = vrow ? s_slot[row] : 0;
+        const float wgt = (KIND == kDown && vrow) ? p.rw[slot] : 1.f;
+        float v[4];
+        float mx = 0.f;
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
           const int col = n0 + w * 64 + f * 16 + lr;
-          if (col < H) p.stage[(size_t)slot * H + col] = wgt * acc[mb][f][i];
+          v[f] = (vrow && col < H) ? wgt * acc[mb][f][i] : 0.f;
+          mx = fmaxf(mx, fabsf(v[f]));
+        }
+        const int pe = pow2_exponent_for(row16_max(mx));
+        if (vrow && lr == 0 && n0 + w * 64 < H) p.stexp[(size_t)slot * p.st_nch + chunk] = pe;
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          const int col = n0 + w * 64 + f * 16 + lr;
+          if (vrow && col < H) p.stage[(size_t)slot * H + col] = float_to_half_bits(ldexpf(v[f], pe));
         }
       }
   } else {  // kDownBwd
@@ -849,7 +864,9 @@ void launch_gemm(GemmKind kind, const Dims& d, const WsMap& w, void* ws, const L
   p.hh = ws_ptr<uint16_t>(ws, w.hh);
   p.hexp = ws_ptr<int32_t>(ws, w.hexp);
   p.h_nch = (int)w.h_nch;
-  p.stage = ws_ptr<float>(ws, w.stage);
+  p.stage = ws_ptr<uint16_t>(ws, w.stage);
+  p.stexp = ws_ptr<int32_t>(ws, w.stexp);
+  p.st_nch = (int)w.st_nch;
   p.dgu = ws_ptr<uint16_t>(ws, w.dgu);
   p.dguexp = ws_ptr<int32_t>(ws, w.dguexp);
   p.dg_nch = (int)w.dg_nch;

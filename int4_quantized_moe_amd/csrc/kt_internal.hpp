@@ -16,6 +16,7 @@ constexpr int kHChunk = 128;       // columns of I per gate/up tile
 constexpr int kNT = 256;           // output columns per tile of the other GEMMs
 constexpr int kHExp = 32;          // columns of h per exponent (one wave's share of a gate/up tile)
 constexpr int kDgExp = 64;         // columns of dG (or dU) per exponent (one wave's share of a down-dX tile)
+constexpr int kStageExp = 64;      // columns of a staged per-slot row per exponent (one wave's share of a tile)
 
 // Rows per tile of the LoRA side products for a call: the smallest of
 // 16/32/64/128 that covers the mean number of token-slots per expert (heavier
@@ -110,8 +111,9 @@ struct WsMap {
   size_t xh, xexp, ua, ub, g, u, hh, hexp, ud;
   // the side product feeding the next expert GEMM, as bf16 hi/lo planes (reused by all four)
   size_t lsplit;
-  // transient staging of per-slot rows (forward y, backward dx)
-  size_t stage;
+  // transient staging of per-slot rows (forward y * rw, backward dx): fp16 [Ms][H] with one
+  // power-of-two exponent per (row, kStageExp columns) [Ms][st_nch]
+  size_t stage, stexp;
   // backward
   size_t dyh, dyexp, dyb, dgu, dguexp, dgb, dub, drpart;
   // LoRA gradients: narrow-operand planes ([Ms][GradGeom::row] 16-bit) and per-expert exponents [E][2]
@@ -119,7 +121,7 @@ struct WsMap {
   size_t group_end;  // bytes needed by the grouping alone
   size_t total;
   int64_t nb, mt, max_tiles, h_nch, dg_nch, dr_nt;
-  int64_t gbulk, max_gtiles;  // GEMM tiles: full height and bound on their number
+  int64_t gbulk, max_gtiles, st_nch;  // GEMM tiles: full height and bound on their number
   bool gmixed;
 };
 
@@ -185,7 +187,8 @@ void launch_scales_t(const uint16_t* s, int64_t E, int64_t rows, int64_t G, cons
 void launch_normalize_chunks(uint16_t* buf, int32_t* exps, const int32_t* nrows, int64_t max_rows, int64_t cols,
                              int64_t split, int nch, int chunkw, hipStream_t st);
 
-void launch_combine(const Dims& d, const float* stage, const int64_t* ids, uint16_t* out, hipStream_t st);
+void launch_combine(const Dims& d, const uint16_t* stage, const int32_t* stexp, int64_t st_nch, const int64_t* ids,
+                    uint16_t* out, hipStream_t st);
 void launch_droute(const Dims& d, const WsMap& w, void* ws, float* grad_route, hipStream_t st);
 void launch_init_counters(void* ws, const WsMap& w, hipStream_t st);
 
