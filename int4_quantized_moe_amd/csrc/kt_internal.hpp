@@ -121,7 +121,10 @@ struct WsMap {
   size_t group_end;  // bytes needed by the grouping alone
   size_t total;
   int64_t nb, mt, max_tiles, h_nch, dg_nch, dr_nt;
-  int64_t gbulk, max_gtiles, st_nch;  // GEMM tiles: full height and bound on their number
+  int64_t gbulk, max_gtiles, st_nch;
+  // LoRA side products: contraction ranges per tile and their partial sums [ksplit][Ms][2R]
+  int64_t side_ksplit;
+  size_t side_part;  // GEMM tiles: full height and bound on their number
   bool gmixed;
 };
 

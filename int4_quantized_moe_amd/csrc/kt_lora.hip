@@ -22,6 +22,8 @@
 // ds_read_tr16_b64, which hands each lane 4 consecutive rows of one column.
 #include <limits.h>
 
+#include <algorithm>
+
 #include "kt_common.hpp"
 #include "kt_internal.hpp"
 
@@ -67,7 +69,36 @@ struct SideArgs {
   uint16_t* split;  // bf16 hi/lo planes [Ms][2][split_ld] of the product times split_scale
   int64_t split_ld, split_off, split_off2;
   float split_scale;
+  int ksplit;   // contraction ranges (blockIdx.y); above 1 the blocks write partial sums
+  float* part;  // [ksplit][Ms][nq] partial sums, reduced in order by k_side_reduce
+  int64_t Ms;
+  const int32_t* nrows;  // rows routed to an expert (offsets[E])
 };
+
+// product column col of sorted row m: the fp32 output and its bf16 hi/lo planes
+__device__ __forceinline__ void side_store(const SideArgs& a, int64_t m, int col, float v) {
+  const int R = a.R;
+  if (col < R)
+    a.out[m * R + col] = v;
+  else
+    a.out2[m * R + (col - R)] = v;
+  uint16_t hi, lo;
+  split_bf16(v * a.split_scale, hi, lo);
+  const int64_t sc = col < R ? a.split_off + col : a.split_off2 + (col - R);
+  a.split[m * 2 * a.split_ld + sc] = hi;
+  a.split[m * 2 * a.split_ld + a.split_ld + sc] = lo;
+}
+
+// sum of the partial products over the contraction ranges, in range order
+__global__ __launch_bounds__(256) void k_side_reduce(SideArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t m = i / a.nq;
+  const int col = (int)(i % a.nq);
+  if (m >= *a.nrows) return;  // only rows routed to an expert were multiplied
+  float v = 0.f;
+  for (int ks = 0; ks < a.ksplit; ++ks) v += a.part[((int64_t)ks * a.Ms + m) * a.nq + col];
+  side_store(a, m, col, v);
+}
 
 // slot t of an aligned group of 8 in the within-8 permuted order holds logical offset:
 __device__ __forceinline__ int perm_src(int t) { return (t & 1) ? 4 + (t >> 1) : (t >> 1); }
@@ -199,13 +230,16 @@ __global__ __launch_bounds__(256) void k_lora_side(SideArgs a) {
     for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
   const int cw = w * 16 * NB;  // this wave's first column
   const int asw = (lr >> 2) & 3;
-  const int nsteps = kdim / kSK;
-  load(0);
+  // this block's contraction range: steps [s0, s1) of kSK values
+  const int ksteps = kdim / kSK, ks = blockIdx.y;
+  const int s0 = (int)((int64_t)ksteps * ks / a.ksplit), s1 = (int)((int64_t)ksteps * (ks + 1) / a.ksplit);
+  const int nsteps = s1 - s0;
+  load(s0 * kSK);
   store(0);
   __syncthreads();
   for (int s = 0; s < nsteps; ++s) {
     const int cur = s & 1;
-    if (s + 1 < nsteps) load((s + 1) * kSK);
+    if (s + 1 < nsteps) load((s0 + s + 1) * kSK);
     if (cw < a.nq) {
       u32x4 bh[NB], bl[NB];
 #pragma unroll
@@ -257,21 +291,16 @@ __global__ __launch_bounds__(256) void k_lora_side(SideArgs a) {
         const int col = cw + 16 * nb + lr;
         if (col >= a.nq) continue;
         const float v = HALF ? ldexpf(acc[mb][nb][i], -ex) : acc[mb][nb][i];
-        if (col < R)
-          a.out[m * R + col] = v;
+        if (a.ksplit > 1)
+          a.part[((int64_t)ks * a.Ms + m) * a.nq + col] = v;
         else
-          a.out2[m * R + (col - R)] = v;
-        uint16_t hi, lo;
-        split_bf16(v * a.split_scale, hi, lo);
-        const int64_t sc = col < R ? a.split_off + col : a.split_off2 + (col - R);
-        a.split[m * 2 * a.split_ld + sc] = hi;
-        a.split[m * 2 * a.split_ld + a.split_ld + sc] = lo;
+          side_store(a, m, col, v);
       }
     }
 }
 
 template <int MT, int NB>
-static void launch_side_nb(bool half, unsigned grid, const SideArgs& a, hipStream_t st) {
+static void launch_side_nb(bool half, dim3 grid, const SideArgs& a, hipStream_t st) {
   if (half)
     k_lora_side<MT, NB, true><<<grid, 256, 0, st>>>(a);
   else
@@ -279,7 +308,7 @@ static void launch_side_nb(bool half, unsigned grid, const SideArgs& a, hipStrea
 }
 
 template <int MT>
-static void launch_side_mt(int nb, bool half, unsigned grid, const SideArgs& a, hipStream_t st) {
+static void launch_side_mt(int nb, bool half, dim3 grid, const SideArgs& a, hipStream_t st) {
   if (nb <= 1)
     launch_side_nb<MT, 1>(half, grid, a, st);
   else if (nb == 2)
@@ -320,7 +349,14 @@ void launch_lora_rowproj(const Dims& d, const WsMap& w, void* ws, const RowView&
   a.split_scale = d.sc;
   const bool half = src.kind == kSrcHalfChunked;
   const int nb = (a.nq + 63) / 64;
-  const unsigned grid = (unsigned)w.max_tiles;
+  // few tiles (small token counts) leave most CUs idle through a long
+  // contraction: split it over blocks and reduce the partial sums in order
+  a.ksplit = (int)std::min<int64_t>(w.side_ksplit, kdim / (4 * kSK));
+  if (a.ksplit < 1) a.ksplit = 1;
+  a.part = ws_ptr<float>(ws, w.side_part);
+  a.Ms = d.Ms;
+  a.nrows = a.offsets + d.E;
+  const dim3 grid((unsigned)w.max_tiles, (unsigned)a.ksplit);
   switch (w.mt) {
     case 16:
       launch_side_mt<16>(nb, half, grid, a, st);
@@ -334,6 +370,10 @@ void launch_lora_rowproj(const Dims& d, const WsMap& w, void* ws, const RowView&
     default:
       launch_side_mt<128>(nb, half, grid, a, st);
       break;
+  }
+  if (a.ksplit > 1) {
+    const int64_t n = d.Ms * a.nq;
+    k_side_reduce<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(a);
   }
 }
 
