@@ -58,11 +58,11 @@ extern "C" {
  * gate and up have N = I, K = H; down has N = H, K = I.  Weight rows must be
  * 16-byte aligned (true for any base pointer aligned to 16 bytes).
  *
- * Numeric domain: nonzero scales must lie in [2^-14, 8160] in magnitude (every
+ * Numeric domain: nonzero scales must lie in [2^-14, 2720] in magnitude (every
  * bf16 scale of a practical int4 checkpoint does).  There each decoded weight
  * is exact in fp16, which is what the kernels multiply with.  Scales outside
- * the domain are counted (see kt_rawint4_moe_diagnostics) and computed with
- * reduced precision.
+ * the domain are counted (see kt_rawint4_moe_diagnostics); results computed
+ * with them are not defined (they may be inf or NaN).
  *
  * LoRA tensors (fp32): gate_lora_a [E, r, H], gate_lora_b [E, I, r],
  * up_lora_a [E, r, H], up_lora_b [E, I, r], down_lora_a [E, r, I],

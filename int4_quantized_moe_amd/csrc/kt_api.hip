@@ -346,7 +346,7 @@ int kt_rawint4_moe_fwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const ui
   {
     PhaseScope ph(kPhLoraXA, st);
     launch_lora_rowproj(d, w, ws, xv, d.H, L.ag, L.au, true, ws_ptr<float>(ws, w.ua), ws_ptr<float>(ws, w.ub),
-                        2 * lora_half_width(d.R), 0, lora_half_width(d.R), st);
+                        2 * lora_half_width(d.R), 0, lora_half_width(d.R), ws_ptr<int32_t>(ws, w.xexp), st);
   }
   {
     PhaseScope ph(kPhGemmGateUp, st);
@@ -361,7 +361,7 @@ int kt_rawint4_moe_fwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const ui
   {
     PhaseScope ph(kPhLoraHA, st);
     launch_lora_rowproj(d, w, ws, hv, d.I, L.ad, nullptr, true, ws_ptr<float>(ws, w.ud), nullptr,
-                        lora_half_width(d.R), 0, 0, st);
+                        lora_half_width(d.R), 0, 0, nullptr, st);
   }
   {
     PhaseScope ph(kPhGemmDown, st);
@@ -416,7 +416,7 @@ int kt_rawint4_moe_bwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const ui
   {
     PhaseScope ph(kPhLoraDyB, st);
     launch_lora_rowproj(d, w, ws, dyv, d.H, L.bd, nullptr, false, ws_ptr<float>(ws, w.dyb), nullptr,
-                        lora_half_width(d.R), 0, 0, st);
+                        lora_half_width(d.R), 0, 0, ws_ptr<int32_t>(ws, w.dyexp), st);
   }
   {
     PhaseScope ph(kPhGemmDownBwd, st);
@@ -433,9 +433,9 @@ int kt_rawint4_moe_bwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const ui
   {
     PhaseScope ph(kPhLoraDgB, st);
     launch_lora_rowproj(d, w, ws, dgv, d.I, L.bg, nullptr, false, ws_ptr<float>(ws, w.dgb), nullptr,
-                        2 * lora_half_width(d.R), 0, 0, st);
+                        2 * lora_half_width(d.R), 0, 0, nullptr, st);
     launch_lora_rowproj(d, w, ws, duv, d.I, L.bu, nullptr, false, ws_ptr<float>(ws, w.dub), nullptr,
-                        2 * lora_half_width(d.R), lora_half_width(d.R), 0, st);
+                        2 * lora_half_width(d.R), lora_half_width(d.R), 0, nullptr, st);
   }
   {
     PhaseScope ph(kPhGemmGateUpBwd, st);

@@ -257,14 +257,17 @@ __global__ void k_dequant(const uint8_t* __restrict__ packed, const uint16_t* __
   if (i >= n * dwords_per_row) return;
   const int64_t row = i / dwords_per_row, d = i % dwords_per_row;
   const uint32_t wv = reinterpret_cast<const uint32_t*>(packed + row * (k / 2))[d];
+  // the decoder of the forward matrix kernels (codes along the packed row)
   const _Float16 s = (_Float16)bf16_to_float(scales[row * (k / kGroup) + (d * 8) / kGroup]);
-  const u32x4 r = decode_dword(wv, half2_t{s, s});
-  const uint32_t words[4] = {r.x, r.y, r.z, r.w};
+  const half2_t s2 = {s, s};
+  const u32x4 r = decode_dword_fma(wv, s2 * (half2_t){16.f16, 16.f16}, s2 * (half2_t){-24.f16, -24.f16},
+                                   decode_consts());
+  const uint32_t words[4] = {r.x, r.y, r.z, r.w};  // (k0, k4), (k1, k5), (k2, k6), (k3, k7)
   float* o = out + row * k + d * 8;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    o[2 * j] = half_bits_to_float((uint16_t)(words[j] & 0xffffu));
-    o[2 * j + 1] = half_bits_to_float((uint16_t)(words[j] >> 16));
+    o[j] = half_bits_to_float((uint16_t)(words[j] & 0xffffu));
+    o[j + 4] = half_bits_to_float((uint16_t)(words[j] >> 16));
   }
 }
 

@@ -69,21 +69,12 @@ __device__ __forceinline__ void split8(const float* v, u32x4& hi, u32x4& lo) {
 
 // ---------------------------------------------------------------- RAWINT4 decode
 
-// Nonzero scales in [2^-14, 8160] make (c - 8) * scale exact in fp16.
+// Nonzero scales in [2^-14, 2720] make both decoders exact: (c - 8) * scale is
+// an fp16 value, and so are 16 * scale and 24 * scale (24 * 2720 is the largest
+// multiple below fp16's maximum that a bf16 scale reaches).
 __device__ __forceinline__ bool scale_in_domain(float s) {
   float a = fabsf(s);
-  return a == 0.f || (a >= 6.103515625e-05f && a <= 8160.f);
-}
-
-// fp16 pair ((c0 - 8) * s0, (c1 - 8) * s1) from nibble codes c0, c1 in [0, 15].
-// 0x6400 | c is the fp16 value 1024 + c; subtracting 1032 leaves c - 8 exactly,
-// and the product with an in-domain scale is exact.
-__device__ __forceinline__ uint32_t decode_pair(uint32_t c0, uint32_t c1, half2_t s) {
-  uint32_t magic = c0 | (c1 << 16) | 0x64006400u;
-  half2_t v = __builtin_bit_cast(half2_t, magic);
-  const half2_t bias = {(_Float16)1032.0f, (_Float16)1032.0f};
-  v = (v - bias) * s;
-  return __builtin_bit_cast(uint32_t, v);
+  return a == 0.f || (a >= 6.103515625e-05f && a <= 2720.f);
 }
 
 // Activation rows in fp16 are stored with every aligned group of 8 elements in
@@ -91,17 +82,32 @@ __device__ __forceinline__ uint32_t decode_pair(uint32_t c0, uint32_t c1, half2_
 // produces weights; the position of logical element k:
 __host__ __device__ __forceinline__ int perm_pos(int k) { return (k & ~7) | ((k & 3) << 1) | ((k >> 2) & 1); }
 
-// The decode's nibble mask and fp16 magic as values the compiler cannot see
-// through: with them (w & m) | o becomes one v_and_or_b32 (literal operands
-// would make it split the and-or in two).  Made once per kernel.
+// The decoders' nibble masks and fp16 magic values as values the compiler
+// cannot see through: with them (w & m) | o becomes one v_and_or_b32 (literal
+// operands would make it split the and-or in two).  Made once per kernel.
 struct DecodeConsts {
-  uint32_t m, o;
+  uint32_t m, o;    // nibble at bits 0-3 of each half; 1024 + c
+  uint32_t m6, o6;  // nibble at bits 6-9 of each half; 1 + c / 16
 };
 __device__ __forceinline__ DecodeConsts decode_consts() {
-  uint32_t m = 0x000F000Fu, o = 0x64006400u;
-  asm volatile("" : "+s"(m));
-  asm volatile("" : "+v"(o));
-  return DecodeConsts{m, o};
+  uint32_t m = 0x000F000Fu, o = 0x64006400u, m6 = 0x03C003C0u, o6 = 0x3C003C00u;
+  asm volatile("" : "+s"(m), "+s"(m6));
+  asm volatile("" : "+v"(o), "+v"(o6));
+  return DecodeConsts{m, o, m6, o6};
+}
+
+// 8 codes of one packed dword, each with one scale s per pair of halves, in the
+// order k0 k4 k1 k5 k2 k6 k3 k7, by one fused multiply-add per pair: the code
+// sits in the top four mantissa bits of an fp16 1.0 (h = 1 + c / 16), and
+// h * 16s - 24s = (c - 8) s.  The product is exact inside the fma, 16s and 24s
+// are exact fp16 values for in-domain scales, and so is the result: one
+// rounding of an exact value.  s16 = 16 s, b24 = -24 s.
+__device__ __forceinline__ u32x4 decode_dword_fma(uint32_t w, half2_t s16, half2_t b24, DecodeConsts dc) {
+  auto pair = [&](uint32_t t) {
+    const half2_t h = __builtin_bit_cast(half2_t, (t & dc.m6) | dc.o6);
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(h, s16, b24));
+  };
+  return u32x4{pair(w << 6), pair(w << 2), pair(w >> 2), pair(w >> 6)};
 }
 
 // 8 codes of one packed dword (nibble i = code k_i) -> fp16 weights in the order
@@ -119,15 +125,18 @@ __device__ __forceinline__ u32x4 decode_dword_perm(uint32_t w, half2_t s0, half2
   return r;
 }
 
-// 8 consecutive codes of one packed dword (low nibble first) -> 8 fp16 values
-// in natural k order, all with scale s.
-__device__ __forceinline__ u32x4 decode_dword(uint32_t w, half2_t s) {
-  u32x4 r;
-  r.x = decode_pair(w & 15u, (w >> 4) & 15u, s);
-  r.y = decode_pair((w >> 8) & 15u, (w >> 12) & 15u, s);
-  r.z = decode_pair((w >> 16) & 15u, (w >> 20) & 15u, s);
-  r.w = decode_pair((w >> 24) & 15u, w >> 28, s);
-  return r;
+// 8 fp32 -> bf16 hi (top 16 bits) and lo (top 16 bits of the exact remainder)
+__device__ __forceinline__ void split8_trunc(const float* v, u32x4& hi, u32x4& lo) {
+  uint32_t h[8], l[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t u = __float_as_uint(v[i]);
+    h[i] = u & 0xffff0000u;
+    l[i] = __float_as_uint(v[i] - __uint_as_float(h[i]));
+  }
+  hi = u32x4{(h[0] >> 16) | h[1], (h[2] >> 16) | h[3], (h[4] >> 16) | h[5], (h[6] >> 16) | h[7]};
+  lo = u32x4{(l[0] >> 16) | (l[1] & 0xffff0000u), (l[2] >> 16) | (l[3] & 0xffff0000u),
+             (l[4] >> 16) | (l[5] & 0xffff0000u), (l[6] >> 16) | (l[7] & 0xffff0000u)};
 }
 
 // ---------------------------------------------------------------- MFMA
@@ -140,6 +149,27 @@ __device__ __forceinline__ floatx4 mfma_f16(u32x4 a, u32x4 b, floatx4 c) {
 __device__ __forceinline__ floatx4 mfma_bf16(u32x4 a, u32x4 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
                                                  0, 0, 0);
+}
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+// 16x16x16 bf16: lane l holds row (A) or column (B) l % 16, contraction values 4 (l / 16) .. + 3
+__device__ __forceinline__ floatx4 mfma_bf16_k16(u32x2 a, u32x2 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, a), __builtin_bit_cast(short4_t, b), c,
+                                                   0, 0, 0);
+}
+
+// 4 fp32 -> bf16 hi (top 16 bits) and lo (top 16 bits of the exact remainder)
+__device__ __forceinline__ void split4_trunc(float4 v, u32x2& hi, u32x2& lo) {
+  const float x[4] = {v.x, v.y, v.z, v.w};
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = __float_as_uint(x[i]) & 0xffff0000u;
+    l[i] = __float_as_uint(x[i] - __uint_as_float(h[i]));
+  }
+  hi = u32x2{(h[0] >> 16) | h[1], (h[2] >> 16) | h[3]};
+  lo = u32x2{(l[0] >> 16) | (l[1] & 0xffff0000u), (l[2] >> 16) | (l[3] & 0xffff0000u)};
 }
 
 // ---------------------------------------------------------------- 16-lane reductions (DPP)

@@ -10,27 +10,30 @@
 //
 // A work tile is MT token-slot rows of one expert (rows sorted by the grouping)
 // by kNT = 256 output columns; the four waves of a workgroup split the columns
-// (64 each) and share the activation tile.  Operands move through a three-stage
-// LDS ring of 64 contraction values per stage, filled by direct global-to-LDS
-// 16-byte loads (no register staging): while one stage is multiplied the next
-// two are in flight.  The ring waits are explicit (vmcnt) around a bare
-// s_barrier, so the compiler's conservative drain at __syncthreads does not
-// serialise the ring.  Blocks are mapped to tiles so that each XCD (blocks are
-// dealt to the eight XCDs in turn) works through a contiguous range of tiles:
-// the column tiles of one row tile, and the row tiles of one expert, then share
-// that XCD's L2.
+// (64 each) and share the activation tile.  Each expert's rows take full
+// 128-row tiles and one tile of the smallest height (16/32/64/128) that holds
+// the rest; one launch covers every height.  Operands move through an LDS ring
+// of 64 contraction values per stage, filled by direct global-to-LDS 16-byte
+// loads (no register staging): three stages for 64/128-row tiles, five or six
+// for 32/16-row tiles, whose fragments of the next stage are read and decoded
+// while the current one is multiplied.  The ring waits are explicit (vmcnt)
+// around a bare s_barrier, so the compiler's conservative drain at
+// __syncthreads does not serialise the ring.  Blocks are mapped to tiles so that
+// each XCD (blocks are dealt to the eight XCDs in turn) works through a
+// contiguous range of tiles: the column tiles of one row tile, and the row tiles
+// of one expert, then share that XCD's L2.
 //
 // Weights are decoded on the fly into exact fp16 ((c - 8) * scale fits fp16's
 // 11-bit significand) and multiplied on v_mfma_f32_16x16x32_f16 with fp32
 // accumulation.  In the stored orientation (kGateUp, kDown: contraction along
 // the packed K) each column's 32 packed bytes of a stage sit in LDS and a lane
-// reads its 16 nibbles with one 8-byte read.  The two gradient GEMMs contract
-// over the weight rows: the raw packed rows are copied into LDS as they are and
-// read back with ds_read_tr4_b64, which hands each lane 16 consecutive rows of
-// one column; this is the transpose-free dX of transpose_free_rawint4_dx with
-// the transpose done by the LDS read.  Scales pass through registers into LDS
-// one stage ahead, converted to fp16 on the way (the transposed orientation
-// stores them transposed, in the activation's permuted order).
+// reads its 16 nibbles with one 8-byte read; one fused multiply-add per pair of
+// weights decodes them (decode_dword_fma).  The two gradient GEMMs contract over
+// the weight rows: the raw packed rows are copied into LDS as they are and read
+// back with ds_read_tr4_b64, which hands each lane 16 consecutive rows of one
+// column; this is the transpose-free dX of transpose_free_rawint4_dx with the
+// transpose done by the LDS read.  The scales come from the forward's fp16
+// transposed copy ([E][K/32][N], rows within-8 permuted) by the same copies.
 //
 // LDS tiles are XOR-swizzled in 16-byte units so that the fragment reads of a
 // wave spread over the banks: activation row r keeps chunk c in slot
@@ -141,15 +144,44 @@ __device__ __forceinline__ void clamp_swiglu(float g, float u, float limit, floa
   }
 }
 
+// Ring depth of a tile height: the 128-row ring sets the LDS of the kernel
+// (two workgroups per CU), and shorter tiles spend the same LDS on more stages
+// in flight, which is what keeps memory busy when there are few rows to multiply.
+__host__ __device__ constexpr int gemm_stages(int MT) { return MT == 16 ? 6 : MT == 32 ? 5 : 3; }
 // LDS bytes of the ring of a tile height (the LoRA K-steps reuse it).
 __host__ __device__ constexpr int gemm_ring_bytes(int MT) {
-  const int a = MT * 128, st = (MT <= 32 ? 4 : 3) * (a + kWBytes + kScBytes), lora = a + 64 * kLBP;
+  const int a = MT * 128, st = gemm_stages(MT) * (a + kWBytes + kScBytes), lora = a + 64 * kLBP;
   return st > lora ? st : lora;
 }
-constexpr int kRingMax = gemm_ring_bytes(128) > gemm_ring_bytes(32) ? gemm_ring_bytes(128) : gemm_ring_bytes(32);
+constexpr int kRingMax = gemm_ring_bytes(128);
+static_assert(gemm_ring_bytes(16) <= kRingMax && gemm_ring_bytes(32) <= kRingMax && gemm_ring_bytes(64) <= kRingMax,
+              "the 128-row ring is the largest");
 
-// One work tile of height MT; the LDS belongs to the calling kernel.
-template <int KIND, int MT>
+// s_waitcnt vmcnt <= n * D (lgkmcnt 0) for a run-time n in [0, 4]
+template <int D>
+__device__ __forceinline__ void wait_stages(int n) {
+  switch (n) {
+    case 0:
+      wait_vm_lgkm<0>();
+      break;
+    case 1:
+      wait_vm_lgkm<D>();
+      break;
+    case 2:
+      wait_vm_lgkm<2 * D>();
+      break;
+    case 3:
+      wait_vm_lgkm<3 * D>();
+      break;
+    default:
+      wait_vm_lgkm<4 * D>();
+      break;
+  }
+}
+
+// One work tile of height MT; the LDS belongs to the calling kernel.  LDMA:
+// the LoRA matrix is copied by DMA in whole 16-byte runs (rank a multiple of 4).
+template <int KIND, int MT, bool LDMA>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt, uint8_t* ring, int32_t* s_src,
                                           int32_t* s_exp, int32_t* s_slot) {
   constexpr int MB = MT / 16;
@@ -160,12 +192,14 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
   constexpr int kAInst = MT == 16 ? 1 : MT / 32;     // activation DMA instructions per wave per stage
   constexpr int kDmaPerStage = kAInst + 3;           // plus two weight and one scale DMA instructions
   // Up to 32 rows the fragments of the next stage are read and decoded while
-  // the current one is multiplied (kPipe; stages s + 2 .. s + 3 in flight).
-  // Taller tiles need the registers for accumulators: each stage is decoded
-  // and multiplied in turn, two workgroups per CU overlap each other, and
-  // stages s + 1 .. s + 2 are in flight.
+  // the current one is multiplied (kPipe; stages s + 2 .. s + kStages - 1 in
+  // flight).  Taller tiles need the registers for accumulators: each stage is
+  // decoded and multiplied in turn, two workgroups per CU overlap each other,
+  // and stages s + 1 .. s + 2 are in flight.
   constexpr bool kPipe = MT <= 32;
-  constexpr int kStages = kPipe ? 4 : 3;
+  constexpr int kStages = gemm_stages(MT);
+  static_assert(!kPipe || (kStages >= 4 && kStages - 3 <= 4), "pipelined ring depth");
+  static_assert(kPipe || kStages == 3, "ring depth");
   static_assert(gemm_ring_bytes(MT) <= kRingMax, "ring");
   // the ring holds the activation tiles of all slots, then their weight tiles,
   // then their scales, so that a slot known at compile time is an immediate offset
@@ -445,13 +479,17 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
         const uint32_t sh = Sc[(lg >> 1) * kNT + local_col<KIND>(w, f) + perm_pos(lr)];
         bs[f] = sh | (sh << 16);
       }
+      half2_t s16[4], b24[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const half2_t s2 = __builtin_bit_cast(half2_t, bs[f]);
+        s16[f] = s2 * (half2_t){16.f16, 16.f16};
+        b24[f] = s2 * (half2_t){-24.f16, -24.f16};
+      }
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
-          const half2_t s2 = __builtin_bit_cast(half2_t, bs[f]);
-          bf[j][f] = decode_dword_perm(raw[f][j], s2, s2, s2, s2, dc);
-        }
+        for (int f = 0; f < 4; ++f) bf[j][f] = decode_dword_fma(raw[f][j], s16[f], b24[f], dc);
     }
   };
   // activation fragments of one stage from its slot
@@ -479,16 +517,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
   // read and its weights decoded.
   auto step = [&](int ss, const u32x4 (&acur)[2][MB], const u32x4 (&bcur)[2][4], u32x4 (&anxt)[2][MB],
                   u32x4 (&bnxt)[2][4]) {
-    static_assert(!kPipe || kStages == 4, "ring depth");
-    if (ss + 1 < nss) {
-      const int later = min(kStages - 3, nss - 2 - ss);  // stages issued after stage ss + 1
-      if (later >= 2)
-        wait_vm_lgkm<2 * kDmaPerStage>();
-      else if (later == 1)
-        wait_vm_lgkm<kDmaPerStage>();
-      else
-        wait_vm_lgkm<0>();
-    }
+    if (ss + 1 < nss) wait_stages<kDmaPerStage>(min(kStages - 3, nss - 2 - ss));  // stages issued after ss + 1
     __builtin_amdgcn_s_barrier();
     if (ss + kStages - 1 < nss) issue(ss + kStages - 1);
     const int sn = min(ss + 1, nss - 1);  // (re-reads the last stage at the end; unused)
@@ -510,13 +539,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
     u32x4 afa[2][MB], afb[2][MB], bfa[2][4], bfb[2][4];
     {
       // stage 0 landed: the stages issued after it may still be in flight
-      const int later = min(kStages - 2, nss - 1);
-      if (later >= 2)
-        wait_vm_lgkm<2 * kDmaPerStage>();
-      else if (later == 1)
-        wait_vm_lgkm<kDmaPerStage>();
-      else
-        wait_vm_lgkm<0>();
+      wait_stages<kDmaPerStage>(min(kStages - 2, nss - 1));
       __builtin_amdgcn_s_barrier();
       read_a(0, afa);
       decode(0, bfa);
@@ -559,29 +582,162 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
   }
   __syncthreads();  // every wave is done with the ring before it is reused
 
-  // out of the row's power-of-two scaled domain
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ex = s_exp[mb * 16 + lg * 4 + i];
-#pragma unroll
-      for (int f = 0; f < 4; ++f) acc[mb][f][i] = ldexpf(acc[mb][f][i], -ex);
-    }
-
   // ---------------------------------------------------------------- LoRA K-steps (bf16 hi/lo)
-  // One 32-value group of the LoRA contraction at a time, both operands staged
-  // in the (now idle) ring: the side product arrives as bf16 hi/lo planes
-  // already times the LoRA scale and is copied by DMA into the activation
+  // One group of the LoRA contraction at a time, both operands staged in the
+  // (now idle) ring: the side product arrives as bf16 hi/lo planes already
+  // times the LoRA scale and the row's exponent and is copied by DMA into the activation
   // layout (hi chunks 0..3, lo chunks 4..7); the fp32 LoRA matrix entries are
-  // split into bf16 hi/lo on the way in.  For gate/up the two halves of the
-  // contraction (x A_g^T | x A_u^T) meet only their own half of the columns.
+  // split into bf16 hi/lo.  For gate/up the two halves of the contraction
+  // (x A_g^T | x A_u^T) meet only their own half of the columns.
   {
     constexpr bool kTwoHalves = (KIND == kGateUp || KIND == kGateUpBwd);
     const int RP = (R + kGroup - 1) / kGroup * kGroup;  // one padded half
     const int KLP = kTwoHalves ? 2 * RP : RP;
-    uint8_t* la = ring;            // [MT][8 chunks of 16 B], activation swizzle
-    uint8_t* lb = ring + kABytes;  // stored: [256 columns][8 chunks]; transposed: hi, lo planes [32][kLBP]
+    // plane columns at or past R within the half hold no product: mask them (they may be stale)
+    auto keep_mask = [&](int qh) {
+      const int nval = min(max(R - (qh + 8 * lg), 0), 8);
+      u32x4 keep;
+      keep.x = (nval > 0 ? 0xffffu : 0u) | (nval > 1 ? 0xffff0000u : 0u);
+      keep.y = (nval > 2 ? 0xffffu : 0u) | (nval > 3 ? 0xffff0000u : 0u);
+      keep.z = (nval > 4 ? 0xffffu : 0u) | (nval > 5 ? 0xffff0000u : 0u);
+      keep.w = (nval > 6 ? 0xffffu : 0u) | (nval > 7 ? 0xffff0000u : 0u);
+      return keep;
+    };
+    // the lane index as a value the compiler cannot see through: the copy
+    // addresses below are then computed here, not hoisted above the main loop
+    // where their registers would compete with its fragments
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    // side-product planes of the group starting at q0 into la (activation layout)
+    auto copy_planes = [&](int q0, uint8_t* la) {
+#pragma unroll
+      for (int i = 0; i < kAInst; ++i) {
+        const int u = w * kAInst + i;
+        const int row = kRowsPerInst * u + ((lane >> 3) & (kRowsPerInst - 1));
+        const int c = (lane & 7) ^ ((row & 7) ^ ((row >> 3) & 1));
+        const size_t m = (size_t)(m0 + min(row, mlen - 1));
+        const uint16_t* g = p.lsplit + m * (size_t)(2 * KLP) + (c >> 2) * KLP + q0 + 8 * (c & 3);
+        if (MT != 16 || lane < 32) dma16(g, lds_addr(la) + 128 * kRowsPerInst * u);
+      }
+    };
+    if constexpr (LDMA) {
+      // 16-value sub-groups on 16x16x16 bf16 MFMAs.  Each sub-group's side-product
+      // planes and the matching fp32 block of the LoRA matrix (whole 16-byte runs,
+      // zeros past the rank or in the other half) are copied by DMA into one of
+      // two buffers, so the next sub-group's copies run under this one's MFMAs;
+      // the matrix is split into bf16 hi/lo as its fragments are read.
+      constexpr int kLA = MT * 64;  // planes of one sub-group: [MT][hi 16 | lo 16] bf16
+      constexpr int kLB = 16384;    // fp32 matrix block: [256 columns][16] or [16][256 columns]
+      constexpr int kLBuf = 3;      // sub-groups in the ring: s + 1 and s + 2 are in flight while s is multiplied
+      static_assert(kLBuf * (kLA + kLB) <= kRingMax, "LoRA staging");
+      constexpr int kPI = MT >= 64 ? MT / 64 : 1;   // plane copies per wave per sub-group
+      constexpr int kRPI = MT >= 64 ? 16 : MT / 4;  // rows per plane copy (4 lanes per row)
+      const int nsg = KLP / 16;
+      auto issue_lora = [&](int sg) {
+        const int q0 = 16 * sg, half = q0 >= RP ? 1 : 0, qh = q0 - half * RP;
+        const int b = sg % kLBuf;
+        const uint32_t la = lds_addr(ring) + b * kLA, lb = lds_addr(ring) + kLBuf * kLA + b * kLB;
+        // planes: 4 lanes per row, chunk c (0, 1 hi; 2, 3 lo) at c ^ ((row >> 1) & 3)
+#pragma unroll
+        for (int i = 0; i < kPI; ++i) {
+          const int u = w * kPI + i;
+          const int row = kRPI * u + (lane >> 2);
+          const int c = (lane & 3) ^ ((row >> 1) & 3);
+          const size_t m = (size_t)(m0 + min(row, mlen - 1));
+          const uint16_t* g = p.lsplit + m * (size_t)(2 * KLP) + (c >> 1) * KLP + q0 + 8 * (c & 1);
+          if (lane < 4 * kRPI) dma16(g, la + 64 * kRPI * u);
+        }
+        // matrix: 4 copies of 1 KB per wave
+#pragma unroll 1
+        for (int i = 0; i < 4; ++i) {
+          const int u = w * 4 + i;
+          const void* src;
+          if constexpr (!kT) {
+            // columns 16u .. 16u + 15, 4 lanes per column, chunk c (values 4c .. 4c + 3) at c ^ (column & 3)
+            const int lc = 16 * u + (lane >> 2);
+            const int c = (lane & 3) ^ (lc & 3);
+            const float* mat;
+            int n, nrows;
+            bool in_half = true;
+            if constexpr (KIND == kGateUp) {
+              mat = lc < kHChunk ? p.L.bg : p.L.bu;
+              n = n0 + (lc & (kHChunk - 1));
+              nrows = I;
+              in_half = (lc < kHChunk) == (half == 0);
+            } else {
+              mat = p.L.bd;
+              n = n0 + lc;
+              nrows = H;
+            }
+            const int q = qh + 4 * c;
+            src = (in_half && q < R && n < nrows) ? (const void*)(mat + ((size_t)e * nrows + n) * R + q) : p.zero;
+          } else {
+            // contraction row u of the sub-group, columns 4l .. 4l + 3
+            const int q = qh + u, c = n0 + 4 * lane;
+            const float* mat;
+            int ncols;
+            if constexpr (KIND == kDownBwd) {
+              mat = p.L.ad;
+              ncols = I;
+            } else {
+              mat = half ? p.L.au : p.L.ag;
+              ncols = H;
+            }
+            src = (q < R && c < nout) ? (const void*)(mat + ((size_t)e * R + q) * ncols + c) : p.zero;
+          }
+          dma16(src, lb + 1024 * u);
+        }
+      };
+      issue_lora(0);
+      if (nsg > 1) issue_lora(1);
+      for (int sg = 0; sg < nsg; ++sg) {
+        const int q0 = 16 * sg, half = q0 >= RP ? 1 : 0, qh = q0 - half * RP;
+        // sub-group sg has landed once at most sub-group sg + 1's copies are outstanding
+        if (sg + 1 < nsg)
+          wait_vm_lgkm<kPI + 4>();
+        else
+          wait_vm_lgkm<0>();
+        __builtin_amdgcn_s_barrier();  // also: every wave is done with the buffers sub-group sg + 2 refills
+        asm volatile("" ::: "memory");
+        if (sg + 2 < nsg) issue_lora(sg + 2);
+        const uint8_t* la = ring + (sg % kLBuf) * kLA;
+        const uint8_t* lb = ring + kLBuf * kLA + (sg % kLBuf) * kLB;
+        // matrix fragments: column lc + lr, values 4 lg .. 4 lg + 3 of the sub-group
+        u32x2 bh[4], bl[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          const int col = local_col<KIND>(w, f) + lr;
+          float4 v;
+          if constexpr (!kT) {
+            v = *reinterpret_cast<const float4*>(lb + col * 64 + 16 * (lg ^ (col & 3)));
+          } else {
+            const float* fb = reinterpret_cast<const float*>(lb);
+            v = float4{fb[(4 * lg) * 256 + col], fb[(4 * lg + 1) * 256 + col], fb[(4 * lg + 2) * 256 + col],
+                       fb[(4 * lg + 3) * 256 + col]};
+          }
+          split4_trunc(v, bh[f], bl[f]);
+        }
+        // plane values at or past R within the half hold no product (they may be stale): mask them
+        const int nval = min(max(R - (qh + 4 * lg), 0), 4);
+        const u32x2 keep = {(nval > 0 ? 0xffffu : 0u) | (nval > 1 ? 0xffff0000u : 0u),
+                            (nval > 2 ? 0xffffu : 0u) | (nval > 3 ? 0xffff0000u : 0u)};
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int row = 16 * mb + lr, sw = (row >> 1) & 3;
+          const uint8_t* rb = la + row * 64 + 8 * (lg & 1);
+          const u32x2 ah = *reinterpret_cast<const u32x2*>(rb + 16 * ((lg >> 1) ^ sw)) & keep;
+          const u32x2 al = *reinterpret_cast<const u32x2*>(rb + 16 * ((2 + (lg >> 1)) ^ sw)) & keep;
+#pragma unroll
+          for (int f = 0; f < 4; ++f) {  // (gate/up: B is zero in the other half's columns)
+            acc[mb][f] = mfma_bf16_k16(ah, bh[f], acc[mb][f]);
+            acc[mb][f] = mfma_bf16_k16(ah, bl[f], acc[mb][f]);
+            acc[mb][f] = mfma_bf16_k16(al, bh[f], acc[mb][f]);
+          }
+        }
+      }
+    } else {
+      uint8_t* la = ring;            // [MT][8 chunks of 16 B], activation swizzle
+      uint8_t* lb = ring + kABytes;  // stored: [256 columns][8 chunks]; transposed: hi, lo planes [32][kLBP]
     for (int q0 = 0; q0 < KLP; q0 += kGroup) {
       const int half = q0 >= RP ? 1 : 0;
       const int qh = q0 - half * RP;  // first contraction index of the group within its half
@@ -687,7 +843,18 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
       }
       __syncthreads();  // the group is consumed before the next one (or the epilogue) reuses the ring
     }
+    }
   }
+
+  // out of the row's power-of-two scaled domain (the LoRA planes carry the same exponent)
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ex = s_exp[mb * 16 + lg * 4 + i];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) acc[mb][f][i] = ldexpf(acc[mb][f][i], -ex);
+    }
 
   // ---------------------------------------------------------------- epilogues
   // acc holds the plain sums.  One pass: every exponent belongs to one wave's
@@ -813,7 +980,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
 // under the MFMA time.  One launch covers tiles of every height (each expert's
 // rows: full tiles of the largest height, then one tile of the smallest height
 // that holds the rest); a tile's height selects its code path.
-template <int KIND>
+template <int KIND, bool LDMA>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm(GemmParams p) {
   __shared__ __align__(16) uint8_t ring[kRingMax];
   __shared__ int32_t s_src[128], s_exp[128], s_slot[128];
@@ -827,18 +994,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int nt = (int)(item % (unsigned)p.n_ntiles);
   switch (p.tile_mt[tile]) {
     case 16:
-      gemm_tile<KIND, 16>(p, tile, nt, ring, s_src, s_exp, s_slot);
+      gemm_tile<KIND, 16, LDMA>(p, tile, nt, ring, s_src, s_exp, s_slot);
       break;
     case 32:
-      gemm_tile<KIND, 32>(p, tile, nt, ring, s_src, s_exp, s_slot);
+      gemm_tile<KIND, 32, LDMA>(p, tile, nt, ring, s_src, s_exp, s_slot);
       break;
     case 64:
-      gemm_tile<KIND, 64>(p, tile, nt, ring, s_src, s_exp, s_slot);
+      gemm_tile<KIND, 64, LDMA>(p, tile, nt, ring, s_src, s_exp, s_slot);
       break;
     default:
-      gemm_tile<KIND, 128>(p, tile, nt, ring, s_src, s_exp, s_slot);
+      gemm_tile<KIND, 128, LDMA>(p, tile, nt, ring, s_src, s_exp, s_slot);
       break;
   }
+}
+
+template <int KIND>
+static void launch_kind(bool ldma, unsigned grid, const GemmParams& p, hipStream_t st) {
+  // the gate/up kernel keeps register-staged LoRA steps: with the copied ones
+  // its 128-row main loop no longer fits the register file
+  if constexpr (KIND != kGateUp) {
+    if (ldma) {
+      k_gemm<KIND, true><<<grid, 256, 0, st>>>(p);
+      return;
+    }
+  }
+  k_gemm<KIND, false><<<grid, 256, 0, st>>>(p);
 }
 
 void launch_gemm(GemmKind kind, const Dims& d, const WsMap& w, void* ws, const LayerPtrs& L,
@@ -909,16 +1089,16 @@ void launch_gemm(GemmKind kind, const Dims& d, const WsMap& w, void* ws, const L
   if (grid == 0) return;
   switch (kind) {
     case kGateUp:
-      k_gemm<kGateUp><<<grid, 256, 0, st>>>(p);
+      launch_kind<kGateUp>(false, grid, p, st);
       break;
     case kDown:
-      k_gemm<kDown><<<grid, 256, 0, st>>>(p);
+      launch_kind<kDown>(d.R % 4 == 0, grid, p, st);
       break;
     case kDownBwd:
-      k_gemm<kDownBwd><<<grid, 256, 0, st>>>(p);
+      launch_kind<kDownBwd>(d.R % 4 == 0, grid, p, st);
       break;
     case kGateUpBwd:
-      k_gemm<kGateUpBwd><<<grid, 256, 0, st>>>(p);
+      launch_kind<kGateUpBwd>(d.R % 4 == 0, grid, p, st);
       break;
   }
 }

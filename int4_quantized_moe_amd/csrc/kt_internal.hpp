@@ -168,11 +168,12 @@ struct RowView {
 // out[m, q] = sum_k src(m, k) * W(e, q, k), q < R, k < kdim; W is [E, R, kdim]
 // (rk = true) or [E, kdim, R] (rk = false).  With W2 set, a second product with
 // the same rows goes to out2.  Also writes the product (both halves side by
-// side) times the LoRA scale into the workspace's bf16 hi/lo planes that the
-// next expert GEMM reads.
+// side) times the LoRA scale and times 2^(the next expert GEMM's row exponent)
+// into the workspace's bf16 hi/lo planes that the GEMM reads: fp16 sources
+// carry that exponent themselves, token rows take tok_exp[token].
 void launch_lora_rowproj(const Dims& d, const WsMap& w, void* ws, const RowView& src, int64_t kdim, const float* W,
                          const float* W2, bool rk, float* out, float* out2, int64_t split_ld, int64_t split_off,
-                         int64_t split_off2, hipStream_t st);
+                         int64_t split_off2, const int32_t* tok_exp, hipStream_t st);
 // The six LoRA gradients, G = (accumulate ? G : 0) + scale * dL/dG / sc, from the
 // saved side products, h, dG|dU and the caller's inputs and grad_output.
 struct LoraGradOut {

@@ -32,19 +32,6 @@ namespace kt {
 typedef short v4s_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s_t* lds_v4s_ptr;
 
-// 8 fp32 -> bf16 hi (top 16 bits) and lo (top 16 bits of the exact remainder)
-__device__ __forceinline__ void split8_trunc(const float* v, u32x4& hi, u32x4& lo) {
-  uint32_t h[8], l[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t u = __float_as_uint(v[i]);
-    h[i] = u & 0xffff0000u;
-    l[i] = __float_as_uint(v[i] - __uint_as_float(h[i]));
-  }
-  hi = u32x4{(h[0] >> 16) | h[1], (h[2] >> 16) | h[3], (h[4] >> 16) | h[5], (h[6] >> 16) | h[7]};
-  lo = u32x4{(l[0] >> 16) | (l[1] & 0xffff0000u), (l[2] >> 16) | (l[3] & 0xffff0000u),
-             (l[4] >> 16) | (l[5] & 0xffff0000u), (l[6] >> 16) | (l[7] & 0xffff0000u)};
-}
 
 // ================================================================ side products
 
@@ -73,17 +60,29 @@ struct SideArgs {
   float* part;  // [ksplit][Ms][nq] partial sums, reduced in order by k_side_reduce
   int64_t Ms;
   const int32_t* nrows;  // rows routed to an expert (offsets[E])
+  // The planes go to an expert GEMM whose activation row m carries a power-of-two
+  // exponent (the one of its fp16 row): the planes carry it too, so that the
+  // GEMM adds them to its scaled sums.  fp16 sources: the source row's own
+  // exponent (exps); token rows: tok_exp[token] (nullptr: 0).
+  const int32_t* tok_exp;
 };
 
+// exponent of the consuming GEMM's activation row m
+__device__ __forceinline__ int side_plane_exp(const SideArgs& a, int64_t m) {
+  if (a.exps) return a.exps[m * a.exp_ld + a.exp_off];
+  return a.tok_exp ? a.tok_exp[a.sorted_slot[m] / a.topk] : 0;
+}
+
 // product column col of sorted row m: the fp32 output and its bf16 hi/lo planes
-__device__ __forceinline__ void side_store(const SideArgs& a, int64_t m, int col, float v) {
+// (times the LoRA scale and 2^pe)
+__device__ __forceinline__ void side_store(const SideArgs& a, int64_t m, int col, float v, int pe) {
   const int R = a.R;
   if (col < R)
     a.out[m * R + col] = v;
   else
     a.out2[m * R + (col - R)] = v;
   uint16_t hi, lo;
-  split_bf16(v * a.split_scale, hi, lo);
+  split_bf16(ldexpf(v * a.split_scale, pe), hi, lo);
   const int64_t sc = col < R ? a.split_off + col : a.split_off2 + (col - R);
   a.split[m * 2 * a.split_ld + sc] = hi;
   a.split[m * 2 * a.split_ld + a.split_ld + sc] = lo;
@@ -97,7 +96,7 @@ __global__ __launch_bounds__(256) void k_side_reduce(SideArgs a) {
   if (m >= *a.nrows) return;  // only rows routed to an expert were multiplied
   float v = 0.f;
   for (int ks = 0; ks < a.ksplit; ++ks) v += a.part[((int64_t)ks * a.Ms + m) * a.nq + col];
-  side_store(a, m, col, v);
+  side_store(a, m, col, v, side_plane_exp(a, m));
 }
 
 // slot t of an aligned group of 8 in the within-8 permuted order holds logical offset:
@@ -112,7 +111,7 @@ __global__ __launch_bounds__(256) void k_lora_side(SideArgs a) {
   constexpr int kAC = MT * 4 > 256 ? MT * 4 / 256 : 1;  // activation chunks (8 values) per thread
   __shared__ __align__(16) uint8_t Ah[2][MT * 64], Al[2][HALF ? MT * 64 : 16];
   __shared__ __align__(16) uint8_t Bh[2][kBB], Bl[2][kBB];
-  __shared__ int32_t s_src[MT], s_ex[MT];
+  __shared__ int32_t s_src[MT], s_ex[MT], s_pex[MT];
 
   const int tile = blockIdx.x;
   if ((unsigned long long)tile >= a.counters[kNumTiles]) return;
@@ -124,6 +123,7 @@ __global__ __launch_bounds__(256) void k_lora_side(SideArgs a) {
     const int m = m0 + min(tid, mlen - 1);  // rows past the tile's end repeat its last row
     s_src[tid] = HALF ? m : a.sorted_slot[m] / a.topk;
     s_ex[tid] = HALF ? a.exps[(int64_t)m * a.exp_ld + a.exp_off] : 0;
+    s_pex[tid] = side_plane_exp(a, m);
   }
   __syncthreads();
 
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(256) void k_lora_side(SideArgs a) {
         if (a.ksplit > 1)
           a.part[((int64_t)ks * a.Ms + m) * a.nq + col] = v;
         else
-          side_store(a, m, col, v);
+          side_store(a, m, col, v, s_pex[row]);
       }
     }
 }
@@ -319,7 +319,7 @@ static void launch_side_mt(int nb, bool half, dim3 grid, const SideArgs& a, hipS
 
 void launch_lora_rowproj(const Dims& d, const WsMap& w, void* ws, const RowView& src, int64_t kdim, const float* W,
                          const float* W2, bool rk, float* out, float* out2, int64_t split_ld, int64_t split_off,
-                         int64_t split_off2, hipStream_t st) {
+                         int64_t split_off2, const int32_t* tok_exp, hipStream_t st) {
   if (w.max_tiles == 0) return;
   SideArgs a{};
   a.topk = (int)d.K;
@@ -347,6 +347,7 @@ void launch_lora_rowproj(const Dims& d, const WsMap& w, void* ws, const RowView&
   a.split_off = split_off;
   a.split_off2 = split_off2;
   a.split_scale = d.sc;
+  a.tok_exp = tok_exp;
   const bool half = src.kind == kSrcHalfChunked;
   const int nb = (a.nq + 63) / 64;
   // few tiles (small token counts) leave most CUs idle through a long

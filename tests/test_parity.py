@@ -85,7 +85,7 @@ def test_dequant_bit_exact(dev):
     packed[1, :16] = 0xFF
     scales = W.f32_to_bf16_bits(rng.uniform(0.01, 0.07, size=(n, k // 32)).astype(np.float32))
     scales[2, 1] = 0
-    scales[3, :] = W.f32_to_bf16_bits(np.array([6.103515625e-05, 8160.0, -0.5, 1.0, 3.0, -7.5, 0.1, 100.0],
+    scales[3, :] = W.f32_to_bf16_bits(np.array([6.103515625e-05, 2720.0, -0.5, 1.0, 3.0, -7.5, 0.1, -2720.0],
                                                dtype=np.float32))
     out = torch.empty((n, k), dtype=torch.float32, device="cuda")
     _lib.kt_rawint4_dequant(torch.from_numpy(packed).cuda(), dev.bf16_tensor(scales, "cuda"), n, k, out)
