@@ -183,6 +183,20 @@ int kt_rawint4_moe_diagnostics(const void* workspace, size_t workspace_bytes, in
                                void* stream);
 
 /*
+ * The gate and up pre-activations g = W_g x + sc B_g A_g x and
+ * u = W_u x + sc B_u A_u x of every slot, as the latest forward in `workspace`
+ * saved them for the backward (page "rawint4_sft_reference.py",
+ * routed_rawint4_lora / rawint4_swiglu: the values the clamp masks are decided
+ * on).  `layer` and `qlen` are those of that forward.  gate and up are device
+ * fp32 arrays [qlen * top_k][I] in slot order (slot = token * top_k + j); a
+ * dropped slot's row is zero.  Enqueued on `stream`; nothing is allocated.
+ * Use: checking the masks against another computation of the layer, where a
+ * value on a clamp bound to within rounding may fall either side.
+ */
+int kt_rawint4_moe_saved_preactivations(const kt_rawint4_moe_layer* layer, int32_t qlen, const void* workspace,
+                                        size_t workspace_bytes, float* gate, float* up, void* stream);
+
+/*
  * Per-phase timing of the layer's launches, for measurement.  While enabled,
  * every forward/backward records a hipEvent pair around each phase (grouping,
  * activation conversion, LoRA side products, each grouped GEMM, combine,

@@ -75,6 +75,7 @@ def load_library() -> ctypes.CDLL:
         "kt_rawint4_group_workspace_bytes": (sz, [i32, i32, i32]),
         "kt_rawint4_group": (ctypes.c_int, [_vp, i32, i32, i32, _vp, _vp, _vp, sz, _vp]),
         "kt_rawint4_moe_diagnostics": (ctypes.c_int, [_vp, sz, ctypes.POINTER(i64), ctypes.POINTER(i64), _vp]),
+        "kt_rawint4_moe_saved_preactivations": (ctypes.c_int, [lp, i32, _vp, sz, _vp, _vp, _vp]),
         "kt_rawint4_profile_enable": (ctypes.c_int, [i32]),
         "kt_rawint4_profile_read": (ctypes.c_int, [_vp, _vp, i32]),
         "kt_rawint4_profile_phase_name": (ctypes.c_char_p, [i32]),
@@ -180,6 +181,12 @@ def kt_rawint4_moe_diagnostics(workspace, stream=None):
     _check(load_library().kt_rawint4_moe_diagnostics(_ptr(workspace), _nbytes(workspace), ctypes.byref(a),
                                                      ctypes.byref(b), _stream(stream)))
     return int(a.value), int(b.value)
+
+
+def kt_rawint4_moe_saved_preactivations(layer, qlen, workspace, gate, up, stream=None) -> None:
+    _check(load_library().kt_rawint4_moe_saved_preactivations(ctypes.byref(layer), int(qlen), _ptr(workspace),
+                                                              _nbytes(workspace), _ptr(gate), _ptr(up),
+                                                              _stream(stream)))
 
 
 def kt_rawint4_profile_enable(on: bool) -> None:

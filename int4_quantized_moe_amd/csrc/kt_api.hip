@@ -526,6 +526,23 @@ int kt_rawint4_moe_diagnostics(const void* workspace, size_t workspace_bytes, in
   return KT_RAWINT4_OK;
 }
 
+int kt_rawint4_moe_saved_preactivations(const kt_rawint4_moe_layer* layer, int32_t qlen, const void* workspace,
+                                        size_t workspace_bytes, float* gate, float* up, void* stream) {
+  Dims d;
+  int rc = check_layer(layer, qlen, &d);
+  if (rc) return rc;
+  if (qlen == 0) {
+    g_last_error.clear();
+    return KT_RAWINT4_OK;
+  }
+  if (!gate || !up) return fail(KT_RAWINT4_EINVAL, "gate and up must be non-NULL");
+  const WsMap w = plan_workspace(d);
+  rc = check_workspace(const_cast<void*>(workspace), workspace_bytes, w.total);
+  if (rc) return rc;
+  launch_saved_preact(d, w, workspace, gate, up, static_cast<hipStream_t>(stream));
+  return launched();
+}
+
 int kt_rawint4_profile_enable(int32_t on) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof_on = on != 0;

@@ -234,6 +234,26 @@ void launch_droute(const Dims& d, const WsMap& w, void* ws, float* grad_route, h
                                                            grad_route);
 }
 
+// gate/up pre-activations the forward saved per grouped row, gathered into slot
+// order; a dropped slot's row is zero
+__global__ void k_saved_preact(const int32_t* __restrict__ row_of_slot, const float* __restrict__ g,
+                               const float* __restrict__ u, int64_t I, float* __restrict__ gate,
+                               float* __restrict__ up) {
+  const int64_t s = blockIdx.x;
+  const int m = row_of_slot[s];
+  for (int64_t c = threadIdx.x; c < I; c += blockDim.x) {
+    gate[s * I + c] = m >= 0 ? g[(int64_t)m * I + c] : 0.f;
+    up[s * I + c] = m >= 0 ? u[(int64_t)m * I + c] : 0.f;
+  }
+}
+
+void launch_saved_preact(const Dims& d, const WsMap& w, const void* ws, float* gate, float* up, hipStream_t st) {
+  if (d.Ms == 0) return;
+  void* base = const_cast<void*>(ws);
+  k_saved_preact<<<(unsigned)d.Ms, 256, 0, st>>>(ws_ptr<int32_t>(base, w.row_of_slot), ws_ptr<float>(base, w.g),
+                                                 ws_ptr<float>(base, w.u), d.I, gate, up);
+}
+
 // ---------------------------------------------------------------- codec hooks
 
 __global__ void k_unpack(const uint8_t* __restrict__ packed, int64_t nbytes, int8_t* __restrict__ codes) {

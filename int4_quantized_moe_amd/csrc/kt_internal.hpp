@@ -194,6 +194,7 @@ void launch_normalize_chunks(uint16_t* buf, int32_t* exps, const int32_t* nrows,
 void launch_combine(const Dims& d, const uint16_t* stage, const int32_t* stexp, int64_t st_nch, const int64_t* ids,
                     uint16_t* out, hipStream_t st);
 void launch_droute(const Dims& d, const WsMap& w, void* ws, float* grad_route, hipStream_t st);
+void launch_saved_preact(const Dims& d, const WsMap& w, const void* ws, float* gate, float* up, hipStream_t st);
 void launch_init_counters(void* ws, const WsMap& w, hipStream_t st);
 
 void launch_unpack(const uint8_t* packed, int64_t n, int64_t k, int8_t* codes, hipStream_t st);

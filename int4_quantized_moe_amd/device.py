@@ -69,6 +69,14 @@ class DeviceLayer:
                                 stream)
         return grad_input, grad_route
 
+    def saved_preactivations(self, qlen, workspace, stream=None):
+        """Gate and up pre-activations of the latest forward in ``workspace``, [qlen, k, I] fp32 each."""
+        shape = (qlen, self.cfg.top_k, self.cfg.intermediate)
+        gate = torch.empty(shape, dtype=torch.float32, device=self.device)
+        up = torch.empty(shape, dtype=torch.float32, device=self.device)
+        _lib.kt_rawint4_moe_saved_preactivations(self.layer, qlen, workspace, gate, up, stream)
+        return gate, up
+
 
 class DeviceBatch:
     def __init__(self, batch, device="cuda"):

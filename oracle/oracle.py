@@ -89,6 +89,8 @@ def _load():
     lib.orc_moe.argtypes = [ctypes.POINTER(OrcLayer), ctypes.c_int64, _f64p, _i64p, _f64p, _f64p, _f64p, _f64p,
                             _f64p] + [_f64p] * 6
     lib.orc_moe.restype = ctypes.c_int
+    lib.orc_moe_decided.argtypes = lib.orc_moe.argtypes + [_f64p, _f64p, ctypes.c_double, _f64p, _f64p]
+    lib.orc_moe_decided.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -187,13 +189,20 @@ def _bf16_to_f64(bits: np.ndarray) -> np.ndarray:
 
 
 def moe(cfg, weights, inputs, expert_ids, route_weights, grad_output=None, *, fp32_intermediates=True,
-        inputs_are_bf16=True, lora: Optional[Dict[str, np.ndarray]] = None):
+        inputs_are_bf16=True, lora: Optional[Dict[str, np.ndarray]] = None, sides=None, band=0.0,
+        preactivations=False):
     """Forward (and, with ``grad_output``, backward) of the routed layer.
 
     ``inputs`` / ``grad_output`` are bf16 bit patterns when ``inputs_are_bf16``,
     else float arrays used as given.  Returns a dict with ``out`` [qlen, H] and,
     for the backward, ``dx``, ``droute`` [qlen, k] and the six raw LoRA
     gradients (sums over this call's tokens, before the window rule).
+
+    ``sides = (gate, up)``, each [qlen, k, I]: pre-activations found by the
+    computation under test; where the oracle's own value is within ``band`` of
+    a clamp bound, its mask follows the side of the supplied value (the mask is
+    not unique there).  ``preactivations`` adds the oracle's own ``pre_g`` /
+    ``pre_u`` [qlen, k, I] (zero for dropped slots).
     """
     lib = _load()
     lora = weights.lora if lora is None else lora
@@ -220,8 +229,18 @@ def moe(cfg, weights, inputs, expert_ids, route_weights, grad_output=None, *, fp
         droute = np.empty(ids.shape)
         shapes = cfg.lora_shapes()
         grads = [np.empty(shapes[n]) for n in LORA_NAMES]
-    rc = lib.orc_moe(ctypes.byref(layer), qlen, _ptr(x, _f64p), _ptr(ids, _i64p), _ptr(rw, _f64p), _ptr(dy, _f64p),
-                     _ptr(out, _f64p), _ptr(dx, _f64p), _ptr(droute, _f64p), *(_ptr(g, _f64p) for g in grads))
+    side_g = side_u = pre_g = pre_u = None
+    if sides is not None:
+        side_g, side_u = (np.ascontiguousarray(a, dtype=np.float64).reshape(ids.shape + (i,)) for a in sides)
+    if preactivations:
+        pre_g = np.zeros(ids.shape + (i,))
+        pre_u = np.zeros(ids.shape + (i,))
+        res["pre_g"] = pre_g
+        res["pre_u"] = pre_u
+    rc = lib.orc_moe_decided(ctypes.byref(layer), qlen, _ptr(x, _f64p), _ptr(ids, _i64p), _ptr(rw, _f64p),
+                             _ptr(dy, _f64p), _ptr(out, _f64p), _ptr(dx, _f64p), _ptr(droute, _f64p),
+                             *(_ptr(g, _f64p) for g in grads), _ptr(side_g, _f64p), _ptr(side_u, _f64p), float(band),
+                             _ptr(pre_g, _f64p), _ptr(pre_u, _f64p))
     if rc:
         raise RuntimeError(f"oracle failed with code {rc}")
     if dy is not None:

@@ -30,7 +30,10 @@
  *   - the clamp is boundary-inclusive on both sides: the gate passes its
  *     gradient where g <= L, the up projection where -L <= u <= L; L = 0 turns
  *     the clamp off;
- *   - the LoRA scale is alpha / rank.
+ *   - the LoRA scale is alpha / rank;
+ *   - a pre-activation on a clamp bound to within the accuracy of the
+ *     computation being checked has no unique mask; orc_moe_decided lets the
+ *     caller fix the side there (and only there).
  *
  * Loop order: experts outermost; each active expert is dequantised once and its
  * routed slots are processed together, parallel over output features.  Every
@@ -185,9 +188,12 @@ static double silu_grad(double z) {
 
 /* rawint4_swiglu's clamp: gate clamped from above only, up clamped to [-L, L];
  * the mask is 1 where the un-clamped value passes its gradient (boundaries
- * included); limit 0 means no clamp. */
-static void clamp_gate(double g, double limit, double* clamped, double* mask) {
-  if (limit > 0 && !(g <= limit)) {
+ * included); limit 0 means no clamp.  The decision is taken on `side` (the
+ * value itself unless a decision is supplied, see orc_moe_decided); the
+ * clamped value is the value itself where it passes, the bound it is beyond
+ * otherwise. */
+static void clamp_gate(double g, double side, double limit, double* clamped, double* mask) {
+  if (limit > 0 && !(side <= limit)) {
     *clamped = limit;
     *mask = 0.0;
   } else {
@@ -195,11 +201,11 @@ static void clamp_gate(double g, double limit, double* clamped, double* mask) {
     *mask = 1.0;
   }
 }
-static void clamp_up(double u, double limit, double* clamped, double* mask) {
-  if (limit > 0 && u < -limit) {
+static void clamp_up(double u, double side, double limit, double* clamped, double* mask) {
+  if (limit > 0 && side < -limit) {
     *clamped = -limit;
     *mask = 0.0;
-  } else if (limit > 0 && u > limit) {
+  } else if (limit > 0 && side > limit) {
     *clamped = limit;
     *mask = 0.0;
   } else {
@@ -271,10 +277,21 @@ static void transposed_products(const float* W, int64_t Rn, int64_t C, const dou
  *   dB_d += sc dyw (x) ud,  dA_d += sc dyB (x) h
  *   dB_g += sc dg (x) ua,   dA_g += sc dgB (x) x    (likewise for up)
  * The six LoRA gradients returned are these raw sums (no window scaling).
+ *
+ * The clamp masks are discontinuous at g = L and u = -L, L: a pre-activation
+ * that another computation (another summation order, another precision) holds
+ * only to within `band` may fall on either side there, and either mask is then
+ * a correct result.  With side_g / side_u given ([qlen * top_k][I] in slot
+ * order, the pre-activations that computation found), an element whose own
+ * value lies within `band` of a bound takes its decision from the supplied
+ * value; everywhere else, and with NULL, the oracle decides on its own value.
+ * pre_g / pre_u, when given ([qlen * top_k][I], slot order), receive the
+ * oracle's own pre-activations of every valid slot (other rows untouched).
  */
-int orc_moe(const orc_layer* L, int64_t qlen, const double* x, const int64_t* ids, const double* rw,
-            const double* dy, double* out, double* dx, double* droute, double* d_gate_a, double* d_gate_b,
-            double* d_up_a, double* d_up_b, double* d_down_a, double* d_down_b) {
+int orc_moe_decided(const orc_layer* L, int64_t qlen, const double* x, const int64_t* ids, const double* rw,
+                    const double* dy, double* out, double* dx, double* droute, double* d_gate_a, double* d_gate_b,
+                    double* d_up_a, double* d_up_b, double* d_down_a, double* d_down_b, const double* side_g,
+                    const double* side_u, double band, double* pre_g, double* pre_u) {
   if (!L || qlen < 0) return -1;
   const int64_t E = L->num_experts, K = L->top_k, H = L->hidden, I = L->intermediate, R = L->rank;
   if (E < 1 || K < 1 || R < 1 || H % ORC_GROUP_SIZE || I % ORC_GROUP_SIZE || H <= 0 || I <= 0) return -1;
@@ -359,8 +376,15 @@ int orc_moe(const orc_layer* L, int64_t qlen, const double* x, const int64_t* id
         g = fp32_round(fr, g);
         u = fp32_round(fr, u);
         int64_t idx = j * I + n;
-        clamp_gate(g, limit, &gp[idx], &mg[idx]);
-        clamp_up(u, limit, &upc[idx], &mu[idx]);
+        const int64_t sidx = (int64_t)rows[j] * I + n;
+        if (pre_g) pre_g[sidx] = g;
+        if (pre_u) pre_u[sidx] = u;
+        /* within `band` of a bound the mask is not unique: take the supplied side */
+        const double sg = (side_g && limit > 0 && fabs(g - limit) <= band) ? side_g[sidx] : g;
+        const double su =
+            (side_u && limit > 0 && (fabs(u - limit) <= band || fabs(u + limit) <= band)) ? side_u[sidx] : u;
+        clamp_gate(g, sg, limit, &gp[idx], &mg[idx]);
+        clamp_up(u, su, limit, &upc[idx], &mu[idx]);
         hh[idx] = fp32_round(fr, silu(gp[idx]) * upc[idx]);
       }
     }
@@ -517,4 +541,11 @@ int orc_moe(const orc_layer* L, int64_t qlen, const double* x, const int64_t* id
 done:
   free(counts); free(offsets); free(sorted); free(yslot); free(dxslot); free(wg); free(wu); free(wd);
   return status;
+}
+
+int orc_moe(const orc_layer* L, int64_t qlen, const double* x, const int64_t* ids, const double* rw,
+            const double* dy, double* out, double* dx, double* droute, double* d_gate_a, double* d_gate_b,
+            double* d_up_a, double* d_up_b, double* d_down_a, double* d_down_b) {
+  return orc_moe_decided(L, qlen, x, ids, rw, dy, out, dx, droute, d_gate_a, d_gate_b, d_up_a, d_up_b, d_down_a,
+                         d_down_b, NULL, NULL, 0.0, NULL, NULL);
 }

@@ -225,6 +225,55 @@ def test_hand_case_closed_form(limit):
         assert np.all(res["dx"][6] == 0.0)
 
 
+def test_supplied_clamp_side_hand_case():
+    # the hand case at L = 2 (g = u = v / 2 in every column, B = 0): within the
+    # band of a bound the supplied side decides the masks, elsewhere it is ignored
+    limit, band = 2.0, 0.1
+    cfg = _cfg(1, 1, 32, 32, 4, 8.0, 7, limit)  # sc = 2
+    w = _uniform_weights(cfg, 0x99, BF16_HALF)
+    a = 0.25
+    w.lora["gate_lora_a"][0, 0, 0] = a
+    vs = [-4.125, -4.0, -3.875, 0.0, 3.875, 4.0, 4.125]
+    x = np.zeros((7, 32))
+    x[:, 0] = vs
+    ids = np.zeros((7, 1), dtype=np.int64)
+    rw = np.full((7, 1), 0.75)
+    dy = np.ones((7, 32))
+    # v = -4.125: u beyond -L, side inside; v = -4: u on -L, side beyond; v = +-3.875
+    # and 0: side = own value, or far from every bound (side ignored); v = 4: g and u on
+    # L, side beyond; v = 4.125: both beyond L, side inside
+    sides = np.array([-1.99, -2.01, -1.9375, 5.0, 1.9375, 2.01, 1.99])
+    side = np.repeat(sides[:, None, None], 32, axis=2)
+    res = O.moe(cfg, w, x, ids, rw, dy, fp32_intermediates=False, inputs_are_bf16=False, sides=(side, side),
+                band=band, preactivations=True)
+    np.testing.assert_array_equal(res["pre_g"][:, 0, :], np.repeat(np.array(vs)[:, None] / 2, 32, axis=1))
+    np.testing.assert_array_equal(res["pre_u"], res["pre_g"])
+    # masks and clamped values by hand: (gate passes, g', up passes, u')
+    decided = {-4.125: (1, -2.0625, 1, -2.0625), -4.0: (1, -2.0, 0, -2.0), -3.875: (1, -1.9375, 1, -1.9375),
+               0.0: (1, 0.0, 1, 0.0), 3.875: (1, 1.9375, 1, 1.9375), 4.0: (0, 2.0, 0, 2.0),
+               4.125: (1, 2.0625, 1, 2.0625)}
+    sc = 2.0
+    dbg = np.zeros((32, 4))
+    for t, v in enumerate(vs):
+        mg, gp, mu, up = decided[v]
+        y = 16.0 * _silu(gp) * up
+        dgv = 12.0 * up * _dsilu(gp) * mg
+        duv = 12.0 * _silu(gp) * mu
+        np.testing.assert_allclose(res["out"][t], 0.75 * y, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(res["droute"][t, 0], 32.0 * y, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(res["dx"][t], 16.0 * (dgv + duv), rtol=1e-12, atol=1e-12)
+        dbg[:, 0] += sc * dgv * a * v
+    np.testing.assert_allclose(res["grads"]["gate_lora_b"][0], dbg, rtol=1e-12, atol=1e-12)
+    # supplying the oracle's own values changes nothing, to the bit
+    plain = O.moe(cfg, w, x, ids, rw, dy, fp32_intermediates=False, inputs_are_bf16=False)
+    own = O.moe(cfg, w, x, ids, rw, dy, fp32_intermediates=False, inputs_are_bf16=False,
+                sides=(res["pre_g"], res["pre_u"]), band=10.0)
+    for key in ("out", "dx", "droute"):
+        np.testing.assert_array_equal(own[key], plain[key])
+    for n in O.LORA_NAMES:
+        np.testing.assert_array_equal(own["grads"][n], plain["grads"][n])
+
+
 def _page_clamp_case(golden, fp32):
     rows = golden("clamp_example.txt")
     cfg = _cfg(4, 2, 256, 256, 8, 16.0, 9, 2.0)

@@ -11,6 +11,7 @@ import pytest
 
 import oracle as O
 from int4_quantized_moe_amd import workloads as W
+from tests.clamp_sides import reference
 
 torch = pytest.importorskip("torch")
 
@@ -125,13 +126,21 @@ def _run_gpu(dev, cfg, weights, batch, grads_fill=7.0, accumulate=False, grad_sc
     db = dev.DeviceBatch(batch)
     ws = dl.workspace(db.qlen)
     out = dl.forward(db.inputs, db.expert_ids, db.route_weights, ws)
+    pre_g, pre_u = dl.saved_preactivations(db.qlen, ws)
     grads = dl.grad_buffers(fill=grads_fill)
     droute = torch.empty(batch.expert_ids.shape, dtype=torch.float32, device="cuda")
     dx, _ = dl.backward(db.inputs, db.expert_ids, db.route_weights, db.grad_output, ws, grads, accumulate=accumulate,
                         grad_scale=grad_scale, grad_route=droute)
     torch.cuda.synchronize()
     return dl, db, ws, {"out": _bits_f32(out), "dx": _bits_f32(dx), "droute": droute.cpu().numpy(),
-                        "grads": {n: g.cpu().numpy() for n, g in grads.items()}}
+                        "grads": {n: g.cpu().numpy() for n, g in grads.items()},
+                        "sides": (pre_g.cpu().numpy(), pre_u.cpu().numpy())}
+
+
+def _reference(cfg, weights, batch, gpu):
+    """The oracle on the whole batch, taking the GPU's clamp side within rounding of a bound."""
+    return reference(cfg, weights, batch.inputs, batch.expert_ids, batch.route_weights, batch.grad_output,
+                     gpu["sides"], _say)
 
 
 def _check_all(tag, gpu, ref, active, grad_scale=1.0):
@@ -157,7 +166,7 @@ def test_layer_small_configs(dev, index):
     _say("layer", cfg.name)
     before = O.base_storage_hash(weights)
     dl, _, ws, gpu = _run_gpu(dev, cfg, weights, batch, grad_scale=0.5)
-    ref = O.moe(cfg, weights, batch.inputs, batch.expert_ids, batch.route_weights, batch.grad_output)
+    ref = _reference(cfg, weights, batch, gpu)
     _check_all(cfg.name, gpu, ref, set(batch.expert_ids.ravel().tolist()), grad_scale=0.5)
     assert _hash_device(dl) == before
     bad_ids, bad_scales = __import__("int4_quantized_moe_amd")._lib.kt_rawint4_moe_diagnostics(ws)
@@ -177,7 +186,7 @@ def test_layer_ragged_shapes(dev):
     batch.expert_ids[: 30, 2] = np.where(batch.expert_ids[:30, 2] == batch.expert_ids[:30, 1], 5,
                                          batch.expert_ids[:30, 2])
     _, _, _, gpu = _run_gpu(dev, cfg, weights, batch)
-    ref = O.moe(cfg, weights, batch.inputs, batch.expert_ids, batch.route_weights, batch.grad_output)
+    ref = _reference(cfg, weights, batch, gpu)
     _check_all("ragged", gpu, ref, set(batch.expert_ids.ravel().tolist()))
 
 
@@ -200,8 +209,31 @@ def test_layer_every_tile_height(dev, rows, monkeypatch):
         counts = np.bincount(batch.expert_ids.ravel(), minlength=cfg.num_experts)
         assert counts.max() > 128 and 0 < counts[counts > 0].min() <= 64
     _, _, _, gpu = _run_gpu(dev, cfg, weights, batch)
-    ref = O.moe(cfg, weights, batch.inputs, batch.expert_ids, batch.route_weights, batch.grad_output)
+    ref = _reference(cfg, weights, batch, gpu)
     _check_all(f"rows{rows or 'mixed'}", gpu, ref, set(batch.expert_ids.ravel().tolist()))
+
+
+@pytest.mark.parametrize("rows", [16, 32, 64, 128, 0])
+def test_layer_every_tile_height_rank64(dev, rows, monkeypatch):
+    # as above with a rank that is a multiple of 4 (the LoRA K-steps then copy
+    # the LoRA matrices by DMA) and two halves of 64: one expert takes
+    # 2 * 128 + 8 rows, so the default mix has a 16-row rest tile
+    cfg = W.LayerConfig("heights64", 4, 2, 256, 192, 64, 128.0, 264, 3.0, x_std=2.0)
+    _say("layer tile height rank 64", rows or "mixed")
+    weights = W.make_weights(cfg, 93)
+    batch = W.make_batch(cfg, 93)
+    batch.expert_ids[:, 1] = np.where(batch.expert_ids[:, 1] == 1, batch.expert_ids[:, 0], batch.expert_ids[:, 1])
+    batch.expert_ids[:, 0] = 1
+    batch.expert_ids[:, 1] = np.where(batch.expert_ids[:, 1] == 1, 3, batch.expert_ids[:, 1])
+    counts = np.bincount(batch.expert_ids.ravel(), minlength=cfg.num_experts)
+    if rows:
+        monkeypatch.setenv("KT_RAWINT4_GEMM_ROWS", str(rows))
+    else:
+        monkeypatch.delenv("KT_RAWINT4_GEMM_ROWS", raising=False)
+    _say("rows per expert", counts.tolist())
+    _, _, _, gpu = _run_gpu(dev, cfg, weights, batch)
+    ref = _reference(cfg, weights, batch, gpu)
+    _check_all(f"r64rows{rows or 'mixed'}", gpu, ref, set(batch.expert_ids.ravel().tolist()))
 
 
 def test_layer_dropped_ids_and_window(dev):
@@ -311,5 +343,5 @@ def test_layer_k2_qlen32_full(dev):
     cfg, weights, batch = W.make_workload(2)
     _say("layer", cfg.name, "(full oracle)")
     _, _, ws, gpu = _run_gpu(dev, cfg, weights, batch)
-    ref = O.moe(cfg, weights, batch.inputs, batch.expert_ids, batch.route_weights, batch.grad_output)
+    ref = _reference(cfg, weights, batch, gpu)
     _check_all(cfg.name, gpu, ref, set(batch.expert_ids.ravel().tolist()))

@@ -14,6 +14,10 @@ redo them whole, so it checks what it can compute piece by piece:
   includes the most loaded expert, whose rows span many tiles;
 * at any size: experts no slot reaches get exactly zero gradients.
 
+The GPU's saved gate/up pre-activations of those slots are checked against the
+oracle's element by element, and within rounding of a clamp bound the oracle
+takes the GPU's side of the mask (tests/clamp_sides.py).
+
 Bars as in test_parity: relative L2 <= 5e-3 and cosine >= 0.9999 (dRoute
 3e-2).  Each step prints what it does first.
 """
@@ -23,6 +27,7 @@ import pytest
 
 import oracle as O
 from int4_quantized_moe_amd import workloads as W
+from tests.clamp_sides import reference
 
 torch = pytest.importorskip("torch")
 
@@ -62,6 +67,7 @@ def test_full_size_sampled(index):
     db = device.DeviceBatch(batch)
     ws = dl.workspace(db.qlen)
     out = dl.forward(db.inputs, db.expert_ids, db.route_weights, ws)
+    pre_g, pre_u = dl.saved_preactivations(db.qlen, ws)
     grads = dl.grad_buffers(fill=7.0)
     droute = torch.empty(batch.expert_ids.shape, dtype=torch.float32, device="cuda")
     dx, _ = dl.backward(db.inputs, db.expert_ids, db.route_weights, db.grad_output, ws, grads, accumulate=False,
@@ -73,8 +79,12 @@ def test_full_size_sampled(index):
     rng = np.random.default_rng(4242 + index)
     toks = np.unique(np.concatenate([[0, cfg.qlen - 1], rng.choice(cfg.qlen, N_TOKENS, replace=False)]))
     _say(f"{cfg.name}: oracle on tokens {toks.tolist()}")
-    ref = O.moe(cfg, weights, batch.inputs[toks], batch.expert_ids[toks], batch.route_weights[toks],
-                batch.grad_output[toks])
+    def sides(rows):
+        index = torch.from_numpy(rows).cuda()
+        return pre_g[index].cpu().numpy(), pre_u[index].cpu().numpy()
+
+    ref = reference(cfg, weights, batch.inputs[toks], batch.expert_ids[toks], batch.route_weights[toks],
+                    batch.grad_output[toks], sides(toks), _say)
     failures = []
     for name, a, e, rel, cos in (
             ("forward", out.float().cpu().numpy()[toks], ref["out"], REL_L2, COSINE),
@@ -93,7 +103,8 @@ def test_full_size_sampled(index):
         rows = np.flatnonzero((batch.expert_ids == e).any(axis=1))
         ids = np.where(batch.expert_ids[rows] == e, e, -1).astype(np.int64)
         _say(f"{cfg.name}: oracle LoRA gradients of expert {e} ({counts[e]} slots)")
-        ref_e = O.moe(cfg, weights, batch.inputs[rows], ids, batch.route_weights[rows], batch.grad_output[rows])
+        ref_e = reference(cfg, weights, batch.inputs[rows], ids, batch.route_weights[rows], batch.grad_output[rows],
+                          sides(rows), _say)
         for n in O.LORA_NAMES:
             try:
                 _close(f"{cfg.name}.expert{e}.{n}", g[n][e], ref_e["grads"][n][e])
