@@ -660,10 +660,12 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
             int n, nrows;
             bool in_half = true;
             if constexpr (KIND == kGateUp) {
-              mat = lc < kHChunk ? p.L.bg : p.L.bu;
-              n = n0 + (lc & (kHChunk - 1));
+              // copies 0..7 (waves 0, 1) hold gate columns, 8..15 (waves 2, 3) up columns
+              const bool up = w >= 2;
+              mat = up ? p.L.bu : p.L.bg;
+              n = n0 + 16 * (u & 7) + (lane >> 2);
               nrows = I;
-              in_half = (lc < kHChunk) == (half == 0);
+              in_half = up == (half == 1);
             } else {
               mat = p.L.bd;
               n = n0 + lc;
@@ -1010,15 +1012,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 
 template <int KIND>
 static void launch_kind(bool ldma, unsigned grid, const GemmParams& p, hipStream_t st) {
-  // the gate/up kernel keeps register-staged LoRA steps: with the copied ones
-  // its 128-row main loop no longer fits the register file
-  if constexpr (KIND != kGateUp) {
-    if (ldma) {
-      k_gemm<KIND, true><<<grid, 256, 0, st>>>(p);
-      return;
-    }
-  }
-  k_gemm<KIND, false><<<grid, 256, 0, st>>>(p);
+  if (ldma)
+    k_gemm<KIND, true><<<grid, 256, 0, st>>>(p);
+  else
+    k_gemm<KIND, false><<<grid, 256, 0, st>>>(p);
 }
 
 void launch_gemm(GemmKind kind, const Dims& d, const WsMap& w, void* ws, const LayerPtrs& L,
@@ -1089,7 +1086,7 @@ void launch_gemm(GemmKind kind, const Dims& d, const WsMap& w, void* ws, const L
   if (grid == 0) return;
   switch (kind) {
     case kGateUp:
-      launch_kind<kGateUp>(false, grid, p, st);
+      launch_kind<kGateUp>(d.R % 4 == 0, grid, p, st);
       break;
     case kDown:
       launch_kind<kDown>(d.R % 4 == 0, grid, p, st);
