@@ -99,6 +99,7 @@ WsMap plan_workspace(const Dims& d) {
   w.side_part = pl.take(w.side_ksplit > 1 ? 4 * (size_t)w.side_ksplit * Ms * 2 * R : 0);
   w.gplanes = pl.take(2 * Ms * (size_t)grad_geom(d.R).row);
   w.gexp = pl.take(4 * 2 * (size_t)d.E);
+  w.eorder = pl.take(4 * (size_t)d.E);
   w.total = pl.off;
   return w;
 }

@@ -397,19 +397,35 @@ struct GradPrepArgs {
   int64_t row, r16;
   int64_t off_x, np_x, off_dy, np_dy, off_h, np_h, off_g, np_g;  // np_g: one half
   int32_t* gexp;                                                 // [E][2]: h family, dG|dU family
+  int E;
+  int32_t* eorder;  // [E]: experts by descending row count (ties: lower index first)
 };
 
 // Per expert, the power-of-two exponent S of each fp16 narrow family that puts
 // its largest magnitude into [2^14, 2^15): h family rw * dyB * 2^-hexp, dG|dU
 // family ua | ub * 2^-dgexp (hexp, dgexp: the wide row's own exponent, so the
-// wide fp16 values can be used as they are).  One block per expert.
+// wide fp16 values can be used as they are).  Also the expert's place in the
+// order the gradient kernels deal their work out: most rows first, so that a
+// heavily loaded expert's long contractions start at once rather than last.
+// One block per expert.
 __global__ __launch_bounds__(256) void k_grad_exps(GradPrepArgs a) {
   __shared__ int s_max[2];
+  __shared__ int s_rank;
   const int e = blockIdx.x;
   const int m0 = a.offsets[e], m1 = a.offsets[e + 1];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (threadIdx.x < 2) s_max[threadIdx.x] = INT_MIN;
+  if (threadIdx.x == 0) s_rank = 0;
   __syncthreads();
+  {
+    const int n = m1 - m0;
+    int before = 0;
+    for (int f = threadIdx.x; f < a.E; f += blockDim.x) {
+      const int nf = a.offsets[f + 1] - a.offsets[f];
+      before += (nf > n || (nf == n && f < e)) ? 1 : 0;
+    }
+    atomicAdd(&s_rank, before);
+  }
   int mh = INT_MIN, mg = INT_MIN;
   for (int m = m0 + w; m < m1; m += 4) {
     const float rw = a.rw[a.sorted_slot[m]];
@@ -436,6 +452,7 @@ __global__ __launch_bounds__(256) void k_grad_exps(GradPrepArgs a) {
     const int mx = s_max[threadIdx.x];
     a.gexp[2 * e + threadIdx.x] = mx == INT_MIN ? 0 : 15 - mx;
   }
+  if (threadIdx.x == 0) a.eorder[s_rank] = e;
 }
 
 // The narrow planes of one row tile: every row's four families as 16-bit hi/lo
@@ -531,6 +548,7 @@ struct GradArgs {
   int nu;                  // narrow tiles
   int64_t usplit;          // narrow index where the second output starts
   const int32_t* gexp;
+  const int32_t* eorder;  // experts, most rows first
   int gexp_sel;  // -1: no exponent
   float* out0;
   float* out1;
@@ -567,15 +585,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   __shared__ __align__(16) uint8_t ring[kStages * kStage];
   __shared__ __align__(16) int32_t ridx[kGather ? 4 * kGK : 4];
 
-  // work item (expert, narrow tile, half, wide tile), wide tiles fastest; each
-  // XCD (blocks are dealt to the eight in turn) takes a contiguous range
+  // work item (expert, narrow tile, half, wide tile), wide tiles fastest.  The
+  // experts, most rows first, are dealt to the eight XCDs in turn (blocks reach
+  // them in turn too), and each XCD runs its experts' items in that order: a
+  // heavily loaded expert (whose items contract over all its rows) starts with
+  // the first blocks, and an expert's items share one XCD's L2
   const unsigned per_e = (unsigned)(a.nu * a.nhalves * a.nvh);
-  const unsigned total = (unsigned)a.E * per_e;
-  if (blockIdx.x >= total) return;
-  const unsigned xq = total / 8u, xr = total % 8u, xcd = blockIdx.x % 8u;
-  const unsigned item = xcd * xq + min(xcd, xr) + blockIdx.x / 8u;
-  const int e = (int)(item / per_e);
-  const unsigned rem = item % per_e;
+  const unsigned xcd = blockIdx.x % 8u, local = blockIdx.x / 8u;
+  const unsigned rank = xcd + 8u * (local / per_e);
+  if (rank >= (unsigned)a.E) return;
+  const int e = a.eorder[rank];
+  const unsigned rem = local % per_e;
   const int ut = (int)(rem / (unsigned)(a.nhalves * a.nvh));
   const int half = (int)((rem / (unsigned)a.nvh) % (unsigned)a.nhalves);
   const int vt = (int)(rem % (unsigned)a.nvh);
@@ -792,6 +812,8 @@ void launch_lora_grads(const Dims& d, const WsMap& w, void* ws, const uint16_t* 
   p.off_g = G.off_g;
   p.np_g = G.g.np;
   p.gexp = ws_ptr<int32_t>(ws, w.gexp);
+  p.E = (int)d.E;
+  p.eorder = ws_ptr<int32_t>(ws, w.eorder);
   k_grad_exps<<<(unsigned)d.E, 256, 0, st>>>(p);
   if (w.max_tiles > 0) k_grad_planes<<<(unsigned)w.max_tiles, 256, 0, st>>>(p);
 
@@ -802,12 +824,14 @@ void launch_lora_grads(const Dims& d, const WsMap& w, void* ws, const uint16_t* 
   a.tok_of_row = ws_ptr<int32_t>(ws, w.tok_of_row);
   a.prow = G.row;
   a.gexp = p.gexp;
+  a.eorder = p.eorder;
   a.accumulate = accumulate;
   a.scale = scale;
   a.zero = ws_ptr<unsigned long long>(ws, w.counters) + kZeroWord;
   const uint16_t* planes = p.planes;
   auto tiles = [](int64_t n) { return (int)((n + 255) / 256); };
-  auto grid = [&](const GradFam& f) { return (unsigned)(a.E * f.nu * a.nhalves * a.nvh); };
+  // whole rounds of eight experts (one per XCD); blocks past the last expert return
+  auto grid = [&](const GradFam& f) { return (unsigned)((a.E + 7) / 8 * 8 * f.nu * a.nhalves * a.nvh); };
   // dA_g, dA_u = sc sum [dG B_g | dU B_u] (x) x
   a.wide = inputs;
   a.wld = d.H;
