@@ -11,10 +11,10 @@
 // A work tile is MT token-slot rows of one expert (rows sorted by the grouping)
 // by kNT = 256 output columns; the four waves of a workgroup split the columns
 // (64 each) and share the activation tile.  Each expert's rows take full
-// 128-row tiles and one tile of the smallest height (16/32/64/128) that holds
-// the rest; one launch covers every height.  Operands move through an LDS ring
-// of 64 contraction values per stage, filled by direct global-to-LDS 16-byte
-// loads (no register staging): three stages for 64/128-row tiles, five or six
+// 128-row tiles and one tile of the smallest height (16/32/64/96/128) that
+// holds the rest; one launch covers every height.  Operands move through an LDS
+// ring of 64 contraction values per stage, filled by direct global-to-LDS 16-byte
+// loads (no register staging): three stages for 64/96/128-row tiles, five or six
 // for 32/16-row tiles, whose fragments of the next stage are read and decoded
 // while the current one is multiplied.  The ring waits are explicit (vmcnt)
 // around a bare s_barrier, so the compiler's conservative drain at
@@ -154,7 +154,8 @@ __host__ __device__ constexpr int gemm_ring_bytes(int MT) {
   return st > lora ? st : lora;
 }
 constexpr int kRingMax = gemm_ring_bytes(128);
-static_assert(gemm_ring_bytes(16) <= kRingMax && gemm_ring_bytes(32) <= kRingMax && gemm_ring_bytes(64) <= kRingMax,
+static_assert(gemm_ring_bytes(16) <= kRingMax && gemm_ring_bytes(32) <= kRingMax && gemm_ring_bytes(64) <= kRingMax &&
+                  gemm_ring_bytes(96) <= kRingMax,
               "the 128-row ring is the largest");
 
 // s_waitcnt vmcnt <= n * D (lgkmcnt 0) for a run-time n in [0, 4]
@@ -630,8 +631,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
       constexpr int kLB = 16384;    // fp32 matrix block: [256 columns][16] or [16][256 columns]
       constexpr int kLBuf = 3;      // sub-groups in the ring: s + 1 and s + 2 are in flight while s is multiplied
       static_assert(kLBuf * (kLA + kLB) <= kRingMax, "LoRA staging");
-      constexpr int kPI = MT >= 64 ? MT / 64 : 1;   // plane copies per wave per sub-group
       constexpr int kRPI = MT >= 64 ? 16 : MT / 4;  // rows per plane copy (4 lanes per row)
+      constexpr int kPC = MT / kRPI;                // plane copies per sub-group
+      constexpr int kPI = (kPC + 3) / 4;            // plane copies per wave per sub-group
+      static_assert(kPC * kRPI == MT && kPC <= 4 * kPI && 4 * kPI - kPC <= kPC, "plane copies");
       const int nsg = KLP / 16;
       auto issue_lora = [&](int sg) {
         const int q0 = 16 * sg, half = q0 >= RP ? 1 : 0, qh = q0 - half * RP;
@@ -640,7 +643,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
         // planes: 4 lanes per row, chunk c (0, 1 hi; 2, 3 lo) at c ^ ((row >> 1) & 3)
 #pragma unroll
         for (int i = 0; i < kPI; ++i) {
-          const int u = w * kPI + i;
+          // every wave issues kPI copies (the waits count on it); past the last
+          // copy a wave repeats one of the final copies (same bytes, same place)
+          const int u0 = w * kPI + i, u = u0 < kPC ? u0 : u0 - (4 * kPI - kPC);
           const int row = kRPI * u + (lane >> 2);
           const int c = (lane & 3) ^ ((row >> 1) & 3);
           const size_t m = (size_t)(m0 + min(row, mlen - 1));
@@ -1003,6 +1008,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       break;
     case 64:
       gemm_tile<KIND, 64, LDMA>(p, tile, nt, ring, s_src, s_exp, s_slot);
+      break;
+    case 96:
+      gemm_tile<KIND, 96, LDMA>(p, tile, nt, ring, s_src, s_exp, s_slot);
       break;
     default:
       gemm_tile<KIND, 128, LDMA>(p, tile, nt, ring, s_src, s_exp, s_slot);

@@ -59,7 +59,7 @@ __device__ int block_inclusive_scan(int v, int32_t* buf) {
 // Height of the tile that holds the last r rows of an expert (r <= bulk): the
 // smallest of 16, 32, 64, 128 that covers them.
 __device__ __forceinline__ int rest_tile_rows(int r, int bulk) {
-  const int h = r <= 16 ? 16 : r <= 32 ? 32 : r <= 64 ? 64 : 128;
+  const int h = r <= 16 ? 16 : r <= 32 ? 32 : r <= 64 ? 64 : r <= 96 ? 96 : 128;
   return h < bulk ? h : bulk;
 }
 

@@ -21,18 +21,19 @@ constexpr int kStageExp = 64;      // columns of a staged per-slot row per expon
 // Rows per tile of the LoRA side products for a call: the smallest of
 // 16/32/64/128 that covers the mean number of token-slots per expert (heavier
 // experts take several tiles).  The expert GEMMs instead take full 128-row
-// tiles of each expert and one tile of the smallest height that holds the rest.
-// KT_RAWINT4_GEMM_ROWS=16|32|64|128 makes every tile of both lists that tall
-// (tuning and tests).
+// tiles of each expert and one tile of the smallest of 16/32/64/96/128 rows that
+// holds the rest.  KT_RAWINT4_GEMM_ROWS=16|32|64|96|128 makes every GEMM tile
+// that tall, and the side-product tiles too except for 96 (tuning and tests).
 inline int forced_gemm_rows() {
   if (const char* env = getenv("KT_RAWINT4_GEMM_ROWS")) {
     const int v = atoi(env);
-    if (v == 16 || v == 32 || v == 64 || v == 128) return v;
+    if (v == 16 || v == 32 || v == 64 || v == 96 || v == 128) return v;
   }
   return 0;
 }
 inline int choose_gemm_rows(int64_t Ms, int64_t E) {
-  if (const int v = forced_gemm_rows()) return v;
+  // (a forced GEMM height also sets the side products' tiles, which have no 96-row form)
+  if (const int v = forced_gemm_rows(); v && v != 96) return v;
   const int64_t active = E < Ms ? E : Ms;
   const int64_t mean = active > 0 ? (Ms + active - 1) / active : 0;
   if (mean <= 16) return 16;

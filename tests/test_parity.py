@@ -190,7 +190,7 @@ def test_layer_ragged_shapes(dev):
     _check_all("ragged", gpu, ref, set(batch.expert_ids.ravel().tolist()))
 
 
-@pytest.mark.parametrize("rows", [16, 32, 64, 128, 0])
+@pytest.mark.parametrize("rows", [16, 32, 64, 96, 128, 0])
 def test_layer_every_tile_height(dev, rows, monkeypatch):
     # one expert with 157 slots (several tiles of every forced height) plus
     # lighter experts; rows = 0 keeps the default, where the GEMM tiles of one
@@ -213,7 +213,7 @@ def test_layer_every_tile_height(dev, rows, monkeypatch):
     _check_all(f"rows{rows or 'mixed'}", gpu, ref, set(batch.expert_ids.ravel().tolist()))
 
 
-@pytest.mark.parametrize("rows", [16, 32, 64, 128, 0])
+@pytest.mark.parametrize("rows", [16, 32, 64, 96, 128, 0])
 def test_layer_every_tile_height_rank64(dev, rows, monkeypatch):
     # as above with a rank that is a multiple of 4 (the LoRA K-steps then copy
     # the LoRA matrices by DMA) and two halves of 64: one expert takes
