@@ -36,6 +36,10 @@ typedef __attribute__((address_space(3))) v4s_t* lds_v4s_ptr;
 // ================================================================ side products
 
 constexpr int kSK = 32;  // contraction values per step
+template <int V>
+struct IntTag {
+  static constexpr int value = V;
+};
 
 struct SideArgs {
   int topk;
@@ -127,9 +131,13 @@ __global__ __launch_bounds__(256) void k_lora_side(SideArgs a) {
   }
   __syncthreads();
 
-  u32x4 areg[kAC];
-  float breg[NB][8];
-  auto load = [&](int k0) {
+  // two register sets: step s + 2's loads are in flight while step s is
+  // multiplied and step s + 1 is written to LDS
+  u32x4 areg2[2][kAC];
+  float breg2[2][NB][8];
+  auto load = [&](int k0, auto rs) {
+    u32x4(&areg)[kAC] = areg2[decltype(rs)::value];
+    float(&breg)[NB][8] = breg2[decltype(rs)::value];
 #pragma unroll
     for (int i = 0; i < kAC; ++i) {
       const int q = tid + 256 * i, row = (q >> 2) & (MT - 1), c = q & 3;
@@ -174,7 +182,9 @@ __global__ __launch_bounds__(256) void k_lora_side(SideArgs a) {
       }
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&](int buf, auto rs) {
+    const u32x4(&areg)[kAC] = areg2[decltype(rs)::value];
+    const float(&breg)[NB][8] = breg2[decltype(rs)::value];
 #pragma unroll
     for (int i = 0; i < kAC; ++i) {
       const int q = tid + 256 * i;
@@ -234,12 +244,16 @@ __global__ __launch_bounds__(256) void k_lora_side(SideArgs a) {
   const int ksteps = kdim / kSK, ks = blockIdx.y;
   const int s0 = (int)((int64_t)ksteps * ks / a.ksplit), s1 = (int)((int64_t)ksteps * (ks + 1) / a.ksplit);
   const int nsteps = s1 - s0;
-  load(s0 * kSK);
-  store(0);
+  const IntTag<0> r0{};
+  const IntTag<1> r1{};
+  load(s0 * kSK, r0);
+  store(0, r0);
+  if (nsteps > 1) load((s0 + 1) * kSK, r1);
   __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
+  // step s: registers rn hold step s + 1, registers rf are free for step s + 2
+  auto body = [&](int s, auto rn, auto rf) {
     const int cur = s & 1;
-    if (s + 1 < nsteps) load((s0 + s + 1) * kSK);
+    if (s + 2 < nsteps) load((s0 + s + 2) * kSK, rf);
     if (cw < a.nq) {
       u32x4 bh[NB], bl[NB];
 #pragma unroll
@@ -274,8 +288,12 @@ __global__ __launch_bounds__(256) void k_lora_side(SideArgs a) {
         }
       }
     }
-    if (s + 1 < nsteps) store(cur ^ 1);
+    if (s + 1 < nsteps) store(cur ^ 1, rn);
     __syncthreads();
+  };
+  for (int s = 0; s < nsteps; s += 2) {
+    body(s, r1, r0);
+    if (s + 1 < nsteps) body(s + 1, r0, r1);
   }
 
 #pragma unroll
