@@ -100,6 +100,7 @@ WsMap plan_workspace(const Dims& d) {
   w.gplanes = pl.take(2 * Ms * (size_t)grad_geom(d.R).row);
   w.gexp = pl.take(4 * 2 * (size_t)d.E);
   w.eorder = pl.take(4 * (size_t)d.E);
+  w.gtmax = pl.take(4 * 2 * (size_t)std::max<int64_t>(w.max_tiles, 1));
   w.total = pl.off;
   return w;
 }

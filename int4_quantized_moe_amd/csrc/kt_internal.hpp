@@ -118,8 +118,9 @@ struct WsMap {
   // backward
   size_t dyh, dyexp, dyb, dgu, dguexp, dgb, dub, drpart;
   // LoRA gradients: narrow-operand planes ([Ms][GradGeom::row] 16-bit), per-expert exponents [E][2]
-  // and the experts in the order their gradient work is dealt out (most rows first) [E]
-  size_t gplanes, gexp, eorder;
+  // and the experts in the order their gradient work is dealt out (most rows first) [E];
+  // per side-product tile, the largest binary exponents the exponents are made from [max_tiles][2]
+  size_t gplanes, gexp, eorder, gtmax;
   size_t group_end;  // bytes needed by the grouping alone
   size_t total;
   int64_t nb, mt, max_tiles, h_nch, dg_nch, dr_nt;

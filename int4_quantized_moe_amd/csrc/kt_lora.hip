@@ -417,51 +417,76 @@ struct GradPrepArgs {
   int32_t* gexp;                                                 // [E][2]: h family, dG|dU family
   int E;
   int32_t* eorder;  // [E]: experts by descending row count (ties: lower index first)
+  int32_t* gtmax;   // [tiles][2]: largest exponents of the h and dG|dU families in a row tile
 };
 
+// Per row tile (side-product tiles, one expert's rows each), the largest binary
+// exponent of each fp16 narrow family: h family rw * dyB * 2^-hexp, dG|dU family
+// ua | ub * 2^-dgexp (hexp, dgexp: the wide row's own exponent, so the wide fp16
+// values can be used as they are); INT_MIN for a family with no finite nonzero value.
+__global__ __launch_bounds__(256) void k_grad_tile_max(GradPrepArgs a) {
+  __shared__ int s_max[2];
+  const int tile = blockIdx.x;
+  if ((unsigned long long)tile >= a.counters[kNumTiles]) return;
+  const int e = a.tile_e[tile], m0 = a.tile_m0[tile];
+  const int mlen = min(a.mt, a.offsets[e + 1] - m0);
+  if (threadIdx.x < 2) s_max[threadIdx.x] = INT_MIN;
+  __syncthreads();
+  int mh = INT_MIN, mg = INT_MIN;
+  for (int idx = threadIdx.x; idx < mlen * a.R; idx += blockDim.x) {
+    const int64_t m = m0 + idx / a.R;
+    const int pq = idx % a.R;
+    const float rw = a.rw[a.sorted_slot[m]];
+    const int he = a.hexp[m * a.h_nch], ge = a.dgexp[m * a.dg_nch];
+    const int64_t i = m * a.R + pq;
+    int ex;
+    const float vh = fabsf(a.dyb[i] * rw);
+    if (vh > 0.f && vh < INFINITY) {
+      (void)frexpf(vh, &ex);
+      mh = max(mh, ex - he);
+    }
+    const float vg = fmaxf(fabsf(a.ua[i]), fabsf(a.ub[i]));
+    if (vg > 0.f && vg < INFINITY) {
+      (void)frexpf(vg, &ex);
+      mg = max(mg, ex - ge);
+    }
+  }
+  atomicMax(&s_max[0], mh);
+  atomicMax(&s_max[1], mg);
+  __syncthreads();
+  if (threadIdx.x < 2) a.gtmax[2 * tile + threadIdx.x] = s_max[threadIdx.x];
+}
+
 // Per expert, the power-of-two exponent S of each fp16 narrow family that puts
-// its largest magnitude into [2^14, 2^15): h family rw * dyB * 2^-hexp, dG|dU
-// family ua | ub * 2^-dgexp (hexp, dgexp: the wide row's own exponent, so the
-// wide fp16 values can be used as they are).  Also the expert's place in the
-// order the gradient kernels deal their work out: most rows first, so that a
-// heavily loaded expert's long contractions start at once rather than last.
-// One block per expert.
+// its largest magnitude into [2^14, 2^15), from its row tiles' maxima (the
+// expert's tiles are the ceil(rows / mt) that follow those of the experts
+// before it).  Also the expert's place in the order the gradient kernels deal
+// their work out: most rows first, so that a heavily loaded expert's long
+// contractions start at once rather than last.  One block per expert.
 __global__ __launch_bounds__(256) void k_grad_exps(GradPrepArgs a) {
   __shared__ int s_max[2];
-  __shared__ int s_rank;
+  __shared__ int s_rank, s_t0;
   const int e = blockIdx.x;
-  const int m0 = a.offsets[e], m1 = a.offsets[e + 1];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int n = a.offsets[e + 1] - a.offsets[e];
   if (threadIdx.x < 2) s_max[threadIdx.x] = INT_MIN;
-  if (threadIdx.x == 0) s_rank = 0;
+  if (threadIdx.x == 0) s_rank = 0, s_t0 = 0;
   __syncthreads();
   {
-    const int n = m1 - m0;
-    int before = 0;
+    int before = 0, t0 = 0;
     for (int f = threadIdx.x; f < a.E; f += blockDim.x) {
       const int nf = a.offsets[f + 1] - a.offsets[f];
       before += (nf > n || (nf == n && f < e)) ? 1 : 0;
+      if (f < e) t0 += (nf + a.mt - 1) / a.mt;
     }
     atomicAdd(&s_rank, before);
+    atomicAdd(&s_t0, t0);
   }
+  __syncthreads();
+  const int t0 = s_t0, nt = (n + a.mt - 1) / a.mt;
   int mh = INT_MIN, mg = INT_MIN;
-  for (int m = m0 + w; m < m1; m += 4) {
-    const float rw = a.rw[a.sorted_slot[m]];
-    const int he = a.hexp[(int64_t)m * a.h_nch], ge = a.dgexp[(int64_t)m * a.dg_nch];
-    for (int p = lane; p < a.R; p += 64) {
-      const int64_t i = (int64_t)m * a.R + p;
-      int ex;
-      const float vh = fabsf(a.dyb[i] * rw);
-      if (vh > 0.f && vh < INFINITY) {
-        (void)frexpf(vh, &ex);
-        mh = max(mh, ex - he);
-      }
-      const float vg = fmaxf(fabsf(a.ua[i]), fabsf(a.ub[i]));
-      if (vg > 0.f && vg < INFINITY) {
-        (void)frexpf(vg, &ex);
-        mg = max(mg, ex - ge);
-      }
-    }
+  for (int t = threadIdx.x; t < nt; t += blockDim.x) {
+    mh = max(mh, a.gtmax[2 * (t0 + t)]);
+    mg = max(mg, a.gtmax[2 * (t0 + t) + 1]);
   }
   atomicMax(&s_max[0], mh);
   atomicMax(&s_max[1], mg);
@@ -832,6 +857,8 @@ void launch_lora_grads(const Dims& d, const WsMap& w, void* ws, const uint16_t* 
   p.gexp = ws_ptr<int32_t>(ws, w.gexp);
   p.E = (int)d.E;
   p.eorder = ws_ptr<int32_t>(ws, w.eorder);
+  p.gtmax = ws_ptr<int32_t>(ws, w.gtmax);
+  if (w.max_tiles > 0) k_grad_tile_max<<<(unsigned)w.max_tiles, 256, 0, st>>>(p);
   k_grad_exps<<<(unsigned)d.E, 256, 0, st>>>(p);
   if (w.max_tiles > 0) k_grad_planes<<<(unsigned)w.max_tiles, 256, 0, st>>>(p);
 
