@@ -19,20 +19,40 @@ __device__ __forceinline__ float wave_max(float v) {
 // One block per row: p = exponent that maps the row's largest magnitude below
 // 2^15, then every element is stored as fp16(x * 2^p) (exact for bf16 values
 // within 2^-24..2^15 of the scaled range), at its within-8 permuted position.
+// Each thread moves 16-byte chunks of 8 values (cols is a multiple of 8; the
+// permutation stays inside a chunk).
 __global__ __launch_bounds__(256) void k_rows_to_half(const uint16_t* __restrict__ src, int64_t cols,
                                                       uint16_t* __restrict__ dst, int32_t* __restrict__ exps) {
   __shared__ float red[4];
   const int64_t row = blockIdx.x;
-  const uint16_t* s = src + row * cols;
+  const u32x4* s = reinterpret_cast<const u32x4*>(src + row * cols);
+  u32x4* d = reinterpret_cast<u32x4*>(dst + row * cols);
+  const int64_t n8 = cols / 8;
   float mx = 0.f;
-  for (int64_t c = threadIdx.x; c < cols; c += blockDim.x) mx = fmaxf(mx, fabsf(bf16_to_float(s[c])));
+  for (int64_t c = threadIdx.x; c < n8; c += blockDim.x) {
+    const u32x4 v = s[c];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      mx = fmaxf(mx, fmaxf(fabsf(bf16_to_float((uint16_t)(w[q] & 0xffffu))), fabsf(bf16_to_float((uint16_t)(w[q] >> 16)))));
+  }
   mx = wave_max(mx);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
   __syncthreads();
   mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const int p = pow2_exponent_for(mx);
-  for (int64_t c = threadIdx.x; c < cols; c += blockDim.x)
-    dst[row * cols + perm_pos((int)c)] = float_to_half_bits(ldexpf(bf16_to_float(s[c]), p));
+  for (int64_t c = threadIdx.x; c < n8; c += blockDim.x) {
+    const u32x4 v = s[c];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint16_t o[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint16_t b = (uint16_t)((k & 1) ? (w[k >> 1] >> 16) : (w[k >> 1] & 0xffffu));
+      o[perm_pos(k)] = float_to_half_bits(ldexpf(bf16_to_float(b), p));
+    }
+    d[c] = u32x4{o[0] | ((uint32_t)o[1] << 16), o[2] | ((uint32_t)o[3] << 16), o[4] | ((uint32_t)o[5] << 16),
+                 o[6] | ((uint32_t)o[7] << 16)};
+  }
   if (threadIdx.x == 0) exps[row] = p;
 }
 
@@ -184,35 +204,42 @@ void launch_fill_zero_f32(float* p, int64_t n, hipStream_t st) {
 // ---------------------------------------------------------------- combine and dRoute
 
 // out[t, c] = sum over valid slots s of stage[t*k + s, c] * 2^-p(t*k + s, c / 64), in slot
-// order, in fp32, then to bf16 (round to nearest even); staged values are fp16
+// order, in fp32, then to bf16 (round to nearest even); staged values are fp16.  Each
+// thread sums 8 columns (one 16-byte staged chunk per slot).
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ stage, const int32_t* __restrict__ stexp,
                                                  int64_t st_nch, const int64_t* __restrict__ ids, int topk, int E,
                                                  int64_t H, uint16_t* __restrict__ out) {
   const int64_t t = blockIdx.x;
-  const int64_t c = ((int64_t)blockIdx.y * blockDim.x + threadIdx.x) * 4;
+  const int64_t c = ((int64_t)blockIdx.y * blockDim.x + threadIdx.x) * 8;
   if (c >= H) return;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < topk; ++s) {
     const int64_t slot = t * topk + s;
     const int64_t e = ids[slot];
     if (e < 0 || e >= E) continue;
-    const uint2 v = *reinterpret_cast<const uint2*>(stage + slot * H + c);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + slot * H + c);
     const int ex = -stexp[slot * st_nch + c / kStageExp];
-    acc.x += ldexpf(half_bits_to_float((uint16_t)(v.x & 0xffffu)), ex);
-    acc.y += ldexpf(half_bits_to_float((uint16_t)(v.x >> 16)), ex);
-    acc.z += ldexpf(half_bits_to_float((uint16_t)(v.y & 0xffffu)), ex);
-    acc.w += ldexpf(half_bits_to_float((uint16_t)(v.y >> 16)), ex);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc[2 * q] += ldexpf(half_bits_to_float((uint16_t)(w[q] & 0xffffu)), ex);
+      acc[2 * q + 1] += ldexpf(half_bits_to_float((uint16_t)(w[q] >> 16)), ex);
+    }
   }
-  uint2 o;
-  o.x = float_to_bf16(acc.x) | ((uint32_t)float_to_bf16(acc.y) << 16);
-  o.y = float_to_bf16(acc.z) | ((uint32_t)float_to_bf16(acc.w) << 16);
-  *reinterpret_cast<uint2*>(out + t * H + c) = o;
+  // two 8-byte stores: the output is only required to be 8-byte aligned
+  uint2 o0, o1;
+  o0.x = float_to_bf16(acc[0]) | ((uint32_t)float_to_bf16(acc[1]) << 16);
+  o0.y = float_to_bf16(acc[2]) | ((uint32_t)float_to_bf16(acc[3]) << 16);
+  o1.x = float_to_bf16(acc[4]) | ((uint32_t)float_to_bf16(acc[5]) << 16);
+  o1.y = float_to_bf16(acc[6]) | ((uint32_t)float_to_bf16(acc[7]) << 16);
+  *reinterpret_cast<uint2*>(out + t * H + c) = o0;
+  *reinterpret_cast<uint2*>(out + t * H + c + 4) = o1;
 }
 
 void launch_combine(const Dims& d, const uint16_t* stage, const int32_t* stexp, int64_t st_nch, const int64_t* ids,
                     uint16_t* out, hipStream_t st) {
   if (d.qlen == 0) return;
-  dim3 grid((unsigned)d.qlen, (unsigned)((d.H / 4 + 255) / 256));
+  dim3 grid((unsigned)d.qlen, (unsigned)((d.H / 8 + 255) / 256));
   k_combine<<<grid, 256, 0, st>>>(stage, stexp, st_nch, ids, (int)d.K, (int)d.E, d.H, out);
 }
 
