@@ -94,8 +94,9 @@ WsMap plan_workspace(const Dims& d) {
   w.dgb = pl.take(4 * Ms * R);
   w.dub = pl.take(4 * Ms * R);
   w.drpart = pl.take(4 * Ms * (size_t)w.dr_nt);
-  // enough blocks to cover the CUs a few times over when the tiles are few
-  w.side_ksplit = std::min<int64_t>(16, std::max<int64_t>(1, (1024 + w.max_tiles - 1) / std::max<int64_t>(w.max_tiles, 1)));
+  // ~4096 blocks (the side-product steps are latency-bound, so more blocks in
+  // flight pay for the partial sums) when the tiles are fewer
+  w.side_ksplit = std::min<int64_t>(16, std::max<int64_t>(1, (4096 + w.max_tiles - 1) / std::max<int64_t>(w.max_tiles, 1)));
   w.side_part = pl.take(w.side_ksplit > 1 ? 4 * (size_t)w.side_ksplit * Ms * 2 * R : 0);
   w.gplanes = pl.take(2 * Ms * (size_t)grad_geom(d.R).row);
   w.gexp = pl.take(4 * 2 * (size_t)d.E);
