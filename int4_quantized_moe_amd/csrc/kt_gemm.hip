@@ -18,10 +18,10 @@
 // for 32/16-row tiles, whose fragments of the next stage are read and decoded
 // while the current one is multiplied.  The ring waits are explicit (vmcnt)
 // around a bare s_barrier, so the compiler's conservative drain at
-// __syncthreads does not serialise the ring.  Blocks are mapped to tiles so that
-// each XCD (blocks are dealt to the eight XCDs in turn) works through a
-// contiguous range of tiles: the column tiles of one row tile, and the row tiles
-// of one expert, then share that XCD's L2.
+// __syncthreads does not serialise the ring.  Row tiles are dealt to the eight
+// XCDs in turn (as blocks are), each XCD running all column tiles of its row
+// tiles: the column tiles of one row tile share that XCD's L2, and a heavily
+// loaded expert's row tiles spread over every XCD.
 //
 // Weights are decoded on the fly into exact fp16 ((c - 8) * scale fits fp16's
 // 11-bit significand) and multiplied on v_mfma_f32_16x16x32_f16 with fp32
@@ -991,14 +991,16 @@ template <int KIND, bool LDMA>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm(GemmParams p) {
   __shared__ __align__(16) uint8_t ring[kRingMax];
   __shared__ int32_t s_src[128], s_exp[128], s_slot[128];
-  // work item: (tile, column tile), column tiles fastest; each XCD (blocks are
-  // dealt to the eight in turn) takes a contiguous range
-  const unsigned total = (unsigned)p.counters[kNumGemmTiles] * (unsigned)p.n_ntiles;
-  if (blockIdx.x >= total) return;
-  const unsigned xq = total / 8u, xr = total % 8u, xcd = blockIdx.x % 8u;
-  const unsigned item = xcd * xq + min(xcd, xr) + blockIdx.x / 8u;
-  const int tile = (int)(item / (unsigned)p.n_ntiles);
-  const int nt = (int)(item % (unsigned)p.n_ntiles);
+  // work item: (tile, column tile).  Whole tiles are dealt to the eight XCDs in
+  // turn (blocks reach them in turn too) and each XCD runs its tiles' column
+  // tiles in order: a tile's activation rows stay in one XCD's L2, and an
+  // expert with many rows (skewed routing) spreads over all eight
+  const unsigned nn = (unsigned)p.n_ntiles, ntl = (unsigned)p.counters[kNumGemmTiles];
+  const unsigned xcd = blockIdx.x % 8u, local = blockIdx.x / 8u;
+  const unsigned tile_u = xcd + 8u * (local / nn);
+  if (tile_u >= ntl) return;
+  const int tile = (int)tile_u;
+  const int nt = (int)(local % nn);
   switch (p.tile_mt[tile]) {
     case 16:
       gemm_tile<KIND, 16, LDMA>(p, tile, nt, ring, s_src, s_exp, s_slot);
@@ -1090,7 +1092,7 @@ void launch_gemm(GemmKind kind, const Dims& d, const WsMap& w, void* ws, const L
       p.lda = 2 * d.I;
       break;
   }
-  const unsigned grid = (unsigned)(w.max_gtiles * p.n_ntiles);
+  const unsigned grid = (unsigned)((w.max_gtiles + 7) / 8 * 8 * p.n_ntiles);  // whole rounds of 8 tiles
   if (grid == 0) return;
   switch (kind) {
     case kGateUp:
