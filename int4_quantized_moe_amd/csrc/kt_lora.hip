@@ -131,6 +131,35 @@ __global__ __launch_bounds__(256) void k_lora_side(SideArgs a) {
   }
   __syncthreads();
 
+  // per-thread source pointers of the contraction's start, advanced by k0 (A
+  // rows, rk matrices) or k0 rows (k-major matrices) per step
+  const uint16_t* pA[kAC];
+#pragma unroll
+  for (int i = 0; i < kAC; ++i) {
+    const int q = tid + 256 * i, row = (q >> 2) & (MT - 1), c = q & 3;
+    pA[i] = a.src + (int64_t)s_src[row] * a.ld + a.col_off + 8 * c;
+  }
+  const float* pB[NB];
+  bool okB[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int q = tid + 256 * i;
+    if (a.rk) {  // W[e][col][k]: thread -> (column, 8 consecutive k)
+      const int col = q >> 2, c = q & 3;
+      const bool second = col >= R;
+      const float* Wm = second ? a.W2 : a.W;
+      const int qq = min(second ? col - R : col, R - 1);
+      okB[i] = col < a.nq;
+      pB[i] = (Wm ? Wm : a.W) + ((int64_t)e * R + qq) * kdim + 8 * c;
+    } else {  // W[e][k][col]: thread -> (k, 8 consecutive columns), whole 16-byte runs where possible
+      const int kr = q / (NQ / 8), c8 = q % (NQ / 8);
+      const int col0 = 8 * c8;
+      const bool second0 = col0 >= R;
+      const int cc = second0 ? col0 - R : col0;
+      okB[i] = (R & 3) == 0 && cc + 8 <= R && col0 + 8 <= a.nq;
+      pB[i] = (second0 && a.W2 ? a.W2 : a.W) + ((int64_t)e * kdim + kr) * R + cc;
+    }
+  }
   // two register sets: step s + 2's loads are in flight while step s is
   // multiplied and step s + 1 is written to LDS
   u32x4 areg2[2][kAC];
@@ -139,45 +168,29 @@ __global__ __launch_bounds__(256) void k_lora_side(SideArgs a) {
     u32x4(&areg)[kAC] = areg2[decltype(rs)::value];
     float(&breg)[NB][8] = breg2[decltype(rs)::value];
 #pragma unroll
-    for (int i = 0; i < kAC; ++i) {
-      const int q = tid + 256 * i, row = (q >> 2) & (MT - 1), c = q & 3;
-      areg[i] = *reinterpret_cast<const u32x4*>(a.src + (int64_t)s_src[row] * a.ld + a.col_off + k0 + 8 * c);
-    }
+    for (int i = 0; i < kAC; ++i) areg[i] = *reinterpret_cast<const u32x4*>(pA[i] + k0);
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      const int q = tid + 256 * i;
-      if (a.rk) {  // W[e][col][k]: thread -> (column, 8 consecutive k)
-        const int col = q >> 2, c = q & 3;
-        const bool second = col >= R;
-        const float* Wm = second ? a.W2 : a.W;
-        const int qq = min(second ? col - R : col, R - 1);
-        const bool ok = col < a.nq;
-        const float* p = (Wm ? Wm : a.W) + ((int64_t)e * R + qq) * kdim + k0 + 8 * c;
+      if (okB[i]) {
+        const float* p = pB[i] + (a.rk ? (int64_t)k0 : (int64_t)k0 * R);
         const float4 x0 = *reinterpret_cast<const float4*>(p), x1 = *reinterpret_cast<const float4*>(p + 4);
-        const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        breg[i][0] = x0.x, breg[i][1] = x0.y, breg[i][2] = x0.z, breg[i][3] = x0.w;
+        breg[i][4] = x1.x, breg[i][5] = x1.y, breg[i][6] = x1.z, breg[i][7] = x1.w;
+      } else if (a.rk) {  // a column past the product's width
 #pragma unroll
-        for (int t = 0; t < 8; ++t) breg[i][t] = ok ? v[t] : 0.f;
-      } else {  // W[e][k][col]: thread -> (k, 8 consecutive columns)
-        const int kr = q / (NQ / 8), c8 = q % (NQ / 8);
+        for (int t = 0; t < 8; ++t) breg[i][t] = 0.f;
+      } else {  // k-major columns one at a time (rank not a multiple of 4, or the run crosses a matrix)
+        const int q = tid + 256 * i;
+        const int kr = q / (NQ / 8), col0 = 8 * (q % (NQ / 8));
         const float* row = a.W + ((int64_t)e * kdim + k0 + kr) * R;
         const float* row2 = a.W2 ? a.W2 + ((int64_t)e * kdim + k0 + kr) * R : row;
-        const int col0 = 8 * c8;
-        const bool second0 = col0 >= R;
-        const int cc = second0 ? col0 - R : col0;
-        if ((R & 3) == 0 && cc + 8 <= R && col0 + 8 <= a.nq) {  // 8 columns inside one matrix, 16-byte aligned
-          const float* p = (second0 ? row2 : row) + cc;
-          const float4 x0 = *reinterpret_cast<const float4*>(p), x1 = *reinterpret_cast<const float4*>(p + 4);
-          breg[i][0] = x0.x, breg[i][1] = x0.y, breg[i][2] = x0.z, breg[i][3] = x0.w;
-          breg[i][4] = x1.x, breg[i][5] = x1.y, breg[i][6] = x1.z, breg[i][7] = x1.w;
-        } else {
 #pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const int col = col0 + t;
-            const bool second = col >= R;
-            const int qq = min(second ? col - R : col, R - 1);
-            const float x = (second ? row2 : row)[qq];
-            breg[i][t] = col < a.nq ? x : 0.f;
-          }
+        for (int t = 0; t < 8; ++t) {
+          const int col = col0 + t;
+          const bool second = col >= R;
+          const int qq = min(second ? col - R : col, R - 1);
+          const float x = (second ? row2 : row)[qq];
+          breg[i][t] = col < a.nq ? x : 0.f;
         }
       }
     }
