@@ -38,6 +38,7 @@ static void plan_group_part(Planner& pl, WsMap& w, int64_t Ms, int64_t E) {
   w.counters = pl.take(sizeof(unsigned long long) * kCounterWords);
   w.counts = pl.take(sizeof(int32_t) * (size_t)E);
   w.offsets = pl.take(sizeof(int32_t) * (size_t)(E + 1));
+  w.qoffsets = pl.take(sizeof(int32_t) * (size_t)(E + 1));
   w.blockcnt = pl.take(sizeof(int32_t) * (size_t)(w.nb * E));
   w.sorted_slot = pl.take(sizeof(int32_t) * (size_t)Ms);
   w.row_of_slot = pl.take(sizeof(int32_t) * (size_t)Ms);
@@ -77,8 +78,9 @@ WsMap plan_workspace(const Dims& d) {
   w.xexp = pl.take(4 * q);
   w.ua = pl.take(4 * Ms * R);
   w.ub = pl.take(4 * Ms * R);
-  w.g = pl.take(4 * Ms * I);
-  w.u = pl.take(4 * Ms * I);
+  // g, u: quad-row layout, each expert's rows from a multiple of 4 (qoffsets)
+  w.g = pl.take(4 * (Ms + 3 * d.E) * I);
+  w.u = pl.take(4 * (Ms + 3 * d.E) * I);
   w.hh = pl.take(2 * Ms * I);
   w.hexp = pl.take(4 * Ms * (size_t)w.h_nch);
   w.ud = pl.take(4 * Ms * R);

@@ -261,24 +261,42 @@ void launch_droute(const Dims& d, const WsMap& w, void* ws, float* grad_route, h
                                                            grad_route);
 }
 
-// gate/up pre-activations the forward saved per grouped row, gathered into slot
-// order; a dropped slot's row is zero
-__global__ void k_saved_preact(const int32_t* __restrict__ row_of_slot, const float* __restrict__ g,
+// gate/up pre-activations the forward saved (quad-row layout: row m of expert e
+// at position q = qoffsets[e] + m - offsets[e], element (q / 4, col, q % 4)),
+// gathered into slot order; a dropped slot's row is zero
+__global__ void k_saved_preact(const int32_t* __restrict__ row_of_slot, const int32_t* __restrict__ offsets,
+                               const int32_t* __restrict__ qoffsets, int E, const float* __restrict__ g,
                                const float* __restrict__ u, int64_t I, float* __restrict__ gate,
                                float* __restrict__ up) {
   const int64_t s = blockIdx.x;
   const int m = row_of_slot[s];
+  int64_t q = 0;
+  if (m >= 0) {
+    int lo = 0, hi = E - 1;  // the expert e with offsets[e] <= m < offsets[e + 1]
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) / 2;
+      if (offsets[mid] <= m)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    q = (int64_t)qoffsets[lo] + (m - offsets[lo]);
+  }
   for (int64_t c = threadIdx.x; c < I; c += blockDim.x) {
-    gate[s * I + c] = m >= 0 ? g[(int64_t)m * I + c] : 0.f;
-    up[s * I + c] = m >= 0 ? u[(int64_t)m * I + c] : 0.f;
+    const int64_t at = ((q >> 2) * I + c) * 4 + (q & 3);
+    gate[s * I + c] = m >= 0 ? g[at] : 0.f;
+    up[s * I + c] = m >= 0 ? u[at] : 0.f;
   }
 }
 
 void launch_saved_preact(const Dims& d, const WsMap& w, const void* ws, float* gate, float* up, hipStream_t st) {
   if (d.Ms == 0) return;
   void* base = const_cast<void*>(ws);
-  k_saved_preact<<<(unsigned)d.Ms, 256, 0, st>>>(ws_ptr<int32_t>(base, w.row_of_slot), ws_ptr<float>(base, w.g),
-                                                 ws_ptr<float>(base, w.u), d.I, gate, up);
+  k_saved_preact<<<(unsigned)d.Ms, 256, 0, st>>>(ws_ptr<int32_t>(base, w.row_of_slot),
+                                                 ws_ptr<int32_t>(base, w.offsets),
+                                                 ws_ptr<int32_t>(base, w.qoffsets), (int)d.E,
+                                                 ws_ptr<float>(base, w.g), ws_ptr<float>(base, w.u), d.I, gate,
+                                                 up);
 }
 
 // ---------------------------------------------------------------- codec hooks

@@ -90,8 +90,12 @@ struct GemmParams {
   const uint16_t* sct1;    // up
   const float* rw;  // route weights per flat slot
   const void* zero;  // 16 zero bytes
+  // saved pre-activations in quad-row layout: row m of expert e sits at
+  // position q = qoffsets[e] + (m - offsets[e]), element (q >> 2, col, q & 3) of
+  // [rows / 4][I][4], so a lane's four rows of one column are one 16-byte run
   float* gsave;
   float* usave;
+  const int32_t* qoffsets;
   uint16_t* hh;
   int32_t* hexp;
   int h_nch;
@@ -867,8 +871,34 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
   // acc holds the plain sums.  One pass: every exponent belongs to one wave's
   // columns of one row, so a 16-lane reduction finds it.
   const float limit = p.limit;
+  // first quad-row position of the tile (the expert's tiles start at multiples of 4 rows)
+  const int64_t qb = (int64_t)p.qoffsets[e] + (m0 - p.offsets[e]);
   if constexpr (KIND == kGateUp) {
-    // g, u saved in fp32; h in fp16 times 2^p, p per (row, this wave's 32 columns)
+    // g, u saved in fp32, a lane's four rows of a column as one 16-byte store
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int r0 = mb * 16 + lg * 4;
+      const int64_t qrow = (qb + r0) >> 2;
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const int col = n0 + w * 32 + f * 16 + lr;
+        if (col >= I || r0 >= mlen) continue;
+        float* gd = p.gsave + (qrow * I + col) * 4;
+        float* ud = p.usave + (qrow * I + col) * 4;
+        if (r0 + 3 < mlen) {
+          *reinterpret_cast<floatx4*>(gd) = acc[mb][f];
+          *reinterpret_cast<floatx4*>(ud) = acc[mb][f + 2];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (r0 + i < mlen) {
+              gd[i] = acc[mb][f][i];
+              ud[i] = acc[mb][f + 2][i];
+            }
+        }
+      }
+    }
+    // h in fp16 times 2^p, p per (row, this wave's 32 columns)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -884,10 +914,6 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
           const bool valid = vrow && col < I;
           const float g = acc[mb][f][i];
           const float u = acc[mb][f + 2][i];
-          if (valid) {
-            p.gsave[m * I + col] = g;
-            p.usave[m * I + col] = u;
-          }
           float gp, up, mg, mu;
           clamp_swiglu(g, u, limit, gp, up, mg, mu);
           h[f] = valid ? gp * sigmoid_f(gp) * up : 0.f;
@@ -935,7 +961,23 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
     const int half_nch = p.dg_nch / 2;
     const int chunk = (n0 + w * 64) / kDgExp;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb) {
+      // the saved g, u of this lane's four rows of each column: one 16-byte load each
+      // (quads past the tile's rows are not read: they may lie past the buffer)
+      const int r0 = mb * 16 + lg * 4;
+      const int64_t qrow = (qb + r0) >> 2;
+      floatx4 gq[4], uq[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const int cc = min(n0 + w * 64 + f * 16 + lr, I - 1);
+        if (r0 < mlen) {
+          gq[f] = *reinterpret_cast<const floatx4*>(p.gsave + (qrow * I + cc) * 4);
+          uq[f] = *reinterpret_cast<const floatx4*>(p.usave + (qrow * I + cc) * 4);
+        } else {
+          gq[f] = floatx4{0.f, 0.f, 0.f, 0.f};
+          uq[f] = gq[f];
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = mb * 16 + lg * 4 + i;
@@ -948,10 +990,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
         for (int f = 0; f < 4; ++f) {
           const int col = n0 + w * 64 + f * 16 + lr;
           const bool valid = vrow && col < I;
-          const int cc = min(col, I - 1);
           const float gh = acc[mb][f][i];
           float gp, up, mg, mu;
-          clamp_swiglu(p.gsave[m * I + cc], p.usave[m * I + cc], limit, gp, up, mg, mu);
+          clamp_swiglu(gq[f][i], uq[f][i], limit, gp, up, mg, mu);
           const float sg = sigmoid_f(gp);
           const float si = gp * sg;
           const float dsi = sg * (1.f + gp * (1.f - sg));
@@ -979,6 +1020,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
           p.dgu[m * (size_t)(2 * I) + I + pc] = float_to_half_bits(ldexpf(du[f], pu));
         }
       }
+    }
   }
 }
 
@@ -1048,6 +1090,7 @@ void launch_gemm(GemmKind kind, const Dims& d, const WsMap& w, void* ws, const L
   p.rw = route_weights;
   p.gsave = ws_ptr<float>(ws, w.g);
   p.usave = ws_ptr<float>(ws, w.u);
+  p.qoffsets = ws_ptr<int32_t>(ws, w.qoffsets);
   p.hh = ws_ptr<uint16_t>(ws, w.hh);
   p.hexp = ws_ptr<int32_t>(ws, w.hexp);
   p.h_nch = (int)w.h_nch;

@@ -63,14 +63,17 @@ __device__ __forceinline__ int rest_tile_rows(int r, int bulk) {
   return h < bulk ? h : bulk;
 }
 
-// One block: expert totals, exclusive offsets, per-block placement bases
+// One block: expert totals, exclusive offsets (and the same with every expert's
+// rows rounded up to a multiple of 4, for the quad-row layout of the saved
+// pre-activations), per-block placement bases
 // (blockcnt is rewritten in place), and two lists of (expert, first row) tiles:
 // tiles of `mt` rows for the LoRA side products, and tiles for the expert GEMMs
 // -- full tiles of `gbulk` rows, then (if `gmixed`) one tile of the smallest
 // height that holds the rest of the expert's rows.
 __global__ __launch_bounds__(1024) void k_group_scan(int E, int64_t nb, int mt, int gbulk, int gmixed,
                                                      int32_t* __restrict__ blockcnt, int32_t* __restrict__ counts,
-                                                     int32_t* __restrict__ offsets, int32_t* __restrict__ tile_e,
+                                                     int32_t* __restrict__ offsets, int32_t* __restrict__ qoffsets,
+                                                     int32_t* __restrict__ tile_e,
                                                      int32_t* __restrict__ tile_m0, int32_t* __restrict__ gtile_e,
                                                      int32_t* __restrict__ gtile_m0, int32_t* __restrict__ gtile_mt,
                                                      unsigned long long* __restrict__ counters) {
@@ -78,22 +81,26 @@ __global__ __launch_bounds__(1024) void k_group_scan(int E, int64_t nb, int mt, 
   const int T = blockDim.x;
   const int per = (E + T - 1) / T;
   const int e0 = min(E, (int)threadIdx.x * per), e1 = min(E, e0 + per);
-  int local = 0, ltiles = 0, lgt = 0;
+  int local = 0, ltiles = 0, lgt = 0, lq = 0;
   for (int e = e0; e < e1; ++e) {
     int c = 0;
     for (int64_t b = 0; b < nb; ++b) c += blockcnt[b * E + e];
     counts[e] = c;
     local += c;
+    lq += (c + 3) & ~3;
     ltiles += (c + mt - 1) / mt;
     lgt += (c + gbulk - 1) / gbulk;
   }
   const int incl = block_inclusive_scan(local, buf);
+  const int qincl = block_inclusive_scan(lq, buf);
   const int tincl = block_inclusive_scan(ltiles, buf);
   const int gincl = block_inclusive_scan(lgt, buf);
-  int run = incl - local, trun = tincl - ltiles, grun = gincl - lgt;
+  int run = incl - local, qrun = qincl - lq, trun = tincl - ltiles, grun = gincl - lgt;
   for (int e = e0; e < e1; ++e) {
     const int c = counts[e];
     offsets[e] = run;
+    qoffsets[e] = qrun;
+    qrun += (c + 3) & ~3;
     int base = run;
     for (int64_t b = 0; b < nb; ++b) {
       const int v = blockcnt[b * E + e];
@@ -118,6 +125,7 @@ __global__ __launch_bounds__(1024) void k_group_scan(int E, int64_t nb, int mt, 
   }
   if ((int)threadIdx.x == T - 1) {
     offsets[E] = incl;
+    qoffsets[E] = qincl;
     counters[kNumTiles] = (unsigned long long)tincl;
     counters[kNumGemmTiles] = (unsigned long long)gincl;
   }
@@ -174,7 +182,7 @@ void launch_group(const Dims& d, const WsMap& w, void* ws, const int64_t* ids, h
   if (w.nb > 0) k_group_count<<<(unsigned)w.nb, 256, lds, st>>>(ids, d.Ms, E, blockcnt, counters);
   k_group_scan<<<1, 1024, 0, st>>>(E, w.nb, (int)w.mt, (int)w.gbulk, w.gmixed ? 1 : 0, blockcnt,
                                    ws_ptr<int32_t>(ws, w.counts), ws_ptr<int32_t>(ws, w.offsets),
-                                   ws_ptr<int32_t>(ws, w.tile_e), ws_ptr<int32_t>(ws, w.tile_m0),
+                                   ws_ptr<int32_t>(ws, w.qoffsets), ws_ptr<int32_t>(ws, w.tile_e), ws_ptr<int32_t>(ws, w.tile_m0),
                                    ws_ptr<int32_t>(ws, w.gtile_e), ws_ptr<int32_t>(ws, w.gtile_m0),
                                    ws_ptr<int32_t>(ws, w.gtile_mt), counters);
   if (w.nb > 0)

@@ -106,7 +106,7 @@ struct WsMap {
   // fp16 transposed scales of the three projections ([E][K/32][rows]), made by the forward
   size_t sct_g, sct_u, sct_d;
   // grouping
-  size_t counters, counts, offsets, blockcnt, sorted_slot, row_of_slot, tok_of_row, tile_e, tile_m0;
+  size_t counters, counts, offsets, qoffsets, blockcnt, sorted_slot, row_of_slot, tok_of_row, tile_e, tile_m0;
   size_t gtile_e, gtile_m0, gtile_mt;  // expert GEMM tiles (mixed heights)
   // forward state kept for the backward
   size_t xh, xexp, ua, ub, g, u, hh, hexp, ud;
