@@ -7,6 +7,9 @@ free dX, LoRA side products and the six LoRA gradient reductions) over one
 synthetic batch already resident in HBM.  Prints ONE JSON line on stdout;
 progress goes to stderr.
 
+``--infer lora|base`` times the inference forward instead (kt_rawint4_moe_infer:
+with the LoRA, or the frozen base alone); the default line is the training step.
+
 Default workload: 384 experts, top-8, hidden 7168, intermediate 2048, LoRA rank 64
 (alpha 128), 16384 tokens, SwiGLU clamp 7, uniform routing.  ``--config`` picks
 another of the five workloads of ``int4_quantized_moe_amd.workloads.CONFIGS``.
@@ -15,6 +18,7 @@ another of the five workloads of ``int4_quantized_moe_amd.workloads.CONFIGS``.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -24,6 +28,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "routed-expert fwd+bwd tokens/sec per layer; % MFMA peak / % HBM BW"
+METRIC_INFER = "routed-expert inference forward tokens/sec per layer; % MFMA peak / % HBM BW"
+FWD_PHASES = ("gemm_gate_up", "gemm_down", "lora_a_gate_up", "lora_a_down")
 PEAK_MFMA_FP16 = 2.5e15  # dense fp16/bf16 MFMA, FLOP/s
 PEAK_HBM = 8.0e12  # bytes/s
 
@@ -56,15 +62,21 @@ def phase_work(cfg, slots):
     }
 
 
-def cpu_baseline(cfg, weights, batch, target_s):
-    """The oracle, as it stands, on the first n tokens of the same batch."""
+def cpu_baseline(cfg, weights, batch, target_s, infer=None):
+    """The oracle, as it stands, on the first n tokens of the same batch (forward
+    only for an inference run; zero LoRA for the base alone)."""
     import numpy as np
 
     import oracle as O
 
+    lora = None
+    if infer == "base":
+        lora = {n: np.zeros(s) for n, s in cfg.lora_shapes().items()}
+
     def run(n):
         t0 = time.perf_counter()
-        O.moe(cfg, weights, batch.inputs[:n], batch.expert_ids[:n], batch.route_weights[:n], batch.grad_output[:n])
+        O.moe(cfg, weights, batch.inputs[:n], batch.expert_ids[:n], batch.route_weights[:n],
+              None if infer else batch.grad_output[:n], lora=lora)
         return time.perf_counter() - t0
 
     n = min(8, cfg.qlen)
@@ -81,7 +93,7 @@ def cpu_baseline(cfg, weights, batch, target_s):
         "cores": O.num_threads(),
         "kind": "oracle",
         "sample": f"first {n} of {cfg.qlen} tokens ({n * cfg.top_k} token-slots, {active} active experts), "
-                  f"fwd+bwd, fp64 accumulation, {t:.1f} s wall",
+                  f"{'forward' if infer else 'fwd+bwd'}, fp64 accumulation, {t:.1f} s wall",
     }
 
 
@@ -93,6 +105,9 @@ def main():
     ap.add_argument("--config", type=int, default=4, help="index into workloads.CONFIGS")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--infer", choices=("lora", "base"), default=None,
+                    help="time the inference forward (with the LoRA, or the frozen base alone) instead of the "
+                         "training step")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after timing, run one plain elementwise copy (torch.neg, fp32) of this many MiB: "
                          "the calibration kernel for hardware byte counters")
@@ -117,19 +132,26 @@ def main():
     weights = workloads.make_weights(cfg, seed)
     batch = workloads.make_batch(cfg, seed)
     log(f"generated in {time.perf_counter() - t0:.1f}s; uploading")
-    dl = device.DeviceLayer(cfg, weights, "cuda:0")
+    dl = device.DeviceLayer(cfg, weights, "cuda:0", base_only=args.infer == "base")
     db = device.DeviceBatch(batch, "cuda:0")
-    ws = dl.workspace(db.qlen)
-    grads = dl.grad_buffers(fill=0.0)
     out = torch.empty((db.qlen, cfg.hidden), dtype=torch.bfloat16, device="cuda:0")
-    dx = torch.empty_like(out)
-    droute = torch.empty((db.qlen, cfg.top_k), dtype=torch.float32, device="cuda:0")
     stream = torch.cuda.current_stream()
+    if args.infer:
+        ws = dl.infer_workspace(db.qlen)
 
-    def step():
-        dl.forward(db.inputs, db.expert_ids, db.route_weights, ws, output=out, stream=stream)
-        dl.backward(db.inputs, db.expert_ids, db.route_weights, db.grad_output, ws, grads, accumulate=False,
-                    grad_scale=1.0, grad_input=dx, grad_route=droute, stream=stream)
+        def step():
+            dl.infer(db.inputs, db.expert_ids, db.route_weights, ws, output=out, stream=stream)
+    else:
+        ws = dl.workspace(db.qlen)
+        grads = dl.grad_buffers(fill=0.0)
+        dx = torch.empty_like(out)
+        droute = torch.empty((db.qlen, cfg.top_k), dtype=torch.float32, device="cuda:0")
+
+        def step():
+            dl.forward(db.inputs, db.expert_ids, db.route_weights, ws, output=out, stream=stream)
+            dl.backward(db.inputs, db.expert_ids, db.route_weights, db.grad_output, ws, grads, accumulate=False,
+                        grad_scale=1.0, grad_input=dx, grad_route=droute, stream=stream)
+    log(f"workspace {ws.numel() / 2**30:.2f} GiB")
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -156,7 +178,7 @@ def main():
 
     slots = int(np.count_nonzero((batch.expert_ids >= 0) & (batch.expert_ids < cfg.num_experts)))
     active = int(np.unique(batch.expert_ids).size)
-    work = phase_work(cfg, slots)
+    work = phase_work(cfg if args.infer != "base" else dataclasses.replace(cfg, rank=0), slots)
     per_step = {}
     for name, (ms, n) in phases.items():
         if n:
@@ -177,12 +199,18 @@ def main():
     # (profiles/hbm_traffic_<phase>_<workload>.txt), only while it was taken from these sources
     from int4_quantized_moe_amd import profsum
 
-    measured = profsum.read_traffic(os.path.join(ROOT, "profiles", f"hbm_traffic_{dom}_{cfg.name}.txt"))
+    mode = f"_infer_{args.infer}" if args.infer else ""
+    measured = profsum.read_traffic(os.path.join(ROOT, "profiles", f"hbm_traffic_{dom}_{cfg.name}{mode}.txt"))
     traffic = None if measured is None else int(round(measured["read"] + measured["write"]))
     roof.update({"kernel": dom, "achieved": round(achieved, 2), "peak": peak, "frac": round(achieved / peak, 4),
                  "traffic": traffic, "avg_ms": round(dom_ms, 4)})
-    total_flops = slots * (12 * cfg.hidden * cfg.intermediate + 18 * cfg.rank * (cfg.hidden + cfg.intermediate))
-    total_wbytes = 2 * 3 * active * (cfg.hidden * cfg.intermediate // 2 + cfg.hidden * cfg.intermediate // 16)
+    if args.infer:  # the forward alone: gate/up and down, with their LoRA terms unless the base runs alone
+        r = cfg.rank if args.infer == "lora" else 0
+        total_flops = sum(work[p][0] for p in FWD_PHASES) if r else slots * 6 * cfg.hidden * cfg.intermediate
+        total_wbytes = 3 * active * (cfg.hidden * cfg.intermediate // 2 + cfg.hidden * cfg.intermediate // 16)
+    else:
+        total_flops = slots * (12 * cfg.hidden * cfg.intermediate + 18 * cfg.rank * (cfg.hidden + cfg.intermediate))
+        total_wbytes = 2 * 3 * active * (cfg.hidden * cfg.intermediate // 2 + cfg.hidden * cfg.intermediate // 16)
     log(f"step: {total_flops / (ms_per_step / 1e3) / 1e12:.1f} TFLOP/s "
         f"({100 * total_flops / (ms_per_step / 1e3) / PEAK_MFMA_FP16:.2f}% MFMA), packed weights "
         f"{total_wbytes / (ms_per_step / 1e3) / 1e9:.1f} GB/s ({100 * total_wbytes / (ms_per_step / 1e3) / PEAK_HBM:.2f}% HBM)")
@@ -199,11 +227,11 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, weights, batch, args.cpu_seconds)
+        cpu = cpu_baseline(cfg, weights, batch, args.cpu_seconds, args.infer)
         log(f"cpu baseline {cpu['value']:.2f} tokens/s on {cpu['cores']} threads")
 
     line = {
-        "metric": METRIC,
+        "metric": METRIC_INFER if args.infer else METRIC,
         "value": round(value, 2),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -217,7 +245,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "experts": cfg.num_experts, "top_k": cfg.top_k, "hidden": cfg.hidden,
                    "intermediate": cfg.intermediate, "rank": cfg.rank, "alpha": cfg.alpha, "qlen": cfg.qlen,
-                   "swiglu_limit": cfg.swiglu_limit, "routing": cfg.routing, "active_experts": active},
+                   "swiglu_limit": cfg.swiglu_limit, "routing": cfg.routing, "active_experts": active,
+                   **({"mode": f"inference ({'LoRA' if args.infer == 'lora' else 'frozen base alone'})"}
+                      if args.infer else {})},
         "mfma_frac_step": round(total_flops / (ms_per_step / 1e3) / PEAK_MFMA_FP16, 4),
         "hbm_frac_step": round(total_wbytes / (ms_per_step / 1e3) / PEAK_HBM, 4),
         "phase_ms_per_step": per_step,

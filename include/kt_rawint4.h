@@ -121,6 +121,24 @@ int kt_rawint4_moe_fwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const ui
                        size_t workspace_bytes, void* stream);
 
 /*
+ * Inference forward: the same output as kt_rawint4_moe_fwd (bit for bit, with
+ * LoRA), keeping nothing for a backward (page "rawint4_sft_reference.py",
+ * routed_rawint4_lora; page "test_rawint4_sft_numerical.py", the inference
+ * regression, where a frozen-base inference kernel is checked against the
+ * reference with zero LoRA and the base storage hash).  With all six LoRA
+ * pointers NULL the layer is the frozen base alone (rank and alpha are not
+ * used); otherwise every LoRA pointer must be given, as for the training
+ * forward.  Arguments, alignment and errors as for kt_rawint4_moe_fwd; the
+ * workspace (kt_rawint4_moe_infer_workspace_bytes, smaller: no saved
+ * pre-activations, no backward buffers, no side products without LoRA) cannot
+ * feed a backward.
+ */
+size_t kt_rawint4_moe_infer_workspace_bytes(const kt_rawint4_moe_layer* layer, int32_t qlen);
+int kt_rawint4_moe_infer(const kt_rawint4_moe_layer* layer, int32_t qlen, const uint16_t* inputs,
+                         const int64_t* expert_ids, const float* route_weights, uint16_t* output, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
  * Backward of the same call (page "rawint4_sft_reference.py",
  * run_routed_reference: autograd with grad_output as the cotangent).  Must use
  * the workspace of the latest forward with the same layer, qlen, inputs,

@@ -19,6 +19,8 @@ from ._lib import (  # noqa: F401
     kt_rawint4_moe_bwd,
     kt_rawint4_moe_diagnostics,
     kt_rawint4_moe_fwd,
+    kt_rawint4_moe_infer,
+    kt_rawint4_moe_infer_workspace_bytes,
     kt_rawint4_moe_layer,
     kt_rawint4_moe_workspace_bytes,
     kt_rawint4_profile_enable,

@@ -69,6 +69,8 @@ def load_library() -> ctypes.CDLL:
     sigs = {
         "kt_rawint4_moe_workspace_bytes": (sz, [lp, i32]),
         "kt_rawint4_moe_fwd": (ctypes.c_int, [lp, i32, _vp, _vp, _vp, _vp, _vp, sz, _vp]),
+        "kt_rawint4_moe_infer_workspace_bytes": (sz, [lp, i32]),
+        "kt_rawint4_moe_infer": (ctypes.c_int, [lp, i32, _vp, _vp, _vp, _vp, _vp, sz, _vp]),
         "kt_rawint4_moe_bwd": (ctypes.c_int, [lp, i32, _vp, _vp, _vp, _vp, _vp, _vp] + [_vp] * 6 + [i32, f32, _vp, sz, _vp]),
         "kt_rawint4_unpack": (ctypes.c_int, [_vp, i64, i64, _vp, _vp]),
         "kt_rawint4_dequant": (ctypes.c_int, [_vp, _vp, i64, i64, _vp, _vp]),
@@ -141,6 +143,19 @@ def kt_rawint4_moe_fwd(layer, qlen, inputs, expert_ids, route_weights, output, w
     _check(load_library().kt_rawint4_moe_fwd(ctypes.byref(layer), int(qlen), _ptr(inputs), _ptr(expert_ids),
                                              _ptr(route_weights), _ptr(output), _ptr(workspace),
                                              _nbytes(workspace) if workspace is not None else 0, _stream(stream)))
+
+
+def kt_rawint4_moe_infer_workspace_bytes(layer: kt_rawint4_moe_layer, qlen: int) -> int:
+    n = load_library().kt_rawint4_moe_infer_workspace_bytes(ctypes.byref(layer), int(qlen))
+    if n == 0:
+        raise KtRawInt4Error(KT_RAWINT4_EINVAL, kt_rawint4_last_error())
+    return int(n)
+
+
+def kt_rawint4_moe_infer(layer, qlen, inputs, expert_ids, route_weights, output, workspace, stream=None) -> None:
+    _check(load_library().kt_rawint4_moe_infer(ctypes.byref(layer), int(qlen), _ptr(inputs), _ptr(expert_ids),
+                                               _ptr(route_weights), _ptr(output), _ptr(workspace),
+                                               _nbytes(workspace) if workspace is not None else 0, _stream(stream)))
 
 
 def kt_rawint4_moe_bwd(layer, qlen, inputs, expert_ids, route_weights, grad_output, grad_input, grad_route, d_gate_a,

@@ -64,6 +64,8 @@ WsMap plan_group_workspace(int64_t qlen, int64_t top_k, int64_t E) {
 }
 
 WsMap plan_workspace(const Dims& d) {
+  // an inference forward (d.train false) keeps only what the forward itself
+  // uses; without LoRA (d.R == 0) no side products either
   WsMap w{};
   Planner pl;
   plan_group_part(pl, w, d.Ms, d.E);
@@ -74,43 +76,57 @@ WsMap plan_workspace(const Dims& d) {
   w.dr_nt = (d.I + kDgExp - 1) / kDgExp;
   w.dg_nch = 2 * w.dr_nt;
   const size_t Ms = (size_t)d.Ms, q = (size_t)d.qlen, H = (size_t)d.H, I = (size_t)d.I, R = (size_t)d.R;
+  const bool lora = d.R > 0;
+  w.saves = d.train;
   w.xh = pl.take(2 * q * H);
   w.xexp = pl.take(4 * q);
-  w.ua = pl.take(4 * Ms * R);
-  w.ub = pl.take(4 * Ms * R);
-  // g, u: quad-row layout, each expert's rows from a multiple of 4 (qoffsets)
-  w.g = pl.take(4 * (Ms + 3 * d.E) * I);
-  w.u = pl.take(4 * (Ms + 3 * d.E) * I);
+  if (lora) {
+    w.ua = pl.take(4 * Ms * R);
+    w.ub = pl.take(4 * Ms * R);
+  }
+  if (d.train) {
+    // g, u: quad-row layout, each expert's rows from a multiple of 4 (qoffsets)
+    w.g = pl.take(4 * (Ms + 3 * d.E) * I);
+    w.u = pl.take(4 * (Ms + 3 * d.E) * I);
+  }
   w.hh = pl.take(2 * Ms * I);
   w.hexp = pl.take(4 * Ms * (size_t)w.h_nch);
-  w.ud = pl.take(4 * Ms * R);
-  w.lsplit = pl.take(2 * 2 * Ms * 2 * (size_t)lora_half_width((int64_t)R));
+  if (lora) {
+    w.ud = pl.take(4 * Ms * R);
+    w.lsplit = pl.take(2 * 2 * Ms * 2 * (size_t)lora_half_width((int64_t)R));
+  }
   w.st_nch = (d.H + kStageExp - 1) / kStageExp;
   w.stage = pl.take(2 * Ms * H);
   w.stexp = pl.take(4 * Ms * (size_t)w.st_nch);
-  w.dyh = pl.take(2 * q * H);
-  w.dyexp = pl.take(4 * q);
-  w.dyb = pl.take(4 * Ms * R);
-  w.dgu = pl.take(2 * Ms * 2 * I);
-  w.dguexp = pl.take(4 * Ms * (size_t)w.dg_nch);
-  w.dgb = pl.take(4 * Ms * R);
-  w.dub = pl.take(4 * Ms * R);
-  w.drpart = pl.take(4 * Ms * (size_t)w.dr_nt);
+  if (d.train) {
+    w.dyh = pl.take(2 * q * H);
+    w.dyexp = pl.take(4 * q);
+    w.dyb = pl.take(4 * Ms * R);
+    w.dgu = pl.take(2 * Ms * 2 * I);
+    w.dguexp = pl.take(4 * Ms * (size_t)w.dg_nch);
+    w.dgb = pl.take(4 * Ms * R);
+    w.dub = pl.take(4 * Ms * R);
+    w.drpart = pl.take(4 * Ms * (size_t)w.dr_nt);
+  }
   // ~4096 blocks (the side-product steps are latency-bound, so more blocks in
   // flight pay for the partial sums) when the tiles are fewer
   w.side_ksplit = std::min<int64_t>(16, std::max<int64_t>(1, (4096 + w.max_tiles - 1) / std::max<int64_t>(w.max_tiles, 1)));
-  w.side_part = pl.take(w.side_ksplit > 1 ? 4 * (size_t)w.side_ksplit * Ms * 2 * R : 0);
-  w.gplanes = pl.take(2 * Ms * (size_t)grad_geom(d.R).row);
-  w.gexp = pl.take(4 * 2 * (size_t)d.E);
-  w.eorder = pl.take(4 * (size_t)d.E);
-  w.gtmax = pl.take(4 * 2 * (size_t)std::max<int64_t>(w.max_tiles, 1));
+  if (lora) w.side_part = pl.take(w.side_ksplit > 1 ? 4 * (size_t)w.side_ksplit * Ms * 2 * R : 0);
+  if (d.train) {
+    w.gplanes = pl.take(2 * Ms * (size_t)grad_geom(d.R).row);
+    w.gexp = pl.take(4 * 2 * (size_t)d.E);
+    w.eorder = pl.take(4 * (size_t)d.E);
+    w.gtmax = pl.take(4 * 2 * (size_t)std::max<int64_t>(w.max_tiles, 1));
+  }
   w.total = pl.off;
   return w;
 }
 
 static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-static int check_layer(const kt_rawint4_moe_layer* L, int32_t qlen, Dims* d) {
+// allow_base: an inference call may give all six LoRA pointers as NULL (the
+// frozen base alone; rank and alpha are then not used)
+static int check_layer(const kt_rawint4_moe_layer* L, int32_t qlen, Dims* d, bool allow_base = false) {
   if (!L) return fail(KT_RAWINT4_EINVAL, "layer is NULL");
   if (L->num_experts < 1 || L->num_experts > KT_RAWINT4_MAX_EXPERTS)
     return fail(KT_RAWINT4_EINVAL, "num_experts must be in [1, 8192]");
@@ -119,8 +135,11 @@ static int check_layer(const kt_rawint4_moe_layer* L, int32_t qlen, Dims* d) {
     return fail(KT_RAWINT4_EINVAL, "hidden must be a positive multiple of 32 (at most 65536)");
   if (L->intermediate <= 0 || L->intermediate % KT_RAWINT4_GROUP_SIZE || L->intermediate > 65536)
     return fail(KT_RAWINT4_EINVAL, "intermediate must be a positive multiple of 32 (at most 65536)");
-  if (L->rank < 1 || L->rank > KT_RAWINT4_MAX_RANK) return fail(KT_RAWINT4_EINVAL, "rank must be in [1, 128]");
-  if (!isfinite(L->alpha)) return fail(KT_RAWINT4_EINVAL, "alpha must be finite");
+  const bool base = allow_base && !L->gate_lora_a && !L->gate_lora_b && !L->up_lora_a && !L->up_lora_b &&
+                    !L->down_lora_a && !L->down_lora_b;
+  if (!base && (L->rank < 1 || L->rank > KT_RAWINT4_MAX_RANK))
+    return fail(KT_RAWINT4_EINVAL, "rank must be in [1, 128]");
+  if (!base && !isfinite(L->alpha)) return fail(KT_RAWINT4_EINVAL, "alpha must be finite");
   if (!isfinite(L->swiglu_limit) || L->swiglu_limit < 0.f)
     return fail(KT_RAWINT4_EINVAL, "swiglu_limit must be finite and non-negative");
   if (qlen < 0) return fail(KT_RAWINT4_EINVAL, "qlen must be non-negative");
@@ -128,23 +147,24 @@ static int check_layer(const kt_rawint4_moe_layer* L, int32_t qlen, Dims* d) {
   const void* ptrs[] = {L->gate_packed, L->up_packed,   L->down_packed, L->gate_scale,  L->up_scale,
                         L->down_scale,  L->gate_lora_a, L->gate_lora_b, L->up_lora_a,   L->up_lora_b,
                         L->down_lora_a, L->down_lora_b};
-  for (const void* p : ptrs)
-    if (!p) return fail(KT_RAWINT4_EINVAL, "a weight, scale or LoRA pointer is NULL");
+  for (int i = 0; i < (base ? 6 : 12); ++i)
+    if (!ptrs[i]) return fail(KT_RAWINT4_EINVAL, "a weight, scale or LoRA pointer is NULL");
   if (!aligned(L->gate_packed, 16) || !aligned(L->up_packed, 16) || !aligned(L->down_packed, 16))
     return fail(KT_RAWINT4_EINVAL, "packed weights must be 16-byte aligned");
   if (!aligned(L->gate_scale, 2) || !aligned(L->up_scale, 2) || !aligned(L->down_scale, 2))
     return fail(KT_RAWINT4_EINVAL, "scales must be 2-byte aligned");
   const float* lora[] = {L->gate_lora_a, L->gate_lora_b, L->up_lora_a, L->up_lora_b, L->down_lora_a, L->down_lora_b};
-  for (const float* p : lora)
-    if (!aligned(p, 16)) return fail(KT_RAWINT4_EINVAL, "LoRA tensors must be 16-byte aligned");
+  if (!base)
+    for (const float* p : lora)
+      if (!aligned(p, 16)) return fail(KT_RAWINT4_EINVAL, "LoRA tensors must be 16-byte aligned");
   d->E = L->num_experts;
   d->K = L->top_k;
   d->H = L->hidden;
   d->I = L->intermediate;
-  d->R = L->rank;
+  d->R = base ? 0 : L->rank;
   d->qlen = qlen;
   d->Ms = (int64_t)qlen * L->top_k;
-  d->sc = L->alpha / (float)L->rank;
+  d->sc = base ? 0.f : L->alpha / (float)L->rank;
   d->limit = L->swiglu_limit;
   return KT_RAWINT4_OK;
 }
@@ -309,13 +329,12 @@ size_t kt_rawint4_moe_workspace_bytes(const kt_rawint4_moe_layer* layer, int32_t
   return plan_workspace(d).total;
 }
 
-int kt_rawint4_moe_fwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const uint16_t* inputs,
-                       const int64_t* expert_ids, const float* route_weights, uint16_t* output, void* workspace,
-                       size_t workspace_bytes, void* stream) {
-  Dims d;
-  int rc = check_layer(layer, qlen, &d);
-  if (rc) return rc;
-  if (qlen == 0) {
+// The forward of a training call (train: saves what the backward needs) or of
+// an inference call (nothing saved; d.R == 0: the base without LoRA).
+static int run_forward(const kt_rawint4_moe_layer* layer, Dims d, const uint16_t* inputs, const int64_t* expert_ids,
+                       const float* route_weights, uint16_t* output, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (d.qlen == 0) {
     g_last_error.clear();
     return KT_RAWINT4_OK;
   }
@@ -324,11 +343,12 @@ int kt_rawint4_moe_fwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const ui
   if (!aligned(inputs, 16) || !aligned(output, 8) || !aligned(expert_ids, 8) || !aligned(route_weights, 4))
     return fail(KT_RAWINT4_EINVAL, "inputs must be 16-byte aligned, output and expert_ids 8-byte aligned");
   const WsMap w = plan_workspace(d);
-  rc = check_workspace(workspace, workspace_bytes, w.total);
+  const int rc = check_workspace(workspace, workspace_bytes, w.total);
   if (rc) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const LayerPtrs L = layer_ptrs(layer);
   void* ws = workspace;
+  const bool lora = d.R > 0;
 
   {
     PhaseScope ph(kPhGroup, st);
@@ -348,7 +368,7 @@ int kt_rawint4_moe_fwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const ui
     launch_rows_to_half(inputs, d.qlen, d.H, ws_ptr<uint16_t>(ws, w.xh), ws_ptr<int32_t>(ws, w.xexp), st);
   }
   const RowView xv = view_tok_bf16(inputs, d.H);
-  {
+  if (lora) {
     PhaseScope ph(kPhLoraXA, st);
     launch_lora_rowproj(d, w, ws, xv, d.H, L.ag, L.au, true, ws_ptr<float>(ws, w.ua), ws_ptr<float>(ws, w.ub),
                         2 * lora_half_width(d.R), 0, lora_half_width(d.R), ws_ptr<int32_t>(ws, w.xexp), st);
@@ -363,7 +383,7 @@ int kt_rawint4_moe_fwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const ui
                             ws_ptr<int32_t>(ws, w.offsets) + d.E, d.Ms, d.I, d.I, (int)w.h_nch, kHExp, st);
   }
   const RowView hv = view_half(ws_ptr<uint16_t>(ws, w.hh), d.I, 0, ws_ptr<int32_t>(ws, w.hexp), w.h_nch, 0, kHExp);
-  {
+  if (lora) {
     PhaseScope ph(kPhLoraHA, st);
     launch_lora_rowproj(d, w, ws, hv, d.I, L.ad, nullptr, true, ws_ptr<float>(ws, w.ud), nullptr,
                         lora_half_width(d.R), 0, 0, nullptr, st);
@@ -378,6 +398,32 @@ int kt_rawint4_moe_fwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const ui
                    st);
   }
   return launched();
+}
+
+int kt_rawint4_moe_fwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const uint16_t* inputs,
+                       const int64_t* expert_ids, const float* route_weights, uint16_t* output, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  Dims d;
+  const int rc = check_layer(layer, qlen, &d);
+  if (rc) return rc;
+  return run_forward(layer, d, inputs, expert_ids, route_weights, output, workspace, workspace_bytes, stream);
+}
+
+size_t kt_rawint4_moe_infer_workspace_bytes(const kt_rawint4_moe_layer* layer, int32_t qlen) {
+  Dims d;
+  if (check_layer(layer, qlen, &d, true) != KT_RAWINT4_OK) return 0;
+  d.train = false;
+  return plan_workspace(d).total;
+}
+
+int kt_rawint4_moe_infer(const kt_rawint4_moe_layer* layer, int32_t qlen, const uint16_t* inputs,
+                         const int64_t* expert_ids, const float* route_weights, uint16_t* output, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  Dims d;
+  const int rc = check_layer(layer, qlen, &d, true);
+  if (rc) return rc;
+  d.train = false;
+  return run_forward(layer, d, inputs, expert_ids, route_weights, output, workspace, workspace_bytes, stream);
 }
 
 int kt_rawint4_moe_bwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const uint16_t* inputs,

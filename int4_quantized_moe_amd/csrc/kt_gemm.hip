@@ -593,8 +593,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
   // times the LoRA scale and the row's exponent and is copied by DMA into the activation
   // layout (hi chunks 0..3, lo chunks 4..7); the fp32 LoRA matrix entries are
   // split into bf16 hi/lo.  For gate/up the two halves of the contraction
-  // (x A_g^T | x A_u^T) meet only their own half of the columns.
-  {
+  // (x A_g^T | x A_u^T) meet only their own half of the columns.  Rank 0 (an
+  // inference of the base alone) has no LoRA steps.
+  if (R > 0) {
     constexpr bool kTwoHalves = (KIND == kGateUp || KIND == kGateUpBwd);
     const int RP = (R + kGroup - 1) / kGroup * kGroup;  // one padded half
     const int KLP = kTwoHalves ? 2 * RP : RP;
@@ -874,9 +875,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
   // first quad-row position of the tile (the expert's tiles start at multiples of 4 rows)
   const int64_t qb = (int64_t)p.qoffsets[e] + (m0 - p.offsets[e]);
   if constexpr (KIND == kGateUp) {
-    // g, u saved in fp32, a lane's four rows of a column as one 16-byte store
+    // g, u saved in fp32 (training), a lane's four rows of a column as one 16-byte store
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
+    for (int mb = 0; mb < MB && p.gsave; ++mb) {
       const int r0 = mb * 16 + lg * 4;
       const int64_t qrow = (qb + r0) >> 2;
 #pragma unroll
@@ -1088,8 +1089,8 @@ void launch_gemm(GemmKind kind, const Dims& d, const WsMap& w, void* ws, const L
   p.counters = ws_ptr<unsigned long long>(ws, w.counters);
   p.L = L;
   p.rw = route_weights;
-  p.gsave = ws_ptr<float>(ws, w.g);
-  p.usave = ws_ptr<float>(ws, w.u);
+  p.gsave = w.saves ? ws_ptr<float>(ws, w.g) : nullptr;  // inference: nothing saved
+  p.usave = w.saves ? ws_ptr<float>(ws, w.u) : nullptr;
   p.qoffsets = ws_ptr<int32_t>(ws, w.qoffsets);
   p.hh = ws_ptr<uint16_t>(ws, w.hh);
   p.hexp = ws_ptr<int32_t>(ws, w.hexp);

@@ -98,8 +98,9 @@ inline GradGeom grad_geom(int64_t R) {
 }
 
 struct Dims {
-  int64_t E, K, H, I, R, qlen, Ms;
+  int64_t E, K, H, I, R, qlen, Ms;  // R = 0: no LoRA (inference of the base alone)
   float sc, limit;
+  bool train = true;  // false: inference forward (nothing saved for a backward)
 };
 
 struct WsMap {
@@ -123,6 +124,7 @@ struct WsMap {
   size_t gplanes, gexp, eorder, gtmax;
   size_t group_end;  // bytes needed by the grouping alone
   size_t total;
+  bool saves;  // the gate/up pre-activations are kept (g, u allocated)
   int64_t nb, mt, max_tiles, h_nch, dg_nch, dr_nt;
   int64_t gbulk, max_gtiles, st_nch;
   // LoRA side products: contraction ranges per tile and their partial sums [ksplit][Ms][2R]

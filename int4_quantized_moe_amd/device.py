@@ -25,7 +25,12 @@ def bf16_bits(t: torch.Tensor) -> np.ndarray:
 
 
 class DeviceLayer:
-    def __init__(self, cfg: LayerConfig, weights: Weights, device="cuda", lora: Optional[Dict[str, np.ndarray]] = None):
+    """One MoE layer in device memory.  ``base_only=True`` uploads no LoRA and
+    passes NULL for all six LoRA pointers: such a layer serves only the
+    inference forward of the frozen base."""
+
+    def __init__(self, cfg: LayerConfig, weights: Weights, device="cuda", lora: Optional[Dict[str, np.ndarray]] = None,
+                 base_only: bool = False):
         self.cfg = cfg
         self.device = torch.device(device)
         dev = self.device
@@ -35,8 +40,12 @@ class DeviceLayer:
         self.gate_scale = bf16_tensor(weights.gate_scale, dev)
         self.up_scale = bf16_tensor(weights.up_scale, dev)
         self.down_scale = bf16_tensor(weights.down_scale, dev)
-        src = weights.lora if lora is None else lora
-        self.lora = {n: torch.from_numpy(np.ascontiguousarray(src[n], dtype=np.float32)).to(dev) for n in LORA_NAMES}
+        if base_only:
+            self.lora = {n: None for n in LORA_NAMES}
+        else:
+            src = weights.lora if lora is None else lora
+            self.lora = {n: torch.from_numpy(np.ascontiguousarray(src[n], dtype=np.float32)).to(dev)
+                         for n in LORA_NAMES}
         self.layer = _lib.make_layer(cfg.num_experts, cfg.top_k, cfg.hidden, cfg.intermediate, cfg.rank, cfg.alpha,
                                      cfg.swiglu_limit, self.gate_packed, self.up_packed, self.down_packed,
                                      self.gate_scale, self.up_scale, self.down_scale,
@@ -44,6 +53,10 @@ class DeviceLayer:
 
     def workspace(self, qlen: int) -> torch.Tensor:
         n = _lib.kt_rawint4_moe_workspace_bytes(self.layer, qlen)
+        return torch.empty(n, dtype=torch.uint8, device=self.device)
+
+    def infer_workspace(self, qlen: int) -> torch.Tensor:
+        n = _lib.kt_rawint4_moe_infer_workspace_bytes(self.layer, qlen)
         return torch.empty(n, dtype=torch.uint8, device=self.device)
 
     def grad_buffers(self, fill: Optional[float] = None) -> Dict[str, torch.Tensor]:
@@ -57,6 +70,14 @@ class DeviceLayer:
         if output is None:
             output = torch.empty((qlen, self.cfg.hidden), dtype=torch.bfloat16, device=self.device)
         _lib.kt_rawint4_moe_fwd(self.layer, qlen, inputs, expert_ids, route_weights, output, workspace, stream)
+        return output
+
+    def infer(self, inputs, expert_ids, route_weights, workspace, output=None, stream=None) -> torch.Tensor:
+        """Forward that keeps nothing for a backward (the output equals forward()'s)."""
+        qlen = inputs.shape[0]
+        if output is None:
+            output = torch.empty((qlen, self.cfg.hidden), dtype=torch.bfloat16, device=self.device)
+        _lib.kt_rawint4_moe_infer(self.layer, qlen, inputs, expert_ids, route_weights, output, workspace, stream)
         return output
 
     def backward(self, inputs, expert_ids, route_weights, grad_output, workspace, grads, accumulate=False,

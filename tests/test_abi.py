@@ -23,7 +23,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(_lib.LIBRARY_PATH)
     names = _declared()
-    assert len(names) == 14
+    assert len(names) == 16
     for name in names:
         assert hasattr(lib, name), name
 
@@ -128,3 +128,25 @@ def test_hook_argument_checks():
     need = kt.kt_rawint4_group_workspace_bytes(4, 2, 8)
     assert lib.kt_rawint4_group(FAKE, 4, 2, 8, FAKE, FAKE, FAKE, need - 1, None) == kt.KT_RAWINT4_EWORKSPACE
     assert lib.kt_rawint4_moe_diagnostics(None, 0, None, None, None) == kt.KT_RAWINT4_EINVAL
+
+
+def test_inference_workspace_and_base_only_layer():
+    layer = _layer()
+    train = kt.kt_rawint4_moe_workspace_bytes(layer, 500)
+    infer = kt.kt_rawint4_moe_infer_workspace_bytes(layer, 500)
+    assert 0 < infer < train and infer % 256 == 0
+    base = _layer(**{n: None for n in ("a0", "a1", "a2", "a3", "a4", "a5")}, rank=0, alpha=float("nan"))
+    # all six LoRA pointers NULL: only the inference forward accepts it, and rank/alpha are not used
+    assert 0 < kt.kt_rawint4_moe_infer_workspace_bytes(base, 500) < infer
+    with pytest.raises(kt.KtRawInt4Error, match="rank"):
+        kt.kt_rawint4_moe_workspace_bytes(base, 500)
+    partial = _layer(a3=None)
+    with pytest.raises(kt.KtRawInt4Error, match="NULL"):
+        kt.kt_rawint4_moe_infer_workspace_bytes(partial, 500)
+    lib = _lib.load_library()
+    need = kt.kt_rawint4_moe_infer_workspace_bytes(base, 4)
+    assert lib.kt_rawint4_moe_infer(ctypes.byref(base), 4, FAKE, FAKE, FAKE, FAKE, FAKE, need - 256, None) == \
+        kt.KT_RAWINT4_EWORKSPACE
+    assert lib.kt_rawint4_moe_infer(ctypes.byref(base), 4, None, FAKE, FAKE, FAKE, FAKE, need, None) == \
+        kt.KT_RAWINT4_EINVAL
+    assert lib.kt_rawint4_moe_infer(ctypes.byref(base), 0, None, None, None, None, None, 0, None) == kt.KT_RAWINT4_OK
