@@ -8,7 +8,9 @@ synthetic batch already resident in HBM.  Prints ONE JSON line on stdout;
 progress goes to stderr.
 
 ``--infer lora|base`` times the inference forward instead (kt_rawint4_moe_infer:
-with the LoRA, or the frozen base alone); the default line is the training step.
+with the LoRA, or the frozen base alone); ``--recompute`` times the training step
+in its checkpointed form (an inference forward that keeps nothing, then
+kt_rawint4_moe_bwd_recompute).  The default line is the training step.
 
 Default workload: 384 experts, top-8, hidden 7168, intermediate 2048, LoRA rank 64
 (alpha 128), 16384 tokens, SwiGLU clamp 7, uniform routing.  ``--config`` picks
@@ -108,6 +110,8 @@ def main():
     ap.add_argument("--infer", choices=("lora", "base"), default=None,
                     help="time the inference forward (with the LoRA, or the frozen base alone) instead of the "
                          "training step")
+    ap.add_argument("--recompute", action="store_true",
+                    help="training step with an inference forward and the checkpoint-recompute backward")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after timing, run one plain elementwise copy (torch.neg, fp32) of this many MiB: "
                          "the calibration kernel for hardware byte counters")
@@ -136,6 +140,9 @@ def main():
     db = device.DeviceBatch(batch, "cuda:0")
     out = torch.empty((db.qlen, cfg.hidden), dtype=torch.bfloat16, device="cuda:0")
     stream = torch.cuda.current_stream()
+    if args.infer and args.recompute:
+        print("--infer and --recompute exclude each other", file=sys.stderr)
+        sys.exit(2)
     if args.infer:
         ws = dl.infer_workspace(db.qlen)
 
@@ -147,10 +154,15 @@ def main():
         dx = torch.empty_like(out)
         droute = torch.empty((db.qlen, cfg.top_k), dtype=torch.float32, device="cuda:0")
 
+        ws_fwd = dl.infer_workspace(db.qlen) if args.recompute else ws
+
         def step():
-            dl.forward(db.inputs, db.expert_ids, db.route_weights, ws, output=out, stream=stream)
+            if args.recompute:
+                dl.infer(db.inputs, db.expert_ids, db.route_weights, ws_fwd, output=out, stream=stream)
+            else:
+                dl.forward(db.inputs, db.expert_ids, db.route_weights, ws, output=out, stream=stream)
             dl.backward(db.inputs, db.expert_ids, db.route_weights, db.grad_output, ws, grads, accumulate=False,
-                        grad_scale=1.0, grad_input=dx, grad_route=droute, stream=stream)
+                        grad_scale=1.0, grad_input=dx, grad_route=droute, stream=stream, recompute=args.recompute)
     log(f"workspace {ws.numel() / 2**30:.2f} GiB")
 
     log(f"warmup {args.warmup} steps")
@@ -199,7 +211,7 @@ def main():
     # (profiles/hbm_traffic_<phase>_<workload>.txt), only while it was taken from these sources
     from int4_quantized_moe_amd import profsum
 
-    mode = f"_infer_{args.infer}" if args.infer else ""
+    mode = f"_infer_{args.infer}" if args.infer else ("_recompute" if args.recompute else "")
     measured = profsum.read_traffic(os.path.join(ROOT, "profiles", f"hbm_traffic_{dom}_{cfg.name}{mode}.txt"))
     traffic = None if measured is None else int(round(measured["read"] + measured["write"]))
     roof.update({"kernel": dom, "achieved": round(achieved, 2), "peak": peak, "frac": round(achieved / peak, 4),
@@ -247,7 +259,9 @@ def main():
                    "intermediate": cfg.intermediate, "rank": cfg.rank, "alpha": cfg.alpha, "qlen": cfg.qlen,
                    "swiglu_limit": cfg.swiglu_limit, "routing": cfg.routing, "active_experts": active,
                    **({"mode": f"inference ({'LoRA' if args.infer == 'lora' else 'frozen base alone'})"}
-                      if args.infer else {})},
+                      if args.infer else {}),
+                   **({"mode": "checkpoint recompute (inference forward + recompute backward)"}
+                      if args.recompute else {})},
         "mfma_frac_step": round(total_flops / (ms_per_step / 1e3) / PEAK_MFMA_FP16, 4),
         "hbm_frac_step": round(total_wbytes / (ms_per_step / 1e3) / PEAK_HBM, 4),
         "phase_ms_per_step": per_step,

@@ -142,7 +142,9 @@ int kt_rawint4_moe_infer(const kt_rawint4_moe_layer* layer, int32_t qlen, const 
  * Backward of the same call (page "rawint4_sft_reference.py",
  * run_routed_reference: autograd with grad_output as the cotangent).  Must use
  * the workspace of the latest forward with the same layer, qlen, inputs,
- * expert_ids and route_weights.
+ * expert_ids and route_weights: a second forward into a workspace replaces
+ * what the first saved (the one pending cache of the page
+ * "test_rawint4_sft_numerical.py", cache-replacement check).
  *   grad_input [qlen, H] bf16: dL/dinputs (round to nearest even);
  *   grad_route [qlen, k] fp32 or NULL: dL/droute_weights (0 for dropped slots);
  *   d_gate_a .. d_down_b: the six LoRA gradient buffers, fp32, shapes as the
@@ -163,6 +165,28 @@ int kt_rawint4_moe_bwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const ui
                        uint16_t* grad_input, float* grad_route, float* d_gate_a, float* d_gate_b, float* d_up_a,
                        float* d_up_b, float* d_down_a, float* d_down_b, int32_t accumulate, float grad_scale,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward that needs no saved forward: the checkpoint-recompute form (page
+ * "test_rawint4_sft_numerical.py", the cache-replacement check, where a second
+ * saved forward before the backward stands for the recompute of an activation
+ * checkpoint; page "ext_bindings.cpp" commit log, the checkpoint forward reuse
+ * for LoRA).  It first reruns, into the workspace, the forward kernels whose
+ * results the backward reads (grouping, transposed scales, LoRA side products,
+ * the gate/up GEMM with its saved pre-activations, the rows of h) -- every
+ * kernel but the down GEMM and the output combine -- then runs
+ * kt_rawint4_moe_bwd.  All kernels are deterministic, so the results equal
+ * those of kt_rawint4_moe_fwd followed by kt_rawint4_moe_bwd bit for bit.
+ * The workspace (kt_rawint4_moe_workspace_bytes) may hold anything on entry:
+ * a caller that keeps no activations runs the forward with kt_rawint4_moe_infer
+ * and lends a training-size workspace to the backward alone.  Arguments,
+ * window rule and errors as for kt_rawint4_moe_bwd.
+ */
+int kt_rawint4_moe_bwd_recompute(const kt_rawint4_moe_layer* layer, int32_t qlen, const uint16_t* inputs,
+                                 const int64_t* expert_ids, const float* route_weights, const uint16_t* grad_output,
+                                 uint16_t* grad_input, float* grad_route, float* d_gate_a, float* d_gate_b,
+                                 float* d_up_a, float* d_up_b, float* d_down_a, float* d_down_b, int32_t accumulate,
+                                 float grad_scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Test hook, the codec of page "rawint4_sft_reference.py" (unpack_rawint4):

@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     kt_rawint4_group_workspace_bytes,
     kt_rawint4_last_error,
     kt_rawint4_moe_bwd,
+    kt_rawint4_moe_bwd_recompute,
     kt_rawint4_moe_diagnostics,
     kt_rawint4_moe_fwd,
     kt_rawint4_moe_infer,

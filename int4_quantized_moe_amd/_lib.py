@@ -72,6 +72,8 @@ def load_library() -> ctypes.CDLL:
         "kt_rawint4_moe_infer_workspace_bytes": (sz, [lp, i32]),
         "kt_rawint4_moe_infer": (ctypes.c_int, [lp, i32, _vp, _vp, _vp, _vp, _vp, sz, _vp]),
         "kt_rawint4_moe_bwd": (ctypes.c_int, [lp, i32, _vp, _vp, _vp, _vp, _vp, _vp] + [_vp] * 6 + [i32, f32, _vp, sz, _vp]),
+        "kt_rawint4_moe_bwd_recompute": (ctypes.c_int,
+                                         [lp, i32, _vp, _vp, _vp, _vp, _vp, _vp] + [_vp] * 6 + [i32, f32, _vp, sz, _vp]),
         "kt_rawint4_unpack": (ctypes.c_int, [_vp, i64, i64, _vp, _vp]),
         "kt_rawint4_dequant": (ctypes.c_int, [_vp, _vp, i64, i64, _vp, _vp]),
         "kt_rawint4_group_workspace_bytes": (sz, [i32, i32, i32]),
@@ -162,6 +164,16 @@ def kt_rawint4_moe_bwd(layer, qlen, inputs, expert_ids, route_weights, grad_outp
                        d_gate_b, d_up_a, d_up_b, d_down_a, d_down_b, accumulate, grad_scale, workspace,
                        stream=None) -> None:
     _check(load_library().kt_rawint4_moe_bwd(
+        ctypes.byref(layer), int(qlen), _ptr(inputs), _ptr(expert_ids), _ptr(route_weights), _ptr(grad_output),
+        _ptr(grad_input), _ptr(grad_route), _ptr(d_gate_a), _ptr(d_gate_b), _ptr(d_up_a), _ptr(d_up_b),
+        _ptr(d_down_a), _ptr(d_down_b), int(bool(accumulate)), float(grad_scale), _ptr(workspace),
+        _nbytes(workspace) if workspace is not None else 0, _stream(stream)))
+
+
+def kt_rawint4_moe_bwd_recompute(layer, qlen, inputs, expert_ids, route_weights, grad_output, grad_input, grad_route,
+                                 d_gate_a, d_gate_b, d_up_a, d_up_b, d_down_a, d_down_b, accumulate, grad_scale,
+                                 workspace, stream=None) -> None:
+    _check(load_library().kt_rawint4_moe_bwd_recompute(
         ctypes.byref(layer), int(qlen), _ptr(inputs), _ptr(expert_ids), _ptr(route_weights), _ptr(grad_output),
         _ptr(grad_input), _ptr(grad_route), _ptr(d_gate_a), _ptr(d_gate_b), _ptr(d_up_a), _ptr(d_up_b),
         _ptr(d_down_a), _ptr(d_down_b), int(bool(accumulate)), float(grad_scale), _ptr(workspace),

@@ -329,27 +329,14 @@ size_t kt_rawint4_moe_workspace_bytes(const kt_rawint4_moe_layer* layer, int32_t
   return plan_workspace(d).total;
 }
 
-// The forward of a training call (train: saves what the backward needs) or of
-// an inference call (nothing saved; d.R == 0: the base without LoRA).
-static int run_forward(const kt_rawint4_moe_layer* layer, Dims d, const uint16_t* inputs, const int64_t* expert_ids,
-                       const float* route_weights, uint16_t* output, void* workspace, size_t workspace_bytes,
-                       void* stream) {
-  if (d.qlen == 0) {
-    g_last_error.clear();
-    return KT_RAWINT4_OK;
-  }
-  if (!inputs || !expert_ids || !route_weights || !output)
-    return fail(KT_RAWINT4_EINVAL, "inputs, expert_ids, route_weights and output must be non-NULL");
-  if (!aligned(inputs, 16) || !aligned(output, 8) || !aligned(expert_ids, 8) || !aligned(route_weights, 4))
-    return fail(KT_RAWINT4_EINVAL, "inputs must be 16-byte aligned, output and expert_ids 8-byte aligned");
-  const WsMap w = plan_workspace(d);
-  const int rc = check_workspace(workspace, workspace_bytes, w.total);
-  if (rc) return rc;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const LayerPtrs L = layer_ptrs(layer);
-  void* ws = workspace;
+// The forward's kernels up to what a backward reads: grouping, transposed
+// scales, fp16 rows of x, the side products x A_g^T | x A_u^T, the gate/up GEMM
+// with SwiGLU (saving the pre-activations when d.train), the rows of h and
+// h A_d^T.  Without LoRA (d.R == 0) no side product runs.
+static void launch_forward_front(const kt_rawint4_moe_layer* layer, const Dims& d, const WsMap& w, void* ws,
+                                 const LayerPtrs& L, const uint16_t* inputs, const int64_t* expert_ids,
+                                 const float* route_weights, hipStream_t st) {
   const bool lora = d.R > 0;
-
   {
     PhaseScope ph(kPhGroup, st);
     launch_init_counters(ws, w, st);
@@ -388,6 +375,28 @@ static int run_forward(const kt_rawint4_moe_layer* layer, Dims d, const uint16_t
     launch_lora_rowproj(d, w, ws, hv, d.I, L.ad, nullptr, true, ws_ptr<float>(ws, w.ud), nullptr,
                         lora_half_width(d.R), 0, 0, nullptr, st);
   }
+}
+
+// The forward of a training call (train: saves what the backward needs) or of
+// an inference call (nothing saved; d.R == 0: the base without LoRA).
+static int run_forward(const kt_rawint4_moe_layer* layer, Dims d, const uint16_t* inputs, const int64_t* expert_ids,
+                       const float* route_weights, uint16_t* output, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (d.qlen == 0) {
+    g_last_error.clear();
+    return KT_RAWINT4_OK;
+  }
+  if (!inputs || !expert_ids || !route_weights || !output)
+    return fail(KT_RAWINT4_EINVAL, "inputs, expert_ids, route_weights and output must be non-NULL");
+  if (!aligned(inputs, 16) || !aligned(output, 8) || !aligned(expert_ids, 8) || !aligned(route_weights, 4))
+    return fail(KT_RAWINT4_EINVAL, "inputs must be 16-byte aligned, output and expert_ids 8-byte aligned");
+  const WsMap w = plan_workspace(d);
+  const int rc = check_workspace(workspace, workspace_bytes, w.total);
+  if (rc) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const LayerPtrs L = layer_ptrs(layer);
+  void* ws = workspace;
+  launch_forward_front(layer, d, w, ws, L, inputs, expert_ids, route_weights, st);
   {
     PhaseScope ph(kPhGemmDown, st);
     launch_gemm(kDown, d, w, ws, L, route_weights, st);
@@ -426,11 +435,13 @@ int kt_rawint4_moe_infer(const kt_rawint4_moe_layer* layer, int32_t qlen, const 
   return run_forward(layer, d, inputs, expert_ids, route_weights, output, workspace, workspace_bytes, stream);
 }
 
-int kt_rawint4_moe_bwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const uint16_t* inputs,
-                       const int64_t* expert_ids, const float* route_weights, const uint16_t* grad_output,
-                       uint16_t* grad_input, float* grad_route, float* d_gate_a, float* d_gate_b, float* d_up_a,
-                       float* d_up_b, float* d_down_a, float* d_down_b, int32_t accumulate, float grad_scale,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+// The backward; recompute: first rerun the forward's front into the workspace
+// (the checkpoint-recompute form, no saved forward needed).
+static int run_backward(const kt_rawint4_moe_layer* layer, int32_t qlen, const uint16_t* inputs,
+                        const int64_t* expert_ids, const float* route_weights, const uint16_t* grad_output,
+                        uint16_t* grad_input, float* grad_route, float* d_gate_a, float* d_gate_b, float* d_up_a,
+                        float* d_up_b, float* d_down_a, float* d_down_b, int32_t accumulate, float grad_scale,
+                        void* workspace, size_t workspace_bytes, void* stream, bool recompute) {
   Dims d;
   int rc = check_layer(layer, qlen, &d);
   if (rc) return rc;
@@ -458,6 +469,7 @@ int kt_rawint4_moe_bwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const ui
   if (rc) return rc;
   const LayerPtrs L = layer_ptrs(layer);
   void* ws = workspace;
+  if (recompute) launch_forward_front(layer, d, w, ws, L, inputs, expert_ids, route_weights, st);
 
   {
     PhaseScope ph(kPhDyHalf, st);
@@ -506,6 +518,26 @@ int kt_rawint4_moe_bwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const ui
   LoraGradOut go{d_gate_a, d_gate_b, d_up_a, d_up_b, d_down_a, d_down_b};
   launch_lora_grads(d, w, ws, inputs, grad_output, route_weights, go, accumulate, grad_scale * d.sc, st);
   return launched();
+}
+
+int kt_rawint4_moe_bwd(const kt_rawint4_moe_layer* layer, int32_t qlen, const uint16_t* inputs,
+                       const int64_t* expert_ids, const float* route_weights, const uint16_t* grad_output,
+                       uint16_t* grad_input, float* grad_route, float* d_gate_a, float* d_gate_b, float* d_up_a,
+                       float* d_up_b, float* d_down_a, float* d_down_b, int32_t accumulate, float grad_scale,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return run_backward(layer, qlen, inputs, expert_ids, route_weights, grad_output, grad_input, grad_route, d_gate_a,
+                      d_gate_b, d_up_a, d_up_b, d_down_a, d_down_b, accumulate, grad_scale, workspace,
+                      workspace_bytes, stream, false);
+}
+
+int kt_rawint4_moe_bwd_recompute(const kt_rawint4_moe_layer* layer, int32_t qlen, const uint16_t* inputs,
+                                 const int64_t* expert_ids, const float* route_weights, const uint16_t* grad_output,
+                                 uint16_t* grad_input, float* grad_route, float* d_gate_a, float* d_gate_b,
+                                 float* d_up_a, float* d_up_b, float* d_down_a, float* d_down_b, int32_t accumulate,
+                                 float grad_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_backward(layer, qlen, inputs, expert_ids, route_weights, grad_output, grad_input, grad_route, d_gate_a,
+                      d_gate_b, d_up_a, d_up_b, d_down_a, d_down_b, accumulate, grad_scale, workspace,
+                      workspace_bytes, stream, true);
 }
 
 int kt_rawint4_unpack(const uint8_t* packed, int64_t n, int64_t k, int8_t* codes, void* stream) {

@@ -81,13 +81,14 @@ class DeviceLayer:
         return output
 
     def backward(self, inputs, expert_ids, route_weights, grad_output, workspace, grads, accumulate=False,
-                 grad_scale=1.0, grad_input=None, grad_route=None, stream=None):
+                 grad_scale=1.0, grad_input=None, grad_route=None, stream=None, recompute=False):
+        """recompute=True: the workspace need not hold this call's forward (it is rerun first)."""
         qlen = inputs.shape[0]
         if grad_input is None:
             grad_input = torch.empty((qlen, self.cfg.hidden), dtype=torch.bfloat16, device=self.device)
-        _lib.kt_rawint4_moe_bwd(self.layer, qlen, inputs, expert_ids, route_weights, grad_output, grad_input,
-                                grad_route, *(grads[n] for n in LORA_NAMES), accumulate, grad_scale, workspace,
-                                stream)
+        fn = _lib.kt_rawint4_moe_bwd_recompute if recompute else _lib.kt_rawint4_moe_bwd
+        fn(self.layer, qlen, inputs, expert_ids, route_weights, grad_output, grad_input, grad_route,
+           *(grads[n] for n in LORA_NAMES), accumulate, grad_scale, workspace, stream)
         return grad_input, grad_route
 
     def saved_preactivations(self, qlen, workspace, stream=None):

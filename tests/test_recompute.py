@@ -1,0 +1,159 @@
+"""GPU: the one pending cache and the checkpoint-recompute backward.
+
+* Cache replacement (page "test_rawint4_sft_numerical.py", the cache-replacement
+  check): forward(first), forward(second), backward(second), forward(first),
+  backward(first, accumulate).  A second forward into the workspace replaces
+  the first one's saved state, so each backward matches its own batch; the
+  gradient buffers hold grad_scale times the sum of both batches' gradients.
+  Checked against the oracle at the training bars (the pages use 0.03 / 0.995).
+* kt_rawint4_moe_bwd_recompute from a workspace that holds no forward (filled
+  with 0xFF bytes, which read as NaN in fp32), after an inference forward:
+  grad_input, grad_route and the six LoRA gradients equal those of forward +
+  backward bit for bit -- on the small workloads and on both full-size ones.
+
+Each case prints its name first.
+"""
+
+import numpy as np
+import pytest
+
+import oracle as O
+from int4_quantized_moe_amd import workloads as W
+from tests.clamp_sides import reference
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 5e-3
+COSINE = 0.9999
+DROUTE_REL_L2 = 3e-2
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from int4_quantized_moe_amd import device
+
+    return device
+
+
+def _say(*a):
+    print("[recompute]", *a, flush=True)
+
+
+def _close(name, actual, expected, rel=REL_L2, cos=COSINE):
+    a = np.asarray(actual, dtype=np.float64)
+    e = np.asarray(expected, dtype=np.float64)
+    assert np.isfinite(a).all(), f"{name}: non-finite values"
+    assert np.count_nonzero(e), f"{name}: reference has no signal"
+    r, c = O.relative_l2_and_cosine(a, e)
+    _say(f"{name}: rel_l2={r:.3e} cos={c:.7f}")
+    assert r <= rel and c >= cos, f"{name}: rel_l2 {r:.3e} cos {c:.7f}"
+
+
+def test_second_forward_replaces_the_pending_cache(dev):
+    cfg, weights, _ = W.make_workload(1)
+    _say("cache replacement", cfg.name)
+    first = W.make_batch(cfg, 5001)
+    second = W.make_batch(cfg, 5002)
+    dl = dev.DeviceLayer(cfg, weights)
+    grads = dl.grad_buffers(fill=3.0)
+    d1, d2 = dev.DeviceBatch(first), dev.DeviceBatch(second)
+    ws = dl.workspace(d1.qlen)
+    gs = 0.25
+    dl.forward(d1.inputs, d1.expert_ids, d1.route_weights, ws)
+    dl.forward(d2.inputs, d2.expert_ids, d2.route_weights, ws)
+    side2 = dl.saved_preactivations(d2.qlen, ws)
+    dr2 = torch.empty(second.expert_ids.shape, dtype=torch.float32, device="cuda")
+    dx2, _ = dl.backward(d2.inputs, d2.expert_ids, d2.route_weights, d2.grad_output, ws, grads, accumulate=False,
+                         grad_scale=gs, grad_route=dr2)
+    dl.forward(d1.inputs, d1.expert_ids, d1.route_weights, ws)
+    side1 = dl.saved_preactivations(d1.qlen, ws)
+    dr1 = torch.empty(first.expert_ids.shape, dtype=torch.float32, device="cuda")
+    dx1, _ = dl.backward(d1.inputs, d1.expert_ids, d1.route_weights, d1.grad_output, ws, grads, accumulate=True,
+                         grad_scale=gs, grad_route=dr1)
+    torch.cuda.synchronize()
+    sides = {}
+    for tag, b, side in (("first", first, side1), ("second", second, side2)):
+        sides[tag] = reference(cfg, weights, b.inputs, b.expert_ids, b.route_weights, b.grad_output,
+                               tuple(t.cpu().numpy() for t in side), _say)
+    failures = []
+    for tag, dx, dr in (("second", dx2, dr2), ("first", dx1, dr1)):
+        for name, a, e, rel, cos in ((f"{tag}.dX", dx.float().cpu().numpy(), sides[tag]["dx"], REL_L2, COSINE),
+                                     (f"{tag}.dRoute", dr.cpu().numpy(), sides[tag]["droute"], DROUTE_REL_L2, 0.995)):
+            try:
+                _close(name, a, e, rel, cos)
+            except AssertionError as err:
+                failures.append(str(err))
+    for n, g in grads.items():
+        want = gs * (sides["second"]["grads"][n] + sides["first"]["grads"][n])
+        try:
+            _close(f"window.{n}", g.cpu().numpy(), want)
+        except AssertionError as err:
+            failures.append(str(err))
+    assert not failures, "; ".join(failures)
+
+
+def _bits(t):
+    return t.detach().contiguous().view(torch.int32 if t.dtype == torch.float32 else torch.int16).cpu().numpy()
+
+
+def _recompute_equals(dev, cfg, weights, batch):
+    dl = dev.DeviceLayer(cfg, weights)
+    db = dev.DeviceBatch(batch)
+    ws = dl.workspace(db.qlen)
+    out = dl.forward(db.inputs, db.expert_ids, db.route_weights, ws)
+    g_ref = dl.grad_buffers(fill=1.5)
+    dr_ref = torch.empty(batch.expert_ids.shape, dtype=torch.float32, device="cuda")
+    dx_ref, _ = dl.backward(db.inputs, db.expert_ids, db.route_weights, db.grad_output, ws, g_ref, accumulate=True,
+                            grad_scale=0.5, grad_route=dr_ref)
+    del ws
+    # the checkpointed form: an inference forward keeps nothing, the backward reruns what it reads
+    out_inf = dl.infer(db.inputs, db.expert_ids, db.route_weights, dl.infer_workspace(db.qlen))
+    ws2 = torch.full((dl.workspace(db.qlen).numel(),), 0xFF, dtype=torch.uint8, device="cuda")
+    g = dl.grad_buffers(fill=1.5)
+    dr = torch.empty(batch.expert_ids.shape, dtype=torch.float32, device="cuda")
+    dx, _ = dl.backward(db.inputs, db.expert_ids, db.route_weights, db.grad_output, ws2, g, accumulate=True,
+                        grad_scale=0.5, grad_route=dr, recompute=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(out_inf), _bits(out)), "inference output differs"
+    for name, a, b in [("dX", dx, dx_ref), ("dRoute", dr, dr_ref)] + [(n, g[n], g_ref[n]) for n in g]:
+        x, y = _bits(a), _bits(b)
+        assert np.array_equal(x, y), f"{cfg.name}.{name}: {np.count_nonzero(x != y)} elements differ"
+    _say(f"{cfg.name}: recompute backward bit-equal ({db.qlen} tokens)")
+
+
+@pytest.mark.parametrize("index", [0, 1])
+def test_recompute_backward_bit_equal(dev, index):
+    cfg, weights, batch = W.make_workload(index)
+    _say("recompute", cfg.name)
+    _recompute_equals(dev, cfg, weights, batch)
+
+
+@pytest.mark.parametrize("index", [3, 4])
+def test_recompute_backward_bit_equal_full_size(dev, index):
+    cfg = W.CONFIGS[index]
+    _say(f"recompute {cfg.name}: generating")
+    cfg, weights, batch = W.make_workload(index)
+    _recompute_equals(dev, cfg, weights, batch)
+
+
+def test_recompute_empty_call(dev):
+    cfg, weights, _ = W.make_workload(0)
+    _say("recompute, empty call")
+    dl = dev.DeviceLayer(cfg, weights)
+    g = dl.grad_buffers(fill=2.0)
+    empty_x = torch.empty((0, cfg.hidden), dtype=torch.bfloat16, device="cuda")
+    empty_ids = torch.empty((0, cfg.top_k), dtype=torch.int64, device="cuda")
+    empty_rw = torch.empty((0, cfg.top_k), dtype=torch.float32, device="cuda")
+    ws = dl.workspace(1)
+    dl.backward(empty_x, empty_ids, empty_rw, empty_x, ws, g, accumulate=True, grad_scale=1.0, grad_input=empty_x,
+                recompute=True)
+    torch.cuda.synchronize()
+    assert all(bool((t == 2.0).all()) for t in g.values())
+    dl.backward(empty_x, empty_ids, empty_rw, empty_x, ws, g, accumulate=False, grad_scale=1.0, grad_input=empty_x,
+                recompute=True)
+    torch.cuda.synchronize()
+    assert all(int(torch.count_nonzero(t)) == 0 for t in g.values())
