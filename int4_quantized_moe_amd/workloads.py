@@ -10,6 +10,10 @@ Distributions follow the contract test of the pages ("test_rawint4_sft_numerical
 * packed codes: uniform random bytes, i.e. two independent uniform nibbles,
   low nibble first;
 * group scales: fp32 uniform in [0.01, 0.07), rounded to bf16 (round to nearest even);
+* MXFP4 weights (``weight_format="mxfp4"``): the same uniform bytes read as E2M1
+  nibbles, and UE8M0 scale exponents uniform in [121, 124] (2^-6 .. 2^-3, so
+  that the weights' magnitudes match the RAWINT4 recipe's), handed over as bf16
+  by the loader's bit-cast ``e << 7``;
 * activations and output gradients: N(0, 1) times a per-config std, rounded to bf16;
 * LoRA A and B: fp32 N(0, 0.02);
 * routing: ``top_k`` distinct experts per token, uniform or Zipf(s) over a seeded
@@ -44,6 +48,7 @@ class LayerConfig:
     qlen: int
     swiglu_limit: float
     routing: str = "uniform"  # "uniform" or "zipf"
+    weight_format: str = "rawint4"  # "rawint4" or "mxfp4"
     zipf_s: float = 1.1
     x_std: float = 1.0
     dy_std: float = 1.0
@@ -137,17 +142,29 @@ def _scales(rng: np.random.Generator, shape) -> np.ndarray:
     return f32_to_bf16_bits(rng.uniform(0.01, 0.07, size=shape).astype(np.float32))
 
 
+def ue8m0_to_bf16_bits(exponents: np.ndarray) -> np.ndarray:
+    """UE8M0 scale bytes to bf16 bit patterns by the loaders' bit-cast (e << 7)."""
+    return (np.asarray(exponents, dtype=np.uint16) << 7).astype(np.uint16)
+
+
+def _ue8m0_scales(rng: np.random.Generator, shape) -> np.ndarray:
+    return ue8m0_to_bf16_bits(rng.integers(121, 125, size=shape))
+
+
 def make_weights(cfg: LayerConfig, seed: int) -> Weights:
     """Draw the layer's packed codes, bf16 scales and fp32 LoRA tensors."""
     rs = _streams(seed, 12)
     e, h, i = cfg.num_experts, cfg.hidden, cfg.intermediate
+    if cfg.weight_format not in ("rawint4", "mxfp4"):
+        raise ValueError(f"unknown weight format {cfg.weight_format!r}")
+    scales = _ue8m0_scales if cfg.weight_format == "mxfp4" else _scales
     w = Weights(
         gate_packed=_codes(rs[0], (e, i, h // 2)),
         up_packed=_codes(rs[1], (e, i, h // 2)),
         down_packed=_codes(rs[2], (e, h, i // 2)),
-        gate_scale=_scales(rs[3], (e, i, h // 32)),
-        up_scale=_scales(rs[4], (e, i, h // 32)),
-        down_scale=_scales(rs[5], (e, h, i // 32)),
+        gate_scale=scales(rs[3], (e, i, h // 32)),
+        up_scale=scales(rs[4], (e, i, h // 32)),
+        down_scale=scales(rs[5], (e, h, i // 32)),
     )
     for j, (name, shape) in enumerate(cfg.lora_shapes().items()):
         w.lora[name] = rs[6 + j].normal(0.0, 0.02, size=shape).astype(np.float32)

@@ -31,6 +31,10 @@ _lib = None
 
 LORA_NAMES = ("gate_lora_a", "gate_lora_b", "up_lora_a", "up_lora_b", "down_lora_a", "down_lora_b")
 
+# weight formats: signed group-32 RAWINT4, or MXFP4 (E2M1 nibbles, power-of-two
+# UE8M0 group scales handed over as bf16)
+FORMATS = {"rawint4": 0, "mxfp4": 1}
+
 _u8p = ctypes.POINTER(ctypes.c_uint8)
 _i8p = ctypes.POINTER(ctypes.c_int8)
 _u16p = ctypes.POINTER(ctypes.c_uint16)
@@ -48,6 +52,7 @@ class OrcLayer(ctypes.Structure):
         ("intermediate", ctypes.c_int32),
         ("rank", ctypes.c_int32),
         ("fp32_intermediates", ctypes.c_int32),
+        ("weight_format", ctypes.c_int32),
         ("alpha", ctypes.c_double),
         ("swiglu_limit", ctypes.c_double),
         ("gate_packed", _u8p),
@@ -82,8 +87,14 @@ def _load():
     lib.orc_validate_layout.restype = ctypes.c_int
     lib.orc_dequant.argtypes = [_u8p, _u16p, ctypes.c_int64, ctypes.c_int64, _f32p]
     lib.orc_dequant.restype = ctypes.c_int
+    lib.orc_dequant_format.argtypes = [_u8p, _u16p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, _f32p]
+    lib.orc_dequant_format.restype = ctypes.c_int
+    lib.orc_e2m1_table.argtypes = [_f64p]
     lib.orc_transpose_free_dx.argtypes = [_f64p, ctypes.c_int64, _u8p, _u16p, ctypes.c_int64, ctypes.c_int64, _f64p]
     lib.orc_transpose_free_dx.restype = ctypes.c_int
+    lib.orc_transpose_free_dx_format.argtypes = [_f64p, ctypes.c_int64, _u8p, _u16p, ctypes.c_int64,
+                                                 ctypes.c_int64, ctypes.c_int32, _f64p]
+    lib.orc_transpose_free_dx_format.restype = ctypes.c_int
     lib.orc_group.argtypes = [_i64p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _i32p, _i32p, _i32p, _i64p]
     lib.orc_group.restype = ctypes.c_int
     lib.orc_moe.argtypes = [ctypes.POINTER(OrcLayer), ctypes.c_int64, _f64p, _i64p, _f64p, _f64p, _f64p, _f64p,
@@ -146,22 +157,32 @@ def validate_layout(packed: np.ndarray, scales: np.ndarray, group_size: int = 32
     return packed.shape[0], packed.shape[1] * 2
 
 
-def dequant(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
-    n, k = validate_layout(packed, scales)
-    out = np.empty((n, k), dtype=np.float32)
-    _load().orc_dequant(_ptr(np.ascontiguousarray(packed), _u8p), _ptr(np.ascontiguousarray(scales), _u16p), n, k,
-                        _ptr(out, _f32p))
+def e2m1_table() -> np.ndarray:
+    """Value of each E2M1 nibble 0..15 (unscaled)."""
+    out = np.empty(16)
+    _load().orc_e2m1_table(_ptr(out, _f64p))
     return out
 
 
-def transpose_free_dx(dy: np.ndarray, packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
+def dequant(packed: np.ndarray, scales: np.ndarray, weight_format: str = "rawint4") -> np.ndarray:
+    n, k = validate_layout(packed, scales)
+    out = np.empty((n, k), dtype=np.float32)
+    rc = _load().orc_dequant_format(_ptr(np.ascontiguousarray(packed), _u8p), _ptr(np.ascontiguousarray(scales), _u16p),
+                                    n, k, FORMATS[weight_format], _ptr(out, _f32p))
+    assert rc == 0
+    return out
+
+
+def transpose_free_dx(dy: np.ndarray, packed: np.ndarray, scales: np.ndarray, weight_format: str = "rawint4") -> np.ndarray:
     n, k = validate_layout(packed, scales)
     d = np.ascontiguousarray(dy, dtype=np.float64)
     if d.ndim != 2 or d.shape[1] != n:
         raise ValueError(f"grad_output must have shape [M, {n}]")
     out = np.empty((d.shape[0], k), dtype=np.float64)
-    _load().orc_transpose_free_dx(_ptr(d, _f64p), d.shape[0], _ptr(np.ascontiguousarray(packed), _u8p),
-                                  _ptr(np.ascontiguousarray(scales), _u16p), n, k, _ptr(out, _f64p))
+    rc = _load().orc_transpose_free_dx_format(_ptr(d, _f64p), d.shape[0], _ptr(np.ascontiguousarray(packed), _u8p),
+                                              _ptr(np.ascontiguousarray(scales), _u16p), n, k,
+                                              FORMATS[weight_format], _ptr(out, _f64p))
+    assert rc == 0
     return out
 
 
@@ -210,7 +231,8 @@ def moe(cfg, weights, inputs, expert_ids, route_weights, grad_output=None, *, fp
     keep = {name: np.ascontiguousarray(lora[name], dtype=np.float64) for name in LORA_NAMES}
     arrays = [np.ascontiguousarray(a) for a in (weights.gate_packed, weights.up_packed, weights.down_packed,
                                                  weights.gate_scale, weights.up_scale, weights.down_scale)]
-    layer = OrcLayer(e, cfg.top_k, h, i, r, 1 if fp32_intermediates else 0, float(cfg.alpha), float(cfg.swiglu_limit),
+    fmt = FORMATS[getattr(cfg, "weight_format", "rawint4")]
+    layer = OrcLayer(e, cfg.top_k, h, i, r, 1 if fp32_intermediates else 0, fmt, float(cfg.alpha), float(cfg.swiglu_limit),
                      _ptr(arrays[0], _u8p), _ptr(arrays[1], _u8p), _ptr(arrays[2], _u8p), _ptr(arrays[3], _u16p),
                      _ptr(arrays[4], _u16p), _ptr(arrays[5], _u16p), *(_ptr(keep[n], _f64p) for n in LORA_NAMES))
     x = _bf16_to_f64(inputs) if inputs_are_bf16 else np.ascontiguousarray(inputs, dtype=np.float64)

@@ -9,6 +9,14 @@
  *   - the codec: a byte holds two biased nibbles, low nibble first; nibble c
  *     decodes to (c - 8) times the bf16 scale of its 32-wide group
  *     (module docstring, unpack_rawint4, dequantize_rawint4);
+ *   - the MXFP4 weight format of the same layer (page "ext_bindings.cpp"
+ *     commit log: MXFP4_SFT_MOE, E2M1 nibbles with a UE8M0 scale per group of
+ *     32, the scale handed over as bf16 by a bit-cast; page "backend.py",
+ *     layout "mxfp4-e2m1-ue8m0-g32"): nibble c is the E2M1 number of the OCP
+ *     microscaling formats -- sign bit 3, exponent bits 2..1 with bias 1,
+ *     mantissa bit 0, exponent 0 subnormal -- times the bf16 scale.  Readings:
+ *     nibble order as for RAWINT4 (low nibble first), and everything but the
+ *     decode (grouping, LoRA, clamp, gradients) as for RAWINT4;
  *   - the layout checks (_validate_rawint4_layout);
  *   - the group-at-a-time transpose-free dX (transpose_free_rawint4_dx);
  *   - the routed LoRA equation (routed_rawint4_lora, _base_linear,
@@ -50,9 +58,12 @@
 
 #define ORC_GROUP_SIZE 32
 
+#define ORC_FORMAT_RAWINT4 0
+#define ORC_FORMAT_MXFP4 1
+
 typedef struct {
   int32_t num_experts, top_k, hidden, intermediate, rank;
-  int32_t fp32_intermediates;
+  int32_t fp32_intermediates, weight_format; /* ORC_FORMAT_* */
   double alpha, swiglu_limit;
   const uint8_t *gate_packed, *up_packed, *down_packed;    /* [E,I,H/2] [E,I,H/2] [E,H,I/2] */
   const uint16_t *gate_scale, *up_scale, *down_scale;      /* bf16 bits, [E,I,H/32] [E,I,H/32] [E,H,I/32] */
@@ -107,26 +118,50 @@ int orc_validate_layout(int64_t n, int64_t packed_cols, int64_t scale_rows, int6
   return 0;
 }
 
-static double weight_at(const uint8_t* packed, const uint16_t* scales, int64_t k, int64_t row, int64_t col) {
-  uint8_t byte = packed[row * (k / 2) + col / 2];
-  int nib = (col & 1) ? (byte >> 4) : (byte & 0x0F);
-  return (double)(nib - 8) * bf16_value(scales[row * (k / ORC_GROUP_SIZE) + col / ORC_GROUP_SIZE]);
+/* E2M1 (OCP microscaling FP4): (-1)^s * 2^(e - 1) * (1 + m / 2) for e > 0,
+ * (-1)^s * m / 2 for e == 0 (subnormal; bias 1). */
+static double e2m1_value(int nib) {
+  const int sign = (nib >> 3) & 1, e = (nib >> 1) & 3, m = nib & 1;
+  const double mag = e ? ldexp(1.0 + 0.5 * m, e - 1) : 0.5 * m;
+  return sign ? -mag : mag;
 }
 
-/* dequantize_rawint4: dense [N, K]; (c - 8) * scale is exact in fp32. */
-int orc_dequant(const uint8_t* packed, const uint16_t* scales, int64_t n, int64_t k, float* w) {
+/* the unscaled value of one nibble in either weight format */
+static double code_value(int fmt, int nib) { return fmt == ORC_FORMAT_MXFP4 ? e2m1_value(nib) : (double)(nib - 8); }
+
+/* E2M1 value of each nibble 0..15 (the table the pins compare). */
+void orc_e2m1_table(double* out) {
+  for (int c = 0; c < 16; ++c) out[c] = e2m1_value(c);
+}
+
+static double weight_at(int fmt, const uint8_t* packed, const uint16_t* scales, int64_t k, int64_t row,
+                        int64_t col) {
+  uint8_t byte = packed[row * (k / 2) + col / 2];
+  int nib = (col & 1) ? (byte >> 4) : (byte & 0x0F);
+  return code_value(fmt, nib) * bf16_value(scales[row * (k / ORC_GROUP_SIZE) + col / ORC_GROUP_SIZE]);
+}
+
+/* dequantize_rawint4 (and its MXFP4 twin): dense [N, K]; a code value times a
+ * bf16 scale has at most 3 + 8 significant bits, exact in fp32 (in range). */
+int orc_dequant_format(const uint8_t* packed, const uint16_t* scales, int64_t n, int64_t k, int32_t fmt, float* w) {
   if (k % ORC_GROUP_SIZE) return -2;
+  if (fmt != ORC_FORMAT_RAWINT4 && fmt != ORC_FORMAT_MXFP4) return -3;
 #pragma omp parallel for schedule(static)
   for (int64_t row = 0; row < n; ++row)
-    for (int64_t col = 0; col < k; ++col) w[row * k + col] = (float)weight_at(packed, scales, k, row, col);
+    for (int64_t col = 0; col < k; ++col) w[row * k + col] = (float)weight_at(fmt, packed, scales, k, row, col);
   return 0;
+}
+
+int orc_dequant(const uint8_t* packed, const uint16_t* scales, int64_t n, int64_t k, float* w) {
+  return orc_dequant_format(packed, scales, n, k, ORC_FORMAT_RAWINT4, w);
 }
 
 /* transpose_free_rawint4_dx: dX[M,K] = dY[M,N] W[N,K] using only original rows,
  * one 32-wide group of one row decoded at a time. */
-int orc_transpose_free_dx(const double* dy, int64_t m, const uint8_t* packed, const uint16_t* scales,
-                          int64_t n, int64_t k, double* dx) {
+int orc_transpose_free_dx_format(const double* dy, int64_t m, const uint8_t* packed, const uint16_t* scales,
+                                 int64_t n, int64_t k, int32_t fmt, double* dx) {
   if (k % ORC_GROUP_SIZE) return -2;
+  if (fmt != ORC_FORMAT_RAWINT4 && fmt != ORC_FORMAT_MXFP4) return -3;
   memset(dx, 0, sizeof(double) * (size_t)(m * k));
   for (int64_t group = 0; group < k / ORC_GROUP_SIZE; ++group) {
     int64_t k0 = group * ORC_GROUP_SIZE;
@@ -135,8 +170,8 @@ int orc_transpose_free_dx(const double* dy, int64_t m, const uint8_t* packed, co
       double scale = bf16_value(scales[row * (k / ORC_GROUP_SIZE) + group]);
       for (int j = 0; j < ORC_GROUP_SIZE / 2; ++j) {
         uint8_t byte = packed[row * (k / 2) + k0 / 2 + j];
-        values[2 * j] = (double)((int)(byte & 0x0F) - 8) * scale;
-        values[2 * j + 1] = (double)((int)(byte >> 4) - 8) * scale;
+        values[2 * j] = code_value(fmt, byte & 0x0F) * scale;
+        values[2 * j + 1] = code_value(fmt, byte >> 4) * scale;
       }
       for (int64_t i = 0; i < m; ++i) {
         double g = dy[i * n + row];
@@ -145,6 +180,11 @@ int orc_transpose_free_dx(const double* dy, int64_t m, const uint8_t* packed, co
     }
   }
   return 0;
+}
+
+int orc_transpose_free_dx(const double* dy, int64_t m, const uint8_t* packed, const uint16_t* scales, int64_t n,
+                          int64_t k, double* dx) {
+  return orc_transpose_free_dx_format(dy, m, packed, scales, n, k, ORC_FORMAT_RAWINT4, dx);
 }
 
 /* ---------------------------------------------------------------- routing */
@@ -296,6 +336,7 @@ int orc_moe_decided(const orc_layer* L, int64_t qlen, const double* x, const int
   const int64_t E = L->num_experts, K = L->top_k, H = L->hidden, I = L->intermediate, R = L->rank;
   if (E < 1 || K < 1 || R < 1 || H % ORC_GROUP_SIZE || I % ORC_GROUP_SIZE || H <= 0 || I <= 0) return -1;
   if (!(L->swiglu_limit >= 0.0) || !isfinite(L->swiglu_limit)) return -1;
+  if (L->weight_format != ORC_FORMAT_RAWINT4 && L->weight_format != ORC_FORMAT_MXFP4) return -1;
   const int fr = L->fp32_intermediates;
   const double sc = L->alpha / (double)R, limit = L->swiglu_limit;
   const int64_t slots = qlen * K;
@@ -334,9 +375,9 @@ int orc_moe_decided(const orc_layer* L, int64_t qlen, const double* x, const int
     const int64_t m = counts[e];
     if (m == 0) continue;
     const int32_t* rows = sorted + offsets[e];
-    orc_dequant(L->gate_packed + e * I * (H / 2), L->gate_scale + e * I * (H / 32), I, H, wg);
-    orc_dequant(L->up_packed + e * I * (H / 2), L->up_scale + e * I * (H / 32), I, H, wu);
-    orc_dequant(L->down_packed + e * H * (I / 2), L->down_scale + e * H * (I / 32), H, I, wd);
+    orc_dequant_format(L->gate_packed + e * I * (H / 2), L->gate_scale + e * I * (H / 32), I, H, L->weight_format, wg);
+    orc_dequant_format(L->up_packed + e * I * (H / 2), L->up_scale + e * I * (H / 32), I, H, L->weight_format, wu);
+    orc_dequant_format(L->down_packed + e * H * (I / 2), L->down_scale + e * H * (I / 32), H, I, L->weight_format, wd);
     const double* ag = L->gate_a + e * R * H;
     const double* bg = L->gate_b + e * I * R;
     const double* au = L->up_a + e * R * H;

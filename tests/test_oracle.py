@@ -123,6 +123,92 @@ def test_transpose_free_dx_is_dy_times_w():
     np.testing.assert_allclose(O.transpose_free_dx(dy, packed, scales), dy @ dense, rtol=1e-13, atol=1e-13)
 
 
+# ------------------------------------------------------------------ MXFP4 codec
+
+
+def test_e2m1_table_against_the_fp16_bit_layout():
+    # An E2M1 nibble (sign, two exponent bits with bias 1, one mantissa bit) placed
+    # into an fp16 word as sign bit 15 and exponent/mantissa bits 11..9 is the same
+    # number times 2^-14: fp16 has bias 15 and its own subnormals.  numpy's fp16
+    # decoder is independent of the oracle's closed form.
+    table = O.e2m1_table()
+    bits = np.array([((c & 8) << 12) | ((c & 7) << 9) for c in range(16)], dtype=np.uint16)
+    assert np.array_equal(table, bits.view(np.float16).astype(np.float64) * 2.0 ** 14)
+    # and the format's known facts: largest magnitude 6, smallest nonzero 0.5, symmetric
+    assert table[7] == 6.0 and table[1] == 0.5 and table[0] == 0.0
+    assert np.all(np.diff(table[:8]) > 0) and np.array_equal(table[8:], -table[:8])
+
+
+def test_mxfp4_dequant_nibble_order_and_scale():
+    # byte 0x21: low nibble 1 (0.5) first, then 2 (1.0); 0x7F: 15 (-6) then 7 (6);
+    # scale 2^-4 (UE8M0 123) and a zero scale (UE8M0 0, bit-cast to +0)
+    packed = np.zeros((1, 32), dtype=np.uint8)
+    packed[0, 0] = 0x21
+    packed[0, 1] = 0x7F
+    packed[0, 16:] = 0x77
+    scales = W.ue8m0_to_bf16_bits(np.array([[123, 0]]))
+    assert scales.tolist() == [[BF16_SIXTEENTH, 0]]
+    w = O.dequant(packed, scales, "mxfp4")
+    assert w[0, :4].tolist() == [0.5 / 16, 1.0 / 16, -6.0 / 16, 6.0 / 16]
+    assert np.all(w[0, 4:32] == 0.0) and np.all(w[0, 32:] == 0.0)
+
+
+def test_ue8m0_bit_cast_is_a_power_of_two():
+    e = np.arange(1, 255)
+    vals = W.bf16_bits_to_f32(W.ue8m0_to_bf16_bits(e)).astype(np.float64)
+    assert np.array_equal(vals, np.array([math.ldexp(1.0, int(k) - 127) for k in e]))
+
+
+def test_mxfp4_transpose_free_dx_is_dy_times_w():
+    rng = np.random.default_rng(8)
+    n, k, m = 40, 64, 3
+    packed = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    scales = W.ue8m0_to_bf16_bits(rng.integers(118, 130, size=(n, k // 32)))
+    dy = rng.standard_normal((m, n))
+    dense = O.dequant(packed, scales, "mxfp4").astype(np.float64)
+    np.testing.assert_allclose(O.transpose_free_dx(dy, packed, scales, "mxfp4"), dy @ dense, rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("limit", [0.0, 1.5])
+def test_mxfp4_layer_reduces_to_rawint4(limit):
+    # An MXFP4 layer whose codes stay within |E2M1| <= 3 is the RAWINT4 layer with
+    # code 8 + 2 v and half the scale: the same dense weights, so the oracle must
+    # give identical forward and backward results in both formats.
+    cfg = W.LayerConfig("m", 3, 2, 64, 96, 4, 8.0, 7, limit, x_std=2.0)
+    rng = np.random.default_rng(11)
+    table = O.e2m1_table()
+    small = np.flatnonzero(np.abs(table) <= 3)  # nibbles 0..5 and 8..13
+    w = W.make_weights(cfg, 3)
+    mx = W.Weights(gate_packed=w.gate_packed, up_packed=w.up_packed, down_packed=w.down_packed,
+                   gate_scale=w.gate_scale, up_scale=w.up_scale, down_scale=w.down_scale, lora=w.lora)
+    ri = W.Weights(gate_packed=w.gate_packed, up_packed=w.up_packed, down_packed=w.down_packed,
+                   gate_scale=w.gate_scale, up_scale=w.up_scale, down_scale=w.down_scale, lora=w.lora)
+    for name in ("gate", "up", "down"):
+        shape = getattr(w, name + "_packed").shape
+        lo = rng.choice(small, size=shape)
+        hi = rng.choice(small, size=shape)
+        setattr(mx, name + "_packed", (lo | (hi << 4)).astype(np.uint8))
+        to_int = {int(c): int(8 + 2 * table[c]) for c in small}
+        lo_i = np.vectorize(to_int.get)(lo)
+        hi_i = np.vectorize(to_int.get)(hi)
+        setattr(ri, name + "_packed", (lo_i | (hi_i << 4)).astype(np.uint8))
+        e = rng.integers(120, 126, size=getattr(w, name + "_scale").shape)
+        setattr(mx, name + "_scale", W.ue8m0_to_bf16_bits(e))
+        setattr(ri, name + "_scale", W.ue8m0_to_bf16_bits(e - 1))
+    batch = W.make_batch(cfg, 5)
+    cfg_mx = W.LayerConfig("m", 3, 2, 64, 96, 4, 8.0, 7, limit, x_std=2.0, weight_format="mxfp4")
+    a = O.moe(cfg_mx, mx, batch.inputs, batch.expert_ids, batch.route_weights, batch.grad_output)
+    b = O.moe(cfg, ri, batch.inputs, batch.expert_ids, batch.route_weights, batch.grad_output)
+    assert np.count_nonzero(a["out"]) and np.array_equal(a["out"], b["out"])
+    assert np.array_equal(a["dx"], b["dx"]) and np.array_equal(a["droute"], b["droute"])
+    for n in O.LORA_NAMES:
+        assert np.array_equal(a["grads"][n], b["grads"][n]), n
+    # and the full nibble range differs from any RAWINT4 reading
+    full = W.make_weights(cfg_mx, 3)
+    assert not np.array_equal(O.dequant(full.gate_packed[0], full.gate_scale[0], "mxfp4"),
+                              O.dequant(full.gate_packed[0], full.gate_scale[0]))
+
+
 # ------------------------------------------------------------------ grouping
 
 
