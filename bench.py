@@ -14,7 +14,8 @@ kt_rawint4_moe_bwd_recompute).  The default line is the training step.
 
 Default workload: 384 experts, top-8, hidden 7168, intermediate 2048, LoRA rank 64
 (alpha 128), 16384 tokens, SwiGLU clamp 7, uniform routing.  ``--config`` picks
-another of the five workloads of ``int4_quantized_moe_amd.workloads.CONFIGS``.
+another of the five workloads of ``int4_quantized_moe_amd.workloads.CONFIGS``;
+``--format mxfp4`` gives it an MXFP4 base (E2M1 codes, power-of-two scales).
 """
 
 from __future__ import annotations
@@ -110,6 +111,8 @@ def main():
     ap.add_argument("--infer", choices=("lora", "base"), default=None,
                     help="time the inference forward (with the LoRA, or the frozen base alone) instead of the "
                          "training step")
+    ap.add_argument("--format", choices=("rawint4", "mxfp4"), default="rawint4",
+                    help="weight format of the frozen base (the workload's shapes and seeds either way)")
     ap.add_argument("--recompute", action="store_true",
                     help="training step with an inference forward and the checkpoint-recompute backward")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -130,6 +133,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     cfg = workloads.CONFIGS[args.config]
+    if args.format != cfg.weight_format:
+        cfg = dataclasses.replace(cfg, name=f"{cfg.name}_{args.format}", weight_format=args.format)
     seed = workloads.config_seed(args.config)
     log(f"workload {cfg.name}: generating (seed {seed})")
     t0 = time.perf_counter()
@@ -258,6 +263,7 @@ def main():
         "config": {"workload": cfg.name, "experts": cfg.num_experts, "top_k": cfg.top_k, "hidden": cfg.hidden,
                    "intermediate": cfg.intermediate, "rank": cfg.rank, "alpha": cfg.alpha, "qlen": cfg.qlen,
                    "swiglu_limit": cfg.swiglu_limit, "routing": cfg.routing, "active_experts": active,
+                   "weight_format": cfg.weight_format,
                    **({"mode": f"inference ({'LoRA' if args.infer == 'lora' else 'frozen base alone'})"}
                       if args.infer else {}),
                    **({"mode": "checkpoint recompute (inference forward + recompute backward)"}

@@ -41,6 +41,8 @@ extern "C" {
 #define KT_RAWINT4_EHIP (-3)
 
 #define KT_RAWINT4_GROUP_SIZE 32
+#define KT_RAWINT4_FORMAT_RAWINT4 0
+#define KT_RAWINT4_FORMAT_MXFP4 1
 #define KT_RAWINT4_MAX_EXPERTS 8192
 #define KT_RAWINT4_MAX_RANK 128
 
@@ -63,6 +65,18 @@ extern "C" {
  * is exact in fp16, which is what the kernels multiply with.  Scales outside
  * the domain are counted (see kt_rawint4_moe_diagnostics); results computed
  * with them are not defined (they may be inf or NaN).
+ *
+ * weight_format = KT_RAWINT4_FORMAT_MXFP4 selects the MXFP4 base of the same
+ * layer (page "ext_bindings.cpp" commit log: MXFP4_SFT_MOE, E2M1 weights with
+ * a UE8M0 scale per group of 32; page "backend.py", layout
+ * "mxfp4-e2m1-ue8m0-g32").  Same shapes and nibble order; nibble c is the E2M1
+ * number of the OCP microscaling formats (sign bit 3, exponent bits 2..1 with
+ * bias 1, mantissa bit 0: 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives)
+ * times the group's scale, and the scales are the UE8M0 exponents bit-cast to
+ * bf16 (e << 7, as the pages' loader converts them), i.e. powers of two.  Its
+ * numeric domain: scales 0 or 2^j with -13 <= j <= 13 (UE8M0 114 .. 140);
+ * others are counted as above.  Everything else (LoRA, clamp, gradients,
+ * window rule) is as for RAWINT4.
  *
  * LoRA tensors (fp32): gate_lora_a [E, r, H], gate_lora_b [E, I, r],
  * up_lora_a [E, r, H], up_lora_b [E, I, r], down_lora_a [E, r, I],
@@ -89,6 +103,7 @@ typedef struct kt_rawint4_moe_layer {
   const float* up_lora_b;
   const float* down_lora_a;
   const float* down_lora_b;
+  int32_t weight_format; /* KT_RAWINT4_FORMAT_RAWINT4 (0, the default) or KT_RAWINT4_FORMAT_MXFP4 */
 } kt_rawint4_moe_layer;
 
 /*
@@ -202,6 +217,16 @@ int kt_rawint4_unpack(const uint8_t* packed, int64_t n, int64_t k, int8_t* codes
  */
 int kt_rawint4_dequant(const uint8_t* packed, const uint16_t* scales, int64_t n, int64_t k, float* weights,
                        void* stream);
+
+/*
+ * Test hook, the MXFP4 twin of kt_rawint4_dequant: packed [n, k/2] E2M1 codes
+ * (low nibble first) with bf16 power-of-two scales [n, k/32] -> fp32 weights
+ * [n, k], through the matrix kernels' own MXFP4 decoders.  Both decoders (the
+ * one of the stored orientation and the one of the transposed orientation)
+ * run; a dword where they disagree comes out as NaN.
+ */
+int kt_rawint4_dequant_mxfp4(const uint8_t* packed, const uint16_t* scales, int64_t n, int64_t k, float* weights,
+                             void* stream);
 
 /*
  * Test hook, the token-slot grouping of the layer: offsets [E+1] int32

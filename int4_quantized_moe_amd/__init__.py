@@ -9,10 +9,13 @@ from ._lib import (  # noqa: F401
     KT_RAWINT4_EHIP,
     KT_RAWINT4_EINVAL,
     KT_RAWINT4_EWORKSPACE,
+    KT_RAWINT4_FORMAT_MXFP4,
+    KT_RAWINT4_FORMAT_RAWINT4,
     KT_RAWINT4_OK,
     LIBRARY_PATH,
     KtRawInt4Error,
     kt_rawint4_dequant,
+    kt_rawint4_dequant_mxfp4,
     kt_rawint4_group,
     kt_rawint4_group_workspace_bytes,
     kt_rawint4_last_error,

@@ -21,6 +21,10 @@ KT_RAWINT4_EINVAL = -1
 KT_RAWINT4_EWORKSPACE = -2
 KT_RAWINT4_EHIP = -3
 
+KT_RAWINT4_FORMAT_RAWINT4 = 0
+KT_RAWINT4_FORMAT_MXFP4 = 1
+FORMATS = {"rawint4": KT_RAWINT4_FORMAT_RAWINT4, "mxfp4": KT_RAWINT4_FORMAT_MXFP4}
+
 _vp = ctypes.c_void_p
 
 
@@ -51,6 +55,7 @@ class kt_rawint4_moe_layer(ctypes.Structure):  # noqa: N801 - the C struct's nam
         ("up_lora_b", _vp),
         ("down_lora_a", _vp),
         ("down_lora_b", _vp),
+        ("weight_format", ctypes.c_int32),
     ]
 
 
@@ -76,6 +81,7 @@ def load_library() -> ctypes.CDLL:
                                          [lp, i32, _vp, _vp, _vp, _vp, _vp, _vp] + [_vp] * 6 + [i32, f32, _vp, sz, _vp]),
         "kt_rawint4_unpack": (ctypes.c_int, [_vp, i64, i64, _vp, _vp]),
         "kt_rawint4_dequant": (ctypes.c_int, [_vp, _vp, i64, i64, _vp, _vp]),
+        "kt_rawint4_dequant_mxfp4": (ctypes.c_int, [_vp, _vp, i64, i64, _vp, _vp]),
         "kt_rawint4_group_workspace_bytes": (sz, [i32, i32, i32]),
         "kt_rawint4_group": (ctypes.c_int, [_vp, i32, i32, i32, _vp, _vp, _vp, sz, _vp]),
         "kt_rawint4_moe_diagnostics": (ctypes.c_int, [_vp, sz, ctypes.POINTER(i64), ctypes.POINTER(i64), _vp]),
@@ -125,13 +131,15 @@ def _nbytes(t) -> int:
 
 def make_layer(num_experts, top_k, hidden, intermediate, rank, alpha, swiglu_limit, gate_packed, up_packed,
                down_packed, gate_scale, up_scale, down_scale, gate_lora_a, gate_lora_b, up_lora_a, up_lora_b,
-               down_lora_a, down_lora_b) -> kt_rawint4_moe_layer:
-    """Fill the C layer struct; the caller keeps the tensors alive."""
+               down_lora_a, down_lora_b, weight_format=KT_RAWINT4_FORMAT_RAWINT4) -> kt_rawint4_moe_layer:
+    """Fill the C layer struct; the caller keeps the tensors alive.  weight_format:
+    KT_RAWINT4_FORMAT_* or its name ("rawint4", "mxfp4")."""
+    fmt = FORMATS[weight_format] if isinstance(weight_format, str) else int(weight_format)
     return kt_rawint4_moe_layer(int(num_experts), int(top_k), int(hidden), int(intermediate), int(rank), float(alpha),
                                 float(swiglu_limit), _ptr(gate_packed), _ptr(up_packed), _ptr(down_packed),
                                 _ptr(gate_scale), _ptr(up_scale), _ptr(down_scale), _ptr(gate_lora_a),
                                 _ptr(gate_lora_b), _ptr(up_lora_a), _ptr(up_lora_b), _ptr(down_lora_a),
-                                _ptr(down_lora_b))
+                                _ptr(down_lora_b), fmt)
 
 
 def kt_rawint4_moe_workspace_bytes(layer: kt_rawint4_moe_layer, qlen: int) -> int:
@@ -187,6 +195,11 @@ def kt_rawint4_unpack(packed, n, k, codes, stream=None) -> None:
 def kt_rawint4_dequant(packed, scales, n, k, weights, stream=None) -> None:
     _check(load_library().kt_rawint4_dequant(_ptr(packed), _ptr(scales), int(n), int(k), _ptr(weights),
                                              _stream(stream)))
+
+
+def kt_rawint4_dequant_mxfp4(packed, scales, n, k, weights, stream=None) -> None:
+    _check(load_library().kt_rawint4_dequant_mxfp4(_ptr(packed), _ptr(scales), int(n), int(k), _ptr(weights),
+                                                   _stream(stream)))
 
 
 def kt_rawint4_group_workspace_bytes(qlen, top_k, num_experts) -> int:

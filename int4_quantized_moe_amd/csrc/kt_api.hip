@@ -142,6 +142,8 @@ static int check_layer(const kt_rawint4_moe_layer* L, int32_t qlen, Dims* d, boo
   if (!base && !isfinite(L->alpha)) return fail(KT_RAWINT4_EINVAL, "alpha must be finite");
   if (!isfinite(L->swiglu_limit) || L->swiglu_limit < 0.f)
     return fail(KT_RAWINT4_EINVAL, "swiglu_limit must be finite and non-negative");
+  if (L->weight_format != KT_RAWINT4_FORMAT_RAWINT4 && L->weight_format != KT_RAWINT4_FORMAT_MXFP4)
+    return fail(KT_RAWINT4_EINVAL, "weight_format must be KT_RAWINT4_FORMAT_RAWINT4 or KT_RAWINT4_FORMAT_MXFP4");
   if (qlen < 0) return fail(KT_RAWINT4_EINVAL, "qlen must be non-negative");
   if ((int64_t)qlen * L->top_k >= ((int64_t)1 << 31)) return fail(KT_RAWINT4_EINVAL, "qlen * top_k must be below 2^31");
   const void* ptrs[] = {L->gate_packed, L->up_packed,   L->down_packed, L->gate_scale,  L->up_scale,
@@ -166,6 +168,7 @@ static int check_layer(const kt_rawint4_moe_layer* L, int32_t qlen, Dims* d, boo
   d->Ms = (int64_t)qlen * L->top_k;
   d->sc = base ? 0.f : L->alpha / (float)L->rank;
   d->limit = L->swiglu_limit;
+  d->fmt = L->weight_format;
   return KT_RAWINT4_OK;
 }
 
@@ -346,9 +349,9 @@ static void launch_forward_front(const kt_rawint4_moe_layer* layer, const Dims& 
     PhaseScope ph(kPhScales, st);
     unsigned long long* bad = ws_ptr<unsigned long long>(ws, w.counters) + kBadScales;
     const int32_t* offs = ws_ptr<int32_t>(ws, w.offsets);
-    launch_scales_t(layer->gate_scale, d.E, d.I, d.H / 32, offs, ws_ptr<uint16_t>(ws, w.sct_g), bad, st);
-    launch_scales_t(layer->up_scale, d.E, d.I, d.H / 32, offs, ws_ptr<uint16_t>(ws, w.sct_u), bad, st);
-    launch_scales_t(layer->down_scale, d.E, d.H, d.I / 32, offs, ws_ptr<uint16_t>(ws, w.sct_d), bad, st);
+    launch_scales_t(layer->gate_scale, d.E, d.I, d.H / 32, offs, ws_ptr<uint16_t>(ws, w.sct_g), bad, d.fmt, st);
+    launch_scales_t(layer->up_scale, d.E, d.I, d.H / 32, offs, ws_ptr<uint16_t>(ws, w.sct_u), bad, d.fmt, st);
+    launch_scales_t(layer->down_scale, d.E, d.H, d.I / 32, offs, ws_ptr<uint16_t>(ws, w.sct_d), bad, d.fmt, st);
   }
   {
     PhaseScope ph(kPhXHalf, st);
@@ -554,7 +557,18 @@ int kt_rawint4_dequant(const uint8_t* packed, const uint16_t* scales, int64_t n,
   if (n * k > 0 && (!packed || !scales || !weights))
     return fail(KT_RAWINT4_EINVAL, "packed, scales and weights must be non-NULL");
   if (!aligned(packed, 4)) return fail(KT_RAWINT4_EINVAL, "packed must be 4-byte aligned");
-  launch_dequant(packed, scales, n, k, weights, static_cast<hipStream_t>(stream));
+  launch_dequant(packed, scales, n, k, KT_RAWINT4_FORMAT_RAWINT4, weights, static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+int kt_rawint4_dequant_mxfp4(const uint8_t* packed, const uint16_t* scales, int64_t n, int64_t k, float* weights,
+                             void* stream) {
+  if (n < 0 || k < 0 || k % KT_RAWINT4_GROUP_SIZE)
+    return fail(KT_RAWINT4_EINVAL, "n must be >= 0 and k a multiple of 32");
+  if (n * k > 0 && (!packed || !scales || !weights))
+    return fail(KT_RAWINT4_EINVAL, "packed, scales and weights must be non-NULL");
+  if (!aligned(packed, 4)) return fail(KT_RAWINT4_EINVAL, "packed must be 4-byte aligned");
+  launch_dequant(packed, scales, n, k, KT_RAWINT4_FORMAT_MXFP4, weights, static_cast<hipStream_t>(stream));
   return launched();
 }
 

@@ -73,7 +73,7 @@ void launch_rows_to_half(const uint16_t* src, int64_t rows, int64_t cols, uint16
 // bytes per lane) are both coalesced.
 __global__ __launch_bounds__(256) void k_scales_t(const uint16_t* __restrict__ s, int64_t rows, int64_t G,
                                                    const int32_t* __restrict__ offsets, uint16_t* __restrict__ out,
-                                                   unsigned long long* bad) {
+                                                   unsigned long long* bad, int fmt) {
   __shared__ uint16_t t[64][72];  // [row][group], 144-byte pitch
   __shared__ int nbad_w[4];
   const int64_t e = blockIdx.z;
@@ -102,7 +102,8 @@ __global__ __launch_bounds__(256) void k_scales_t(const uint16_t* __restrict__ s
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const float f = bf16_to_float(v[q]);
-      nbad += (r < rows && g0 + j0 + q < G && !scale_in_domain(f)) ? 1 : 0;
+      const bool ok = fmt ? scale_in_domain_mxfp4(f) : scale_in_domain(f);
+      nbad += (r < rows && g0 + j0 + q < G && !ok) ? 1 : 0;
       t[i][j0 + q] = float_to_half_bits(f);
     }
   }
@@ -142,10 +143,10 @@ __global__ __launch_bounds__(256) void k_scales_t(const uint16_t* __restrict__ s
 }
 
 void launch_scales_t(const uint16_t* s, int64_t E, int64_t rows, int64_t G, const int32_t* offsets, uint16_t* out,
-                     unsigned long long* bad, hipStream_t st) {
+                     unsigned long long* bad, int fmt, hipStream_t st) {
   if (E <= 0 || rows <= 0 || G <= 0) return;
   dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((G + 63) / 64), (unsigned)E);
-  k_scales_t<<<grid, 256, 0, st>>>(s, rows, G, offsets, out, bad);
+  k_scales_t<<<grid, 256, 0, st>>>(s, rows, G, offsets, out, bad, fmt);
 }
 
 // ---------------------------------------------------------------- one exponent per row
@@ -316,7 +317,7 @@ void launch_unpack(const uint8_t* packed, int64_t n, int64_t k, int8_t* codes, h
 
 // the matrix kernels' decoder: one packed dword -> 8 fp16 values -> fp32
 __global__ void k_dequant(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales, int64_t n,
-                          int64_t k, float* __restrict__ out) {
+                          int64_t k, int fmt, float* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // dword index
   const int64_t dwords_per_row = k / 8;
   if (i >= n * dwords_per_row) return;
@@ -325,8 +326,16 @@ __global__ void k_dequant(const uint8_t* __restrict__ packed, const uint16_t* __
   // the decoder of the forward matrix kernels (codes along the packed row)
   const _Float16 s = (_Float16)bf16_to_float(scales[row * (k / kGroup) + (d * 8) / kGroup]);
   const half2_t s2 = {s, s};
-  const u32x4 r = decode_dword_fma(wv, s2 * (half2_t){16.f16, 16.f16}, s2 * (half2_t){-24.f16, -24.f16},
-                                   decode_consts());
+  u32x4 r;
+  if (fmt) {
+    // the MXFP4 decoders of both orientations; a disagreement (none is
+    // expected) shows as NaN in every value of the dword
+    r = decode_dword_e2m1(wv, (float)s);
+    const u32x4 t = decode_dword_perm_e2m1(wv, s2, s2, s2, s2);
+    if (t.x != r.x || t.y != r.y || t.z != r.z || t.w != r.w) r = u32x4{0x7e007e00u, 0x7e007e00u, 0x7e007e00u, 0x7e007e00u};
+  } else {
+    r = decode_dword_fma(wv, s2 * (half2_t){16.f16, 16.f16}, s2 * (half2_t){-24.f16, -24.f16}, decode_consts());
+  }
   const uint32_t words[4] = {r.x, r.y, r.z, r.w};  // (k0, k4), (k1, k5), (k2, k6), (k3, k7)
   float* o = out + row * k + d * 8;
 #pragma unroll
@@ -336,9 +345,10 @@ __global__ void k_dequant(const uint8_t* __restrict__ packed, const uint16_t* __
   }
 }
 
-void launch_dequant(const uint8_t* packed, const uint16_t* scales, int64_t n, int64_t k, float* out, hipStream_t st) {
+void launch_dequant(const uint8_t* packed, const uint16_t* scales, int64_t n, int64_t k, int fmt, float* out,
+                    hipStream_t st) {
   const int64_t total = n * (k / 8);
-  if (total > 0) k_dequant<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(packed, scales, n, k, out);
+  if (total > 0) k_dequant<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(packed, scales, n, k, fmt, out);
 }
 
 }  // namespace kt

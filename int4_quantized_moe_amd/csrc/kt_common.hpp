@@ -125,6 +125,58 @@ __device__ __forceinline__ u32x4 decode_dword_perm(uint32_t w, half2_t s0, half2
   return r;
 }
 
+// ---------------------------------------------------------------- MXFP4 (E2M1 nibbles)
+//
+// The MXFP4 weight format (E2M1 codes, a UE8M0 power-of-two scale per group of
+// 32, handed over as bf16) is decoded by gfx950's v_cvt_scalef32_pk_f16_fp4:
+// one byte (low nibble first) to two fp16 values times 2^(exponent of its fp32
+// scale operand), rounded to nearest even.  It reads only the scale's
+// exponent, which is all an MXFP4 scale has.
+
+// Nonzero MXFP4 scales must be powers of two in [2^-13, 2^13]: every nonzero
+// weight (0.5 .. 6 times the scale) is then a normal fp16 number, exactly.
+__device__ __forceinline__ bool scale_in_domain_mxfp4(float s) {
+  const uint32_t u = __float_as_uint(s);
+  if ((u & 0x7fffffffu) == 0) return true;
+  return (u & 0x807fffffu) == 0 && s >= 0x1p-13f && s <= 0x1p13f;
+}
+
+// The nibbles of one packed dword paired into bytes k_i | k_{i+4} << 4:
+// x holds (k0, k4) in byte 0 and (k2, k6) in byte 1, y holds (k1, k5) and (k3, k7).
+__device__ __forceinline__ void e2m1_pair_bytes(uint32_t w, uint32_t& x, uint32_t& y) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;  // bytes k0 k2 k4 k6 | k1 k3 k5 k7
+  x = lo | (lo >> 12);
+  y = hi | (hi >> 12);
+}
+
+__device__ __forceinline__ uint32_t cvt_e2m1(uint32_t v, float s, int sel) {
+  half2_t r;
+  if (sel == 0)
+    r = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, s, 0);
+  else
+    r = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, s, 1);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// 8 E2M1 codes of one packed dword, all with the scale s, in the order
+// k0 k4 k1 k5 k2 k6 k3 k7 (as decode_dword_fma).
+__device__ __forceinline__ u32x4 decode_dword_e2m1(uint32_t w, float s) {
+  uint32_t x, y;
+  e2m1_pair_bytes(w, x, y);
+  return u32x4{cvt_e2m1(x, s, 0), cvt_e2m1(y, s, 0), cvt_e2m1(x, s, 1), cvt_e2m1(y, s, 1)};
+}
+
+// 8 E2M1 codes (nibble i = code k_i) in the order k0 k4 k1 k5 k2 k6 k3 k7, pair
+// (k_i, k_{i+4}) times the fp16 scales s[i] (as decode_dword_perm): the codes
+// are decoded unscaled and multiplied, exact for in-domain scales.
+__device__ __forceinline__ u32x4 decode_dword_perm_e2m1(uint32_t w, half2_t s0, half2_t s1, half2_t s2, half2_t s3) {
+  uint32_t x, y;
+  e2m1_pair_bytes(w, x, y);
+  auto mul = [](uint32_t v, half2_t sc) { return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, v) * sc); };
+  return u32x4{mul(cvt_e2m1(x, 1.f, 0), s0), mul(cvt_e2m1(y, 1.f, 0), s1), mul(cvt_e2m1(x, 1.f, 1), s2),
+               mul(cvt_e2m1(y, 1.f, 1), s3)};
+}
+
 // 8 fp32 -> bf16 hi (top 16 bits) and lo (top 16 bits of the exact remainder)
 __device__ __forceinline__ void split8_trunc(const float* v, u32x4& hi, u32x4& lo) {
   uint32_t h[8], l[8];

@@ -34,6 +34,9 @@
 // column; this is the transpose-free dX of transpose_free_rawint4_dx with the
 // transpose done by the LDS read.  The scales come from the forward's fp16
 // transposed copy ([E][K/32][N], rows within-8 permuted) by the same copies.
+// MXFP4 weights (E2M1 codes, power-of-two scales; template flag MX) are decoded
+// by gfx950's fp4 conversion instead (decode_dword_e2m1, decode_dword_perm_e2m1),
+// into the same exact fp16 values and the same element order.
 //
 // LDS tiles are XOR-swizzled in 16-byte units so that the fragment reads of a
 // wave spread over the banks: activation row r keeps chunk c in slot
@@ -186,7 +189,8 @@ __device__ __forceinline__ void wait_stages(int n) {
 
 // One work tile of height MT; the LDS belongs to the calling kernel.  LDMA:
 // the LoRA matrix is copied by DMA in whole 16-byte runs (rank a multiple of 4).
-template <int KIND, int MT, bool LDMA>
+// MX: the weights are MXFP4 (E2M1 codes, power-of-two scales) instead of RAWINT4.
+template <int KIND, int MT, bool LDMA, bool MX>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt, uint8_t* ring, int32_t* s_src,
                                           int32_t* s_exp, int32_t* s_slot) {
   constexpr int MB = MT / 16;
@@ -468,8 +472,12 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
           const uint32_t word = j ? (uint32_t)tr[f].y : (uint32_t)tr[f].x;
           // bit-cast whole scalars: clang's bit_cast of an ext-vector component reads component 0
           const uint32_t s0 = sp[j][f].x, s1 = sp[j][f].y, s2 = sp[j][f].z, s3 = sp[j][f].w;
-          bf[j][f] = decode_dword_perm(word, __builtin_bit_cast(half2_t, s0), __builtin_bit_cast(half2_t, s1),
-                                       __builtin_bit_cast(half2_t, s2), __builtin_bit_cast(half2_t, s3), dc);
+          if constexpr (MX)
+            bf[j][f] = decode_dword_perm_e2m1(word, __builtin_bit_cast(half2_t, s0), __builtin_bit_cast(half2_t, s1),
+                                              __builtin_bit_cast(half2_t, s2), __builtin_bit_cast(half2_t, s3));
+          else
+            bf[j][f] = decode_dword_perm(word, __builtin_bit_cast(half2_t, s0), __builtin_bit_cast(half2_t, s1),
+                                         __builtin_bit_cast(half2_t, s2), __builtin_bit_cast(half2_t, s3), dc);
         }
     } else {
       uint32_t raw[4][2];
@@ -484,17 +492,27 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
         const uint32_t sh = Sc[(lg >> 1) * kNT + local_col<KIND>(w, f) + perm_pos(lr)];
         bs[f] = sh | (sh << 16);
       }
-      half2_t s16[4], b24[4];
+      if constexpr (MX) {
+        float sf[4];
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        const half2_t s2 = __builtin_bit_cast(half2_t, bs[f]);
-        s16[f] = s2 * (half2_t){16.f16, 16.f16};
-        b24[f] = s2 * (half2_t){-24.f16, -24.f16};
+        for (int f = 0; f < 4; ++f) sf[f] = (float)__builtin_bit_cast(half2_t, bs[f]).x;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int f = 0; f < 4; ++f) bf[j][f] = decode_dword_e2m1(raw[f][j], sf[f]);
+      } else {
+        half2_t s16[4], b24[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          const half2_t s2 = __builtin_bit_cast(half2_t, bs[f]);
+          s16[f] = s2 * (half2_t){16.f16, 16.f16};
+          b24[f] = s2 * (half2_t){-24.f16, -24.f16};
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int f = 0; f < 4; ++f) bf[j][f] = decode_dword_fma(raw[f][j], s16[f], b24[f], dc);
       }
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int f = 0; f < 4; ++f) bf[j][f] = decode_dword_fma(raw[f][j], s16[f], b24[f], dc);
     }
   };
   // activation fragments of one stage from its slot
@@ -1030,7 +1048,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
 // under the MFMA time.  One launch covers tiles of every height (each expert's
 // rows: full tiles of the largest height, then one tile of the smallest height
 // that holds the rest); a tile's height selects its code path.
-template <int KIND, bool LDMA>
+template <int KIND, bool LDMA, bool MX>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm(GemmParams p) {
   __shared__ __align__(16) uint8_t ring[kRingMax];
   __shared__ int32_t s_src[128], s_exp[128], s_slot[128];
@@ -1046,29 +1064,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int nt = (int)(local % nn);
   switch (p.tile_mt[tile]) {
     case 16:
-      gemm_tile<KIND, 16, LDMA>(p, tile, nt, ring, s_src, s_exp, s_slot);
+      gemm_tile<KIND, 16, LDMA, MX>(p, tile, nt, ring, s_src, s_exp, s_slot);
       break;
     case 32:
-      gemm_tile<KIND, 32, LDMA>(p, tile, nt, ring, s_src, s_exp, s_slot);
+      gemm_tile<KIND, 32, LDMA, MX>(p, tile, nt, ring, s_src, s_exp, s_slot);
       break;
     case 64:
-      gemm_tile<KIND, 64, LDMA>(p, tile, nt, ring, s_src, s_exp, s_slot);
+      gemm_tile<KIND, 64, LDMA, MX>(p, tile, nt, ring, s_src, s_exp, s_slot);
       break;
     case 96:
-      gemm_tile<KIND, 96, LDMA>(p, tile, nt, ring, s_src, s_exp, s_slot);
+      gemm_tile<KIND, 96, LDMA, MX>(p, tile, nt, ring, s_src, s_exp, s_slot);
       break;
     default:
-      gemm_tile<KIND, 128, LDMA>(p, tile, nt, ring, s_src, s_exp, s_slot);
+      gemm_tile<KIND, 128, LDMA, MX>(p, tile, nt, ring, s_src, s_exp, s_slot);
       break;
   }
 }
 
 template <int KIND>
-static void launch_kind(bool ldma, unsigned grid, const GemmParams& p, hipStream_t st) {
-  if (ldma)
-    k_gemm<KIND, true><<<grid, 256, 0, st>>>(p);
-  else
-    k_gemm<KIND, false><<<grid, 256, 0, st>>>(p);
+static void launch_kind(bool ldma, bool mx, unsigned grid, const GemmParams& p, hipStream_t st) {
+  if (mx) {
+    if (ldma)
+      k_gemm<KIND, true, true><<<grid, 256, 0, st>>>(p);
+    else
+      k_gemm<KIND, false, true><<<grid, 256, 0, st>>>(p);
+  } else {
+    if (ldma)
+      k_gemm<KIND, true, false><<<grid, 256, 0, st>>>(p);
+    else
+      k_gemm<KIND, false, false><<<grid, 256, 0, st>>>(p);
+  }
 }
 
 void launch_gemm(GemmKind kind, const Dims& d, const WsMap& w, void* ws, const LayerPtrs& L,
@@ -1140,16 +1165,16 @@ void launch_gemm(GemmKind kind, const Dims& d, const WsMap& w, void* ws, const L
   if (grid == 0) return;
   switch (kind) {
     case kGateUp:
-      launch_kind<kGateUp>(d.R % 4 == 0, grid, p, st);
+      launch_kind<kGateUp>(d.R % 4 == 0, d.fmt == KT_RAWINT4_FORMAT_MXFP4, grid, p, st);
       break;
     case kDown:
-      launch_kind<kDown>(d.R % 4 == 0, grid, p, st);
+      launch_kind<kDown>(d.R % 4 == 0, d.fmt == KT_RAWINT4_FORMAT_MXFP4, grid, p, st);
       break;
     case kDownBwd:
-      launch_kind<kDownBwd>(d.R % 4 == 0, grid, p, st);
+      launch_kind<kDownBwd>(d.R % 4 == 0, d.fmt == KT_RAWINT4_FORMAT_MXFP4, grid, p, st);
       break;
     case kGateUpBwd:
-      launch_kind<kGateUpBwd>(d.R % 4 == 0, grid, p, st);
+      launch_kind<kGateUpBwd>(d.R % 4 == 0, d.fmt == KT_RAWINT4_FORMAT_MXFP4, grid, p, st);
       break;
   }
 }

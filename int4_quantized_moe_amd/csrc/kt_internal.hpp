@@ -101,6 +101,7 @@ struct Dims {
   int64_t E, K, H, I, R, qlen, Ms;  // R = 0: no LoRA (inference of the base alone)
   float sc, limit;
   bool train = true;  // false: inference forward (nothing saved for a backward)
+  int fmt = 0;        // weight format: 0 RAWINT4, 1 MXFP4 (KT_RAWINT4_FORMAT_*)
 };
 
 struct WsMap {
@@ -191,7 +192,7 @@ void launch_fill_zero_f32(float* p, int64_t n, hipStream_t st);
 // scales [E][rows][G] bf16 -> [E][G][rows] fp16, rows within-8 permuted, experts in use only
 // (offsets from the grouping); counts out-of-domain scales
 void launch_scales_t(const uint16_t* s, int64_t E, int64_t rows, int64_t G, const int32_t* offsets, uint16_t* out,
-                     unsigned long long* bad, hipStream_t st);
+                     unsigned long long* bad, int fmt, hipStream_t st);
 // one exponent per row for h ([Ms, I], chunks of kHChunk) and dG|dU ([Ms, 2I], chunks of kNT per half)
 void launch_normalize_chunks(uint16_t* buf, int32_t* exps, const int32_t* nrows, int64_t max_rows, int64_t cols,
                              int64_t split, int nch, int chunkw, hipStream_t st);
@@ -203,6 +204,7 @@ void launch_saved_preact(const Dims& d, const WsMap& w, const void* ws, float* g
 void launch_init_counters(void* ws, const WsMap& w, hipStream_t st);
 
 void launch_unpack(const uint8_t* packed, int64_t n, int64_t k, int8_t* codes, hipStream_t st);
-void launch_dequant(const uint8_t* packed, const uint16_t* scales, int64_t n, int64_t k, float* out, hipStream_t st);
+void launch_dequant(const uint8_t* packed, const uint16_t* scales, int64_t n, int64_t k, int fmt, float* out,
+                    hipStream_t st);
 
 }  // namespace kt

@@ -49,7 +49,7 @@ class DeviceLayer:
         self.layer = _lib.make_layer(cfg.num_experts, cfg.top_k, cfg.hidden, cfg.intermediate, cfg.rank, cfg.alpha,
                                      cfg.swiglu_limit, self.gate_packed, self.up_packed, self.down_packed,
                                      self.gate_scale, self.up_scale, self.down_scale,
-                                     *(self.lora[n] for n in LORA_NAMES))
+                                     *(self.lora[n] for n in LORA_NAMES), weight_format=cfg.weight_format)
 
     def workspace(self, qlen: int) -> torch.Tensor:
         n = _lib.kt_rawint4_moe_workspace_bytes(self.layer, qlen)
