@@ -72,6 +72,18 @@ def trace(directory: str, out: str, command: str) -> None:
     for r in rows:
         lines.append(f"{r['Name'][:64]:64s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:11.1f} "
                      f"{float(r['TotalDurationNs']) / 1e6:10.3f} {float(r['Percentage']):6.2f}")
+    # every dispatch of the expert GEMMs in launch order: the first of each is the
+    # warm-up step's, the rest are the timed steps' (what bench.py's events measure)
+    per = collections.defaultdict(list)
+    for r in sorted(csv.DictReader(open(_find(directory, "kernel_trace.csv"))), key=lambda r: int(r["Start_Timestamp"])):
+        if "k_gemm<" in r["Kernel_Name"]:
+            per[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    if per:
+        lines += ["", "per-dispatch durations (us) of the expert GEMMs, in launch order:"]
+        for name, ds in sorted(per.items()):
+            timed = ds[1:] if len(ds) > 1 else ds
+            lines.append(f"{name[:64]:64s} " + " ".join(f"{d:.1f}" for d in ds) +
+                         f"   avg after the first: {sum(timed) / len(timed):.1f}")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
 
