@@ -150,3 +150,21 @@ def test_inference_workspace_and_base_only_layer():
     assert lib.kt_rawint4_moe_infer(ctypes.byref(base), 4, None, FAKE, FAKE, FAKE, FAKE, need, None) == \
         kt.KT_RAWINT4_EINVAL
     assert lib.kt_rawint4_moe_infer(ctypes.byref(base), 0, None, None, None, None, None, 0, None) == kt.KT_RAWINT4_OK
+
+
+def test_weight_format_is_validated():
+    layer = _layer()
+    assert layer.weight_format == kt.KT_RAWINT4_FORMAT_RAWINT4
+    mx = _layer()
+    mx.weight_format = kt.KT_RAWINT4_FORMAT_MXFP4
+    assert kt.kt_rawint4_moe_workspace_bytes(mx, 7) == kt.kt_rawint4_moe_workspace_bytes(layer, 7)
+    bad = _layer()
+    bad.weight_format = 2
+    with pytest.raises(kt.KtRawInt4Error, match="weight_format"):
+        kt.kt_rawint4_moe_workspace_bytes(bad, 7)
+    lib = _lib.load_library()
+    assert lib.kt_rawint4_moe_infer(ctypes.byref(bad), 4, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == -1
+    assert "weight_format" in kt.kt_rawint4_last_error()
+    assert lib.kt_rawint4_dequant_mxfp4(FAKE, FAKE, 4, 48, FAKE, None) == kt.KT_RAWINT4_EINVAL
+    named = kt.make_layer(8, 2, 512, 384, 8, 16.0, 2.0, *([FAKE] * 12), weight_format="mxfp4")
+    assert named.weight_format == kt.KT_RAWINT4_FORMAT_MXFP4
