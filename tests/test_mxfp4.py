@@ -236,3 +236,40 @@ def test_mxfp4_full_size_sampled(dev):
         except AssertionError as err:
             failures.append(str(err))
     assert not failures, "; ".join(failures)
+
+
+def test_mxfp4_zipf_full_size_recompute_and_inference(dev):
+    # the Zipf-routed workload (one expert with ~3500 rows) with an MXFP4 base:
+    # inference + recompute backward equal forward + backward bit for bit, and
+    # sampled tokens of the forward match the oracle
+    cfg = _mx(W.CONFIGS[3])
+    seed = W.config_seed(3)
+    _say(f"{cfg.name}: generating")
+    weights = W.make_weights(cfg, seed)
+    batch = W.make_batch(cfg, seed)
+    dl = dev.DeviceLayer(cfg, weights)
+    db = dev.DeviceBatch(batch)
+
+    def bits(t):
+        return t.contiguous().view(torch.int32 if t.dtype == torch.float32 else torch.int16).cpu().numpy()
+
+    _say(f"{cfg.name}: forward + backward")
+    ws = dl.workspace(db.qlen)
+    out = dl.forward(db.inputs, db.expert_ids, db.route_weights, ws)
+    g_ref = dl.grad_buffers(fill=0.0)
+    dx_ref, _ = dl.backward(db.inputs, db.expert_ids, db.route_weights, db.grad_output, ws, g_ref)
+    _say(f"{cfg.name}: inference + recompute backward")
+    out_inf = dl.infer(db.inputs, db.expert_ids, db.route_weights, dl.infer_workspace(db.qlen))
+    ws.fill_(0xFF)
+    g = dl.grad_buffers(fill=0.0)
+    dx, _ = dl.backward(db.inputs, db.expert_ids, db.route_weights, db.grad_output, ws, g, recompute=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out_inf), bits(out))
+    assert np.array_equal(bits(dx), bits(dx_ref))
+    for n in O.LORA_NAMES:
+        assert np.array_equal(bits(g[n]), bits(g_ref[n])), n
+    rng = np.random.default_rng(7373)
+    toks = np.unique(np.concatenate([[0, cfg.qlen - 1], rng.choice(cfg.qlen, 6, replace=False)]))
+    _say(f"{cfg.name}: oracle forward on tokens {toks.tolist()}")
+    ref = O.moe(cfg, weights, batch.inputs[toks], batch.expert_ids[toks], batch.route_weights[toks])
+    _close(f"{cfg.name}.forward", out.float().cpu().numpy()[toks], ref["out"])
