@@ -120,7 +120,7 @@ def main():
                          "the calibration kernel for hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (expert parallelism is designed, "
+        print("bench.py measures one GPU: the library has no multi-GPU path (expert parallelism is designed, "
               "not built); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
