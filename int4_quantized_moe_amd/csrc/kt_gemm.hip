@@ -593,11 +593,17 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
         decode(sl, bf);
         const uint8_t* st = ring + sl * kABytes;
         // gate/up and down dX: each activation fragment is read one group of
-        // MFMAs ahead, and the scheduler is asked for that order (measured
-        // faster for these two kinds only)
+        // MFMAs ahead, the scheduler is asked for that order, and the wave's
+        // priority is raised over its MFMAs (measured faster for these two
+        // kinds only)
         constexpr bool kAhead = (KIND == kGateUp || KIND == kDownBwd);
         u32x4 an{};
-        if constexpr (kAhead) an = *reinterpret_cast<const u32x4*>(st + a_off0);
+        if constexpr (kAhead) {
+          an = *reinterpret_cast<const u32x4*>(st + a_off0);
+          // while this wave issues its MFMAs it goes first (the other wave on
+          // the SIMD is decoding or copying): measured faster for these kinds
+          __builtin_amdgcn_s_setprio(2);
+        }
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -617,6 +623,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
               __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                              // then 4 MFMAs
             }
           }
+        if constexpr (kAhead) __builtin_amdgcn_s_setprio(0);
       }
     }
   }
