@@ -592,38 +592,25 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
         u32x4 bf[2][4];
         decode(sl, bf);
         const uint8_t* st = ring + sl * kABytes;
-        // gate/up and down dX: each activation fragment is read one group of
-        // MFMAs ahead, the scheduler is asked for that order, and the wave's
-        // priority is raised over its MFMAs (measured faster for these two
-        // kinds only)
-        constexpr bool kAhead = (KIND == kGateUp || KIND == kDownBwd);
-        u32x4 an{};
-        if constexpr (kAhead) {
-          an = *reinterpret_cast<const u32x4*>(st + a_off0);
-          // while this wave issues its MFMAs it goes first (the other wave on
-          // the SIMD is decoding or copying): measured faster for these kinds
-          __builtin_amdgcn_s_setprio(2);
-        }
+        // Each activation fragment is read one group of MFMAs ahead, the
+        // scheduler is asked for that order, and the wave's priority is raised
+        // over its MFMAs, so that the MFMA pipe gets the SIMD first while the
+        // other wave decodes or copies (measured faster in every kind).
+        u32x4 an = *reinterpret_cast<const u32x4*>(st + a_off0);
+        __builtin_amdgcn_s_setprio(2);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
-            u32x4 af;
-            if constexpr (kAhead) {
-              af = an;
-              const int nj = mb + 1 < MB ? j : j + 1, nmb = mb + 1 < MB ? mb + 1 : 0;
-              if (nj < 2) an = *reinterpret_cast<const u32x4*>(st + nmb * 2048 + (nj ? a_off1 : a_off0));
-            } else {
-              af = *reinterpret_cast<const u32x4*>(st + mb * 2048 + (j ? a_off1 : a_off0));
-            }
+            const u32x4 af = an;
+            const int nj = mb + 1 < MB ? j : j + 1, nmb = mb + 1 < MB ? mb + 1 : 0;
+            if (nj < 2) an = *reinterpret_cast<const u32x4*>(st + nmb * 2048 + (nj ? a_off1 : a_off0));
 #pragma unroll
             for (int f = 0; f < 4; ++f) acc[mb][f] = mfma_f16(af, bf[j][f], acc[mb][f]);
-            if constexpr (kAhead) {
-              if (j == 0 || mb + 1 < MB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-              __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                              // then 4 MFMAs
-            }
+            if (nj < 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);              // then 4 MFMAs
           }
-        if constexpr (kAhead) __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_s_setprio(0);
       }
     }
   }
