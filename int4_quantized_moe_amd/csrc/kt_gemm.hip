@@ -18,7 +18,10 @@
 // for 32/16-row tiles, whose fragments of the next stage are read and decoded
 // while the current one is multiplied.  The ring waits are explicit (vmcnt)
 // around a bare s_barrier, so the compiler's conservative drain at
-// __syncthreads does not serialise the ring.  Row tiles are dealt to the eight
+// __syncthreads does not serialise the ring.  In the 64/96/128-row tiles each
+// wave decodes a stage's weights, then runs its MFMAs at a raised wave priority
+// with every activation fragment read one group of MFMAs ahead: the SIMD's
+// other wave (another workgroup) decodes or copies in the gaps.  Row tiles are dealt to the eight
 // XCDs in turn (as blocks are), each XCD running all column tiles of its row
 // tiles: the column tiles of one row tile share that XCD's L2, and a heavily
 // loaded expert's row tiles spread over every XCD.
