@@ -66,8 +66,12 @@ def phase_work(cfg, slots):
 
 
 def cpu_baseline(cfg, weights, batch, target_s, infer=None):
-    """The oracle, as it stands, on the first n tokens of the same batch (forward
-    only for an inference run; zero LoRA for the base alone)."""
+    """The oracle, as it stands, on whole experts of the same batch: every slot routed
+    to the first n experts (other slots dropped), so that each expert's dequantisation
+    is shared by as many rows as at the full batch.  The oracle's time is linear in
+    the slots at a fixed rows-per-expert mix, so the workload's rate is the sample's
+    slots per second over the workload's slots per token.  Forward only for an
+    inference run; zero LoRA for the base alone."""
     import numpy as np
 
     import oracle as O
@@ -75,28 +79,35 @@ def cpu_baseline(cfg, weights, batch, target_s, infer=None):
     lora = None
     if infer == "base":
         lora = {n: np.zeros(s) for n, s in cfg.lora_shapes().items()}
+    ids_all = batch.expert_ids
+    total_slots = int(np.count_nonzero((ids_all >= 0) & (ids_all < cfg.num_experts)))
+    order = [int(e) for e in np.unique(ids_all[(ids_all >= 0) & (ids_all < cfg.num_experts)])]
 
     def run(n):
+        keep = order[:n]
+        rows = np.flatnonzero(np.isin(ids_all, keep).any(axis=1))
+        ids = np.where(np.isin(ids_all[rows], keep), ids_all[rows], -1).astype(np.int64)
+        slots = int(np.count_nonzero(ids >= 0))
         t0 = time.perf_counter()
-        O.moe(cfg, weights, batch.inputs[:n], batch.expert_ids[:n], batch.route_weights[:n],
-              None if infer else batch.grad_output[:n], lora=lora)
-        return time.perf_counter() - t0
+        O.moe(cfg, weights, batch.inputs[rows], ids, batch.route_weights[rows],
+              None if infer else batch.grad_output[rows], lora=lora)
+        return time.perf_counter() - t0, slots
 
-    n = min(8, cfg.qlen)
-    t = run(n)
-    log(f"cpu oracle pilot: {n} tokens in {t:.2f}s")
-    if t < target_s / 3 and n < cfg.qlen:
-        n = int(min(cfg.qlen, max(n, n * target_s / max(t, 1e-3))))
-        t = run(n)
-        log(f"cpu oracle sample: {n} tokens in {t:.2f}s")
-    active = int(np.unique(batch.expert_ids[:n]).size)
+    n = 1
+    t, slots = run(n)
+    log(f"cpu oracle pilot: 1 expert ({slots} slots) in {t:.2f}s")
+    if t < target_s / 3 and n < len(order):
+        n = int(min(len(order), max(1, target_s / max(t, 1e-3))))
+        t, slots = run(n)
+        log(f"cpu oracle sample: {n} experts ({slots} slots) in {t:.2f}s")
     return {
-        "value": n / t,
+        "value": slots / t * cfg.qlen / total_slots,
         "unit": "tokens/s",
         "cores": O.num_threads(),
         "kind": "oracle",
-        "sample": f"first {n} of {cfg.qlen} tokens ({n * cfg.top_k} token-slots, {active} active experts), "
-                  f"{'forward' if infer else 'fwd+bwd'}, fp64 accumulation, {t:.1f} s wall",
+        "sample": f"every slot of {n} of {len(order)} active experts ({slots} of {total_slots} token-slots), "
+                  f"{'forward' if infer else 'fwd+bwd'}, fp64 accumulation, {t:.1f} s wall; tokens/s = "
+                  f"sample slots per second x qlen / all slots",
     }
 
 
@@ -151,7 +162,7 @@ def main():
     if args.infer:
         ws = dl.infer_workspace(db.qlen)
 
-        def step():
+        def step(mid=None):
             dl.infer(db.inputs, db.expert_ids, db.route_weights, ws, output=out, stream=stream)
     else:
         ws = dl.workspace(db.qlen)
@@ -161,11 +172,13 @@ def main():
 
         ws_fwd = dl.infer_workspace(db.qlen) if args.recompute else ws
 
-        def step():
+        def step(mid=None):
             if args.recompute:
                 dl.infer(db.inputs, db.expert_ids, db.route_weights, ws_fwd, output=out, stream=stream)
             else:
                 dl.forward(db.inputs, db.expert_ids, db.route_weights, ws, output=out, stream=stream)
+            if mid is not None:
+                mid.record(stream)
             dl.backward(db.inputs, db.expert_ids, db.route_weights, db.grad_output, ws, grads, accumulate=False,
                         grad_scale=1.0, grad_input=dx, grad_route=droute, stream=stream, recompute=args.recompute)
     log(f"workspace {ws.numel() / 2**30:.2f} GiB")
@@ -177,13 +190,17 @@ def main():
     _lib.kt_rawint4_profile_read()  # drop anything recorded before
     _lib.kt_rawint4_profile_enable(True)
     log(f"timing {args.steps} steps")
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one event at each step boundary and one between its forward and its backward
+    # (all on the stream every kernel is launched on)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    mids = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    start, stop = marks[0], marks[-1]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
-    for _ in range(args.steps):
-        step()
-    stop.record(stream)
+    for i in range(args.steps):
+        step(None if args.infer else mids[i])
+        marks[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     _lib.kt_rawint4_profile_enable(False)
@@ -192,6 +209,12 @@ def main():
     ms_per_step = gpu_ms / args.steps
     value = db.qlen * args.steps / (gpu_ms / 1e3)
     log(f"{ms_per_step:.3f} ms/step (wall {1e3 * wall / args.steps:.3f}), {value:.1f} tokens/s")
+    if args.infer:
+        t_fwd, t_bwd = ms_per_step, 0.0
+    else:
+        t_fwd = sum(marks[i].elapsed_time(mids[i]) for i in range(args.steps)) / args.steps
+        t_bwd = sum(mids[i].elapsed_time(marks[i + 1]) for i in range(args.steps)) / args.steps
+        log(f"forward {t_fwd:.3f} ms, backward {t_bwd:.3f} ms per step")
 
     slots = int(np.count_nonzero((batch.expert_ids >= 0) & (batch.expert_ids < cfg.num_experts)))
     active = int(np.unique(batch.expert_ids).size)
@@ -219,7 +242,9 @@ def main():
     mode = f"_infer_{args.infer}" if args.infer else ("_recompute" if args.recompute else "")
     measured = profsum.read_traffic(os.path.join(ROOT, "profiles", f"hbm_traffic_{dom}_{cfg.name}{mode}.txt"))
     traffic = None if measured is None else int(round(measured["read"] + measured["write"]))
-    roof.update({"kernel": dom, "achieved": round(achieved, 2), "peak": peak, "frac": round(achieved / peak, 4),
+    roof.update({"scope": f"one kernel: {dom}, the phase with the largest time per launch (the step as a whole "
+                          "is under roofline_step)",
+                 "kernel": dom, "achieved": round(achieved, 2), "peak": peak, "frac": round(achieved / peak, 4),
                  "traffic": traffic, "avg_ms": round(dom_ms, 4)})
     if args.infer:  # the forward alone: gate/up and down, with their LoRA terms unless the base runs alone
         r = cfg.rank if args.infer == "lora" else 0
@@ -228,6 +253,13 @@ def main():
     else:
         total_flops = slots * (12 * cfg.hidden * cfg.intermediate + 18 * cfg.rank * (cfg.hidden + cfg.intermediate))
         total_wbytes = 2 * 3 * active * (cfg.hidden * cfg.intermediate // 2 + cfg.hidden * cfg.intermediate // 16)
+    # the step against the roofline that bounds it (the same flop-per-byte test as for one kernel)
+    if total_flops / max(total_wbytes, 1) > PEAK_MFMA_FP16 / PEAK_HBM:
+        step_bound, step_achieved = "mfma", total_flops / (ms_per_step / 1e3) / 1e12
+        step_frac = step_achieved * 1e12 / PEAK_MFMA_FP16
+    else:
+        step_bound, step_achieved = "hbm", total_wbytes / (ms_per_step / 1e3) / 1e9
+        step_frac = step_achieved * 1e9 / PEAK_HBM
     log(f"step: {total_flops / (ms_per_step / 1e3) / 1e12:.1f} TFLOP/s "
         f"({100 * total_flops / (ms_per_step / 1e3) / PEAK_MFMA_FP16:.2f}% MFMA), packed weights "
         f"{total_wbytes / (ms_per_step / 1e3) / 1e9:.1f} GB/s ({100 * total_wbytes / (ms_per_step / 1e3) / PEAK_HBM:.2f}% HBM)")
@@ -268,8 +300,16 @@ def main():
                       if args.infer else {}),
                    **({"mode": "checkpoint recompute (inference forward + recompute backward)"}
                       if args.recompute else {})},
+        "t_fwd_ms": round(t_fwd, 4),
+        "t_bwd_ms": round(t_bwd, 4),
         "mfma_frac_step": round(total_flops / (ms_per_step / 1e3) / PEAK_MFMA_FP16, 4),
         "hbm_frac_step": round(total_wbytes / (ms_per_step / 1e3) / PEAK_HBM, 4),
+        "roofline_step": {"bound": step_bound, "unit": "TFLOP/s" if step_bound == "mfma" else "GB/s",
+                          "achieved": round(step_achieved, 2),
+                          "peak": PEAK_MFMA_FP16 / 1e12 if step_bound == "mfma" else PEAK_HBM / 1e9,
+                          "frac": round(step_frac, 4),
+                          "work": "algorithmic flops of the whole step" if step_bound == "mfma"
+                                  else "packed weights and scales of the active experts, once per pass"},
         "phase_ms_per_step": per_step,
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -196,10 +196,28 @@ static int check_workspace(void* ws, size_t bytes, size_t need) {
   return KT_RAWINT4_OK;
 }
 
-static int launched() {
+static thread_local hipError_t g_first_launch_error = hipSuccess;
+
+void begin_launches() {
+  (void)hipGetLastError();
+  g_first_launch_error = hipSuccess;
+}
+
+void note_launch() {
   const hipError_t err = hipGetLastError();
-  if (err != hipSuccess) {
-    g_last_error = std::string("HIP launch failed: ") + hipGetErrorString(err);
+  if (err != hipSuccess && g_first_launch_error == hipSuccess) g_first_launch_error = err;
+}
+
+hipError_t first_launch_error() { return g_first_launch_error; }
+
+// The result of an entry point's launches (and of a HIP call whose error it
+// already took, err): the first failure since begin_launches.
+static int launched(hipError_t err = hipSuccess) {
+  note_launch();
+  if (g_first_launch_error == hipSuccess && err != hipSuccess) g_first_launch_error = err;
+  if (g_first_launch_error != hipSuccess) {
+    g_last_error = std::string("HIP launch failed: ") + hipGetErrorString(g_first_launch_error);
+    g_first_launch_error = hipSuccess;
     return KT_RAWINT4_EHIP;
   }
   g_last_error.clear();
@@ -399,6 +417,7 @@ static int run_forward(const kt_rawint4_moe_layer* layer, Dims d, const uint16_t
   hipStream_t st = static_cast<hipStream_t>(stream);
   const LayerPtrs L = layer_ptrs(layer);
   void* ws = workspace;
+  begin_launches();
   launch_forward_front(layer, d, w, ws, L, inputs, expert_ids, route_weights, st);
   {
     PhaseScope ph(kPhGemmDown, st);
@@ -458,6 +477,7 @@ static int run_backward(const kt_rawint4_moe_layer* layer, int32_t qlen, const u
   const int64_t gsz[6] = {d.E * d.R * d.H, d.E * d.I * d.R, d.E * d.R * d.H,
                           d.E * d.I * d.R, d.E * d.R * d.I, d.E * d.H * d.R};
   if (qlen == 0) {
+    begin_launches();
     if (!accumulate)
       for (int j = 0; j < 6; ++j) launch_fill_zero_f32(grads[j], gsz[j], st);
     return launched();
@@ -472,6 +492,7 @@ static int run_backward(const kt_rawint4_moe_layer* layer, int32_t qlen, const u
   if (rc) return rc;
   const LayerPtrs L = layer_ptrs(layer);
   void* ws = workspace;
+  begin_launches();
   if (recompute) launch_forward_front(layer, d, w, ws, L, inputs, expert_ids, route_weights, st);
 
   {
@@ -546,6 +567,7 @@ int kt_rawint4_moe_bwd_recompute(const kt_rawint4_moe_layer* layer, int32_t qlen
 int kt_rawint4_unpack(const uint8_t* packed, int64_t n, int64_t k, int8_t* codes, void* stream) {
   if (n < 0 || k < 0 || k % 2) return fail(KT_RAWINT4_EINVAL, "n must be >= 0 and k a non-negative even number");
   if (n * k > 0 && (!packed || !codes)) return fail(KT_RAWINT4_EINVAL, "packed and codes must be non-NULL");
+  begin_launches();
   launch_unpack(packed, n, k, codes, static_cast<hipStream_t>(stream));
   return launched();
 }
@@ -557,6 +579,7 @@ int kt_rawint4_dequant(const uint8_t* packed, const uint16_t* scales, int64_t n,
   if (n * k > 0 && (!packed || !scales || !weights))
     return fail(KT_RAWINT4_EINVAL, "packed, scales and weights must be non-NULL");
   if (!aligned(packed, 4)) return fail(KT_RAWINT4_EINVAL, "packed must be 4-byte aligned");
+  begin_launches();
   launch_dequant(packed, scales, n, k, KT_RAWINT4_FORMAT_RAWINT4, weights, static_cast<hipStream_t>(stream));
   return launched();
 }
@@ -568,6 +591,7 @@ int kt_rawint4_dequant_mxfp4(const uint8_t* packed, const uint16_t* scales, int6
   if (n * k > 0 && (!packed || !scales || !weights))
     return fail(KT_RAWINT4_EINVAL, "packed, scales and weights must be non-NULL");
   if (!aligned(packed, 4)) return fail(KT_RAWINT4_EINVAL, "packed must be 4-byte aligned");
+  begin_launches();
   launch_dequant(packed, scales, n, k, KT_RAWINT4_FORMAT_MXFP4, weights, static_cast<hipStream_t>(stream));
   return launched();
 }
@@ -596,15 +620,15 @@ int kt_rawint4_group(const int64_t* expert_ids, int32_t qlen, int32_t top_k, int
   d.K = top_k;
   d.qlen = qlen;
   d.Ms = (int64_t)qlen * top_k;
+  begin_launches();
   launch_init_counters(workspace, w, st);
   launch_group(d, w, workspace, expert_ids, st);
-  if (hipMemcpyAsync(offsets, ws_ptr<int32_t>(workspace, w.offsets), sizeof(int32_t) * (size_t)(num_experts + 1),
-                     hipMemcpyDeviceToDevice, st) != hipSuccess)
-    return launched();
-  if (d.Ms > 0 && hipMemcpyAsync(sorted_slot, ws_ptr<int32_t>(workspace, w.sorted_slot), sizeof(int32_t) * (size_t)d.Ms,
-                                 hipMemcpyDeviceToDevice, st) != hipSuccess)
-    return launched();
-  return launched();
+  hipError_t err = hipMemcpyAsync(offsets, ws_ptr<int32_t>(workspace, w.offsets),
+                                  sizeof(int32_t) * (size_t)(num_experts + 1), hipMemcpyDeviceToDevice, st);
+  if (err == hipSuccess && d.Ms > 0)
+    err = hipMemcpyAsync(sorted_slot, ws_ptr<int32_t>(workspace, w.sorted_slot), sizeof(int32_t) * (size_t)d.Ms,
+                         hipMemcpyDeviceToDevice, st);
+  return launched(err);
 }
 
 int kt_rawint4_moe_diagnostics(const void* workspace, size_t workspace_bytes, int64_t* bad_ids, int64_t* bad_scales,
@@ -614,9 +638,10 @@ int kt_rawint4_moe_diagnostics(const void* workspace, size_t workspace_bytes, in
     return fail(KT_RAWINT4_EWORKSPACE, "workspace is smaller than the counter block");
   unsigned long long host[kNumCounters];
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (hipMemcpyAsync(host, workspace, sizeof(host), hipMemcpyDeviceToHost, st) != hipSuccess ||
-      hipStreamSynchronize(st) != hipSuccess)
-    return launched();
+  begin_launches();
+  hipError_t err = hipMemcpyAsync(host, workspace, sizeof(host), hipMemcpyDeviceToHost, st);
+  if (err == hipSuccess) err = hipStreamSynchronize(st);
+  if (err != hipSuccess) return launched(err);
   if (bad_ids) *bad_ids = (int64_t)host[kBadIds];
   if (bad_scales) *bad_scales = (int64_t)host[kBadScales];
   g_last_error.clear();
@@ -636,6 +661,7 @@ int kt_rawint4_moe_saved_preactivations(const kt_rawint4_moe_layer* layer, int32
   const WsMap w = plan_workspace(d);
   rc = check_workspace(const_cast<void*>(workspace), workspace_bytes, w.total);
   if (rc) return rc;
+  begin_launches();
   launch_saved_preact(d, w, workspace, gate, up, static_cast<hipStream_t>(stream));
   return launched();
 }

@@ -58,7 +58,10 @@ __global__ __launch_bounds__(256) void k_rows_to_half(const uint16_t* __restrict
 
 void launch_rows_to_half(const uint16_t* src, int64_t rows, int64_t cols, uint16_t* dst, int32_t* exps,
                          hipStream_t st) {
-  if (rows > 0) k_rows_to_half<<<(unsigned)rows, 256, 0, st>>>(src, cols, dst, exps);
+  if (rows > 0) {
+    k_rows_to_half<<<(unsigned)rows, 256, 0, st>>>(src, cols, dst, exps);
+    note_launch();
+  }
 }
 
 // ---------------------------------------------------------------- scales for the expert GEMMs
@@ -147,6 +150,7 @@ void launch_scales_t(const uint16_t* s, int64_t E, int64_t rows, int64_t G, cons
   if (E <= 0 || rows <= 0 || G <= 0) return;
   dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((G + 63) / 64), (unsigned)E);
   k_scales_t<<<grid, 256, 0, st>>>(s, rows, G, offsets, out, bad, fmt);
+  note_launch();
 }
 
 // ---------------------------------------------------------------- one exponent per row
@@ -189,8 +193,10 @@ __global__ __launch_bounds__(256) void k_normalize_chunks(uint16_t* __restrict__
 
 void launch_normalize_chunks(uint16_t* buf, int32_t* exps, const int32_t* nrows, int64_t max_rows, int64_t cols,
                              int64_t split, int nch, int chunkw, hipStream_t st) {
-  if (max_rows > 0)
+  if (max_rows > 0) {
     k_normalize_chunks<<<(unsigned)((max_rows + 3) / 4), 256, 0, st>>>(buf, exps, nrows, cols, split, nch, chunkw);
+    note_launch();
+  }
 }
 
 __global__ void k_fill_zero(float* p, int64_t n) {
@@ -199,7 +205,10 @@ __global__ void k_fill_zero(float* p, int64_t n) {
 }
 
 void launch_fill_zero_f32(float* p, int64_t n, hipStream_t st) {
-  if (n > 0) k_fill_zero<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(p, n);
+  if (n > 0) {
+    k_fill_zero<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(p, n);
+    note_launch();
+  }
 }
 
 // ---------------------------------------------------------------- combine and dRoute
@@ -242,6 +251,7 @@ void launch_combine(const Dims& d, const uint16_t* stage, const int32_t* stexp, 
   if (d.qlen == 0) return;
   dim3 grid((unsigned)d.qlen, (unsigned)((d.H / 8 + 255) / 256));
   k_combine<<<grid, 256, 0, st>>>(stage, stexp, st_nch, ids, (int)d.K, (int)d.E, d.H, out);
+  note_launch();
 }
 
 __global__ void k_droute(const int32_t* __restrict__ row_of_slot, const float* __restrict__ drpart, int64_t Ms,
@@ -260,6 +270,7 @@ void launch_droute(const Dims& d, const WsMap& w, void* ws, float* grad_route, h
   k_droute<<<(unsigned)((d.Ms + 255) / 256), 256, 0, st>>>(ws_ptr<int32_t>(ws, w.row_of_slot),
                                                            ws_ptr<float>(ws, w.drpart), d.Ms, (int)w.dr_nt,
                                                            grad_route);
+  note_launch();
 }
 
 // gate/up pre-activations the forward saved (quad-row layout: row m of expert e
@@ -298,6 +309,7 @@ void launch_saved_preact(const Dims& d, const WsMap& w, const void* ws, float* g
                                                  ws_ptr<int32_t>(base, w.qoffsets), (int)d.E,
                                                  ws_ptr<float>(base, w.g), ws_ptr<float>(base, w.u), d.I, gate,
                                                  up);
+  note_launch();
 }
 
 // ---------------------------------------------------------------- codec hooks
@@ -312,10 +324,15 @@ __global__ void k_unpack(const uint8_t* __restrict__ packed, int64_t nbytes, int
 
 void launch_unpack(const uint8_t* packed, int64_t n, int64_t k, int8_t* codes, hipStream_t st) {
   const int64_t nbytes = n * (k / 2);
-  if (nbytes > 0) k_unpack<<<(unsigned)((nbytes + 255) / 256), 256, 0, st>>>(packed, nbytes, codes);
+  if (nbytes > 0) {
+    k_unpack<<<(unsigned)((nbytes + 255) / 256), 256, 0, st>>>(packed, nbytes, codes);
+    note_launch();
+  }
 }
 
-// the matrix kernels' decoder: one packed dword -> 8 fp16 values -> fp32
+// the matrix kernels' decoders: one packed dword -> 8 fp16 values -> fp32, by
+// the stored-orientation decoder and the transposed one (one scale for the
+// whole dword here); a dword where they disagree comes out as NaN
 __global__ void k_dequant(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales, int64_t n,
                           int64_t k, int fmt, float* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // dword index
@@ -334,7 +351,11 @@ __global__ void k_dequant(const uint8_t* __restrict__ packed, const uint16_t* __
     const u32x4 t = decode_dword_perm_e2m1(wv, s2, s2, s2, s2);
     if (t.x != r.x || t.y != r.y || t.z != r.z || t.w != r.w) r = u32x4{0x7e007e00u, 0x7e007e00u, 0x7e007e00u, 0x7e007e00u};
   } else {
-    r = decode_dword_fma(wv, s2 * (half2_t){16.f16, 16.f16}, s2 * (half2_t){-24.f16, -24.f16}, decode_consts());
+    // the RAWINT4 decoders of both orientations, likewise
+    const DecodeConsts dc = decode_consts();
+    r = decode_dword_fma(wv, s2 * (half2_t){16.f16, 16.f16}, s2 * (half2_t){-24.f16, -24.f16}, dc);
+    const u32x4 t = decode_dword_perm(wv, s2, s2, s2, s2, dc);
+    if (t.x != r.x || t.y != r.y || t.z != r.z || t.w != r.w) r = u32x4{0x7e007e00u, 0x7e007e00u, 0x7e007e00u, 0x7e007e00u};
   }
   const uint32_t words[4] = {r.x, r.y, r.z, r.w};  // (k0, k4), (k1, k5), (k2, k6), (k3, k7)
   float* o = out + row * k + d * 8;
@@ -348,7 +369,10 @@ __global__ void k_dequant(const uint8_t* __restrict__ packed, const uint16_t* __
 void launch_dequant(const uint8_t* packed, const uint16_t* scales, int64_t n, int64_t k, int fmt, float* out,
                     hipStream_t st) {
   const int64_t total = n * (k / 8);
-  if (total > 0) k_dequant<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(packed, scales, n, k, fmt, out);
+  if (total > 0) {
+    k_dequant<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(packed, scales, n, k, fmt, out);
+    note_launch();
+  }
 }
 
 }  // namespace kt

@@ -268,18 +268,29 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // Issued from asm so that the compiler, which cannot tell which ring slot a
 // later LDS read touches, does not drain every outstanding copy before it; the
 // ring's explicit vmcnt waits order the copies and the reads instead.  M0 is
-// not used by anything else in these kernels.
+// declared clobbered, so the compiler keeps no value of its own in it across
+// a copy (it treats M0 as reserved and warns about naming it; the warning is
+// for a save and restore the kernels do not need).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
   // one wait state between the M0 write and the load that reads it
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(base) : "memory");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(base)
+               : "memory", "m0");
 }
 
 // 4 bytes from global memory to LDS: lane l's bytes land at lds_base + 4 * l.
 __device__ __forceinline__ void dma4(const void* g, uint32_t lds_base) {
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(g), "s"(base) : "memory");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(g), "s"(base)
+               : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // s_waitcnt with vmcnt <= N and lgkmcnt == 0 (gfx9 encoding: vmcnt in bits 3:0
 // and 15:14, expcnt in 6:4 left at its maximum, lgkmcnt in 11:8)

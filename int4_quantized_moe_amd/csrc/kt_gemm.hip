@@ -1108,6 +1108,7 @@ static void launch_kind(bool ldma, bool mx, unsigned grid, const GemmParams& p, 
     else
       k_gemm<KIND, false, false><<<grid, 256, 0, st>>>(p);
   }
+  note_launch();
 }
 
 void launch_gemm(GemmKind kind, const Dims& d, const WsMap& w, void* ws, const LayerPtrs& L,

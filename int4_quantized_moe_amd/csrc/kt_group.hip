@@ -172,6 +172,7 @@ __global__ __launch_bounds__(256) void k_group_place(const int64_t* __restrict__
 
 void launch_init_counters(void* ws, const WsMap& w, hipStream_t st) {
   k_init_counters<<<1, 64, 0, st>>>(ws_ptr<unsigned long long>(ws, w.counters));
+  note_launch();
 }
 
 void launch_group(const Dims& d, const WsMap& w, void* ws, const int64_t* ids, hipStream_t st) {
@@ -179,17 +180,23 @@ void launch_group(const Dims& d, const WsMap& w, void* ws, const int64_t* ids, h
   int32_t* blockcnt = ws_ptr<int32_t>(ws, w.blockcnt);
   unsigned long long* counters = ws_ptr<unsigned long long>(ws, w.counters);
   const size_t lds = sizeof(int32_t) * (size_t)E;
-  if (w.nb > 0) k_group_count<<<(unsigned)w.nb, 256, lds, st>>>(ids, d.Ms, E, blockcnt, counters);
+  if (w.nb > 0) {
+    k_group_count<<<(unsigned)w.nb, 256, lds, st>>>(ids, d.Ms, E, blockcnt, counters);
+    note_launch();
+  }
   k_group_scan<<<1, 1024, 0, st>>>(E, w.nb, (int)w.mt, (int)w.gbulk, w.gmixed ? 1 : 0, blockcnt,
                                    ws_ptr<int32_t>(ws, w.counts), ws_ptr<int32_t>(ws, w.offsets),
                                    ws_ptr<int32_t>(ws, w.qoffsets), ws_ptr<int32_t>(ws, w.tile_e), ws_ptr<int32_t>(ws, w.tile_m0),
                                    ws_ptr<int32_t>(ws, w.gtile_e), ws_ptr<int32_t>(ws, w.gtile_m0),
                                    ws_ptr<int32_t>(ws, w.gtile_mt), counters);
-  if (w.nb > 0)
+  note_launch();
+  if (w.nb > 0) {
     k_group_place<<<(unsigned)w.nb, 256, lds, st>>>(ids, d.Ms, E, (int)d.K, blockcnt,
                                                    ws_ptr<int32_t>(ws, w.sorted_slot),
                                                    ws_ptr<int32_t>(ws, w.row_of_slot),
                                                    ws_ptr<int32_t>(ws, w.tok_of_row));
+    note_launch();
+  }
 }
 
 }  // namespace kt

@@ -142,6 +142,17 @@ inline T* ws_ptr(void* base, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(base) + off);
 }
 
+// ---------------------------------------------------------------- launch errors
+
+// Every kernel launch is followed by note_launch(), which keeps the first
+// launch error of the current entry-point call (hipGetLastError right after
+// the launch, so no later success hides it); begin_launches() clears it and
+// any error left by an earlier call before the first launch, and
+// first_launch_error() reports it at the end.
+void begin_launches();
+void note_launch();
+hipError_t first_launch_error();
+
 // ---------------------------------------------------------------- launchers (enqueue only)
 
 void launch_group(const Dims& d, const WsMap& w, void* ws, const int64_t* ids, hipStream_t st);

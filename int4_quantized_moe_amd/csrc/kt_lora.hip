@@ -336,6 +336,7 @@ static void launch_side_nb(bool half, dim3 grid, const SideArgs& a, hipStream_t 
     k_lora_side<MT, NB, true><<<grid, 256, 0, st>>>(a);
   else
     k_lora_side<MT, NB, false><<<grid, 256, 0, st>>>(a);
+  note_launch();
 }
 
 template <int MT>
@@ -406,6 +407,7 @@ void launch_lora_rowproj(const Dims& d, const WsMap& w, void* ws, const RowView&
   if (a.ksplit > 1) {
     const int64_t n = d.Ms * a.nq;
     k_side_reduce<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(a);
+    note_launch();
   }
 }
 
@@ -820,15 +822,19 @@ static void launch_grad_family(int nut, unsigned grid, const GradArgs& a, hipStr
   switch (nut) {
     case 16:
       k_lora_grad<16, FAM, 4><<<grid, 256, 0, st>>>(a);
+      note_launch();
       break;
     case 32:
       k_lora_grad<32, FAM, 4><<<grid, 256, 0, st>>>(a);
+      note_launch();
       break;
     case 64:
       k_lora_grad<64, FAM, 4><<<grid, 256, 0, st>>>(a);
+      note_launch();
       break;
     default:  // 8 waves: the 128-column narrow block and a three-step ring take one CU's LDS
       k_lora_grad<128, FAM, 8><<<grid, 512, 0, st>>>(a);
+      note_launch();
       break;
   }
 }
@@ -871,9 +877,16 @@ void launch_lora_grads(const Dims& d, const WsMap& w, void* ws, const uint16_t* 
   p.E = (int)d.E;
   p.eorder = ws_ptr<int32_t>(ws, w.eorder);
   p.gtmax = ws_ptr<int32_t>(ws, w.gtmax);
-  if (w.max_tiles > 0) k_grad_tile_max<<<(unsigned)w.max_tiles, 256, 0, st>>>(p);
+  if (w.max_tiles > 0) {
+    k_grad_tile_max<<<(unsigned)w.max_tiles, 256, 0, st>>>(p);
+    note_launch();
+  }
   k_grad_exps<<<(unsigned)d.E, 256, 0, st>>>(p);
-  if (w.max_tiles > 0) k_grad_planes<<<(unsigned)w.max_tiles, 256, 0, st>>>(p);
+  note_launch();
+  if (w.max_tiles > 0) {
+    k_grad_planes<<<(unsigned)w.max_tiles, 256, 0, st>>>(p);
+    note_launch();
+  }
 
   GradArgs a{};
   a.E = (int)d.E;

@@ -41,7 +41,8 @@
  *   - the LoRA scale is alpha / rank;
  *   - a pre-activation on a clamp bound to within the accuracy of the
  *     computation being checked has no unique mask; orc_moe_decided lets the
- *     caller fix the side there (and only there).
+ *     caller fix the side there (and only there), within a band it gives or
+ *     within the a priori error bound of an fp32 computation (preact_bound).
  *
  * Loop order: experts outermost; each active expert is dequantised once and its
  * routed slots are processed together, parallel over output features.  Every
@@ -254,6 +255,36 @@ static void clamp_up(double u, double side, double limit, double* clamped, doubl
   }
 }
 
+/* ---------------------------------------------------------------- a priori error bound
+
+ * How far an fp32 computation of a gate/up pre-activation may lie from the
+ * exact value, before any knowledge of its result.  The computation is taken
+ * to form the base products w x exactly (the decoded weights and the
+ * activations are exact in its arithmetic), the LoRA factors with a relative
+ * error of at most 2^-13 each, and to add everything in fp32 in any order.
+ * The fp32 sums use the probabilistic bound of Higham and Mary ("A new
+ * approach to probabilistic rounding error analysis", SIAM J. Sci. Comput.
+ * 41(5), 2019, Theorem 2.4): the sum of n terms lies within
+ * gamma(n) = exp(lambda sqrt(n) u + n u^2 / (1 - u)) - 1 times the sum of
+ * their magnitudes, with probability at least 1 - 2 n exp(-lambda^2 (1 - u)^2 / 2)
+ * (u = 2^-24; lambda = 8 makes that 1 - 1.8e-10 at n = 7168).  So, for
+ * g = sum_k w_k x_k + sc sum_q B_q a_q with a_q = sum_k A_qk x_k:
+ *
+ *   bound = u |g|                                   (the oracle's own fp32 rounding)
+ *         + gamma(K + R + 1) (sum_k |w_k x_k| + sc sum_q |B_q a_q|)
+ *         + 2^-12 sc (sum_q |B_q a_q| + sum_q |B_q| sum_k |A_qk x_k|)
+ *
+ * the last line covering the relative errors of the LoRA factors (two per
+ * product of the B term; the A products' errors carried through B). */
+static double gamma_prob(double n) {
+  const double u = 0x1p-24, lambda = 8.0;
+  return expm1(lambda * sqrt(n) * u + n * u * u / (1.0 - u));
+}
+
+static double preact_bound(double g, double sw, double sb, double sab, double sc, int64_t K, int64_t R) {
+  return 0x1p-24 * fabs(g) + gamma_prob((double)(K + R + 1)) * (sw + sc * sb) + 0x1p-12 * sc * (sb + sab);
+}
+
 /* ---------------------------------------------------------------- dense helpers */
 
 static double dot_dd(const double* a, const double* b, int64_t n) {
@@ -266,6 +297,17 @@ static double dot_fd(const float* a, const double* b, int64_t n) {
   double acc = 0.0;
 #pragma omp simd reduction(+ : acc)
   for (int64_t i = 0; i < n; ++i) acc += (double)a[i] * b[i];
+  return acc;
+}
+/* sums of the magnitudes of the products (for the error bound) */
+static double absdot_dd(const double* a, const double* b, int64_t n) {
+  double acc = 0.0;
+  for (int64_t i = 0; i < n; ++i) acc += fabs(a[i] * b[i]);
+  return acc;
+}
+static double absdot_fd(const float* a, const double* b, int64_t n) {
+  double acc = 0.0;
+  for (int64_t i = 0; i < n; ++i) acc += fabs((double)a[i] * b[i]);
   return acc;
 }
 
@@ -325,13 +367,16 @@ static void transposed_products(const float* W, int64_t Rn, int64_t C, const dou
  * order, the pre-activations that computation found), an element whose own
  * value lies within `band` of a bound takes its decision from the supplied
  * value; everywhere else, and with NULL, the oracle decides on its own value.
+ * A negative `band` means each element's own a priori bound (preact_bound).
  * pre_g / pre_u, when given ([qlen * top_k][I], slot order), receive the
- * oracle's own pre-activations of every valid slot (other rows untouched).
+ * oracle's own pre-activations of every valid slot (other rows untouched), and
+ * bnd_g / bnd_u their a priori bounds.
  */
 int orc_moe_decided(const orc_layer* L, int64_t qlen, const double* x, const int64_t* ids, const double* rw,
                     const double* dy, double* out, double* dx, double* droute, double* d_gate_a, double* d_gate_b,
                     double* d_up_a, double* d_up_b, double* d_down_a, double* d_down_b, const double* side_g,
-                    const double* side_u, double band, double* pre_g, double* pre_u) {
+                    const double* side_u, double band, double* pre_g, double* pre_u, double* bnd_g,
+                    double* bnd_u) {
   if (!L || qlen < 0) return -1;
   const int64_t E = L->num_experts, K = L->top_k, H = L->hidden, I = L->intermediate, R = L->rank;
   if (E < 1 || K < 1 || R < 1 || H % ORC_GROUP_SIZE || I % ORC_GROUP_SIZE || H <= 0 || I <= 0) return -1;
@@ -393,9 +438,13 @@ int orc_moe_decided(const orc_layer* L, int64_t qlen, const double* x, const int
     double* mg = (double*)malloc(sizeof(double) * (size_t)(m * I));
     double* mu = (double*)malloc(sizeof(double) * (size_t)(m * I));
     double* hh = (double*)malloc(sizeof(double) * (size_t)(m * I));
-    if (!ua || !ub || !ud || !gp || !upc || !mg || !mu || !hh) {
+    /* a priori bounds: sum_k |A_qk x_k| per slot row and rank index */
+    const int need_bound = band < 0 || bnd_g || bnd_u;
+    double* sag = need_bound ? (double*)malloc(sizeof(double) * (size_t)(m * R)) : NULL;
+    double* sau = need_bound ? (double*)malloc(sizeof(double) * (size_t)(m * R)) : NULL;
+    if (!ua || !ub || !ud || !gp || !upc || !mg || !mu || !hh || (need_bound && (!sag || !sau))) {
       status = -9;
-      free(ua); free(ub); free(ud); free(gp); free(upc); free(mg); free(mu); free(hh);
+      free(ua); free(ub); free(ud); free(gp); free(upc); free(mg); free(mu); free(hh); free(sag); free(sau);
       goto done;
     }
 
@@ -406,6 +455,10 @@ int orc_moe_decided(const orc_layer* L, int64_t qlen, const double* x, const int
       const double* xt = x + (rows[j] / K) * H;
       ua[jq] = fp32_round(fr, dot_dd(ag + q * H, xt, H));
       ub[jq] = fp32_round(fr, dot_dd(au + q * H, xt, H));
+      if (need_bound) {
+        sag[jq] = absdot_dd(ag + q * H, xt, H);
+        sau[jq] = absdot_dd(au + q * H, xt, H);
+      }
     }
     /* gate/up pre-activations, clamp, h */
 #pragma omp parallel for schedule(static)
@@ -420,10 +473,28 @@ int orc_moe_decided(const orc_layer* L, int64_t qlen, const double* x, const int
         const int64_t sidx = (int64_t)rows[j] * I + n;
         if (pre_g) pre_g[sidx] = g;
         if (pre_u) pre_u[sidx] = u;
-        /* within `band` of a bound the mask is not unique: take the supplied side */
-        const double sg = (side_g && limit > 0 && fabs(g - limit) <= band) ? side_g[sidx] : g;
+        double band_g = band, band_u = band;
+        if (need_bound) {
+          double sab_g = 0.0, sab_u = 0.0;
+          for (int64_t q = 0; q < R; ++q) {
+            sab_g += fabs(bg[n * R + q]) * sag[j * R + q];
+            sab_u += fabs(bu[n * R + q]) * sau[j * R + q];
+          }
+          const double bg_e = preact_bound(g, absdot_fd(wg + n * H, xt, H), absdot_dd(bg + n * R, ua + j * R, R),
+                                           sab_g, sc, H, R);
+          const double bu_e = preact_bound(u, absdot_fd(wu + n * H, xt, H), absdot_dd(bu + n * R, ub + j * R, R),
+                                           sab_u, sc, H, R);
+          if (bnd_g) bnd_g[sidx] = bg_e;
+          if (bnd_u) bnd_u[sidx] = bu_e;
+          if (band < 0) {
+            band_g = bg_e;
+            band_u = bu_e;
+          }
+        }
+        /* within the band of a bound the mask is not unique: take the supplied side */
+        const double sg = (side_g && limit > 0 && fabs(g - limit) <= band_g) ? side_g[sidx] : g;
         const double su =
-            (side_u && limit > 0 && (fabs(u - limit) <= band || fabs(u + limit) <= band)) ? side_u[sidx] : u;
+            (side_u && limit > 0 && (fabs(u - limit) <= band_u || fabs(u + limit) <= band_u)) ? side_u[sidx] : u;
         clamp_gate(g, sg, limit, &gp[idx], &mg[idx]);
         clamp_up(u, su, limit, &upc[idx], &mu[idx]);
         hh[idx] = fp32_round(fr, silu(gp[idx]) * upc[idx]);
@@ -453,7 +524,7 @@ int orc_moe_decided(const orc_layer* L, int64_t qlen, const double* x, const int
       if (!dyw || !dyb || !dh || !dg || !du || !dgb || !dub) {
         status = -9;
         free(dyw); free(dyb); free(dh); free(dg); free(du); free(dgb); free(dub);
-        free(ua); free(ub); free(ud); free(gp); free(upc); free(mg); free(mu); free(hh);
+        free(ua); free(ub); free(ud); free(gp); free(upc); free(mg); free(mu); free(hh); free(sag); free(sau);
         goto done;
       }
       /* route-weight gradient and the cotangent of y */
@@ -501,7 +572,7 @@ int orc_moe_decided(const orc_layer* L, int64_t qlen, const double* x, const int
       if (!dxs) {
         status = -9;
         free(dyw); free(dyb); free(dh); free(dg); free(du); free(dgb); free(dub);
-        free(ua); free(ub); free(ud); free(gp); free(upc); free(mg); free(mu); free(hh);
+        free(ua); free(ub); free(ud); free(gp); free(upc); free(mg); free(mu); free(hh); free(sag); free(sau);
         goto done;
       }
       transposed_products(wg, I, H, dg, I, m, wu, I, du, I, dxs, H);
@@ -560,7 +631,7 @@ int orc_moe_decided(const orc_layer* L, int64_t qlen, const double* x, const int
       }
       free(dyw); free(dyb); free(dh); free(dg); free(du); free(dgb); free(dub);
     }
-    free(ua); free(ub); free(ud); free(gp); free(upc); free(mg); free(mu); free(hh);
+    free(ua); free(ub); free(ud); free(gp); free(upc); free(mg); free(mu); free(hh); free(sag); free(sau);
   }
 
   /* weighted slot sums per token, slots in order; dropped slots add nothing */
@@ -588,5 +659,5 @@ int orc_moe(const orc_layer* L, int64_t qlen, const double* x, const int64_t* id
             const double* dy, double* out, double* dx, double* droute, double* d_gate_a, double* d_gate_b,
             double* d_up_a, double* d_up_b, double* d_down_a, double* d_down_b) {
   return orc_moe_decided(L, qlen, x, ids, rw, dy, out, dx, droute, d_gate_a, d_gate_b, d_up_a, d_up_b, d_down_a,
-                         d_down_b, NULL, NULL, 0.0, NULL, NULL);
+                         d_down_b, NULL, NULL, 0.0, NULL, NULL, NULL, NULL);
 }

@@ -18,6 +18,7 @@ import pytest
 
 import oracle as O
 from int4_quantized_moe_amd import workloads as W
+from tests import fullsize as F
 from tests.clamp_sides import reference
 
 torch = pytest.importorskip("torch")
@@ -185,6 +186,9 @@ def test_mxfp4_scales_outside_the_domain_are_counted(dev):
 
 
 def test_mxfp4_full_size_sampled(dev):
+    # sampled tokens and experts of the long-sequence workload with an MXFP4 base
+    # (tests/fullsize.py: the heaviest, the lightest and one expert of every
+    # last-tile height class)
     base = W.CONFIGS[4]
     cfg = _mx(base)
     seed = W.config_seed(4)
@@ -211,30 +215,12 @@ def test_mxfp4_full_size_sampled(dev):
 
     rng = np.random.default_rng(6262)
     toks = np.unique(np.concatenate([[0, cfg.qlen - 1], rng.choice(cfg.qlen, 6, replace=False)]))
-    _say(f"{cfg.name}: oracle on tokens {toks.tolist()}")
-    ref = reference(cfg, weights, batch.inputs[toks], batch.expert_ids[toks], batch.route_weights[toks],
-                    batch.grad_output[toks], sides(toks), _say)
-    failures = []
-    for name, a, e, rel, cos in (("forward", out.float().cpu().numpy()[toks], ref["out"], REL_L2, COSINE),
-                                 ("dX", dx.float().cpu().numpy()[toks], ref["dx"], REL_L2, COSINE),
-                                 ("dRoute", droute.cpu().numpy()[toks], ref["droute"], DROUTE_REL_L2, 0.995)):
-        try:
-            _close(f"{cfg.name}.{name}", a, e, rel, cos)
-        except AssertionError as err:
-            failures.append(str(err))
+    failures = F.check_tokens(cfg, weights, batch, out.float().cpu().numpy(), dx.float().cpu().numpy(),
+                              droute.cpu().numpy(), sides, toks, _say)
     g = {n: t.cpu().numpy() for n, t in grads.items()}
     counts = np.bincount(batch.expert_ids.ravel(), minlength=cfg.num_experts)
-    e = int(rng.choice(np.flatnonzero(counts)))
-    rows = np.flatnonzero((batch.expert_ids == e).any(axis=1))
-    ids = np.where(batch.expert_ids[rows] == e, e, -1).astype(np.int64)
-    _say(f"{cfg.name}: oracle LoRA gradients of expert {e} ({counts[e]} slots)")
-    ref_e = reference(cfg, weights, batch.inputs[rows], ids, batch.route_weights[rows], batch.grad_output[rows],
-                      sides(rows), _say)
-    for n in O.LORA_NAMES:
-        try:
-            _close(f"{cfg.name}.expert{e}.{n}", g[n][e], ref_e["grads"][n][e])
-        except AssertionError as err:
-            failures.append(str(err))
+    experts = F.choose_experts(counts, rng, n=4)
+    failures += F.check_experts(cfg, weights, batch, g, sides, experts, _say)
     assert not failures, "; ".join(failures)
 
 

@@ -360,6 +360,100 @@ def test_supplied_clamp_side_hand_case():
         np.testing.assert_array_equal(own["grads"][n], plain["grads"][n])
 
 
+def test_supplied_clamp_side_apriori_band():
+    # with the a priori band, an element exactly on a bound (v = 4 at L = 2:
+    # g = u = 2) takes the supplied side; one 1/16 away from it (v = 3.875) keeps
+    # its own, since its bound is far smaller than that
+    limit = 2.0
+    cfg = _cfg(1, 1, 32, 32, 4, 8.0, 2, limit)
+    w = _uniform_weights(cfg, 0x99, BF16_HALF)
+    w.lora["gate_lora_a"][0, 0, 0] = 0.25
+    x = np.zeros((2, 32))
+    x[:, 0] = [4.0, 3.875]
+    ids = np.zeros((2, 1), dtype=np.int64)
+    rw = np.full((2, 1), 0.75)
+    dy = np.ones((2, 32))
+    side = np.repeat(np.array([2.01, 2.01])[:, None, None], 32, axis=2)
+    res = O.moe(cfg, w, x, ids, rw, dy, fp32_intermediates=False, inputs_are_bf16=False, sides=(side, side),
+                band=O.APRIORI, preactivations=True)
+    assert np.all(res["bound_g"] > 0) and np.all(res["bound_g"][1] < 1e-3)
+    own = O.moe(cfg, w, x, ids, rw, dy, fp32_intermediates=False, inputs_are_bf16=False)
+    # token 0 on the bound: the side beyond L clamps both (no gradient); token 1 unchanged
+    assert np.all(res["dx"][0] == 0.0) and np.any(own["dx"][0] != 0.0)
+    np.testing.assert_array_equal(res["dx"][1], own["dx"][1])
+    np.testing.assert_array_equal(res["out"][1], own["out"][1])
+
+
+def _fp32_preactivation(wrow, x, A, B, sc, rng):
+    """One gate/up pre-activation computed in fp32 by a random summation order, with
+    the LoRA factors perturbed by up to 2^-14 (A) and 2^-13 (B, a) relative."""
+    prods = (wrow.astype(np.float64) * x).astype(np.float32)  # exact: 11 x 8 significant bits
+    acc = np.float32(0.0)
+    for k in rng.permutation(prods.size):
+        acc = np.float32(acc + prods[k])
+    a = np.zeros(A.shape[0], dtype=np.float32)
+    for q in range(A.shape[0]):
+        ap = (A[q] * (1 + rng.uniform(-2**-14, 2**-14, A.shape[1]))).astype(np.float64)
+        t = (ap * x).astype(np.float32)
+        s = np.float32(0.0)
+        for k in rng.permutation(t.size):
+            s = np.float32(s + t[k])
+        a[q] = s
+    lora = np.float32(0.0)
+    for q in rng.permutation(A.shape[0]):
+        bq = B[q] * (1 + rng.uniform(-2**-13, 2**-13))
+        aq = np.float64(a[q]) * (1 + rng.uniform(-2**-13, 2**-13))
+        lora = np.float32(lora + np.float32(sc * bq * aq))
+    return np.float32(acc + lora)
+
+
+@pytest.mark.parametrize("hidden", [256, 7168])
+def test_apriori_bound_covers_fp32_computations(hidden):
+    # the oracle's a priori bound on a pre-activation's fp32 error covers fp32
+    # computations of it in random summation orders with perturbed LoRA factors
+    cfg = _cfg(1, 1, hidden, 32, 8, 16.0, 2, 0.0)
+    w, x, ids, rw, _ = _random_case(cfg, 41, x_std=2.0, lora_std=0.05)
+    x = W.bf16_bits_to_f32(W.f32_to_bf16_bits(x.astype(np.float32))).astype(np.float64)
+    ids[:] = 0
+    res = O.moe(cfg, w, x, ids, rw, None, inputs_are_bf16=False, preactivations=True)
+    wg = O.dequant(w.gate_packed[0], w.gate_scale[0])
+    A, B = w.lora["gate_lora_a"][0].astype(np.float64), w.lora["gate_lora_b"][0].astype(np.float64)
+    sc = cfg.alpha / cfg.rank
+    rng = np.random.default_rng(7)
+    worst = 0.0
+    for t in range(cfg.qlen):
+        for n in range(0, cfg.intermediate, 4):
+            g32 = _fp32_preactivation(wg[n], x[t], A, B[n], sc, rng)
+            dev = abs(float(g32) - res["pre_g"][t, 0, n])
+            bound = res["bound_g"][t, 0, n]
+            assert dev <= bound, (t, n, dev, bound)
+            worst = max(worst, dev / bound)
+    print(f"largest deviation / bound: {worst:.3f}")
+
+
+def test_duplicate_ids_match_autograd():
+    # the routed loop visits every slot: the same expert twice in one token counts twice
+    for limit in (0.0, 1.0):
+        cfg = _cfg(3, 3, 64, 96, 4, 12.0, 5, limit)
+        w, x, ids, rw, dy = _random_case(cfg, 61 + int(limit), x_std=0.5)
+        ids[0] = [1, 1, 2]
+        ids[1] = [0, 0, 0]
+        ids[3] = [2, 0, 2]
+        res = _run64(cfg, w, x, ids, rw, dy)
+        out, dx, drw, grads = _autograd(cfg, w, x, ids, rw, dy)
+        np.testing.assert_allclose(res["out"], out, rtol=1e-11, atol=1e-11)
+        np.testing.assert_allclose(res["dx"], dx, rtol=1e-10, atol=1e-11)
+        np.testing.assert_allclose(res["droute"], drw, rtol=1e-10, atol=1e-11)
+        for n in O.LORA_NAMES:
+            np.testing.assert_allclose(res["grads"][n], grads[n], rtol=1e-10, atol=1e-11, err_msg=n)
+        # a doubled slot with its route weights summed gives the single slot's output
+        ids2, rw2 = ids.copy(), rw.copy()
+        ids2[1] = [0, 1, 2]
+        rw2[1] = [rw[1].sum(), 0.0, 0.0]
+        one = _run64(cfg, w, x, ids2, rw2)
+        np.testing.assert_allclose(res["out"][1], one["out"][1], rtol=1e-12, atol=1e-12)
+
+
 def _page_clamp_case(golden, fp32):
     rows = golden("clamp_example.txt")
     cfg = _cfg(4, 2, 256, 256, 8, 16.0, 9, 2.0)

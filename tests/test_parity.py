@@ -94,6 +94,31 @@ def test_dequant_bit_exact(dev):
     assert np.array_equal(out.cpu().numpy(), O.dequant(packed, scales))
 
 
+def test_rawint4_scales_outside_the_domain_are_counted(dev):
+    # nonzero scales below 2^-14 or above 2720 in magnitude leave the domain where
+    # the decoded weights are exact in fp16; the forward counts them once each
+    cfg, weights, batch = W.make_workload(0)
+    _say("rawint4 scale domain")
+    used = int(batch.expert_ids[0, 0])
+    unused = [e for e in range(cfg.num_experts) if e not in set(batch.expert_ids.ravel().tolist())]
+    out_of_domain = W.f32_to_bf16_bits(np.array([3e-5, 4096.0, -1e-6], dtype=np.float32))
+    weights.gate_scale[used, 0, 0] = out_of_domain[0]
+    weights.up_scale[used, 5, 3] = out_of_domain[1]
+    weights.down_scale[used, 2, 1] = out_of_domain[2]
+    weights.gate_scale[used, 1, 1] = W.f32_to_bf16_bits(np.array([6.103515625e-05], dtype=np.float32))[0]  # 2^-14: in
+    weights.down_scale[used, 3, 0] = W.f32_to_bf16_bits(np.array([-2720.0], dtype=np.float32))[0]  # in
+    weights.up_scale[used, 7, 2] = 0  # zero: in
+    if unused:  # experts no slot reaches are not converted, so not counted
+        weights.gate_scale[unused[0], 0, 0] = out_of_domain[1]
+    dl = dev.DeviceLayer(cfg, weights)
+    db = dev.DeviceBatch(batch)
+    ws = dl.workspace(db.qlen)
+    dl.forward(db.inputs, db.expert_ids, db.route_weights, ws)
+    torch.cuda.synchronize()
+    bad_ids, bad_scales = __import__("int4_quantized_moe_amd")._lib.kt_rawint4_moe_diagnostics(ws)
+    assert bad_ids == 0 and bad_scales == 3
+
+
 @pytest.mark.parametrize("index", range(len(W.CONFIGS)))
 def test_grouping_bit_exact(dev, index):
     from int4_quantized_moe_amd import _lib
@@ -138,7 +163,8 @@ def _run_gpu(dev, cfg, weights, batch, grads_fill=7.0, accumulate=False, grad_sc
 
 
 def _reference(cfg, weights, batch, gpu):
-    """The oracle on the whole batch, taking the GPU's clamp side within rounding of a bound."""
+    """The oracle on the whole batch with its own clamp masks (the GPU's saved
+    pre-activations checked against it, element by element)."""
     return reference(cfg, weights, batch.inputs, batch.expert_ids, batch.route_weights, batch.grad_output,
                      gpu["sides"], _say)
 
@@ -234,6 +260,26 @@ def test_layer_every_tile_height_rank64(dev, rows, monkeypatch):
     _, _, _, gpu = _run_gpu(dev, cfg, weights, batch)
     ref = _reference(cfg, weights, batch, gpu)
     _check_all(f"r64rows{rows or 'mixed'}", gpu, ref, set(batch.expert_ids.ravel().tolist()))
+
+
+@pytest.mark.parametrize("top_k", [2, 3])
+def test_layer_duplicate_ids(dev, top_k):
+    # the routed loop visits every slot, so one expert twice (or three times) in a
+    # token counts once per slot: rows of the same token in one expert's tiles
+    base = W.CONFIGS[1]
+    cfg = W.LayerConfig(f"dup{top_k}", base.num_experts, top_k, base.hidden, base.intermediate, base.rank,
+                        base.alpha, base.qlen, base.swiglu_limit, x_std=3.0)
+    _say("layer duplicate ids", cfg.name)
+    weights = W.make_weights(cfg, 3100 + top_k)
+    batch = W.make_batch(cfg, 3100 + top_k)
+    ids = batch.expert_ids
+    ids[0::3, 1] = ids[0::3, 0]  # every third token: its first expert twice
+    if top_k == 3:
+        ids[1::5, :] = ids[1::5, :1]  # every fifth token from the second: one expert in all three slots
+    assert any(len(set(row.tolist())) < top_k for row in ids)
+    _, _, _, gpu = _run_gpu(dev, cfg, weights, batch)
+    ref = _reference(cfg, weights, batch, gpu)
+    _check_all(cfg.name, gpu, ref, set(ids.ravel().tolist()))
 
 
 def test_layer_dropped_ids_and_window(dev):

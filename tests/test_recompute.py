@@ -8,8 +8,9 @@
   Checked against the oracle at the training bars (the pages use 0.03 / 0.995).
 * kt_rawint4_moe_bwd_recompute from a workspace that holds no forward (filled
   with 0xFF bytes, which read as NaN in fp32), after an inference forward:
-  grad_input, grad_route and the six LoRA gradients equal those of forward +
-  backward bit for bit -- on the small workloads and on both full-size ones.
+  against the oracle at the clamp workload, and bit for bit equal to forward +
+  backward (grad_input, grad_route and the six LoRA gradients) on the small
+  workloads and on both full-size ones.
 
 Each case prints its name first.
 """
@@ -123,6 +124,37 @@ def _recompute_equals(dev, cfg, weights, batch):
         x, y = _bits(a), _bits(b)
         assert np.array_equal(x, y), f"{cfg.name}.{name}: {np.count_nonzero(x != y)} elements differ"
     _say(f"{cfg.name}: recompute backward bit-equal ({db.qlen} tokens)")
+
+
+def test_recompute_backward_against_the_oracle(dev):
+    # the checkpointed form on its own (an inference forward that keeps nothing,
+    # then the recompute backward from a workspace of 0xFF bytes) against the
+    # oracle, at the clamp workload
+    cfg, weights, batch = W.make_workload(1)
+    _say("recompute against the oracle", cfg.name)
+    dl = dev.DeviceLayer(cfg, weights)
+    db = dev.DeviceBatch(batch)
+    out = dl.infer(db.inputs, db.expert_ids, db.route_weights, dl.infer_workspace(db.qlen))
+    ws = torch.full((dl.workspace(db.qlen).numel(),), 0xFF, dtype=torch.uint8, device="cuda")
+    g = dl.grad_buffers(fill=7.0)
+    dr = torch.empty(batch.expert_ids.shape, dtype=torch.float32, device="cuda")
+    dx, _ = dl.backward(db.inputs, db.expert_ids, db.route_weights, db.grad_output, ws, g, accumulate=False,
+                        grad_scale=0.75, grad_route=dr, recompute=True)
+    side = dl.saved_preactivations(db.qlen, ws)
+    torch.cuda.synchronize()
+    ref = reference(cfg, weights, batch.inputs, batch.expert_ids, batch.route_weights, batch.grad_output,
+                    tuple(t.cpu().numpy() for t in side), _say)
+    failures = []
+    checks = [("forward", out.float().cpu().numpy(), ref["out"], REL_L2, COSINE),
+              ("dX", dx.float().cpu().numpy(), ref["dx"], REL_L2, COSINE),
+              ("dRoute", dr.cpu().numpy(), ref["droute"], DROUTE_REL_L2, 0.995)]
+    checks += [(n, g[n].cpu().numpy(), 0.75 * ref["grads"][n], REL_L2, COSINE) for n in O.LORA_NAMES]
+    for name, a, e, rel, cos in checks:
+        try:
+            _close(f"recompute.{name}", a, e, rel, cos)
+        except AssertionError as err:
+            failures.append(str(err))
+    assert not failures, "; ".join(failures)
 
 
 @pytest.mark.parametrize("index", [0, 1])
