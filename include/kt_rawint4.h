@@ -212,8 +212,10 @@ int kt_rawint4_unpack(const uint8_t* packed, int64_t n, int64_t k, int8_t* codes
 
 /*
  * Test hook, dequantize_rawint4 of the same page: packed [n, k/2] with bf16
- * scales [n, k/32] -> fp32 [n, k], (c - 8) * scale.  Uses the decoder of the
- * matrix kernels (exact fp16 values) widened to fp32.  k % 32 == 0.
+ * scales [n, k/32] -> fp32 [n, k], (c - 8) * scale.  Runs both decoders of the
+ * matrix kernels (the one of the stored orientation, whose exact fp16 values
+ * are returned widened to fp32, and the one of the transposed orientation); a
+ * dword where they give different values comes out as NaN.  k % 32 == 0.
  */
 int kt_rawint4_dequant(const uint8_t* packed, const uint16_t* scales, int64_t n, int64_t k, float* weights,
                        void* stream);
@@ -223,7 +225,7 @@ int kt_rawint4_dequant(const uint8_t* packed, const uint16_t* scales, int64_t n,
  * (low nibble first) with bf16 power-of-two scales [n, k/32] -> fp32 weights
  * [n, k], through the matrix kernels' own MXFP4 decoders.  Both decoders (the
  * one of the stored orientation and the one of the transposed orientation)
- * run; a dword where they disagree comes out as NaN.
+ * run; a dword where they give different values comes out as NaN.
  */
 int kt_rawint4_dequant_mxfp4(const uint8_t* packed, const uint16_t* scales, int64_t n, int64_t k, float* weights,
                              void* stream);

@@ -39,6 +39,8 @@ static void plan_group_part(Planner& pl, WsMap& w, int64_t Ms, int64_t E) {
   w.counts = pl.take(sizeof(int32_t) * (size_t)E);
   w.offsets = pl.take(sizeof(int32_t) * (size_t)(E + 1));
   w.qoffsets = pl.take(sizeof(int32_t) * (size_t)(E + 1));
+  w.expert_slot = pl.take(sizeof(int32_t) * (size_t)E);
+  w.nact = E < Ms ? E : Ms;
   w.blockcnt = pl.take(sizeof(int32_t) * (size_t)(w.nb * E));
   w.sorted_slot = pl.take(sizeof(int32_t) * (size_t)Ms);
   w.row_of_slot = pl.take(sizeof(int32_t) * (size_t)Ms);
@@ -48,7 +50,8 @@ static void plan_group_part(Planner& pl, WsMap& w, int64_t Ms, int64_t E) {
   const int forced = forced_gemm_rows();
   w.gbulk = forced ? forced : 128;
   w.gmixed = forced == 0;
-  w.max_gtiles = Ms / w.gbulk + (E < Ms ? E : Ms);
+  // tiles, plus the positions the XCD layout of the list may leave empty
+  w.max_gtiles = Ms / w.gbulk + (E < Ms ? E : Ms) + 16;
   w.gtile_e = pl.take(sizeof(int32_t) * (size_t)w.max_gtiles);
   w.gtile_m0 = pl.take(sizeof(int32_t) * (size_t)w.max_gtiles);
   w.gtile_mt = pl.take(sizeof(int32_t) * (size_t)w.max_gtiles);
@@ -69,9 +72,9 @@ WsMap plan_workspace(const Dims& d) {
   WsMap w{};
   Planner pl;
   plan_group_part(pl, w, d.Ms, d.E);
-  w.sct_g = pl.take(2 * (size_t)d.E * (size_t)d.I * (size_t)(d.H / 32));
-  w.sct_u = pl.take(2 * (size_t)d.E * (size_t)d.I * (size_t)(d.H / 32));
-  w.sct_d = pl.take(2 * (size_t)d.E * (size_t)d.H * (size_t)(d.I / 32));
+  w.sct_g = pl.take(2 * (size_t)w.nact * (size_t)d.I * (size_t)(d.H / 32));
+  w.sct_u = pl.take(2 * (size_t)w.nact * (size_t)d.I * (size_t)(d.H / 32));
+  w.sct_d = pl.take(2 * (size_t)w.nact * (size_t)d.H * (size_t)(d.I / 32));
   w.h_nch = (d.I + kHExp - 1) / kHExp;
   w.dr_nt = (d.I + kDgExp - 1) / kDgExp;
   w.dg_nch = 2 * w.dr_nt;
@@ -366,10 +369,10 @@ static void launch_forward_front(const kt_rawint4_moe_layer* layer, const Dims& 
   {
     PhaseScope ph(kPhScales, st);
     unsigned long long* bad = ws_ptr<unsigned long long>(ws, w.counters) + kBadScales;
-    const int32_t* offs = ws_ptr<int32_t>(ws, w.offsets);
-    launch_scales_t(layer->gate_scale, d.E, d.I, d.H / 32, offs, ws_ptr<uint16_t>(ws, w.sct_g), bad, d.fmt, st);
-    launch_scales_t(layer->up_scale, d.E, d.I, d.H / 32, offs, ws_ptr<uint16_t>(ws, w.sct_u), bad, d.fmt, st);
-    launch_scales_t(layer->down_scale, d.E, d.H, d.I / 32, offs, ws_ptr<uint16_t>(ws, w.sct_d), bad, d.fmt, st);
+    const int32_t* slot = ws_ptr<int32_t>(ws, w.expert_slot);
+    launch_scales_t(layer->gate_scale, d.E, d.I, d.H / 32, slot, ws_ptr<uint16_t>(ws, w.sct_g), bad, d.fmt, st);
+    launch_scales_t(layer->up_scale, d.E, d.I, d.H / 32, slot, ws_ptr<uint16_t>(ws, w.sct_u), bad, d.fmt, st);
+    launch_scales_t(layer->down_scale, d.E, d.H, d.I / 32, slot, ws_ptr<uint16_t>(ws, w.sct_d), bad, d.fmt, st);
   }
   {
     PhaseScope ph(kPhXHalf, st);

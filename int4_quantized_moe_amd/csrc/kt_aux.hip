@@ -66,24 +66,25 @@ void launch_rows_to_half(const uint16_t* src, int64_t rows, int64_t cols, uint16
 
 // ---------------------------------------------------------------- scales for the expert GEMMs
 
-// One scale tensor [E][rows][G] (bf16, G = K / 32) to [E][G][rows] in fp16,
-// rows of every aligned group of 8 in the within-8 permuted order, so that a
-// GEMM stage reads the scales of its column (or contraction-row) block as one
+// One scale tensor [E][rows][G] (bf16, G = K / 32) to [active][G][rows] in
+// fp16, rows of every aligned group of 8 in the within-8 permuted order, so that
+// a GEMM stage reads the scales of its column (or contraction-row) block as one
 // contiguous run in both orientations.  Experts that received no token-slot
-// are skipped.  Scales outside the numeric domain are counted (once each, over
+// are skipped; the others go to their place among the experts in use.  Scales outside the numeric domain are counted (once each, over
 // the experts in use).  64 x 64 tiles pass through LDS so that the reads
 // (along G, 16 bytes per lane where G allows) and the writes (along rows, 16
 // bytes per lane) are both coalesced.
 __global__ __launch_bounds__(256) void k_scales_t(const uint16_t* __restrict__ s, int64_t rows, int64_t G,
-                                                   const int32_t* __restrict__ offsets, uint16_t* __restrict__ out,
-                                                   unsigned long long* bad, int fmt) {
+                                                   const int32_t* __restrict__ expert_slot,
+                                                   uint16_t* __restrict__ out, unsigned long long* bad, int fmt) {
   __shared__ uint16_t t[64][72];  // [row][group], 144-byte pitch
   __shared__ int nbad_w[4];
   const int64_t e = blockIdx.z;
-  if (offsets[e + 1] == offsets[e]) return;
+  const int32_t es = expert_slot[e];
+  if (es < 0) return;
   const int64_t r0 = (int64_t)blockIdx.x * 64, g0 = (int64_t)blockIdx.y * 64;
   const uint16_t* se = s + e * rows * G;
-  uint16_t* oe = out + e * G * rows;
+  uint16_t* oe = out + (int64_t)es * G * rows;
   int nbad = 0;
   {
     const int i = threadIdx.x >> 2, j0 = 16 * (threadIdx.x & 3);  // row r0 + i, groups g0 + j0 .. + 15
@@ -145,11 +146,11 @@ __global__ __launch_bounds__(256) void k_scales_t(const uint16_t* __restrict__ s
   }
 }
 
-void launch_scales_t(const uint16_t* s, int64_t E, int64_t rows, int64_t G, const int32_t* offsets, uint16_t* out,
-                     unsigned long long* bad, int fmt, hipStream_t st) {
+void launch_scales_t(const uint16_t* s, int64_t E, int64_t rows, int64_t G, const int32_t* expert_slot,
+                     uint16_t* out, unsigned long long* bad, int fmt, hipStream_t st) {
   if (E <= 0 || rows <= 0 || G <= 0) return;
   dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((G + 63) / 64), (unsigned)E);
-  k_scales_t<<<grid, 256, 0, st>>>(s, rows, G, offsets, out, bad, fmt);
+  k_scales_t<<<grid, 256, 0, st>>>(s, rows, G, expert_slot, out, bad, fmt);
   note_launch();
 }
 
@@ -330,9 +331,25 @@ void launch_unpack(const uint8_t* packed, int64_t n, int64_t k, int8_t* codes, h
   }
 }
 
+// The 8 fp16 values of two decodes are the same numbers (a zero may differ in
+// sign: the two decoders round an exact zero with different signs, which no
+// product or sum downstream can tell apart).
+__device__ __forceinline__ bool same_values(u32x4 a, u32x4 b) {
+  const uint32_t x[4] = {a.x, a.y, a.z, a.w}, y[4] = {b.x, b.y, b.z, b.w};
+  bool same = true;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t p = (x[i] >> (16 * h)) & 0xffffu, q = (y[i] >> (16 * h)) & 0xffffu;
+      same = same && (p == q || ((p | q) & 0x7fffu) == 0);
+    }
+  return same;
+}
+
 // the matrix kernels' decoders: one packed dword -> 8 fp16 values -> fp32, by
 // the stored-orientation decoder and the transposed one (one scale for the
-// whole dword here); a dword where they disagree comes out as NaN
+// whole dword here); a dword where they give different values comes out as NaN
 __global__ void k_dequant(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales, int64_t n,
                           int64_t k, int fmt, float* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // dword index
@@ -349,13 +366,13 @@ __global__ void k_dequant(const uint8_t* __restrict__ packed, const uint16_t* __
     // expected) shows as NaN in every value of the dword
     r = decode_dword_e2m1(wv, (float)s);
     const u32x4 t = decode_dword_perm_e2m1(wv, s2, s2, s2, s2);
-    if (t.x != r.x || t.y != r.y || t.z != r.z || t.w != r.w) r = u32x4{0x7e007e00u, 0x7e007e00u, 0x7e007e00u, 0x7e007e00u};
+    if (!same_values(t, r)) r = u32x4{0x7e007e00u, 0x7e007e00u, 0x7e007e00u, 0x7e007e00u};
   } else {
     // the RAWINT4 decoders of both orientations, likewise
     const DecodeConsts dc = decode_consts();
     r = decode_dword_fma(wv, s2 * (half2_t){16.f16, 16.f16}, s2 * (half2_t){-24.f16, -24.f16}, dc);
     const u32x4 t = decode_dword_perm(wv, s2, s2, s2, s2, dc);
-    if (t.x != r.x || t.y != r.y || t.z != r.z || t.w != r.w) r = u32x4{0x7e007e00u, 0x7e007e00u, 0x7e007e00u, 0x7e007e00u};
+    if (!same_values(t, r)) r = u32x4{0x7e007e00u, 0x7e007e00u, 0x7e007e00u, 0x7e007e00u};
   }
   const uint32_t words[4] = {r.x, r.y, r.z, r.w};  // (k0, k4), (k1, k5), (k2, k6), (k3, k7)
   float* o = out + row * k + d * 8;

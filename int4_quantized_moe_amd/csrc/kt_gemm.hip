@@ -21,10 +21,12 @@
 // __syncthreads does not serialise the ring.  In the 64/96/128-row tiles each
 // wave decodes a stage's weights, then runs its MFMAs at a raised wave priority
 // with every activation fragment read one group of MFMAs ahead: the SIMD's
-// other wave (another workgroup) decodes or copies in the gaps.  Row tiles are dealt to the eight
-// XCDs in turn (as blocks are), each XCD running all column tiles of its row
-// tiles: the column tiles of one row tile share that XCD's L2, and a heavily
-// loaded expert's row tiles spread over every XCD.
+// other wave (another workgroup) decodes or copies in the gaps.  Position p of
+// the tile list runs on XCD p % 8 (blocks reach the XCDs in turn), each XCD
+// running all column tiles of a row tile together: the column tiles of one row
+// tile share that XCD's L2 for the activation rows, and the grouping places an
+// expert's row tiles on one XCD one after another (a heavily loaded expert's
+// spread over all eight), so that they share it for the weights.
 //
 // Weights are decoded on the fly into exact fp16 ((c - 8) * scale fits fp16's
 // 11-bit significand) and multiplied on v_mfma_f32_16x16x32_f16 with fp32
@@ -84,6 +86,7 @@ struct GemmParams {
   const int32_t* tile_e;
   const int32_t* tile_m0;
   const int32_t* tile_mt;
+  const int32_t* expert_slot;  // place of an expert in the transposed scale tables
   const unsigned long long* counters;
   LayerPtrs L;
   const uint16_t* a_src;      // fp16 activation rows (within-8 permuted order)
@@ -92,7 +95,7 @@ struct GemmParams {
   int a_nch;
   int64_t lda;
   const uint16_t* lsplit;  // side product times the LoRA scale, bf16 hi/lo planes [Ms][2][KLP]
-  const uint16_t* sct0;    // fp16 scales [E][K/32][rows], rows within-8 permuted: gate (or down)
+  const uint16_t* sct0;    // fp16 scales [active expert][K/32][rows], rows within-8 permuted: gate (or down)
   const uint16_t* sct1;    // up
   const float* rw;  // route weights per flat slot
   const void* zero;  // 16 zero bytes
@@ -218,6 +221,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
   constexpr int kWReg = kStages * kABytes, kSReg = kStages * (kABytes + kWBytes);
 
   const int e = p.tile_e[tile], m0 = p.tile_m0[tile];
+  const int es = p.expert_slot[e];  // the expert's place in the scale tables
   const int mlen = min(MT, p.offsets[e + 1] - m0);
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
@@ -313,10 +317,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
         const int cg = min(n0 / kGroup + (q >> 3), nout / kGroup - 1);
         const int kk = min(k0 + 8 * (q & 7), kdim - 8);
         if constexpr (KIND == kDownBwd) {
-          g = p.sct0 + ((size_t)e * (I / kGroup) + cg) * H + kk;
+          g = p.sct0 + ((size_t)es * (I / kGroup) + cg) * H + kk;
         } else {
           const bool up = kk >= I;
-          g = (up ? p.sct1 : p.sct0) + ((size_t)e * (H / kGroup) + cg) * I + (up ? kk - I : kk);
+          g = (up ? p.sct1 : p.sct0) + ((size_t)es * (H / kGroup) + cg) * I + (up ? kk - I : kk);
         }
       } else {
         // group (q >> 5) of the stage, output columns 8 (q & 31) .. + 7 of the tile
@@ -324,10 +328,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
         const int lc = 8 * (q & 31);
         if constexpr (KIND == kGateUp) {
           const int n = min(n0 + (lc & (kHChunk - 1)), I - 8);
-          g = (lc < kHChunk ? p.sct0 : p.sct1) + ((size_t)e * ngroups + gi) * I + n;
+          g = (lc < kHChunk ? p.sct0 : p.sct1) + ((size_t)es * ngroups + gi) * I + n;
         } else {
           const int n = min(n0 + lc, H - 8);
-          g = p.sct0 + ((size_t)e * ngroups + gi) * H + n;
+          g = p.sct0 + ((size_t)es * ngroups + gi) * H + n;
         }
       }
       if (lane < 16) dma16(g, ssc + 256 * w);
@@ -379,20 +383,20 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
     if constexpr (kT) {
       const int cg = min(n0 / kGroup + (q >> 3), nout / kGroup - 1);
       if constexpr (KIND == kDownBwd) {
-        ps = p.sct0 + ((size_t)e * (I / kGroup) + cg) * H + 8 * (q & 7);
+        ps = p.sct0 + ((size_t)es * (I / kGroup) + cg) * H + 8 * (q & 7);
         ps_up = ps;
       } else {
-        ps = p.sct0 + ((size_t)e * (H / kGroup) + cg) * I + 8 * (q & 7);
-        ps_up = p.sct1 + ((int64_t)e * (H / kGroup) + cg) * (int64_t)I + 8 * (q & 7) - I;
+        ps = p.sct0 + ((size_t)es * (H / kGroup) + cg) * I + 8 * (q & 7);
+        ps_up = p.sct1 + ((int64_t)es * (H / kGroup) + cg) * (int64_t)I + 8 * (q & 7) - I;
       }
     } else {
       const int lc = 8 * (q & 31);
       if constexpr (KIND == kGateUp) {
         const int n = min(n0 + (lc & (kHChunk - 1)), I - 8);
-        ps = (lc < kHChunk ? p.sct0 : p.sct1) + ((size_t)e * ngroups + (q >> 5)) * I + n;
+        ps = (lc < kHChunk ? p.sct0 : p.sct1) + ((size_t)es * ngroups + (q >> 5)) * I + n;
       } else {
         const int n = min(n0 + lc, H - 8);
-        ps = p.sct0 + ((size_t)e * ngroups + (q >> 5)) * H + n;
+        ps = p.sct0 + ((size_t)es * ngroups + (q >> 5)) * H + n;
       }
       ps_up = ps;
     }
@@ -1066,15 +1070,16 @@ template <int KIND, bool LDMA, bool MX>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm(GemmParams p) {
   __shared__ __align__(16) uint8_t ring[kRingMax];
   __shared__ int32_t s_src[128], s_exp[128], s_slot[128];
-  // work item: (tile, column tile).  Whole tiles are dealt to the eight XCDs in
-  // turn (blocks reach them in turn too) and each XCD runs its tiles' column
-  // tiles in order: a tile's activation rows stay in one XCD's L2, and an
-  // expert with many rows (skewed routing) spreads over all eight
+  // work item: (list position, column tile).  Position p runs on XCD p % 8
+  // (blocks reach the XCDs in turn) and each XCD runs its positions' column
+  // tiles in order: a tile's activation rows stay in one XCD's L2, and so do
+  // an expert's weights for all its row tiles (the grouping's layout)
   const unsigned nn = (unsigned)p.n_ntiles, ntl = (unsigned)p.counters[kNumGemmTiles];
   const unsigned xcd = blockIdx.x % 8u, local = blockIdx.x / 8u;
   const unsigned tile_u = xcd + 8u * (local / nn);
   if (tile_u >= ntl) return;
   const int tile = (int)tile_u;
+  if (p.tile_e[tile] < 0) return;  // an empty position of the list
   const int nt = (int)(local % nn);
   switch (p.tile_mt[tile]) {
     case 16:
@@ -1126,6 +1131,7 @@ void launch_gemm(GemmKind kind, const Dims& d, const WsMap& w, void* ws, const L
   p.tile_e = ws_ptr<int32_t>(ws, w.gtile_e);
   p.tile_m0 = ws_ptr<int32_t>(ws, w.gtile_m0);
   p.tile_mt = ws_ptr<int32_t>(ws, w.gtile_mt);
+  p.expert_slot = ws_ptr<int32_t>(ws, w.expert_slot);
   p.counters = ws_ptr<unsigned long long>(ws, w.counters);
   p.L = L;
   p.rw = route_weights;

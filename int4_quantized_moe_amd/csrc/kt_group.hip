@@ -65,15 +65,26 @@ __device__ __forceinline__ int rest_tile_rows(int r, int bulk) {
 
 // One block: expert totals, exclusive offsets (and the same with every expert's
 // rows rounded up to a multiple of 4, for the quad-row layout of the saved
-// pre-activations), per-block placement bases
+// pre-activations), each expert's place among the experts in use, per-block
+// placement bases
 // (blockcnt is rewritten in place), and two lists of (expert, first row) tiles:
 // tiles of `mt` rows for the LoRA side products, and tiles for the expert GEMMs
 // -- full tiles of `gbulk` rows, then (if `gmixed`) one tile of the smallest
 // height that holds the rest of the expert's rows.
+//
+// The GEMM list is laid out for the eight XCDs: position p runs on XCD p % 8
+// (blocks reach the XCDs in turn), after the positions p - 8, p - 16, ... of the
+// same XCD.  Tiles of heavy experts (kHeavyTiles or more) come first, dealt to
+// the XCDs in turn, so that every XCD starts with its share of the long-running
+// work; then each XCD takes a contiguous run of the other experts' tiles (the
+// rows of the light part of the list filled XCD by XCD).  An expert's tiles thus
+// sit on one XCD, one after another, and run together there, so its weights
+// stream through that XCD's L2 once for all its row tiles.  Positions left over
+// hold expert -1 (nothing to do).
 __global__ __launch_bounds__(1024) void k_group_scan(int E, int64_t nb, int mt, int gbulk, int gmixed,
                                                      int32_t* __restrict__ blockcnt, int32_t* __restrict__ counts,
                                                      int32_t* __restrict__ offsets, int32_t* __restrict__ qoffsets,
-                                                     int32_t* __restrict__ tile_e,
+                                                     int32_t* __restrict__ expert_slot, int32_t* __restrict__ tile_e,
                                                      int32_t* __restrict__ tile_m0, int32_t* __restrict__ gtile_e,
                                                      int32_t* __restrict__ gtile_m0, int32_t* __restrict__ gtile_mt,
                                                      unsigned long long* __restrict__ counters) {
@@ -81,23 +92,43 @@ __global__ __launch_bounds__(1024) void k_group_scan(int E, int64_t nb, int mt, 
   const int T = blockDim.x;
   const int per = (E + T - 1) / T;
   const int e0 = min(E, (int)threadIdx.x * per), e1 = min(E, e0 + per);
-  int local = 0, ltiles = 0, lgt = 0, lq = 0;
+  __shared__ int32_t totals[2];
+  int local = 0, ltiles = 0, lheavy = 0, llight = 0, lq = 0, lact = 0;
   for (int e = e0; e < e1; ++e) {
     int c = 0;
     for (int64_t b = 0; b < nb; ++b) c += blockcnt[b * E + e];
     counts[e] = c;
     local += c;
+    lact += c > 0;
     lq += (c + 3) & ~3;
     ltiles += (c + mt - 1) / mt;
-    lgt += (c + gbulk - 1) / gbulk;
+    const int ng = (c + gbulk - 1) / gbulk;
+    if (ng >= kHeavyTiles)
+      lheavy += ng;
+    else
+      llight += ng;
   }
   const int incl = block_inclusive_scan(local, buf);
   const int qincl = block_inclusive_scan(lq, buf);
   const int tincl = block_inclusive_scan(ltiles, buf);
-  const int gincl = block_inclusive_scan(lgt, buf);
-  int run = incl - local, qrun = qincl - lq, trun = tincl - ltiles, grun = gincl - lgt;
+  const int hincl = block_inclusive_scan(lheavy, buf);
+  const int lincl = block_inclusive_scan(llight, buf);
+  const int aincl = block_inclusive_scan(lact, buf);
+  if ((int)threadIdx.x == T - 1) {
+    totals[0] = hincl;
+    totals[1] = lincl;
+  }
+  __syncthreads();
+  // GEMM positions: rows of 8 (one per XCD), heavy rows first, then the light rows
+  // filled XCD by XCD; clear them all first
+  const int kh = (totals[0] + 7) / 8, lc = (totals[1] + 7) / 8, npos = 8 * (kh + lc);
+  for (int q = threadIdx.x; q < npos; q += T) gtile_e[q] = -1;
+  __syncthreads();
+  int run = incl - local, qrun = qincl - lq, trun = tincl - ltiles, arun = aincl - lact;
+  int hrun = hincl - lheavy, lrun = lincl - llight;
   for (int e = e0; e < e1; ++e) {
     const int c = counts[e];
+    expert_slot[e] = c > 0 ? arun++ : -1;
     offsets[e] = run;
     qoffsets[e] = qrun;
     qrun += (c + 3) & ~3;
@@ -114,20 +145,31 @@ __global__ __launch_bounds__(1024) void k_group_scan(int E, int64_t nb, int mt, 
     }
     trun += nt;
     const int ng = (c + gbulk - 1) / gbulk;
+    const bool heavy = ng >= kHeavyTiles;
     for (int j = 0; j < ng; ++j) {
       const int rest = c - j * gbulk;
-      gtile_e[grun + j] = e;
-      gtile_m0[grun + j] = run + j * gbulk;
-      gtile_mt[grun + j] = (gmixed && rest < gbulk) ? rest_tile_rows(rest, gbulk) : gbulk;
+      int q;
+      if (heavy) {
+        q = hrun + j;  // XCD q % 8, row q / 8
+      } else {
+        const int l = lrun + j;  // XCD l / lc, row kh + l % lc
+        q = 8 * (kh + l % lc) + l / lc;
+      }
+      gtile_e[q] = e;
+      gtile_m0[q] = run + j * gbulk;
+      gtile_mt[q] = (gmixed && rest < gbulk) ? rest_tile_rows(rest, gbulk) : gbulk;
     }
-    grun += ng;
+    if (heavy)
+      hrun += ng;
+    else
+      lrun += ng;
     run += c;
   }
   if ((int)threadIdx.x == T - 1) {
     offsets[E] = incl;
     qoffsets[E] = qincl;
     counters[kNumTiles] = (unsigned long long)tincl;
-    counters[kNumGemmTiles] = (unsigned long long)gincl;
+    counters[kNumGemmTiles] = (unsigned long long)npos;
   }
 }
 
@@ -186,7 +228,8 @@ void launch_group(const Dims& d, const WsMap& w, void* ws, const int64_t* ids, h
   }
   k_group_scan<<<1, 1024, 0, st>>>(E, w.nb, (int)w.mt, (int)w.gbulk, w.gmixed ? 1 : 0, blockcnt,
                                    ws_ptr<int32_t>(ws, w.counts), ws_ptr<int32_t>(ws, w.offsets),
-                                   ws_ptr<int32_t>(ws, w.qoffsets), ws_ptr<int32_t>(ws, w.tile_e), ws_ptr<int32_t>(ws, w.tile_m0),
+                                   ws_ptr<int32_t>(ws, w.qoffsets), ws_ptr<int32_t>(ws, w.expert_slot),
+                                   ws_ptr<int32_t>(ws, w.tile_e), ws_ptr<int32_t>(ws, w.tile_m0),
                                    ws_ptr<int32_t>(ws, w.gtile_e), ws_ptr<int32_t>(ws, w.gtile_m0),
                                    ws_ptr<int32_t>(ws, w.gtile_mt), counters);
   note_launch();

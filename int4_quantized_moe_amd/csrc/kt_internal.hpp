@@ -17,6 +17,7 @@ constexpr int kNT = 256;           // output columns per tile of the other GEMMs
 constexpr int kHExp = 32;          // columns of h per exponent (one wave's share of a gate/up tile)
 constexpr int kDgExp = 64;         // columns of dG (or dU) per exponent (one wave's share of a down-dX tile)
 constexpr int kStageExp = 64;      // columns of a staged per-slot row per exponent (one wave's share of a tile)
+constexpr int kHeavyTiles = 8;     // an expert with this many GEMM row tiles or more is spread over the XCDs
 
 // Rows per tile of the LoRA side products for a call: the smallest of
 // 16/32/64/128 that covers the mean number of token-slots per expert (heavier
@@ -54,7 +55,7 @@ enum Counter {
   kBadIds = 0,
   kBadScales = 1,
   kNumTiles = 2,      // side-product tiles
-  kNumGemmTiles = 3,  // expert GEMM tiles
+  kNumGemmTiles = 3,  // positions of the expert GEMM tile list (empty ones included)
   kNumCounters = 8,
   kZeroWord = 16,
   kCounterWords = 32
@@ -105,10 +106,13 @@ struct Dims {
 };
 
 struct WsMap {
-  // fp16 transposed scales of the three projections ([E][K/32][rows]), made by the forward
+  // fp16 transposed scales of the three projections ([active expert][K/32][rows], experts
+  // in use only, at their place in expert_slot), made by the forward
   size_t sct_g, sct_u, sct_d;
+  int64_t nact;  // bound on the experts in use: min(E, token-slots)
   // grouping
   size_t counters, counts, offsets, qoffsets, blockcnt, sorted_slot, row_of_slot, tok_of_row, tile_e, tile_m0;
+  size_t expert_slot;  // [E]: place of an expert among those in use (ascending ids), -1 if none of its slots
   size_t gtile_e, gtile_m0, gtile_mt;  // expert GEMM tiles (mixed heights)
   // forward state kept for the backward
   size_t xh, xexp, ua, ub, g, u, hh, hexp, ud;
@@ -200,10 +204,10 @@ void launch_lora_grads(const Dims& d, const WsMap& w, void* ws, const uint16_t* 
                        const float* route_weights, const LoraGradOut& out, int accumulate, float scale,
                        hipStream_t st);
 void launch_fill_zero_f32(float* p, int64_t n, hipStream_t st);
-// scales [E][rows][G] bf16 -> [E][G][rows] fp16, rows within-8 permuted, experts in use only
-// (offsets from the grouping); counts out-of-domain scales
-void launch_scales_t(const uint16_t* s, int64_t E, int64_t rows, int64_t G, const int32_t* offsets, uint16_t* out,
-                     unsigned long long* bad, int fmt, hipStream_t st);
+// scales [E][rows][G] bf16 -> [active][G][rows] fp16, rows within-8 permuted, experts in use
+// only, each at expert_slot[e] (from the grouping); counts out-of-domain scales
+void launch_scales_t(const uint16_t* s, int64_t E, int64_t rows, int64_t G, const int32_t* expert_slot,
+                     uint16_t* out, unsigned long long* bad, int fmt, hipStream_t st);
 // one exponent per row for h ([Ms, I], chunks of kHChunk) and dG|dU ([Ms, 2I], chunks of kNT per half)
 void launch_normalize_chunks(uint16_t* buf, int32_t* exps, const int32_t* nrows, int64_t max_rows, int64_t cols,
                              int64_t split, int nch, int chunkw, hipStream_t st);
