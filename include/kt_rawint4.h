@@ -45,6 +45,8 @@ extern "C" {
 #define KT_RAWINT4_FORMAT_MXFP4 1
 #define KT_RAWINT4_MAX_EXPERTS 8192
 #define KT_RAWINT4_MAX_RANK 128
+/* bytes of the device array kt_rawint4_moe_infer_static works in (per GPU) */
+#define KT_RAWINT4_STATIC_SCRATCH_BYTES (64u << 20)
 
 /*
  * One layer.  E = num_experts, k = top_k, H = hidden, I = intermediate,
@@ -152,6 +154,25 @@ size_t kt_rawint4_moe_infer_workspace_bytes(const kt_rawint4_moe_layer* layer, i
 int kt_rawint4_moe_infer(const kt_rawint4_moe_layer* layer, int32_t qlen, const uint16_t* inputs,
                          const int64_t* expert_ids, const float* route_weights, uint16_t* output, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/*
+ * The inference forward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Arguments, kernels and output as kt_rawint4_moe_infer (equal to
+ * it bit for bit), without a workspace: the call works in a device array of
+ * KT_RAWINT4_STATIC_SCRATCH_BYTES that this library holds on each GPU it runs
+ * on, from the first call there until the process ends, and allocates
+ * nothing.  A call whose kt_rawint4_moe_infer_workspace_bytes exceeds that
+ * size returns KT_RAWINT4_EWORKSPACE (at 384 experts, top-8, hidden 7168,
+ * intermediate 2048: up to 3 tokens per call).  Every call on one GPU uses
+ * the same array, which keeps the last call's contents, so calls that overlap
+ * on one GPU (on other streams, from other host threads) race: order them on
+ * one stream.  The call runs on the current device, records no profiling
+ * events, and otherwise fails like kt_rawint4_moe_infer.
+ */
+int kt_rawint4_moe_infer_static(const kt_rawint4_moe_layer* layer, int32_t qlen, const uint16_t* inputs,
+                                const int64_t* expert_ids, const float* route_weights, uint16_t* output,
+                                void* stream);
 
 /*
  * Backward of the same call (page "rawint4_sft_reference.py",

@@ -21,6 +21,8 @@ KT_RAWINT4_EINVAL = -1
 KT_RAWINT4_EWORKSPACE = -2
 KT_RAWINT4_EHIP = -3
 
+KT_RAWINT4_STATIC_SCRATCH_BYTES = 64 << 20
+
 KT_RAWINT4_FORMAT_RAWINT4 = 0
 KT_RAWINT4_FORMAT_MXFP4 = 1
 FORMATS = {"rawint4": KT_RAWINT4_FORMAT_RAWINT4, "mxfp4": KT_RAWINT4_FORMAT_MXFP4}
@@ -76,6 +78,7 @@ def load_library() -> ctypes.CDLL:
         "kt_rawint4_moe_fwd": (ctypes.c_int, [lp, i32, _vp, _vp, _vp, _vp, _vp, sz, _vp]),
         "kt_rawint4_moe_infer_workspace_bytes": (sz, [lp, i32]),
         "kt_rawint4_moe_infer": (ctypes.c_int, [lp, i32, _vp, _vp, _vp, _vp, _vp, sz, _vp]),
+        "kt_rawint4_moe_infer_static": (ctypes.c_int, [lp, i32, _vp, _vp, _vp, _vp, _vp]),
         "kt_rawint4_moe_bwd": (ctypes.c_int, [lp, i32, _vp, _vp, _vp, _vp, _vp, _vp] + [_vp] * 6 + [i32, f32, _vp, sz, _vp]),
         "kt_rawint4_moe_bwd_recompute": (ctypes.c_int,
                                          [lp, i32, _vp, _vp, _vp, _vp, _vp, _vp] + [_vp] * 6 + [i32, f32, _vp, sz, _vp]),
@@ -166,6 +169,11 @@ def kt_rawint4_moe_infer(layer, qlen, inputs, expert_ids, route_weights, output,
     _check(load_library().kt_rawint4_moe_infer(ctypes.byref(layer), int(qlen), _ptr(inputs), _ptr(expert_ids),
                                                _ptr(route_weights), _ptr(output), _ptr(workspace),
                                                _nbytes(workspace) if workspace is not None else 0, _stream(stream)))
+
+
+def kt_rawint4_moe_infer_static(layer, qlen, inputs, expert_ids, route_weights, output, stream=None) -> None:
+    _check(load_library().kt_rawint4_moe_infer_static(ctypes.byref(layer), int(qlen), _ptr(inputs), _ptr(expert_ids),
+                                                      _ptr(route_weights), _ptr(output), _stream(stream)))
 
 
 def kt_rawint4_moe_bwd(layer, qlen, inputs, expert_ids, route_weights, grad_output, grad_input, grad_route, d_gate_a,

@@ -20,6 +20,8 @@ static int fail(int code, const char* msg) {
   return code;
 }
 
+int set_error(int code, const char* msg) { return fail(code, msg); }
+
 static size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Planner {
@@ -175,6 +177,10 @@ static int check_layer(const kt_rawint4_moe_layer* L, int32_t qlen, Dims* d, boo
   return KT_RAWINT4_OK;
 }
 
+int check_layer_dims(const kt_rawint4_moe_layer* L, int32_t qlen, Dims* d, bool allow_base) {
+  return check_layer(L, qlen, d, allow_base);
+}
+
 static LayerPtrs layer_ptrs(const kt_rawint4_moe_layer* L) {
   LayerPtrs p;
   p.wg = L->gate_packed;
@@ -297,6 +303,8 @@ struct ProfRec {
 
 static std::mutex g_prof_mu;
 static bool g_prof_on = false;
+// set while a call that must create nothing runs on this thread: no profiling events
+static thread_local bool g_no_events = false;
 static std::vector<hipEvent_t> g_prof_pool;
 static std::vector<ProfRec> g_prof_recs;
 
@@ -319,7 +327,7 @@ struct PhaseScope {
   hipEvent_t a = nullptr, b = nullptr;
   PhaseScope(int ph, hipStream_t s) : phase(ph), st(s) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
-    if (!g_prof_on) return;
+    if (!g_prof_on || g_no_events) return;
     a = prof_event();
     b = prof_event();
     if (!a || !b || hipEventRecord(a, st) != hipSuccess) release();
@@ -711,3 +719,12 @@ const char* kt_rawint4_last_error(void) { return g_last_error.c_str(); }
 const char* kt_rawint4_weight_layout(void) { return "compressed-tensors-rawint4-g32-v1"; }
 
 }  // extern "C"
+
+int kt::run_forward_no_alloc(const kt_rawint4_moe_layer* layer, Dims d, const uint16_t* inputs,
+                             const int64_t* expert_ids, const float* route_weights, uint16_t* output,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  g_no_events = true;
+  const int rc = run_forward(layer, d, inputs, expert_ids, route_weights, output, workspace, workspace_bytes, stream);
+  g_no_events = false;
+  return rc;
+}

@@ -157,6 +157,18 @@ void begin_launches();
 void note_launch();
 hipError_t first_launch_error();
 
+// ---------------------------------------------------------------- entry-point helpers
+
+// Argument checks of a layer call (allow_base: all six LoRA pointers may be
+// NULL, the frozen base alone); the error message as kt_rawint4_last_error
+// reports it; the inference forward into a given workspace with no profiling
+// events (so that nothing is created or allocated on the way).
+int check_layer_dims(const kt_rawint4_moe_layer* L, int32_t qlen, Dims* d, bool allow_base);
+int set_error(int code, const char* msg);
+int run_forward_no_alloc(const kt_rawint4_moe_layer* layer, Dims d, const uint16_t* inputs,
+                         const int64_t* expert_ids, const float* route_weights, uint16_t* output, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
 // ---------------------------------------------------------------- launchers (enqueue only)
 
 void launch_group(const Dims& d, const WsMap& w, void* ws, const int64_t* ids, hipStream_t st);

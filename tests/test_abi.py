@@ -23,9 +23,16 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(_lib.LIBRARY_PATH)
     names = _declared()
-    assert len(names) == 18
+    assert len(names) == 19
     for name in names:
         assert hasattr(lib, name), name
+
+
+def test_static_scratch_size_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define KT_RAWINT4_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m, "KT_RAWINT4_STATIC_SCRATCH_BYTES not found"
+    assert _lib.KT_RAWINT4_STATIC_SCRATCH_BYTES == int(m.group(1)) << int(m.group(2))
 
 
 def test_profile_phase_names():
