@@ -62,11 +62,16 @@ extern "C" {
  * gate and up have N = I, K = H; down has N = H, K = I.  Weight rows must be
  * 16-byte aligned (true for any base pointer aligned to 16 bytes).
  *
- * Numeric domain: nonzero scales must lie in [2^-14, 2720] in magnitude (every
- * bf16 scale of a practical int4 checkpoint does).  There each decoded weight
- * is exact in fp16, which is what the kernels multiply with.  Scales outside
- * the domain are counted (see kt_rawint4_moe_diagnostics); results computed
- * with them are not defined (they may be inf or NaN).
+ * Numeric domain: the kernels multiply exact fp16 weights, which nonzero
+ * scales in [2^-14, 2720] in magnitude give.  Any other finite bf16 scale is
+ * handled by a power-of-two shift per expert and projection group (gate and up
+ * together, down alone): the group's scales are taken times 2^-s, s the
+ * smallest integer that brings the largest of them to 2720 or below, and the
+ * sums are taken times 2^s again.  That is exact wherever a group's nonzero
+ * scales span at most the domain's range (a factor of about 2^25).  Scales
+ * that still lie outside (a group spanning more, non-finite scales) are
+ * counted (see kt_rawint4_moe_diagnostics); weights decoded from them are
+ * rounded to fp16 (tiny ones lose precision, non-finite ones stay so).
  *
  * weight_format = KT_RAWINT4_FORMAT_MXFP4 selects the MXFP4 base of the same
  * layer (page "ext_bindings.cpp" commit log: MXFP4_SFT_MOE, E2M1 weights with
@@ -76,9 +81,10 @@ extern "C" {
  * bias 1, mantissa bit 0: 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives)
  * times the group's scale, and the scales are the UE8M0 exponents bit-cast to
  * bf16 (e << 7, as the pages' loader converts them), i.e. powers of two.  Its
- * numeric domain: scales 0 or 2^j with -13 <= j <= 13 (UE8M0 114 .. 140);
- * others are counted as above.  Everything else (LoRA, clamp, gradients,
- * window rule) is as for RAWINT4.
+ * numeric domain: scales 0 or 2^j with -13 <= j <= 13 (UE8M0 114 .. 140), the
+ * group shift above extending it to any power of two within a span of 2^26;
+ * others (not a power of two, negative) are counted as above.  Everything
+ * else (LoRA, clamp, gradients, window rule) is as for RAWINT4.
  *
  * LoRA tensors (fp32): gate_lora_a [E, r, H], gate_lora_b [E, I, r],
  * up_lora_a [E, r, H], up_lora_b [E, I, r], down_lora_a [E, r, I],
@@ -237,6 +243,7 @@ int kt_rawint4_unpack(const uint8_t* packed, int64_t n, int64_t k, int8_t* codes
  * matrix kernels (the one of the stored orientation, whose exact fp16 values
  * are returned widened to fp32, and the one of the transposed orientation); a
  * dword where they give different values comes out as NaN.  k % 32 == 0.
+ * The scales are used as given (no shift): exact for scales in the domain.
  */
 int kt_rawint4_dequant(const uint8_t* packed, const uint16_t* scales, int64_t n, int64_t k, float* weights,
                        void* stream);
@@ -265,8 +272,9 @@ int kt_rawint4_group(const int64_t* expert_ids, int32_t qlen, int32_t top_k, int
 /*
  * Synchronising read of the device-side counters of the latest forward in
  * `workspace` (written by kt_rawint4_moe_fwd or kt_rawint4_group): expert ids
- * outside [0, E) and scales outside the numeric domain (each scale of the
- * three projections of every expert the forward routes to is checked once).
+ * outside [0, E) and scales outside the numeric domain that no shift of their
+ * group brings in (each scale of the three projections of every expert the
+ * forward routes to is checked once).
  * Host pointers out; either may be NULL.
  */
 int kt_rawint4_moe_diagnostics(const void* workspace, size_t workspace_bytes, int64_t* bad_ids, int64_t* bad_scales,

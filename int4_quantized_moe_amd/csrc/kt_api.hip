@@ -77,6 +77,7 @@ WsMap plan_workspace(const Dims& d) {
   w.sct_g = pl.take(2 * (size_t)w.nact * (size_t)d.I * (size_t)(d.H / 32));
   w.sct_u = pl.take(2 * (size_t)w.nact * (size_t)d.I * (size_t)(d.H / 32));
   w.sct_d = pl.take(2 * (size_t)w.nact * (size_t)d.H * (size_t)(d.I / 32));
+  w.sshift = pl.take(sizeof(int32_t) * 2 * (size_t)d.E);
   w.h_nch = (d.I + kHExp - 1) / kHExp;
   w.dr_nt = (d.I + kDgExp - 1) / kDgExp;
   w.dg_nch = 2 * w.dr_nt;
@@ -378,9 +379,12 @@ static void launch_forward_front(const kt_rawint4_moe_layer* layer, const Dims& 
     PhaseScope ph(kPhScales, st);
     unsigned long long* bad = ws_ptr<unsigned long long>(ws, w.counters) + kBadScales;
     const int32_t* slot = ws_ptr<int32_t>(ws, w.expert_slot);
-    launch_scales_t(layer->gate_scale, d.E, d.I, d.H / 32, slot, ws_ptr<uint16_t>(ws, w.sct_g), bad, d.fmt, st);
-    launch_scales_t(layer->up_scale, d.E, d.I, d.H / 32, slot, ws_ptr<uint16_t>(ws, w.sct_u), bad, d.fmt, st);
-    launch_scales_t(layer->down_scale, d.E, d.H, d.I / 32, slot, ws_ptr<uint16_t>(ws, w.sct_d), bad, d.fmt, st);
+    int32_t* sshift = ws_ptr<int32_t>(ws, w.sshift);
+    launch_scales_t(layer->gate_scale, d.E, d.I, d.H / 32, slot, ws_ptr<uint16_t>(ws, w.sct_g), sshift, 0, d.fmt, st);
+    launch_scales_t(layer->up_scale, d.E, d.I, d.H / 32, slot, ws_ptr<uint16_t>(ws, w.sct_u), sshift, 0, d.fmt, st);
+    launch_scales_t(layer->down_scale, d.E, d.H, d.I / 32, slot, ws_ptr<uint16_t>(ws, w.sct_d), sshift, 1, d.fmt, st);
+    launch_scales_fix(L, d, slot, sshift, ws_ptr<uint16_t>(ws, w.sct_g), ws_ptr<uint16_t>(ws, w.sct_u),
+                      ws_ptr<uint16_t>(ws, w.sct_d), bad, st);
   }
   {
     PhaseScope ph(kPhXHalf, st);

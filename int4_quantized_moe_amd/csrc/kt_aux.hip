@@ -70,13 +70,15 @@ void launch_rows_to_half(const uint16_t* src, int64_t rows, int64_t cols, uint16
 // fp16, rows of every aligned group of 8 in the within-8 permuted order, so that
 // a GEMM stage reads the scales of its column (or contraction-row) block as one
 // contiguous run in both orientations.  Experts that received no token-slot
-// are skipped; the others go to their place among the experts in use.  Scales outside the numeric domain are counted (once each, over
-// the experts in use).  64 x 64 tiles pass through LDS so that the reads
-// (along G, 16 bytes per lane where G allows) and the writes (along rows, 16
-// bytes per lane) are both coalesced.
+// are skipped; the others go to their place among the experts in use.  An
+// expert with a scale outside the exact domain is marked (sshift[2 e + grp])
+// for k_scales_fix.  64 x 64 tiles pass through LDS so that the reads (along G,
+// 16 bytes per lane where G allows) and the writes (along rows, 16 bytes per
+// lane) are both coalesced.
 __global__ __launch_bounds__(256) void k_scales_t(const uint16_t* __restrict__ s, int64_t rows, int64_t G,
                                                    const int32_t* __restrict__ expert_slot,
-                                                   uint16_t* __restrict__ out, unsigned long long* bad, int fmt) {
+                                                   uint16_t* __restrict__ out, int32_t* __restrict__ sshift, int grp,
+                                                   int fmt) {
   __shared__ uint16_t t[64][72];  // [row][group], 144-byte pitch
   __shared__ int nbad_w[4];
   const int64_t e = blockIdx.z;
@@ -140,17 +142,122 @@ __global__ __launch_bounds__(256) void k_scales_t(const uint16_t* __restrict__ s
   for (int off = 1; off < 64; off <<= 1) nbad += __shfl_xor(nbad, off);
   if ((threadIdx.x & 63) == 0) nbad_w[threadIdx.x >> 6] = nbad;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const int n = nbad_w[0] + nbad_w[1] + nbad_w[2] + nbad_w[3];
-    if (n) atomicAdd(bad, (unsigned long long)n);
-  }
+  if (threadIdx.x == 0 && nbad_w[0] + nbad_w[1] + nbad_w[2] + nbad_w[3] > 0) atomicOr(&sshift[2 * e + grp], 1);
 }
 
 void launch_scales_t(const uint16_t* s, int64_t E, int64_t rows, int64_t G, const int32_t* expert_slot,
-                     uint16_t* out, unsigned long long* bad, int fmt, hipStream_t st) {
+                     uint16_t* out, int32_t* sshift, int grp, int fmt, hipStream_t st) {
   if (E <= 0 || rows <= 0 || G <= 0) return;
   dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((G + 63) / 64), (unsigned)E);
-  k_scales_t<<<grid, 256, 0, st>>>(s, rows, G, expert_slot, out, bad, fmt);
+  k_scales_t<<<grid, 256, 0, st>>>(s, rows, G, expert_slot, out, sshift, grp, fmt);
+  note_launch();
+}
+
+// The scales of one expert's projection group (gate and up together, since the
+// gate/up dX GEMM contracts over both; down alone) that k_scales_t marked:
+// with s the smallest integer for which the largest magnitude times 2^-s lies
+// at or below the domain's top (2720, or 2^13 for MXFP4), the tables hold
+// scale * 2^-s instead and the GEMMs multiply their sums by 2^s.  The weights
+// are then exact again wherever the group's scales span no more than the
+// domain's range (about 2^25 for RAWINT4); scales still outside are counted.
+// One block per (expert, group); rare, so plain strided loops.
+struct ScaleFixArgs {
+  const uint16_t* s[3];  // bf16 scales [E][rows][G]: gate, up, down
+  uint16_t* out[3];      // fp16 tables [active][G][rows]
+  int64_t rows[3], G[3];
+  const int32_t* expert_slot;
+  int32_t* sshift;
+  unsigned long long* bad;
+  int fmt;
+};
+
+__global__ __launch_bounds__(256) void k_scales_fix(ScaleFixArgs a) {
+  __shared__ float red[2][4];
+  __shared__ int s_shift;
+  const int64_t e = blockIdx.x;
+  const int grp = blockIdx.y;
+  const int32_t es = a.expert_slot[e];
+  if (es < 0) return;
+  const int marked = a.sshift[2 * e + grp];  // every thread reads the mark before it is replaced
+  if (!marked) return;
+  const int first = grp == 0 ? 0 : 2, last = grp == 0 ? 1 : 2;
+  // largest magnitude and smallest nonzero magnitude of the group
+  float mx = 0.f, mn = INFINITY;
+  for (int t = first; t <= last; ++t) {
+    const int64_t n = a.rows[t] * a.G[t];
+    const uint16_t* se = a.s[t] + e * n;
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+      const float v = fabsf(bf16_to_float(se[i]));
+      mx = fmaxf(mx, v);
+      if (v > 0.f) mn = fminf(mn, v);
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    mx = fmaxf(mx, __shfl_xor(mx, off));
+    mn = fminf(mn, __shfl_xor(mn, off));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    red[0][threadIdx.x >> 6] = mx;
+    red[1][threadIdx.x >> 6] = mn;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    mx = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+    const float top = a.fmt ? 0x1p13f : 2720.f;
+    int sh = 0;
+    if (mx < INFINITY) {  // (a non-finite scale stays outside whatever the shift)
+      while (ldexpf(mx, -sh) > top) ++sh;
+      while (sh > -160 && ldexpf(mx, -(sh - 1)) <= top) --sh;
+    }
+    s_shift = sh;
+  }
+  __syncthreads();
+  const int sh = s_shift;
+  int nbad = 0;
+  for (int t = first; t <= last; ++t) {
+    const int64_t rows = a.rows[t], G = a.G[t], n = rows * G;
+    const uint16_t* se = a.s[t] + e * n;
+    uint16_t* oe = a.out[t] + (int64_t)es * G * rows;
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+      const int64_t r = i / G, g = i % G;
+      const float v = ldexpf(bf16_to_float(se[i]), -sh);
+      nbad += (a.fmt ? scale_in_domain_mxfp4(v) : scale_in_domain(v)) ? 0 : 1;
+      oe[g * rows + perm_pos((int)(r & 7)) + (r & ~(int64_t)7)] = float_to_half_bits(v);
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) nbad += __shfl_xor(nbad, off);
+  __syncthreads();  // red[] is reused
+  if ((threadIdx.x & 63) == 0) red[0][threadIdx.x >> 6] = __int_as_float(nbad);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int total = __float_as_int(red[0][0]) + __float_as_int(red[0][1]) + __float_as_int(red[0][2]) +
+                      __float_as_int(red[0][3]);
+    if (total) atomicAdd(a.bad, (unsigned long long)total);
+    a.sshift[2 * e + grp] = sh;
+  }
+}
+
+void launch_scales_fix(const LayerPtrs& L, const Dims& d, const int32_t* expert_slot, int32_t* sshift,
+                       uint16_t* sct_g, uint16_t* sct_u, uint16_t* sct_d, unsigned long long* bad, hipStream_t st) {
+  if (d.E <= 0) return;
+  ScaleFixArgs a;
+  a.s[0] = L.sg;
+  a.s[1] = L.su;
+  a.s[2] = L.sd;
+  a.out[0] = sct_g;
+  a.out[1] = sct_u;
+  a.out[2] = sct_d;
+  a.rows[0] = a.rows[1] = d.I;
+  a.G[0] = a.G[1] = d.H / kGroup;
+  a.rows[2] = d.H;
+  a.G[2] = d.I / kGroup;
+  a.expert_slot = expert_slot;
+  a.sshift = sshift;
+  a.bad = bad;
+  a.fmt = d.fmt;
+  k_scales_fix<<<dim3((unsigned)d.E, 2), 256, 0, st>>>(a);
   note_launch();
 }
 

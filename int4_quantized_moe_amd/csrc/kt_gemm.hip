@@ -87,6 +87,7 @@ struct GemmParams {
   const int32_t* tile_m0;
   const int32_t* tile_mt;
   const int32_t* expert_slot;  // place of an expert in the transposed scale tables
+  const int32_t* sshift;       // [E][2] power-of-two shift of an expert's gate/up and down scale tables
   const unsigned long long* counters;
   LayerPtrs L;
   const uint16_t* a_src;      // fp16 activation rows (within-8 permuted order)
@@ -623,6 +624,20 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
   }
   __syncthreads();  // every wave is done with the ring before it is reused
 
+  // The scale tables hold scale * 2^-s for an expert whose scales lie outside
+  // the exact domain (s = 0 otherwise): the sums get 2^s back before the LoRA terms.
+  {
+    const int sh = p.sshift[2 * e + ((KIND == kGateUp || KIND == kGateUpBwd) ? 0 : 1)];
+    if (sh != 0) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[mb][f][i] = ldexpf(acc[mb][f][i], sh);
+    }
+  }
+
   // ---------------------------------------------------------------- LoRA K-steps (bf16 hi/lo)
   // One group of the LoRA contraction at a time, both operands staged in the
   // (now idle) ring: the side product arrives as bf16 hi/lo planes already
@@ -1132,6 +1147,7 @@ void launch_gemm(GemmKind kind, const Dims& d, const WsMap& w, void* ws, const L
   p.tile_m0 = ws_ptr<int32_t>(ws, w.gtile_m0);
   p.tile_mt = ws_ptr<int32_t>(ws, w.gtile_mt);
   p.expert_slot = ws_ptr<int32_t>(ws, w.expert_slot);
+  p.sshift = ws_ptr<int32_t>(ws, w.sshift);
   p.counters = ws_ptr<unsigned long long>(ws, w.counters);
   p.L = L;
   p.rw = route_weights;

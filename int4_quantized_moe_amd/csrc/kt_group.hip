@@ -84,7 +84,8 @@ __device__ __forceinline__ int rest_tile_rows(int r, int bulk) {
 __global__ __launch_bounds__(1024) void k_group_scan(int E, int64_t nb, int mt, int gbulk, int gmixed,
                                                      int32_t* __restrict__ blockcnt, int32_t* __restrict__ counts,
                                                      int32_t* __restrict__ offsets, int32_t* __restrict__ qoffsets,
-                                                     int32_t* __restrict__ expert_slot, int32_t* __restrict__ tile_e,
+                                                     int32_t* __restrict__ expert_slot, int32_t* __restrict__ sshift,
+                                                     int32_t* __restrict__ tile_e,
                                                      int32_t* __restrict__ tile_m0, int32_t* __restrict__ gtile_e,
                                                      int32_t* __restrict__ gtile_m0, int32_t* __restrict__ gtile_mt,
                                                      unsigned long long* __restrict__ counters) {
@@ -129,6 +130,7 @@ __global__ __launch_bounds__(1024) void k_group_scan(int E, int64_t nb, int mt, 
   for (int e = e0; e < e1; ++e) {
     const int c = counts[e];
     expert_slot[e] = c > 0 ? arun++ : -1;
+    if (sshift) sshift[2 * e] = sshift[2 * e + 1] = 0;
     offsets[e] = run;
     qoffsets[e] = qrun;
     qrun += (c + 3) & ~3;
@@ -229,6 +231,7 @@ void launch_group(const Dims& d, const WsMap& w, void* ws, const int64_t* ids, h
   k_group_scan<<<1, 1024, 0, st>>>(E, w.nb, (int)w.mt, (int)w.gbulk, w.gmixed ? 1 : 0, blockcnt,
                                    ws_ptr<int32_t>(ws, w.counts), ws_ptr<int32_t>(ws, w.offsets),
                                    ws_ptr<int32_t>(ws, w.qoffsets), ws_ptr<int32_t>(ws, w.expert_slot),
+                                   w.sshift ? ws_ptr<int32_t>(ws, w.sshift) : nullptr,
                                    ws_ptr<int32_t>(ws, w.tile_e), ws_ptr<int32_t>(ws, w.tile_m0),
                                    ws_ptr<int32_t>(ws, w.gtile_e), ws_ptr<int32_t>(ws, w.gtile_m0),
                                    ws_ptr<int32_t>(ws, w.gtile_mt), counters);

@@ -109,6 +109,10 @@ struct WsMap {
   // fp16 transposed scales of the three projections ([active expert][K/32][rows], experts
   // in use only, at their place in expert_slot), made by the forward
   size_t sct_g, sct_u, sct_d;
+  // [E][2]: power-of-two shift s of an expert's gate/up (0) and down (1) scales: the tables
+  // hold scale * 2^-s, chosen so that they lie in the exact domain (0 when they already do);
+  // the grouping clears it, the scale conversion marks experts that need one
+  size_t sshift;
   int64_t nact;  // bound on the experts in use: min(E, token-slots)
   // grouping
   size_t counters, counts, offsets, qoffsets, blockcnt, sorted_slot, row_of_slot, tok_of_row, tile_e, tile_m0;
@@ -217,9 +221,14 @@ void launch_lora_grads(const Dims& d, const WsMap& w, void* ws, const uint16_t* 
                        hipStream_t st);
 void launch_fill_zero_f32(float* p, int64_t n, hipStream_t st);
 // scales [E][rows][G] bf16 -> [active][G][rows] fp16, rows within-8 permuted, experts in use
-// only, each at expert_slot[e] (from the grouping); counts out-of-domain scales
+// only, each at expert_slot[e] (from the grouping); an expert with a scale outside the
+// exact domain is marked in sshift[2 e + grp]
 void launch_scales_t(const uint16_t* s, int64_t E, int64_t rows, int64_t G, const int32_t* expert_slot,
-                     uint16_t* out, unsigned long long* bad, int fmt, hipStream_t st);
+                     uint16_t* out, int32_t* sshift, int grp, int fmt, hipStream_t st);
+// for every marked expert: the shift that brings its scales into the domain, the tables
+// converted again with it, and the scales still outside counted into *bad
+void launch_scales_fix(const LayerPtrs& L, const Dims& d, const int32_t* expert_slot, int32_t* sshift,
+                       uint16_t* sct_g, uint16_t* sct_u, uint16_t* sct_d, unsigned long long* bad, hipStream_t st);
 // one exponent per row for h ([Ms, I], chunks of kHChunk) and dG|dU ([Ms, 2I], chunks of kNT per half)
 void launch_normalize_chunks(uint16_t* buf, int32_t* exps, const int32_t* nrows, int64_t max_rows, int64_t cols,
                              int64_t split, int nch, int chunkw, hipStream_t st);

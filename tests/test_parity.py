@@ -94,29 +94,69 @@ def test_dequant_bit_exact(dev):
     assert np.array_equal(out.cpu().numpy(), O.dequant(packed, scales))
 
 
-def test_rawint4_scales_outside_the_domain_are_counted(dev):
-    # nonzero scales below 2^-14 or above 2720 in magnitude leave the domain where
-    # the decoded weights are exact in fp16; the forward counts them once each
+@pytest.mark.parametrize("fmt", ["rawint4", "mxfp4"])
+def test_scales_brought_into_the_domain(dev, fmt):
+    # scales whose weights are not exact in fp16 as they stand: a projection group
+    # scaled by 2^-20 (all tiny), one by 2^16 (above the top), and a stray tiny
+    # scale among ordinary ones.  The conversion shifts such a group's scales by a
+    # power of two into the exact domain and the GEMMs shift their sums back, so
+    # the layer matches the oracle and nothing is counted.
+    import dataclasses
+
+    cfg, weights, batch = W.make_workload(1)
+    if fmt == "mxfp4":
+        cfg = dataclasses.replace(cfg, name="rect_clamp_mxfp4", weight_format="mxfp4")
+        weights = W.make_weights(cfg, W.config_seed(1))
+    _say("scales shifted into the domain", cfg.name)
+    used = sorted(set(batch.expert_ids.ravel().tolist()))
+    assert len(used) >= 3
+
+    def times(bits, k):  # bf16 scale bits times 2^k (exact: exponent only)
+        f = W.bf16_bits_to_f32(bits).astype(np.float64) * 2.0 ** k
+        return W.f32_to_bf16_bits(f.astype(np.float32))
+
+    e0, e1, e2 = used[:3]
+    weights.gate_scale[e0] = times(weights.gate_scale[e0], -20)
+    weights.up_scale[e0] = times(weights.up_scale[e0], -20)
+    weights.down_scale[e1] = times(weights.down_scale[e1], 16)
+    weights.up_scale[e2, 3, 1] = times(weights.up_scale[e2, 3:4, 1:2], -12)[0, 0]
+    dl, _, ws, gpu = _run_gpu(dev, cfg, weights, batch)
+    bad_ids, bad_scales = __import__("int4_quantized_moe_amd")._lib.kt_rawint4_moe_diagnostics(ws)
+    assert bad_ids == 0 and bad_scales == 0
+    ref = _reference(cfg, weights, batch, gpu)
+    _check_all(f"shifted_{fmt}", gpu, ref, set(used))
+    # each shifted expert on its own (its gradients are far smaller than the others')
+    for e in (e0, e1, e2):
+        for n in O.LORA_NAMES:
+            _close(f"shifted_{fmt}.expert{e}.{n}", gpu["grads"][n][e], ref["grads"][n][e])
+    # and the output rows of tokens whose slots all use the shifted experts
+    rows = np.flatnonzero(np.isin(batch.expert_ids, [e0, e1, e2]).all(axis=1))
+    if rows.size:
+        _close(f"shifted_{fmt}.forward_rows", gpu["out"][rows], ref["out"][rows])
+
+
+def test_scales_beyond_the_domain_are_counted(dev):
+    # a group whose scales span more than the domain's range (about 2^25) keeps
+    # scales below it after the shift: those are counted, once each, over the
+    # experts in use only
     cfg, weights, batch = W.make_workload(0)
-    _say("rawint4 scale domain")
+    _say("rawint4 scales beyond the domain")
     used = int(batch.expert_ids[0, 0])
     unused = [e for e in range(cfg.num_experts) if e not in set(batch.expert_ids.ravel().tolist())]
-    out_of_domain = W.f32_to_bf16_bits(np.array([3e-5, 4096.0, -1e-6], dtype=np.float32))
-    weights.gate_scale[used, 0, 0] = out_of_domain[0]
-    weights.up_scale[used, 5, 3] = out_of_domain[1]
-    weights.down_scale[used, 2, 1] = out_of_domain[2]
-    weights.gate_scale[used, 1, 1] = W.f32_to_bf16_bits(np.array([6.103515625e-05], dtype=np.float32))[0]  # 2^-14: in
-    weights.down_scale[used, 3, 0] = W.f32_to_bf16_bits(np.array([-2720.0], dtype=np.float32))[0]  # in
-    weights.up_scale[used, 7, 2] = 0  # zero: in
+    tiny = W.f32_to_bf16_bits(np.array([1e-9, -1e-12], dtype=np.float32))
+    weights.gate_scale[used, 0, 0] = tiny[0]
+    weights.down_scale[used, 2, 1] = tiny[1]
+    weights.gate_scale[used, 1, 1] = W.f32_to_bf16_bits(np.array([6.103515625e-05], dtype=np.float32))[0]
+    weights.up_scale[used, 7, 2] = 0  # zero: in the domain
     if unused:  # experts no slot reaches are not converted, so not counted
-        weights.gate_scale[unused[0], 0, 0] = out_of_domain[1]
+        weights.gate_scale[unused[0], 0, 0] = tiny[0]
     dl = dev.DeviceLayer(cfg, weights)
     db = dev.DeviceBatch(batch)
     ws = dl.workspace(db.qlen)
     dl.forward(db.inputs, db.expert_ids, db.route_weights, ws)
     torch.cuda.synchronize()
     bad_ids, bad_scales = __import__("int4_quantized_moe_amd")._lib.kt_rawint4_moe_diagnostics(ws)
-    assert bad_ids == 0 and bad_scales == 3
+    assert bad_ids == 0 and bad_scales == 2
 
 
 @pytest.mark.parametrize("index", range(len(W.CONFIGS)))
