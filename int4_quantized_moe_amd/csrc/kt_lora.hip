@@ -117,8 +117,15 @@ __global__ __launch_bounds__(256) void k_lora_side(SideArgs a) {
   __shared__ __align__(16) uint8_t Bh[2][kBB], Bl[2][kBB];
   __shared__ int32_t s_src[MT], s_ex[MT], s_pex[MT];
 
-  const int tile = blockIdx.x;
-  if ((unsigned long long)tile >= a.counters[kNumTiles]) return;
+  // Work item (tile, contraction range); block b (in dispatch order) runs on
+  // XCD b % 8, and each XCD takes a contiguous run of the items in use: the
+  // tiles of one expert (consecutive in the list) and the ranges of one tile
+  // share an XCD, and so its L2 for the expert's LoRA matrix.
+  const unsigned nitems = (unsigned)a.counters[kNumTiles] * gridDim.y;
+  const unsigned bid = blockIdx.y * gridDim.x + blockIdx.x, per = (nitems + 7) / 8;
+  const unsigned item = (bid % 8) * per + bid / 8;
+  if (bid / 8 >= per || item >= nitems) return;
+  const int tile = (int)(item / gridDim.y), ks = (int)(item % gridDim.y);
   const int e = a.tile_e[tile], m0 = a.tile_m0[tile];
   const int mlen = min(MT, a.offsets[e + 1] - m0);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
@@ -254,7 +261,7 @@ __global__ __launch_bounds__(256) void k_lora_side(SideArgs a) {
   const int cw = w * 16 * NB;  // this wave's first column
   const int asw = (lr >> 2) & 3;
   // this block's contraction range: steps [s0, s1) of kSK values
-  const int ksteps = kdim / kSK, ks = blockIdx.y;
+  const int ksteps = kdim / kSK;
   const int s0 = (int)((int64_t)ksteps * ks / a.ksplit), s1 = (int)((int64_t)ksteps * (ks + 1) / a.ksplit);
   const int nsteps = s1 - s0;
   const IntTag<0> r0{};
