@@ -76,6 +76,10 @@ template <bool B>
 struct BoolTag {
   static constexpr bool value = B;
 };
+template <int V>
+struct FTag {
+  static constexpr int value = V;
+};
 typedef void __attribute__((address_space(3)))* lds_ptr;
 
 struct GemmParams {
@@ -765,37 +769,51 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
         if (sg + 2 < nsg) issue_lora(sg + 2);
         const uint8_t* la = ring + (sg % kLBuf) * kLA;
         const uint8_t* lb = ring + kLBuf * kLA + (sg % kLBuf) * kLB;
-        // matrix fragments: column lc + lr, values 4 lg .. 4 lg + 3 of the sub-group
-        u32x2 bh[4], bl[4];
+        // column blocks f in [F0, F1): gate/up's gate half meets only the gate
+        // columns (f 0, 1) and its up half only the up columns (f 2, 3), the
+        // other half's B entries being zero; every other kind meets all four
+        auto steps = [&](auto f0_tag) {
+          constexpr int F0 = decltype(f0_tag)::value, F1 = KIND == kGateUp ? F0 + 2 : 4;
+          // matrix fragments: column lc + lr, values 4 lg .. 4 lg + 3 of the sub-group
+          u32x2 bh[4], bl[4];
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
-          const int col = local_col<KIND>(w, f) + lr;
-          float4 v;
-          if constexpr (!kT) {
-            v = *reinterpret_cast<const float4*>(lb + col * 64 + 16 * (lg ^ (col & 3)));
-          } else {
-            const float* fb = reinterpret_cast<const float*>(lb);
-            v = float4{fb[(4 * lg) * 256 + col], fb[(4 * lg + 1) * 256 + col], fb[(4 * lg + 2) * 256 + col],
-                       fb[(4 * lg + 3) * 256 + col]};
+          for (int f = F0; f < F1; ++f) {
+            const int col = local_col<KIND>(w, f) + lr;
+            float4 v;
+            if constexpr (!kT) {
+              v = *reinterpret_cast<const float4*>(lb + col * 64 + 16 * (lg ^ (col & 3)));
+            } else {
+              const float* fb = reinterpret_cast<const float*>(lb);
+              v = float4{fb[(4 * lg) * 256 + col], fb[(4 * lg + 1) * 256 + col], fb[(4 * lg + 2) * 256 + col],
+                         fb[(4 * lg + 3) * 256 + col]};
+            }
+            split4_trunc(v, bh[f], bl[f]);
           }
-          split4_trunc(v, bh[f], bl[f]);
-        }
-        // plane values at or past R within the half hold no product (they may be stale): mask them
-        const int nval = min(max(R - (qh + 4 * lg), 0), 4);
-        const u32x2 keep = {(nval > 0 ? 0xffffu : 0u) | (nval > 1 ? 0xffff0000u : 0u),
-                            (nval > 2 ? 0xffffu : 0u) | (nval > 3 ? 0xffff0000u : 0u)};
+          // plane values at or past R within the half hold no product (they may be stale): mask them
+          const int nval = min(max(R - (qh + 4 * lg), 0), 4);
+          const u32x2 keep = {(nval > 0 ? 0xffffu : 0u) | (nval > 1 ? 0xffff0000u : 0u),
+                              (nval > 2 ? 0xffffu : 0u) | (nval > 3 ? 0xffff0000u : 0u)};
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const int row = 16 * mb + lr, sw = (row >> 1) & 3;
-          const uint8_t* rb = la + row * 64 + 8 * (lg & 1);
-          const u32x2 ah = *reinterpret_cast<const u32x2*>(rb + 16 * ((lg >> 1) ^ sw)) & keep;
-          const u32x2 al = *reinterpret_cast<const u32x2*>(rb + 16 * ((2 + (lg >> 1)) ^ sw)) & keep;
+          for (int mb = 0; mb < MB; ++mb) {
+            const int row = 16 * mb + lr, sw = (row >> 1) & 3;
+            const uint8_t* rb = la + row * 64 + 8 * (lg & 1);
+            const u32x2 ah = *reinterpret_cast<const u32x2*>(rb + 16 * ((lg >> 1) ^ sw)) & keep;
+            const u32x2 al = *reinterpret_cast<const u32x2*>(rb + 16 * ((2 + (lg >> 1)) ^ sw)) & keep;
 #pragma unroll
-          for (int f = 0; f < 4; ++f) {  // (gate/up: B is zero in the other half's columns)
-            acc[mb][f] = mfma_bf16_k16(ah, bh[f], acc[mb][f]);
-            acc[mb][f] = mfma_bf16_k16(ah, bl[f], acc[mb][f]);
-            acc[mb][f] = mfma_bf16_k16(al, bh[f], acc[mb][f]);
+            for (int f = F0; f < F1; ++f) {
+              acc[mb][f] = mfma_bf16_k16(ah, bh[f], acc[mb][f]);
+              acc[mb][f] = mfma_bf16_k16(ah, bl[f], acc[mb][f]);
+              acc[mb][f] = mfma_bf16_k16(al, bh[f], acc[mb][f]);
+            }
           }
+        };
+        if constexpr (KIND == kGateUp) {
+          if (half)
+            steps(FTag<2>{});
+          else
+            steps(FTag<0>{});
+        } else {
+          steps(FTag<0>{});
         }
       }
     } else {
@@ -874,9 +892,12 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
       keep.y = (nval > 2 ? 0xffffu : 0u) | (nval > 3 ? 0xffff0000u : 0u);
       keep.z = (nval > 4 ? 0xffffu : 0u) | (nval > 5 ? 0xffff0000u : 0u);
       keep.w = (nval > 6 ? 0xffffu : 0u) | (nval > 7 ? 0xffff0000u : 0u);
+      // column blocks f in [F0, F1), as in the DMA-fed steps above
+      auto steps = [&](auto f0_tag) {
+      constexpr int F0 = decltype(f0_tag)::value, F1 = KIND == kGateUp ? F0 + 2 : 4;
       u32x4 bh[4], bl[4];
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
+      for (int f = F0; f < F1; ++f) {
         const int lc = local_col<KIND>(w, f);
         if constexpr (!kT) {
           bh[f] = *reinterpret_cast<const u32x4*>(lb + (lc + lr) * 128 + 16 * (lg ^ aswz));
@@ -898,11 +919,20 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
         const u32x4 ah = *reinterpret_cast<const u32x4*>(la + mb * 2048 + lr * 128 + 16 * (lg ^ aswz)) & keep;
         const u32x4 al = *reinterpret_cast<const u32x4*>(la + mb * 2048 + lr * 128 + 16 * ((4 + lg) ^ aswz)) & keep;
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {  // (gate/up: B is zero in the other half's columns)
+        for (int f = F0; f < F1; ++f) {
           acc[mb][f] = mfma_bf16(ah, bh[f], acc[mb][f]);
           acc[mb][f] = mfma_bf16(ah, bl[f], acc[mb][f]);
           acc[mb][f] = mfma_bf16(al, bh[f], acc[mb][f]);
         }
+      }
+      };
+      if constexpr (KIND == kGateUp) {
+        if (half)
+          steps(FTag<2>{});
+        else
+          steps(FTag<0>{});
+      } else {
+        steps(FTag<0>{});
       }
       __syncthreads();  // the group is consumed before the next one (or the epilogue) reuses the ring
     }

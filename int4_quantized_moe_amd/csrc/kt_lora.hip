@@ -120,7 +120,9 @@ __global__ __launch_bounds__(256) void k_lora_side(SideArgs a) {
   // Work item (tile, contraction range); block b (in dispatch order) runs on
   // XCD b % 8, and each XCD takes a contiguous run of the items in use: the
   // tiles of one expert (consecutive in the list) and the ranges of one tile
-  // share an XCD, and so its L2 for the expert's LoRA matrix.
+  // share an XCD, and so its L2 for the expert's LoRA matrix.  (The grid is a
+  // whole number of rounds of 8 blocks, at least the items in use: every XCD
+  // has a block for each of its items.)
   const unsigned nitems = (unsigned)a.counters[kNumTiles] * gridDim.y;
   const unsigned bid = blockIdx.y * gridDim.x + blockIdx.x, per = (nitems + 7) / 8;
   const unsigned item = (bid % 8) * per + bid / 8;
@@ -396,7 +398,8 @@ void launch_lora_rowproj(const Dims& d, const WsMap& w, void* ws, const RowView&
   a.part = ws_ptr<float>(ws, w.side_part);
   a.Ms = d.Ms;
   a.nrows = a.offsets + d.E;
-  const dim3 grid((unsigned)w.max_tiles, (unsigned)a.ksplit);
+  // whole rounds of 8 blocks: every XCD then has a block for each of its items
+  const dim3 grid((unsigned)((w.max_tiles + 7) / 8 * 8), (unsigned)a.ksplit);
   switch (w.mt) {
     case 16:
       launch_side_mt<16>(nb, half, grid, a, st);
