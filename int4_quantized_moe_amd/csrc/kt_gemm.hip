@@ -19,9 +19,13 @@
 // while the current one is multiplied.  The ring waits are explicit (vmcnt)
 // around a bare s_barrier, so the compiler's conservative drain at
 // __syncthreads does not serialise the ring.  In the 64/96/128-row tiles each
-// wave decodes a stage's weights, then runs its MFMAs at a raised wave priority
-// with every activation fragment read one group of MFMAs ahead: the SIMD's
-// other wave (another workgroup) decodes or copies in the gaps.  Position p of
+// wave runs a stage's MFMAs at a raised wave priority, one column block after
+// another, decoding the next column block's weights in between (and reading
+// the next k-step's activation fragments): the SIMD's other wave (another
+// workgroup) decodes or copies in the gaps.  16-row tiles in the stored
+// orientation, bound by the weight stream, use no ring: each wave loads its
+// own codes, scales and activation values straight into registers, several
+// units of 128 contraction values ahead, with no barrier.  Position p of
 // the tile list runs on XCD p % 8 (blocks reach the XCDs in turn), each XCD
 // running all column tiles of a row tile together: the column tiles of one row
 // tile share that XCD's L2 for the activation rows, and the grouping places an
@@ -213,10 +217,12 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
   constexpr int kDmaPerStage = kAInst + 3;           // plus two weight and one scale DMA instructions
   // Up to 32 rows the fragments of the next stage are read and decoded while
   // the current one is multiplied (kPipe; stages s + 2 .. s + kStages - 1 in
-  // flight).  Taller tiles need the registers for accumulators: each stage is
-  // decoded and multiplied in turn, two workgroups per CU overlap each other,
-  // and stages s + 1 .. s + 2 are in flight.
+  // flight).  Taller tiles need the registers for accumulators: each stage's
+  // fragments are decoded one column block ahead of its MFMAs, two workgroups
+  // per CU overlap each other, and stages s + 1 .. s + 2 are in flight.
   constexpr bool kPipe = MT <= 32;
+  // 16-row tiles of the stored orientation stream their operands into registers (no ring)
+  constexpr bool kStream = !kT && MT == 16;
   constexpr int kStages = gemm_stages(MT);
   static_assert(!kPipe || (kStages >= 4 && kStages - 3 <= 4), "pipelined ring depth");
   static_assert(kPipe || kStages == 3, "ring depth");
@@ -449,180 +455,407 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll
-  for (int i = 0; i < kStages - 1; ++i)
-    if (i < nss) issue(i);
-
-  // ---------------------------------------------------------------- main loop (fp16)
   const int aswz = (lr & 7) ^ ((lr >> 3) & 1);  // activation swizzle of rows 16 * mb + lr
-  const int a_off0 = lr * 128 + 16 * ((2 * lg) ^ aswz);
-  const int a_off1 = lr * 128 + 16 * ((2 * lg + 1) ^ aswz);
-  // Weight fragments of one stage: codes and scales read from its slot and
-  // decoded to fp16.  (In a final half stage the values past the contraction's
-  // end are clamped copies; the zero activations there cancel them.)
-  const DecodeConsts dc = decode_consts();
-  auto decode = [&](int sl, u32x4 (&bf)[2][4]) {
-    const uint8_t* Bs = ring + kWReg + sl * kWBytes;
-    const uint16_t* Sc = reinterpret_cast<const uint16_t*>(ring + kSReg + sl * kScBytes);
-    if constexpr (kT) {
-      v2i_t tr[4];
-      u32x4 sp[2][4];
+  if constexpr (kStream) {
+    // -------------------------------------------------------------- main loop, streamed (16 and 32 rows)
+    // Short tiles are bound by the weight stream.  Each wave loads its own
+    // operands straight into registers, kDepth - 1 units of 128 contraction
+    // values ahead, with no LDS and no barrier, so that no wave waits for
+    // another's loads.  In unit u, lane group lg takes quant group 4 u + lg of
+    // its column: one 16-byte run of codes (the four lane groups read 64
+    // contiguous bytes of each weight row, and the next unit the rest of the
+    // line), one scale, and the matching 32 activation values of each row; k-step
+    // j of the unit multiplies values 8 j .. 8 j + 7 of every lane group's run on
+    // both sides, which reorders the contraction but not its terms.  Lane groups
+    // past the last quant group read clamped codes against zero activations.
+    constexpr int kDepth = MT == 16 ? 4 : 3;
+    const int nunits = (ngroups + 3) / 4;
+    const int ncol = KIND == kGateUp ? I : H;  // columns of the projection: the scale table's row length
+    const uint8_t* wp[4];
+    const uint16_t* sp[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const int lc = local_col<KIND>(w, f) + lr;
+      wp[f] = wrow_stored(lc);
+      int n;
+      const uint16_t* tbl;
+      if constexpr (KIND == kGateUp) {
+        n = min(n0 + (lc & (kHChunk - 1)), I - 1);
+        tbl = lc < kHChunk ? p.sct0 : p.sct1;
+      } else {
+        n = min(n0 + lc, H - 1);
+        tbl = p.sct0;
+      }
+      sp[f] = tbl + (size_t)es * ngroups * ncol + perm_pos(n);  // column n of group 0
+    }
+    const uint16_t* ap[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) ap[mb] = p.a_src + (size_t)s_src[16 * mb + lr] * p.lda;
+    struct Unit {
+      u32x4 w[4];      // codes of the lane's quant group, per column block
+      uint32_t s[4];   // its scale (fp16 bits), per column block
+      u32x4 a[MB][4];  // activation values 8 j .. 8 j + 7 of the group, per row block and k-step
+    };
+    auto load = [&](int u, Unit& U) {
+      const int g = 4 * u + lg;
+      if (4 * u + 4 <= ngroups) {  // a whole unit (every unit but a final partial one)
+#pragma unroll
+        for (int f = 0; f < 4; ++f) U.w[f] = *reinterpret_cast<const u32x4*>(wp[f] + 16 * (size_t)g);
+#pragma unroll
+        for (int f = 0; f < 4; ++f) U.s[f] = sp[f][(size_t)g * ncol];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) U.a[mb][j] = *reinterpret_cast<const u32x4*>(ap[mb] + 32 * g + 8 * j);
+      } else {
+        const bool ok = g < ngroups;
+        const int gc = ok ? g : ngroups - 1;
+        const uint16_t* zero = reinterpret_cast<const uint16_t*>(p.zero);
+#pragma unroll
+        for (int f = 0; f < 4; ++f) U.w[f] = *reinterpret_cast<const u32x4*>(wp[f] + 16 * (size_t)gc);
+#pragma unroll
+        for (int f = 0; f < 4; ++f) U.s[f] = sp[f][(size_t)gc * ncol];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            U.a[mb][j] = *reinterpret_cast<const u32x4*>(ok ? ap[mb] + 32 * g + 8 * j : zero);
+      }
+    };
+    const DecodeConsts dc = decode_consts();
+    auto compute = [&](const Unit& U) {
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
-        const int lc = local_col<KIND>(w, f);
-        const int slot = (lc >> 5) ^ ((lr >> 1) & 7);
-        tr[f] = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
-            (lds_v2i_ptr)(Bs + (16 * lg + lr) * 128 + 16 * slot + 8 * ((lc >> 4) & 1)));
+        const uint32_t bs = U.s[f] | (U.s[f] << 16);
+        if constexpr (MX) {
+          const float sf = (float)__builtin_bit_cast(half2_t, bs).x;
 #pragma unroll
-        for (int j = 0; j < 2; ++j)  // 8 fp16 scales written as 16-bit values: copy, do not type-pun
-          __builtin_memcpy(&sp[j][f], &Sc[(lc >> 5) * kKS + 16 * lg + 8 * j], sizeof(u32x4));
+          for (int j = 0; j < 4; ++j) {
+            const u32x4 b = decode_dword_e2m1(U.w[f][j], sf);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) acc[mb][f] = mfma_f16(U.a[mb][j], b, acc[mb][f]);
+          }
+        } else {
+          const half2_t s2 = __builtin_bit_cast(half2_t, bs);
+          const half2_t s16 = s2 * (half2_t){16.f16, 16.f16}, b24 = s2 * (half2_t){-24.f16, -24.f16};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const u32x4 b = decode_dword_fma(U.w[f][j], s16, b24, dc);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) acc[mb][f] = mfma_f16(U.a[mb][j], b, acc[mb][f]);
+          }
+        }
       }
+    };
+    Unit U[kDepth];
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+    for (int d = 0; d < kDepth - 1; ++d)
+      if (d < nunits) load(d, U[d]);
+    for (int u0 = 0; u0 < nunits; u0 += kDepth) {
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) {
+        const int u = u0 + d;
+        if (u >= nunits) break;
+        if (u + kDepth - 1 < nunits) load(u + kDepth - 1, U[(d + kDepth - 1) % kDepth]);
+        compute(U[d]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kStages - 1; ++i)
+      if (i < nss) issue(i);
+
+    // ---------------------------------------------------------------- main loop (fp16)
+    const int a_off0 = lr * 128 + 16 * ((2 * lg) ^ aswz);
+    const int a_off1 = lr * 128 + 16 * ((2 * lg + 1) ^ aswz);
+    // Weight fragments of one stage: codes and scales read from its slot and
+    // decoded to fp16.  (In a final half stage the values past the contraction's
+    // end are clamped copies; the zero activations there cancel them.)
+    const DecodeConsts dc = decode_consts();
+    auto decode = [&](int sl, u32x4 (&bf)[2][4]) {
+      const uint8_t* Bs = ring + kWReg + sl * kWBytes;
+      const uint16_t* Sc = reinterpret_cast<const uint16_t*>(ring + kSReg + sl * kScBytes);
+      if constexpr (kT) {
+        v2i_t tr[4];
+        u32x4 sp[2][4];
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
-          const uint32_t word = j ? (uint32_t)tr[f].y : (uint32_t)tr[f].x;
-          // bit-cast whole scalars: clang's bit_cast of an ext-vector component reads component 0
-          const uint32_t s0 = sp[j][f].x, s1 = sp[j][f].y, s2 = sp[j][f].z, s3 = sp[j][f].w;
-          if constexpr (MX)
-            bf[j][f] = decode_dword_perm_e2m1(word, __builtin_bit_cast(half2_t, s0), __builtin_bit_cast(half2_t, s1),
-                                              __builtin_bit_cast(half2_t, s2), __builtin_bit_cast(half2_t, s3));
-          else
-            bf[j][f] = decode_dword_perm(word, __builtin_bit_cast(half2_t, s0), __builtin_bit_cast(half2_t, s1),
-                                         __builtin_bit_cast(half2_t, s2), __builtin_bit_cast(half2_t, s3), dc);
+          const int lc = local_col<KIND>(w, f);
+          const int slot = (lc >> 5) ^ ((lr >> 1) & 7);
+          tr[f] = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
+              (lds_v2i_ptr)(Bs + (16 * lg + lr) * 128 + 16 * slot + 8 * ((lc >> 4) & 1)));
+#pragma unroll
+          for (int j = 0; j < 2; ++j)  // 8 fp16 scales written as 16-bit values: copy, do not type-pun
+            __builtin_memcpy(&sp[j][f], &Sc[(lc >> 5) * kKS + 16 * lg + 8 * j], sizeof(u32x4));
         }
-    } else {
-      uint32_t raw[4][2];
-      uint32_t bs[4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int f = 0; f < 4; ++f) {
+            const uint32_t word = j ? (uint32_t)tr[f].y : (uint32_t)tr[f].x;
+            // bit-cast whole scalars: clang's bit_cast of an ext-vector component reads component 0
+            const uint32_t s0 = sp[j][f].x, s1 = sp[j][f].y, s2 = sp[j][f].z, s3 = sp[j][f].w;
+            if constexpr (MX)
+              bf[j][f] = decode_dword_perm_e2m1(word, __builtin_bit_cast(half2_t, s0), __builtin_bit_cast(half2_t, s1),
+                                                __builtin_bit_cast(half2_t, s2), __builtin_bit_cast(half2_t, s3));
+            else
+              bf[j][f] = decode_dword_perm(word, __builtin_bit_cast(half2_t, s0), __builtin_bit_cast(half2_t, s1),
+                                           __builtin_bit_cast(half2_t, s2), __builtin_bit_cast(half2_t, s3), dc);
+          }
+      } else {
+        uint32_t raw[4][2];
+        uint32_t bs[4];
+        const int bsw = 16 * ((lg >> 1) ^ ((lr >> 3) & 1)) + 8 * (lg & 1);
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          const int lc = local_col<KIND>(w, f) + lr;
+          const uint2 v = *reinterpret_cast<const uint2*>(Bs + lc * 32 + bsw);
+          raw[f][0] = v.x;
+          raw[f][1] = v.y;
+          const uint32_t sh = Sc[(lg >> 1) * kNT + local_col<KIND>(w, f) + perm_pos(lr)];
+          bs[f] = sh | (sh << 16);
+        }
+        if constexpr (MX) {
+          float sf[4];
+#pragma unroll
+          for (int f = 0; f < 4; ++f) sf[f] = (float)__builtin_bit_cast(half2_t, bs[f]).x;
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int f = 0; f < 4; ++f) bf[j][f] = decode_dword_e2m1(raw[f][j], sf[f]);
+        } else {
+          half2_t s16[4], b24[4];
+#pragma unroll
+          for (int f = 0; f < 4; ++f) {
+            const half2_t s2 = __builtin_bit_cast(half2_t, bs[f]);
+            s16[f] = s2 * (half2_t){16.f16, 16.f16};
+            b24[f] = s2 * (half2_t){-24.f16, -24.f16};
+          }
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int f = 0; f < 4; ++f) bf[j][f] = decode_dword_fma(raw[f][j], s16[f], b24[f], dc);
+        }
+      }
+    };
+    // Stored orientation, one stage's weight operands split in two: the codes and
+    // scales read from the slot (stored_raw), and one fragment decoded from them
+    // (stored_dec), so that a fragment can be decoded right before its MFMAs.
+    auto stored_raw = [&](int sl, uint32_t (&cw)[4][2], uint32_t (&sw)[4][2]) {
+      const uint8_t* Bs = ring + kWReg + sl * kWBytes;
+      const uint16_t* Sc = reinterpret_cast<const uint16_t*>(ring + kSReg + sl * kScBytes);
       const int bsw = 16 * ((lg >> 1) ^ ((lr >> 3) & 1)) + 8 * (lg & 1);
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
         const int lc = local_col<KIND>(w, f) + lr;
         const uint2 v = *reinterpret_cast<const uint2*>(Bs + lc * 32 + bsw);
-        raw[f][0] = v.x;
-        raw[f][1] = v.y;
+        cw[f][0] = v.x;
+        cw[f][1] = v.y;
         const uint32_t sh = Sc[(lg >> 1) * kNT + local_col<KIND>(w, f) + perm_pos(lr)];
-        bs[f] = sh | (sh << 16);
-      }
-      if constexpr (MX) {
-        float sf[4];
-#pragma unroll
-        for (int f = 0; f < 4; ++f) sf[f] = (float)__builtin_bit_cast(half2_t, bs[f]).x;
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int f = 0; f < 4; ++f) bf[j][f] = decode_dword_e2m1(raw[f][j], sf[f]);
-      } else {
-        half2_t s16[4], b24[4];
-#pragma unroll
-        for (int f = 0; f < 4; ++f) {
-          const half2_t s2 = __builtin_bit_cast(half2_t, bs[f]);
-          s16[f] = s2 * (half2_t){16.f16, 16.f16};
-          b24[f] = s2 * (half2_t){-24.f16, -24.f16};
+        const half2_t s2 = __builtin_bit_cast(half2_t, sh | (sh << 16));
+        if constexpr (MX) {
+          sw[f][0] = __float_as_uint((float)s2.x);
+          sw[f][1] = 0u;
+        } else {
+          sw[f][0] = __builtin_bit_cast(uint32_t, s2 * (half2_t){16.f16, 16.f16});
+          sw[f][1] = __builtin_bit_cast(uint32_t, s2 * (half2_t){-24.f16, -24.f16});
         }
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int f = 0; f < 4; ++f) bf[j][f] = decode_dword_fma(raw[f][j], s16[f], b24[f], dc);
       }
-    }
-  };
-  // activation fragments of one stage from its slot
-  auto read_a = [&](int sl, u32x4 (&af)[2][MB]) {
-    const uint8_t* st = ring + sl * kABytes;
+    };
+    auto stored_dec = [&](const uint32_t (&cw)[4][2], const uint32_t (&sw)[4][2], int j, int f) -> u32x4 {
+      if constexpr (MX)
+        return decode_dword_e2m1(cw[f][j], __uint_as_float(sw[f][0]));
+      else
+        return decode_dword_fma(cw[f][j], __builtin_bit_cast(half2_t, sw[f][0]), __builtin_bit_cast(half2_t, sw[f][1]),
+                                dc);
+    };
+    // activation fragments of one stage from its slot
+    auto read_a = [&](int sl, u32x4 (&af)[2][MB]) {
+      const uint8_t* st = ring + sl * kABytes;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        af[j][mb] = *reinterpret_cast<const u32x4*>(st + mb * 2048 + (j ? a_off1 : a_off0));
-  };
-  // MFMAs of one stage, both operands already in registers
-  auto mma = [&](const u32x4 (&af)[2][MB], const u32x4 (&bf)[2][4]) {
+        for (int mb = 0; mb < MB; ++mb)
+          af[j][mb] = *reinterpret_cast<const u32x4*>(st + mb * 2048 + (j ? a_off1 : a_off0));
+    };
+    // MFMAs of one stage, both operands already in registers
+    auto mma = [&](const u32x4 (&af)[2][MB], const u32x4 (&bf)[2][4]) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int f = 0; f < 4; ++f) acc[mb][f] = mfma_f16(af[j][mb], bf[j][f], acc[mb][f]);
-  };
-  // Stage ss: wait until stage ss + 1 has landed (each wave waits for its own
-  // DMAs, the barrier for everyone's; it also frees the slot of stage ss - 1),
-  // refill that slot with stage ss + kStages - 1, then run stage ss's MFMAs from
-  // registers while stage ss + 1's activation fragments and weight codes are
-  // read and its weights decoded.
-  auto step = [&](int ss, const u32x4 (&acur)[2][MB], const u32x4 (&bcur)[2][4], u32x4 (&anxt)[2][MB],
-                  u32x4 (&bnxt)[2][4]) {
-    if (ss + 1 < nss) wait_stages<kDmaPerStage>(min(kStages - 3, nss - 2 - ss));  // stages issued after ss + 1
-    __builtin_amdgcn_s_barrier();
-    if (ss + kStages - 1 < nss) issue(ss + kStages - 1);
-    const int sn = min(ss + 1, nss - 1);  // (re-reads the last stage at the end; unused)
-    read_a(sn % kStages, anxt);
-    decode(sn % kStages, bnxt);
-    mma(acur, bcur);
-    // keep the next stage's reads and decode in this block, next to these
-    // MFMAs, rather than letting them sink into the block that consumes them
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-#pragma unroll
-      for (int f = 0; f < 4; ++f) asm volatile("" : "+v"(bnxt[j][f]));
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) asm volatile("" : "+v"(anxt[j][mb]));
-    }
-  };
-
-  if constexpr (kPipe) {
-    u32x4 afa[2][MB], afb[2][MB], bfa[2][4], bfb[2][4];
-    {
-      // stage 0 landed: the stages issued after it may still be in flight
-      wait_stages<kDmaPerStage>(min(kStages - 2, nss - 1));
+          for (int f = 0; f < 4; ++f) acc[mb][f] = mfma_f16(af[j][mb], bf[j][f], acc[mb][f]);
+    };
+    // Stage ss: wait until stage ss + 1 has landed (each wave waits for its own
+    // DMAs, the barrier for everyone's; it also frees the slot of stage ss - 1),
+    // refill that slot with stage ss + kStages - 1, then run stage ss's MFMAs from
+    // registers while stage ss + 1's activation fragments and weight codes are
+    // read and its weights decoded.
+    auto step = [&](int ss, const u32x4 (&acur)[2][MB], const u32x4 (&bcur)[2][4], u32x4 (&anxt)[2][MB],
+                    u32x4 (&bnxt)[2][4]) {
+      if (ss + 1 < nss) wait_stages<kDmaPerStage>(min(kStages - 3, nss - 2 - ss));  // stages issued after ss + 1
       __builtin_amdgcn_s_barrier();
-      read_a(0, afa);
-      decode(0, bfa);
-    }
-    int ss = 0;
-    for (; ss + 1 < nss; ss += 2) {
-      step(ss, afa, bfa, afb, bfb);
-      step(ss + 1, afb, bfb, afa, bfa);
-    }
-    if (ss < nss) step(ss, afa, bfa, afb, bfb);
-  } else {
-    // unrolled by the ring depth, so that each stage's slot is a constant
-    for (int s0 = 0; s0 < nss; s0 += kStages) {
+      if (ss + kStages - 1 < nss) issue(ss + kStages - 1);
+      const int sn = min(ss + 1, nss - 1);  // (re-reads the last stage at the end; unused)
+      read_a(sn % kStages, anxt);
+      decode(sn % kStages, bnxt);
+      mma(acur, bcur);
+      // keep the next stage's reads and decode in this block, next to these
+      // MFMAs, rather than letting them sink into the block that consumes them
 #pragma unroll
-      for (int sl = 0; sl < kStages; ++sl) {
-        const int ss = s0 + sl;
-        if (ss >= nss) break;
-        // this wave's loads of stage ss have landed once at most the later
-        // stages' DMAs are outstanding; the barrier makes every wave's loads
-        // visible and frees the slot that stage ss + kStages - 1 refills
-        if (ss + 1 < nss)
-          wait_vm_lgkm<kDmaPerStage>();
-        else
-          wait_vm_lgkm<0>();
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) asm volatile("" : "+v"(bnxt[j][f]));
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) asm volatile("" : "+v"(anxt[j][mb]));
+      }
+    };
+
+    if constexpr (kPipe) {
+      u32x4 afa[2][MB], afb[2][MB], bfa[2][4], bfb[2][4];
+      {
+        // stage 0 landed: the stages issued after it may still be in flight
+        wait_stages<kDmaPerStage>(min(kStages - 2, nss - 1));
         __builtin_amdgcn_s_barrier();
-        if (ss + kStages - 1 < nss) issue(ss + kStages - 1);
-        u32x4 bf[2][4];
-        decode(sl, bf);
-        const uint8_t* st = ring + sl * kABytes;
-        // Each activation fragment is read one group of MFMAs ahead, the
-        // scheduler is asked for that order, and the wave's priority is raised
-        // over its MFMAs, so that the MFMA pipe gets the SIMD first while the
-        // other wave decodes or copies (measured faster in every kind).
-        u32x4 an = *reinterpret_cast<const u32x4*>(st + a_off0);
-        __builtin_amdgcn_s_setprio(2);
+        read_a(0, afa);
+        decode(0, bfa);
+      }
+      int ss = 0;
+      for (; ss + 1 < nss; ss += 2) {
+        step(ss, afa, bfa, afb, bfb);
+        step(ss + 1, afb, bfb, afa, bfa);
+      }
+      if (ss < nss) step(ss, afa, bfa, afb, bfb);
+    } else {
+      // unrolled by the ring depth, so that each stage's slot is a constant
+      for (int s0 = 0; s0 < nss; s0 += kStages) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int sl = 0; sl < kStages; ++sl) {
+          const int ss = s0 + sl;
+          if (ss >= nss) break;
+          // this wave's loads of stage ss have landed once at most the later
+          // stages' DMAs are outstanding; the barrier makes every wave's loads
+          // visible and frees the slot that stage ss + kStages - 1 refills
+          if (ss + 1 < nss)
+            wait_vm_lgkm<kDmaPerStage>();
+          else
+            wait_vm_lgkm<0>();
+          __builtin_amdgcn_s_barrier();
+          if (ss + kStages - 1 < nss) issue(ss + kStages - 1);
+          if constexpr (kT) {
+            // As below for the stored orientation: fragment (j, f) is decoded
+            // during the MFMAs of the fragment before it, from codes read once
+            // per stage (a transposing read per column block) and its 8 fp16
+            // scales, which are read one fragment ahead of their decode.
+            const uint8_t* Bs = ring + kWReg + sl * kWBytes;
+            const uint16_t* Sc = reinterpret_cast<const uint16_t*>(ring + kSReg + sl * kScBytes);
+            v2i_t tr[4];
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb) {
-            const u32x4 af = an;
-            const int nj = mb + 1 < MB ? j : j + 1, nmb = mb + 1 < MB ? mb + 1 : 0;
-            if (nj < 2) an = *reinterpret_cast<const u32x4*>(st + nmb * 2048 + (nj ? a_off1 : a_off0));
+            for (int f = 0; f < 4; ++f) {
+              const int lc = local_col<KIND>(w, f);
+              const int slot = (lc >> 5) ^ ((lr >> 1) & 7);
+              tr[f] = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
+                  (lds_v2i_ptr)(Bs + (16 * lg + lr) * 128 + 16 * slot + 8 * ((lc >> 4) & 1)));
+            }
+            // scales of fragment q = 4 j + f: its column group, contraction rows 16 lg + 8 j ..
+            auto scl = [&](int q) {
+              u32x4 v;  // 8 fp16 scales written as 16-bit values: copy, do not type-pun
+              __builtin_memcpy(&v, &Sc[(local_col<KIND>(w, q & 3) >> 5) * kKS + 16 * lg + 8 * (q >> 2)], sizeof(u32x4));
+              return v;
+            };
+            auto dec = [&](int q, const u32x4 sp) -> u32x4 {
+              const uint32_t word = (q >> 2) ? (uint32_t)tr[q & 3].y : (uint32_t)tr[q & 3].x;
+              // bit-cast whole scalars: clang's bit_cast of an ext-vector component reads component 0
+              const uint32_t s0 = sp.x, s1 = sp.y, s2 = sp.z, s3 = sp.w;
+              if constexpr (MX)
+                return decode_dword_perm_e2m1(word, __builtin_bit_cast(half2_t, s0), __builtin_bit_cast(half2_t, s1),
+                                              __builtin_bit_cast(half2_t, s2), __builtin_bit_cast(half2_t, s3));
+              else
+                return decode_dword_perm(word, __builtin_bit_cast(half2_t, s0), __builtin_bit_cast(half2_t, s1),
+                                         __builtin_bit_cast(half2_t, s2), __builtin_bit_cast(half2_t, s3), dc);
+            };
+            const uint8_t* st = ring + sl * kABytes;
+            u32x4 af[MB], an[MB];
 #pragma unroll
-            for (int f = 0; f < 4; ++f) acc[mb][f] = mfma_f16(af, bf[j][f], acc[mb][f]);
-            if (nj < 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);              // then 4 MFMAs
+            for (int mb = 0; mb < MB; ++mb) af[mb] = *reinterpret_cast<const u32x4*>(st + mb * 2048 + a_off0);
+            u32x4 b = dec(0, scl(0));
+            u32x4 sn = scl(1);
+            __builtin_amdgcn_s_setprio(2);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+#pragma unroll
+              for (int f = 0; f < 4; ++f) {
+                const int q = 4 * j + f;
+                const bool more = q < 7;
+                u32x4 bn = b, sn2 = sn;
+                if (more) bn = dec(q + 1, sn);
+                if (q + 2 < 8) sn2 = scl(q + 2);
+                constexpr int kHalf = (MB + 1) / 2;
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                  acc[mb][f] = mfma_f16(af[mb], b, acc[mb][f]);
+                  const int r = f == 2 ? mb : kHalf + mb;  // activation fragment read in this slot
+                  const bool rd = j == 0 && f >= 2 && mb < kHalf && r < MB;
+                  if (rd) an[r] = *reinterpret_cast<const u32x4*>(st + r * 2048 + a_off1);
+                  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                  if (rd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+                  if (mb == 0 && q + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the scales
+                  if (more) __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two decode VALU
+                }
+                b = bn;
+                sn = sn2;
+              }
+              if (j == 0) {
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) af[mb] = an[mb];
+              }
+            }
+            __builtin_amdgcn_s_setprio(0);
+          } else {
+            // The stage's codes, scales and first activation fragments are
+            // read, then each column block's fragment is decoded while the
+            // MFMAs of the one before it run, so that one wave keeps the
+            // matrix pipe fed by itself (the other wave on the SIMD fills in;
+            // the raised priority gives the MFMAs the SIMD first).  The next
+            // k-step's activation fragments are read during the current one's
+            // last two column blocks.
+            uint32_t cw[4][2], sw[4][2];
+            stored_raw(sl, cw, sw);
+            const uint8_t* st = ring + sl * kABytes;
+            u32x4 af[MB], an[MB];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) af[mb] = *reinterpret_cast<const u32x4*>(st + mb * 2048 + a_off0);
+            u32x4 b = stored_dec(cw, sw, 0, 0);
+            __builtin_amdgcn_s_setprio(2);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+#pragma unroll
+              for (int f = 0; f < 4; ++f) {
+                const bool more = f < 3 || j == 0;
+                u32x4 bn = b;
+                if (more) bn = stored_dec(cw, sw, f < 3 ? j : 1, f < 3 ? f + 1 : 0);
+                constexpr int kHalf = (MB + 1) / 2;
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                  acc[mb][f] = mfma_f16(af[mb], b, acc[mb][f]);
+                  const int r = f == 2 ? mb : kHalf + mb;  // activation fragment read in this slot
+                  const bool rd = j == 0 && f >= 2 && mb < kHalf && r < MB;
+                  if (rd) an[r] = *reinterpret_cast<const u32x4*>(st + r * 2048 + a_off1);
+                  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                  if (rd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+                  if (more) __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two decode VALU
+                }
+                b = bn;
+              }
+              if (j == 0) {
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) af[mb] = an[mb];
+              }
+            }
+            __builtin_amdgcn_s_setprio(0);
           }
-        __builtin_amdgcn_s_setprio(0);
+        }
       }
     }
   }
