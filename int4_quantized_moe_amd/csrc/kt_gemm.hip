@@ -457,19 +457,19 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
 
   const int aswz = (lr & 7) ^ ((lr >> 3) & 1);  // activation swizzle of rows 16 * mb + lr
   if constexpr (kStream) {
-    // -------------------------------------------------------------- main loop, streamed (16 and 32 rows)
+    // -------------------------------------------------------------- main loop, streamed (16 rows)
     // Short tiles are bound by the weight stream.  Each wave loads its own
-    // operands straight into registers, kDepth - 1 units of 128 contraction
-    // values ahead, with no LDS and no barrier, so that no wave waits for
-    // another's loads.  In unit u, lane group lg takes quant group 4 u + lg of
-    // its column: one 16-byte run of codes (the four lane groups read 64
-    // contiguous bytes of each weight row, and the next unit the rest of the
-    // line), one scale, and the matching 32 activation values of each row; k-step
-    // j of the unit multiplies values 8 j .. 8 j + 7 of every lane group's run on
-    // both sides, which reorders the contraction but not its terms.  Lane groups
-    // past the last quant group read clamped codes against zero activations.
-    constexpr int kDepth = MT == 16 ? 4 : 3;
-    const int nunits = (ngroups + 3) / 4;
+    // operands straight into registers, with no LDS and no barrier, so that no
+    // wave waits for another's loads.  A unit is 256 contraction values (eight
+    // quant groups); in half h of unit u, lane group lg takes quant group
+    // 8 u + 4 h + lg of its column: one 16-byte run of codes, one scale, and the
+    // matching 32 activation values of each row.  The two halves' code loads go
+    // out back to back, so each weight row's 128-byte line is requested whole.
+    // K-step j of a half multiplies values 8 j .. 8 j + 7 of every lane group's
+    // run on both sides, which reorders the contraction but not its terms.
+    // Codes and scales are loaded two units ahead, activations (which the four
+    // waves share through L2) one unit ahead.
+    const int nunits = (ngroups + 7) / 8;
     const int ncol = KIND == kGateUp ? I : H;  // columns of the projection: the scale table's row length
     const uint8_t* wp[4];
     const uint16_t* sp[4];
@@ -491,73 +491,92 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
     const uint16_t* ap[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) ap[mb] = p.a_src + (size_t)s_src[16 * mb + lr] * p.lda;
-    struct Unit {
-      u32x4 w[4];      // codes of the lane's quant group, per column block
-      uint32_t s[4];   // its scale (fp16 bits), per column block
-      u32x4 a[MB][4];  // activation values 8 j .. 8 j + 7 of the group, per row block and k-step
+    struct Codes {
+      u32x4 w[4][2];     // codes of the lane's quant group, per column block and half
+      uint32_t s[4][2];  // its scale (fp16 bits), per column block and half
     };
-    auto load = [&](int u, Unit& U) {
-      const int g = 4 * u + lg;
-      if (4 * u + 4 <= ngroups) {  // a whole unit (every unit but a final partial one)
+    struct Acts {
+      u32x4 a[MB][2][4];  // activation values 8 j .. 8 j + 7 of the group, per row block, half and k-step
+    };
+    // Every unit is loaded the same way (no branch, so that the compiler cannot
+    // merge or sink the loads of a unit toward the MFMAs that use them): lane
+    // groups past the last quant group, and whole units past the contraction's
+    // end (the loop runs a multiple of four units), read clamped codes and
+    // scales against zero activations, which add nothing.
+    const uint16_t* zero = reinterpret_cast<const uint16_t*>(p.zero);
+    auto load_codes = [&](int u, Codes& C) {
 #pragma unroll
-        for (int f = 0; f < 4; ++f) U.w[f] = *reinterpret_cast<const u32x4*>(wp[f] + 16 * (size_t)g);
+      for (int f = 0; f < 4; ++f)
 #pragma unroll
-        for (int f = 0; f < 4; ++f) U.s[f] = sp[f][(size_t)g * ncol];
+        for (int h = 0; h < 2; ++h) {
+          const int gc = min(8 * u + 4 * h + lg, ngroups - 1);
+          C.w[f][h] = *reinterpret_cast<const u32x4*>(wp[f] + 16 * (size_t)gc);
+        }
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+      for (int f = 0; f < 4; ++f)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) U.a[mb][j] = *reinterpret_cast<const u32x4*>(ap[mb] + 32 * g + 8 * j);
-      } else {
+        for (int h = 0; h < 2; ++h) {
+          const int gc = min(8 * u + 4 * h + lg, ngroups - 1);
+          C.s[f][h] = sp[f][(size_t)gc * ncol];
+        }
+    };
+    auto load_acts = [&](int u, Acts& A) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int g = 8 * u + 4 * h + lg;
         const bool ok = g < ngroups;
-        const int gc = ok ? g : ngroups - 1;
-        const uint16_t* zero = reinterpret_cast<const uint16_t*>(p.zero);
-#pragma unroll
-        for (int f = 0; f < 4; ++f) U.w[f] = *reinterpret_cast<const u32x4*>(wp[f] + 16 * (size_t)gc);
-#pragma unroll
-        for (int f = 0; f < 4; ++f) U.s[f] = sp[f][(size_t)gc * ncol];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            U.a[mb][j] = *reinterpret_cast<const u32x4*>(ok ? ap[mb] + 32 * g + 8 * j : zero);
+            A.a[mb][h][j] = *reinterpret_cast<const u32x4*>(ok ? ap[mb] + 32 * g + 8 * j : zero);
       }
     };
     const DecodeConsts dc = decode_consts();
-    auto compute = [&](const Unit& U) {
+    auto compute = [&](const Codes& C, const Acts& A) {
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        const uint32_t bs = U.s[f] | (U.s[f] << 16);
-        if constexpr (MX) {
-          const float sf = (float)__builtin_bit_cast(half2_t, bs).x;
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const u32x4 b = decode_dword_e2m1(U.w[f][j], sf);
+        for (int f = 0; f < 4; ++f) {
+          const uint32_t bs = C.s[f][h] | (C.s[f][h] << 16);
+          if constexpr (MX) {
+            const float sf = (float)__builtin_bit_cast(half2_t, bs).x;
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) acc[mb][f] = mfma_f16(U.a[mb][j], b, acc[mb][f]);
-          }
-        } else {
-          const half2_t s2 = __builtin_bit_cast(half2_t, bs);
-          const half2_t s16 = s2 * (half2_t){16.f16, 16.f16}, b24 = s2 * (half2_t){-24.f16, -24.f16};
+            for (int j = 0; j < 4; ++j) {
+              const u32x4 b = decode_dword_e2m1(C.w[f][h][j], sf);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const u32x4 b = decode_dword_fma(U.w[f][j], s16, b24, dc);
+              for (int mb = 0; mb < MB; ++mb) acc[mb][f] = mfma_f16(A.a[mb][h][j], b, acc[mb][f]);
+            }
+          } else {
+            const half2_t s2 = __builtin_bit_cast(half2_t, bs);
+            const half2_t s16 = s2 * (half2_t){16.f16, 16.f16}, b24 = s2 * (half2_t){-24.f16, -24.f16};
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) acc[mb][f] = mfma_f16(U.a[mb][j], b, acc[mb][f]);
+            for (int j = 0; j < 4; ++j) {
+              const u32x4 b = decode_dword_fma(C.w[f][h][j], s16, b24, dc);
+#pragma unroll
+              for (int mb = 0; mb < MB; ++mb) acc[mb][f] = mfma_f16(A.a[mb][h][j], b, acc[mb][f]);
+            }
           }
         }
-      }
     };
-    Unit U[kDepth];
+    // (issued in the loop's order, so that the compiler's memory waits for a
+    // unit count only the loads issued after it)
+    Codes C[4];
+    Acts A[2];
+    load_codes(0, C[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    load_codes(1, C[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    load_acts(0, A[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int u0 = 0; u0 < nunits; u0 += 4) {
 #pragma unroll
-    for (int d = 0; d < kDepth - 1; ++d)
-      if (d < nunits) load(d, U[d]);
-    for (int u0 = 0; u0 < nunits; u0 += kDepth) {
-#pragma unroll
-      for (int d = 0; d < kDepth; ++d) {
-        const int u = u0 + d;
-        if (u >= nunits) break;
-        if (u + kDepth - 1 < nunits) load(u + kDepth - 1, U[(d + kDepth - 1) % kDepth]);
-        compute(U[d]);
+      for (int d = 0; d < 4; ++d) {
+        load_codes(u0 + d + 2, C[(d + 2) % 4]);
+        load_acts(u0 + d + 1, A[(d + 1) % 2]);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(C[d], A[d % 2]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   } else {
