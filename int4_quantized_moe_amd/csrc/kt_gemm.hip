@@ -459,16 +459,22 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
   if constexpr (kStream) {
     // -------------------------------------------------------------- main loop, streamed (16 rows)
     // Short tiles are bound by the weight stream.  Each wave loads its own
-    // operands straight into registers, with no LDS and no barrier, so that no
-    // wave waits for another's loads.  A unit is 256 contraction values (eight
-    // quant groups); in half h of unit u, lane group lg takes quant group
-    // 8 u + 4 h + lg of its column: one 16-byte run of codes, one scale, and the
-    // matching 32 activation values of each row.  The two halves' code loads go
-    // out back to back, so each weight row's 128-byte line is requested whole.
-    // K-step j of a half multiplies values 8 j .. 8 j + 7 of every lane group's
-    // run on both sides, which reorders the contraction but not its terms.
-    // Codes and scales are loaded two units ahead, activations (which the four
-    // waves share through L2) one unit ahead.
+    // columns' codes and scales straight into registers, one unit ahead; the
+    // activation rows, which every wave needs, are copied into an LDS ring by
+    // DMA (each wave an eighth of a unit per copy) and read from there, one
+    // barrier per unit.  A unit is 256 contraction values (eight quant groups);
+    // in half h of unit u, lane group lg takes quant group 8 u + 4 h + lg of its
+    // column: one 16-byte run of codes and one scale.  The two halves' code loads
+    // go out back to back, so each weight row's 128-byte line is requested
+    // whole.  K-step j of a half multiplies values 8 j .. 8 j + 7 of every lane
+    // group's run on both sides, which reorders the contraction but not its
+    // terms.
+    static_assert(MT == 16, "the streamed path holds one row block");
+    constexpr int kNA = 4;              // LDS slots
+    constexpr int kSlot = MT * 512;     // one unit of activations: MT rows of 256 fp16 values
+    constexpr int kAIW = MT / 8;        // activation copies per wave per unit (two rows each)
+    constexpr int kCodeVm = 16;         // vector memory instructions of one unit's codes and scales
+    static_assert(kNA * kSlot <= kRingMax, "activation ring");
     const int nunits = (ngroups + 7) / 8;
     const int ncol = KIND == kGateUp ? I : H;  // columns of the projection: the scale table's row length
     const uint8_t* wp[4];
@@ -488,22 +494,35 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
       }
       sp[f] = tbl + (size_t)es * ngroups * ncol + perm_pos(n);  // column n of group 0
     }
-    const uint16_t* ap[MB];
+    // Activation copies: copy i of wave w covers tile rows 2 (kAIW w + i) and the
+    // next; lane l writes slot position 16 l, i.e. row + (l >> 5), position
+    // l & 31, which holds chunk (l & 31) ^ (row & 7) of the unit (the XOR spreads
+    // a k-step's fragment reads over the banks).  Values past the contraction's
+    // end come from the zero chunk.
+    const uint16_t* asrc[kAIW];
+    int achunk[kAIW];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) ap[mb] = p.a_src + (size_t)s_src[16 * mb + lr] * p.lda;
+    for (int i = 0; i < kAIW; ++i) {
+      const int row = 2 * (kAIW * w + i) + (lane >> 5);
+      achunk[i] = (lane & 31) ^ (row & 7);
+      asrc[i] = p.a_src + (size_t)s_src[row] * p.lda + 8 * achunk[i];
+    }
+    auto issue_acts = [&](int u, int slot) {
+#pragma unroll
+      for (int i = 0; i < kAIW; ++i) {
+        const bool ok = 256 * u + 8 * achunk[i] < kdim;
+        dma16(ok ? (const void*)(asrc[i] + 256 * u) : p.zero, lds_addr(ring) + slot * kSlot + 1024 * (kAIW * w + i));
+      }
+    };
     struct Codes {
       u32x4 w[4][2];     // codes of the lane's quant group, per column block and half
       uint32_t s[4][2];  // its scale (fp16 bits), per column block and half
     };
-    struct Acts {
-      u32x4 a[MB][2][4];  // activation values 8 j .. 8 j + 7 of the group, per row block, half and k-step
-    };
-    // Every unit is loaded the same way (no branch, so that the compiler cannot
-    // merge or sink the loads of a unit toward the MFMAs that use them): lane
-    // groups past the last quant group, and whole units past the contraction's
-    // end (the loop runs a multiple of four units), read clamped codes and
-    // scales against zero activations, which add nothing.
-    const uint16_t* zero = reinterpret_cast<const uint16_t*>(p.zero);
+    // Every unit's codes load the same way (no branch, so that the compiler
+    // cannot merge or sink them toward the MFMAs that use them): lane groups past
+    // the last quant group, and the unit past the contraction's end that the last
+    // step loads, read clamped codes and scales (the former meet zero
+    // activations and add nothing; the latter are never multiplied).
     auto load_codes = [&](int u, Codes& C) {
 #pragma unroll
       for (int f = 0; f < 4; ++f)
@@ -520,62 +539,70 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
           C.s[f][h] = sp[f][(size_t)gc * ncol];
         }
     };
-    auto load_acts = [&](int u, Acts& A) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int g = 8 * u + 4 * h + lg;
-        const bool ok = g < ngroups;
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            A.a[mb][h][j] = *reinterpret_cast<const u32x4*>(ok ? ap[mb] + 32 * g + 8 * j : zero);
-      }
-    };
     const DecodeConsts dc = decode_consts();
-    auto compute = [&](const Codes& C, const Acts& A) {
+    auto compute = [&](const Codes& C, int slot) {
+      const uint8_t* st = ring + slot * kSlot + lr * 512;
+      u32x4 a[2][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          a[h][j] = *reinterpret_cast<const u32x4*>(st + 16 * ((16 * h + 4 * lg + j) ^ (lr & 7)));
+      uint32_t s0[4][2], s1[4][2];  // per column block and half: 16 s, -24 s (RAWINT4) or the fp32 scale (MXFP4)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
-          const uint32_t bs = C.s[f][h] | (C.s[f][h] << 16);
+          const half2_t s2 = __builtin_bit_cast(half2_t, C.s[f][h] | (C.s[f][h] << 16));
           if constexpr (MX) {
-            const float sf = (float)__builtin_bit_cast(half2_t, bs).x;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const u32x4 b = decode_dword_e2m1(C.w[f][h][j], sf);
-#pragma unroll
-              for (int mb = 0; mb < MB; ++mb) acc[mb][f] = mfma_f16(A.a[mb][h][j], b, acc[mb][f]);
-            }
+            s0[f][h] = __float_as_uint((float)s2.x);
+            s1[f][h] = 0u;
           } else {
-            const half2_t s2 = __builtin_bit_cast(half2_t, bs);
-            const half2_t s16 = s2 * (half2_t){16.f16, 16.f16}, b24 = s2 * (half2_t){-24.f16, -24.f16};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const u32x4 b = decode_dword_fma(C.w[f][h][j], s16, b24, dc);
-#pragma unroll
-              for (int mb = 0; mb < MB; ++mb) acc[mb][f] = mfma_f16(A.a[mb][h][j], b, acc[mb][f]);
-            }
+            s0[f][h] = __builtin_bit_cast(uint32_t, s2 * (half2_t){16.f16, 16.f16});
+            s1[f][h] = __builtin_bit_cast(uint32_t, s2 * (half2_t){-24.f16, -24.f16});
           }
         }
-    };
-    // (issued in the loop's order, so that the compiler's memory waits for a
-    // unit count only the loads issued after it)
-    Codes C[4];
-    Acts A[2];
-    load_codes(0, C[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    load_codes(1, C[1]);
-    __builtin_amdgcn_sched_barrier(0);
-    load_acts(0, A[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    for (int u0 = 0; u0 < nunits; u0 += 4) {
+      // per accumulator the terms come in the order (h, j); consecutive MFMAs
+      // go to different accumulators
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        load_codes(u0 + d + 2, C[(d + 2) % 4]);
-        load_acts(u0 + d + 1, A[(d + 1) % 2]);
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int f = 0; f < 4; ++f) {
+            u32x4 b;
+            if constexpr (MX)
+              b = decode_dword_e2m1(C.w[f][h][j], __uint_as_float(s0[f][h]));
+            else
+              b = decode_dword_fma(C.w[f][h][j], __builtin_bit_cast(half2_t, s0[f][h]),
+                                   __builtin_bit_cast(half2_t, s1[f][h]), dc);
+            acc[0][f] = mfma_f16(a[h][j], b, acc[0][f]);
+          }
+    };
+    // Unit u (slot u % 4): load the codes of unit u + 1, then wait until only
+    // those are in flight: unit u's codes and unit u + 1's activation copies
+    // (issued one unit ago) have landed.  The wait is one the compiler sees, so
+    // it adds none of its own for the codes (it does not count the copies, which
+    // are issued from asm so that it does not drain them before every LDS read).
+    // Barrier: every wave's copies of unit u + 1 are visible, and every wave is
+    // done with slot u + 2, which is refilled next with unit u + 2's activations.
+    // Then unit u is multiplied.
+    Codes C[2];
+    issue_acts(0, 0);
+    load_codes(0, C[0]);
+    wait_vm_lgkm<0>();
+    __builtin_amdgcn_s_barrier();
+    if (nunits > 1) issue_acts(1, 1);
+    for (int u0 = 0; u0 < nunits; u0 += 2) {
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const int u = u0 + d;
+        load_codes(u + 1, C[d ^ 1]);
+        wait_vm_lgkm<kCodeVm>();
+        __builtin_amdgcn_s_barrier();
+        if (u + 2 < nunits) issue_acts(u + 2, (u + 2) % kNA);  // (no copy is left in flight at the end)
         __builtin_amdgcn_sched_barrier(0);
-        compute(C[d], A[d % 2]);
+        if (u < nunits) compute(C[d], u % kNA);  // (an odd count leaves the loop's last unit empty)
         __builtin_amdgcn_sched_barrier(0);
       }
     }
