@@ -1053,6 +1053,50 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
         // other half's B entries being zero; every other kind meets all four
         auto steps = [&](auto f0_tag) {
           constexpr int F0 = decltype(f0_tag)::value, F1 = KIND == kGateUp ? F0 + 2 : 4;
+          if constexpr (KIND != kGateUp) {
+            // One 16x16x32 MFMA per fragment pair: the contraction runs over the
+            // sub-group's 16 values twice, [hi | lo] of the side product against
+            // the matrix entries rounded to bf16 (nearest) twice, which sums
+            // (hi + lo) * m.  Lane group lg holds values 8 (lg & 1) .. + 7, of
+            // the hi plane for lg < 2 and of the lo plane otherwise.
+            u32x4 bm[4];
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+              const int col = local_col<KIND>(w, f) + lr;
+              float v[8];
+              if constexpr (!kT) {
+                const int c0 = 2 * (lg & 1);
+                const float4 x0 = *reinterpret_cast<const float4*>(lb + col * 64 + 16 * (c0 ^ (col & 3)));
+                const float4 x1 = *reinterpret_cast<const float4*>(lb + col * 64 + 16 * ((c0 + 1) ^ (col & 3)));
+                v[0] = x0.x, v[1] = x0.y, v[2] = x0.z, v[3] = x0.w, v[4] = x1.x, v[5] = x1.y, v[6] = x1.z,
+                v[7] = x1.w;
+              } else {
+                const float* fb = reinterpret_cast<const float*>(lb);
+#pragma unroll
+                for (int t = 0; t < 8; ++t) v[t] = fb[(8 * (lg & 1) + t) * 256 + col];
+              }
+              uint32_t pk[4];
+#pragma unroll
+              for (int t = 0; t < 4; ++t)
+                pk[t] = __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){v[2 * t], v[2 * t + 1]}, bf16x2_t));
+              bm[f] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+            }
+            // plane values at or past R within the half hold no product (they may be stale): mask them
+            const int nval = min(max(R - (qh + 8 * (lg & 1)), 0), 8);
+            u32x4 keep;
+            keep.x = (nval > 0 ? 0xffffu : 0u) | (nval > 1 ? 0xffff0000u : 0u);
+            keep.y = (nval > 2 ? 0xffffu : 0u) | (nval > 3 ? 0xffff0000u : 0u);
+            keep.z = (nval > 4 ? 0xffffu : 0u) | (nval > 5 ? 0xffff0000u : 0u);
+            keep.w = (nval > 6 ? 0xffffu : 0u) | (nval > 7 ? 0xffff0000u : 0u);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+              const int row = 16 * mb + lr, sw = (row >> 1) & 3;
+              const u32x4 ap = *reinterpret_cast<const u32x4*>(la + row * 64 + 16 * (lg ^ sw)) & keep;
+#pragma unroll
+              for (int f = 0; f < 4; ++f) acc[mb][f] = mfma_bf16(ap, bm[f], acc[mb][f]);
+            }
+            return;
+          }
           // matrix fragments: column lc + lr, values 4 lg .. 4 lg + 3 of the sub-group
           u32x2 bh[4], bl[4];
 #pragma unroll
