@@ -1095,38 +1095,48 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
 #pragma unroll
               for (int f = 0; f < 4; ++f) acc[mb][f] = mfma_bf16(ap, bm[f], acc[mb][f]);
             }
-            return;
-          }
-          // matrix fragments: column lc + lr, values 4 lg .. 4 lg + 3 of the sub-group
-          u32x2 bh[4], bl[4];
-#pragma unroll
-          for (int f = F0; f < F1; ++f) {
-            const int col = local_col<KIND>(w, f) + lr;
-            float4 v;
-            if constexpr (!kT) {
-              v = *reinterpret_cast<const float4*>(lb + col * 64 + 16 * (lg ^ (col & 3)));
-            } else {
-              const float* fb = reinterpret_cast<const float*>(lb);
-              v = float4{fb[(4 * lg) * 256 + col], fb[(4 * lg + 1) * 256 + col], fb[(4 * lg + 2) * 256 + col],
-                         fb[(4 * lg + 3) * 256 + col]};
-            }
-            split4_trunc(v, bh[f], bl[f]);
-          }
-          // plane values at or past R within the half hold no product (they may be stale): mask them
-          const int nval = min(max(R - (qh + 4 * lg), 0), 4);
-          const u32x2 keep = {(nval > 0 ? 0xffffu : 0u) | (nval > 1 ? 0xffff0000u : 0u),
-                              (nval > 2 ? 0xffffu : 0u) | (nval > 3 ? 0xffff0000u : 0u)};
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) {
-            const int row = 16 * mb + lr, sw = (row >> 1) & 3;
-            const uint8_t* rb = la + row * 64 + 8 * (lg & 1);
-            const u32x2 ah = *reinterpret_cast<const u32x2*>(rb + 16 * ((lg >> 1) ^ sw)) & keep;
-            const u32x2 al = *reinterpret_cast<const u32x2*>(rb + 16 * ((2 + (lg >> 1)) ^ sw)) & keep;
+          } else {
+            // Gate/up (the pre-activations the masks are decided on): the matrix
+            // entries m are split by truncation into bf16 mh + ml, and two MFMAs
+            // form the same three products as hi*mh + hi*ml + lo*mh: one 16x16x32
+            // over [hi | lo] against [mh | mh] (lane group lg: values 8 (lg & 1) .. + 7),
+            // and one 16x16x16 of hi against ml, whose lane group lg holds the
+            // values 8 (lg & 1) + 4 (lg >> 1) .. + 3 (a subset of the same lane's).
+            u32x4 bm[4];
+            u32x2 bml[4];
 #pragma unroll
             for (int f = F0; f < F1; ++f) {
-              acc[mb][f] = mfma_bf16_k16(ah, bh[f], acc[mb][f]);
-              acc[mb][f] = mfma_bf16_k16(ah, bl[f], acc[mb][f]);
-              acc[mb][f] = mfma_bf16_k16(al, bh[f], acc[mb][f]);
+              const int col = local_col<KIND>(w, f) + lr;
+              const int c0 = 2 * (lg & 1);
+              const float4 x0 = *reinterpret_cast<const float4*>(lb + col * 64 + 16 * (c0 ^ (col & 3)));
+              const float4 x1 = *reinterpret_cast<const float4*>(lb + col * 64 + 16 * ((c0 + 1) ^ (col & 3)));
+              u32x2 h0, l0, h1, l1;
+              split4_trunc(x0, h0, l0);
+              split4_trunc(x1, h1, l1);
+              bm[f] = u32x4{h0.x, h0.y, h1.x, h1.y};
+              bml[f] = (lg >> 1) ? l1 : l0;
+            }
+            // plane values at or past R within the half hold no product (they may be stale): mask them
+            const int q8 = qh + 8 * (lg & 1);
+            const int nval = min(max(R - q8, 0), 8), nval4 = min(max(R - (q8 + 4 * (lg >> 1)), 0), 4);
+            u32x4 keep;
+            keep.x = (nval > 0 ? 0xffffu : 0u) | (nval > 1 ? 0xffff0000u : 0u);
+            keep.y = (nval > 2 ? 0xffffu : 0u) | (nval > 3 ? 0xffff0000u : 0u);
+            keep.z = (nval > 4 ? 0xffffu : 0u) | (nval > 5 ? 0xffff0000u : 0u);
+            keep.w = (nval > 6 ? 0xffffu : 0u) | (nval > 7 ? 0xffff0000u : 0u);
+            const u32x2 keep4 = {(nval4 > 0 ? 0xffffu : 0u) | (nval4 > 1 ? 0xffff0000u : 0u),
+                                 (nval4 > 2 ? 0xffffu : 0u) | (nval4 > 3 ? 0xffff0000u : 0u)};
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+              const int row = 16 * mb + lr, sw = (row >> 1) & 3;
+              const u32x4 ap = *reinterpret_cast<const u32x4*>(la + row * 64 + 16 * (lg ^ sw)) & keep;
+              const u32x2 ah =
+                  *reinterpret_cast<const u32x2*>(la + row * 64 + 16 * ((lg & 1) ^ sw) + 8 * (lg >> 1)) & keep4;
+#pragma unroll
+              for (int f = F0; f < F1; ++f) {
+                acc[mb][f] = mfma_bf16(ap, bm[f], acc[mb][f]);
+                acc[mb][f] = mfma_bf16_k16(ah, bml[f], acc[mb][f]);
+              }
             }
           }
         };

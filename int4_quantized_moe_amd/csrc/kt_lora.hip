@@ -523,14 +523,18 @@ __global__ __launch_bounds__(256) void k_grad_exps(GradPrepArgs a) {
   if (threadIdx.x == 0) a.eorder[s_rank] = e;
 }
 
-// The narrow planes of one row tile: every row's four families as 16-bit hi/lo
-// pairs (bf16 by truncation for the x and dY families, fp16 rounded to nearest
-// for the h and dG|dU families after the expert's exponent), zero past the rank.
+// The narrow planes of one row tile's rows [16 y, 16 y + 16) (y = blockIdx.y):
+// every row's four families as 16-bit hi/lo pairs (bf16 by truncation for the x
+// and dY families, fp16 rounded to nearest for the h and dG|dU families after the
+// expert's exponent), zero past the rank.
+constexpr int kPlaneRows = 16;  // rows of a tile per block
 __global__ __launch_bounds__(256) void k_grad_planes(GradPrepArgs a) {
   const int tile = blockIdx.x;
   if ((unsigned long long)tile >= a.counters[kNumTiles]) return;
-  const int e = a.tile_e[tile], m0 = a.tile_m0[tile];
-  const int mlen = min(a.mt, a.offsets[e + 1] - m0);
+  const int e = a.tile_e[tile];
+  const int m0 = a.tile_m0[tile] + kPlaneRows * (int)blockIdx.y;
+  const int mlen = min(kPlaneRows, a.offsets[e + 1] - m0);
+  if (mlen <= 0) return;
   const int sh = a.gexp[2 * e], sg = a.gexp[2 * e + 1];
   const int R = a.R;
   const int ux = (int)(a.np_x / 8), ud = (int)(a.np_dy / 8), uh = (int)(a.np_h / 8), ug = (int)(a.np_g / 4);
@@ -894,7 +898,7 @@ void launch_lora_grads(const Dims& d, const WsMap& w, void* ws, const uint16_t* 
   k_grad_exps<<<(unsigned)d.E, 256, 0, st>>>(p);
   note_launch();
   if (w.max_tiles > 0) {
-    k_grad_planes<<<(unsigned)w.max_tiles, 256, 0, st>>>(p);
+    k_grad_planes<<<dim3((unsigned)w.max_tiles, (unsigned)((w.mt + kPlaneRows - 1) / kPlaneRows)), 256, 0, st>>>(p);
     note_launch();
   }
 
