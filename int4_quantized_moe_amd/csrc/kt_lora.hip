@@ -605,6 +605,25 @@ __global__ __launch_bounds__(256) void k_grad_planes(GradPrepArgs a) {
   }
 }
 
+// The window rule for experts no row is routed to, when the call does not
+// accumulate: their six gradient slices are zero.  Block (e, g, c) clears chunk c
+// of gradient g's slice of expert e (slices are contiguous [E][...] rows).
+struct GradZeroArgs {
+  const int32_t* offsets;
+  float* g[6];
+  int64_t n[6];  // floats per expert in each gradient
+};
+constexpr int kZeroChunk = 32768;  // floats per block
+__global__ __launch_bounds__(256) void k_grad_zero_unrouted(GradZeroArgs a) {
+  const int e = blockIdx.x, j = blockIdx.y;
+  if (a.offsets[e + 1] != a.offsets[e]) return;
+  const int64_t n = a.n[j], c0 = (int64_t)blockIdx.z * kZeroChunk;
+  if (c0 >= n) return;
+  float* p = a.g[j] + (int64_t)e * n;
+  const int64_t c1 = min<int64_t>(n, c0 + kZeroChunk);
+  for (int64_t i = c0 + threadIdx.x; i < c1; i += blockDim.x) p[i] = 0.f;
+}
+
 struct GradArgs {
   int E, R;
   const int32_t* offsets;
@@ -672,7 +691,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int half = (int)((rem / (unsigned)a.nvh) % (unsigned)a.nhalves);
   const int vt = (int)(rem % (unsigned)a.nvh);
   const int m0 = a.offsets[e], rows = a.offsets[e + 1] - m0;
-  if (rows == 0 && a.accumulate) return;
+  if (rows == 0) return;  // (an expert without rows: its gradient is zeroed by k_grad_zero_unrouted, or kept)
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t v0 = (int64_t)vt * 256;
@@ -899,6 +918,22 @@ void launch_lora_grads(const Dims& d, const WsMap& w, void* ws, const uint16_t* 
   note_launch();
   if (w.max_tiles > 0) {
     k_grad_planes<<<dim3((unsigned)w.max_tiles, (unsigned)((w.mt + kPlaneRows - 1) / kPlaneRows)), 256, 0, st>>>(p);
+    note_launch();
+  }
+
+  if (!accumulate) {
+    GradZeroArgs z{};
+    z.offsets = p.offsets;
+    float* gs[6] = {out.ag, out.au, out.bd, out.ad, out.bg, out.bu};
+    const int64_t ns[6] = {d.R * d.H, d.R * d.H, d.H * d.R, d.R * d.I, d.I * d.R, d.I * d.R};
+    int64_t nmax = 0;
+    for (int j = 0; j < 6; ++j) {
+      z.g[j] = gs[j];
+      z.n[j] = ns[j];
+      nmax = std::max(nmax, ns[j]);
+    }
+    const dim3 zg((unsigned)d.E, 6u, (unsigned)((nmax + kZeroChunk - 1) / kZeroChunk));
+    k_grad_zero_unrouted<<<zg, 256, 0, st>>>(z);
     note_launch();
   }
 
