@@ -974,9 +974,13 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
       constexpr int kPC = MT / kRPI;                // plane copies per sub-group
       constexpr int kPI = (kPC + 3) / 4;            // plane copies per wave per sub-group
       static_assert(kPC * kRPI == MT && kPC <= 4 * kPI && 4 * kPI - kPC <= kPC, "plane copies");
-      const int nsg = KLP / 16;
+      // only the sub-groups that hold contraction values below the rank: a half
+      // is padded to a multiple of 32, and the padding contributes nothing
+      const int nsgh = (R + 15) / 16;               // sub-groups per half
+      const int nsg = (kTwoHalves ? 2 : 1) * nsgh;  // sub-groups in all
+      auto sg_q0 = [&](int sg) { return (sg / nsgh) * RP + 16 * (sg % nsgh); };
       auto issue_lora = [&](int sg) {
-        const int q0 = 16 * sg, half = q0 >= RP ? 1 : 0, qh = q0 - half * RP;
+        const int q0 = sg_q0(sg), half = q0 >= RP ? 1 : 0, qh = q0 - half * RP;
         const int b = sg % kLBuf;
         const uint32_t la = lds_addr(ring) + b * kLA, lb = lds_addr(ring) + kLBuf * kLA + b * kLB;
         // planes: 4 lanes per row, chunk c (0, 1 hi; 2, 3 lo) at c ^ ((row >> 1) & 3)
@@ -1037,7 +1041,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
       issue_lora(0);
       if (nsg > 1) issue_lora(1);
       for (int sg = 0; sg < nsg; ++sg) {
-        const int q0 = 16 * sg, half = q0 >= RP ? 1 : 0, qh = q0 - half * RP;
+        const int q0 = sg_q0(sg), half = q0 >= RP ? 1 : 0, qh = q0 - half * RP;
         // sub-group sg has landed once at most sub-group sg + 1's copies are outstanding
         if (sg + 1 < nsg)
           wait_vm_lgkm<kPI + 4>();
