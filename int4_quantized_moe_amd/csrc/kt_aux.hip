@@ -3,6 +3,8 @@
 // route-weight gradient, and the codec test hooks.
 #include <limits.h>
 
+#include <algorithm>
+
 #include "kt_common.hpp"
 #include "kt_internal.hpp"
 
@@ -323,25 +325,39 @@ void launch_fill_zero_f32(float* p, int64_t n, hipStream_t st) {
 
 // out[t, c] = sum over valid slots s of stage[t*k + s, c] * 2^-p(t*k + s, c / 64), in slot
 // order, in fp32, then to bf16 (round to nearest even); staged values are fp16.  Each
-// thread sums 8 columns (one 16-byte staged chunk per slot).
-__global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ stage, const int32_t* __restrict__ stexp,
-                                                 int64_t st_nch, const int64_t* __restrict__ ids, int topk, int E,
-                                                 int64_t H, uint16_t* __restrict__ out) {
+// thread sums 8 columns (one 16-byte staged chunk per slot); a block covers whole
+// rows of one token.  The slots are read eight at a time, all eight requests out
+// before the first sum (a dropped slot's row is read but not added).
+__global__ __launch_bounds__(1024) void k_combine(const uint16_t* __restrict__ stage,
+                                                  const int32_t* __restrict__ stexp, int64_t st_nch,
+                                                  const int64_t* __restrict__ ids, int topk, int E, int64_t H,
+                                                  uint16_t* __restrict__ out) {
   const int64_t t = blockIdx.x;
   const int64_t c = ((int64_t)blockIdx.y * blockDim.x + threadIdx.x) * 8;
   if (c >= H) return;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < topk; ++s) {
-    const int64_t slot = t * topk + s;
-    const int64_t e = ids[slot];
-    if (e < 0 || e >= E) continue;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + slot * H + c);
-    const int ex = -stexp[slot * st_nch + c / kStageExp];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  for (int s0 = 0; s0 < topk; s0 += 8) {
+    u32x4 v[8];
+    int ex[8];
+    bool ok[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc[2 * q] += ldexpf(half_bits_to_float((uint16_t)(w[q] & 0xffffu)), ex);
-      acc[2 * q + 1] += ldexpf(half_bits_to_float((uint16_t)(w[q] >> 16)), ex);
+    for (int j = 0; j < 8; ++j) {
+      const int s = min(s0 + j, topk - 1);
+      const int64_t slot = t * topk + s;
+      const int64_t e = ids[slot];
+      ok[j] = s0 + j < topk && e >= 0 && e < E;
+      v[j] = *reinterpret_cast<const u32x4*>(stage + slot * H + c);
+      ex[j] = -stexp[slot * st_nch + c / kStageExp];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (!ok[j]) continue;
+      const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += ldexpf(half_bits_to_float((uint16_t)(w[q] & 0xffffu)), ex[j]);
+        acc[2 * q + 1] += ldexpf(half_bits_to_float((uint16_t)(w[q] >> 16)), ex[j]);
+      }
     }
   }
   // two 8-byte stores: the output is only required to be 8-byte aligned
@@ -357,8 +373,11 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ st
 void launch_combine(const Dims& d, const uint16_t* stage, const int32_t* stexp, int64_t st_nch, const int64_t* ids,
                     uint16_t* out, hipStream_t st) {
   if (d.qlen == 0) return;
-  dim3 grid((unsigned)d.qlen, (unsigned)((d.H / 8 + 255) / 256));
-  k_combine<<<grid, 256, 0, st>>>(stage, stexp, st_nch, ids, (int)d.K, (int)d.E, d.H, out);
+  // one block per token row when it fits (up to 1024 threads of 8 columns)
+  const int64_t chunks = d.H / 8;
+  const int64_t thr = std::min<int64_t>(1024, (chunks + 63) / 64 * 64);
+  dim3 grid((unsigned)d.qlen, (unsigned)((chunks + thr - 1) / thr));
+  k_combine<<<grid, (unsigned)thr, 0, st>>>(stage, stexp, st_nch, ids, (int)d.K, (int)d.E, d.H, out);
   note_launch();
 }
 

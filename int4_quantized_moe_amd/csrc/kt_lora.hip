@@ -528,6 +528,25 @@ __global__ __launch_bounds__(256) void k_grad_exps(GradPrepArgs a) {
 // and dY families, fp16 rounded to nearest for the h and dG|dU families after the
 // expert's exponent), zero past the rank.
 constexpr int kPlaneRows = 16;  // rows of a tile per block
+
+// Values c .. c + 7 of an fp32 row of R values (zero past R), times f: two
+// 16-byte loads when R is a multiple of 8 (a run of 8 then lies wholly inside
+// the row or wholly past it, and starts 32-byte aligned), else one at a time.
+__device__ __forceinline__ void load8_scaled(const float* row, int64_t c, int R, float f, float (&v)[8]) {
+  if ((R & 7) == 0) {
+    if (c < R) {
+      const float4 x0 = *reinterpret_cast<const float4*>(row + c), x1 = *reinterpret_cast<const float4*>(row + c + 4);
+      v[0] = x0.x * f, v[1] = x0.y * f, v[2] = x0.z * f, v[3] = x0.w * f;
+      v[4] = x1.x * f, v[5] = x1.y * f, v[6] = x1.z * f, v[7] = x1.w * f;
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) v[t] = 0.f;
+    }
+    return;
+  }
+#pragma unroll
+  for (int t = 0; t < 8; ++t) v[t] = c + t < R ? row[c + t] * f : 0.f;
+}
 __global__ __launch_bounds__(256) void k_grad_planes(GradPrepArgs a) {
   const int tile = blockIdx.x;
   if ((unsigned long long)tile >= a.counters[kNumTiles]) return;
@@ -551,16 +570,14 @@ __global__ __launch_bounds__(256) void k_grad_planes(GradPrepArgs a) {
       const bool second = u >= a.r16;
       const float* src = second ? a.dub : a.dgb;
       const int64_t c = second ? u - a.r16 : u;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) v[t] = c + t < R ? src[m * R + c + t] : 0.f;
+      load8_scaled(src + m * R, c, R, 1.f, v);
       off = a.off_x + u;
       pw = a.np_x;
       f16 = false;
     } else if ((j -= ux) < ud) {  // rw ud
       const int64_t u = 8 * j;
       const float rw = a.rw[a.sorted_slot[m]];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) v[t] = u + t < R ? a.ud[m * R + u + t] * rw : 0.f;
+      load8_scaled(a.ud + m * R, u, R, rw, v);
       off = a.off_dy + u;
       pw = a.np_dy;
       f16 = false;
@@ -568,8 +585,9 @@ __global__ __launch_bounds__(256) void k_grad_planes(GradPrepArgs a) {
       const int64_t u = 8 * j;
       const float rw = a.rw[a.sorted_slot[m]];
       const int k = sh - a.hexp[m * a.h_nch];
+      load8_scaled(a.dyb + m * R, u, R, rw, v);
 #pragma unroll
-      for (int t = 0; t < 8; ++t) v[t] = u + t < R ? ldexpf(a.dyb[m * R + u + t] * rw, k) : 0.f;
+      for (int t = 0; t < 8; ++t) v[t] = ldexpf(v[t], k);
       off = a.off_h + u;
       pw = a.np_h;
       f16 = true;
@@ -580,8 +598,9 @@ __global__ __launch_bounds__(256) void k_grad_planes(GradPrepArgs a) {
       const float* src = second ? a.ub : a.ua;
       const int64_t c = second ? u - a.np_g : u;
       const int k = sg - a.dgexp[m * a.dg_nch];
+      load8_scaled(src + m * R, c, R, 1.f, v);
 #pragma unroll
-      for (int t = 0; t < 8; ++t) v[t] = c + t < R ? ldexpf(src[m * R + c + t], k) : 0.f;
+      for (int t = 0; t < 8; ++t) v[t] = ldexpf(v[t], k);
       off = a.off_g + u;
       pw = 2 * a.np_g;
       f16 = true;
@@ -661,7 +680,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   constexpr int kNRow = 4 * NUT;         // LDS bytes of one narrow row: NUT hi then NUT lo values
   constexpr int kNC = NUT / 4;           // 16-byte chunks per narrow row
   constexpr int kStage = kWBytes + kGK * kNRow;
-  constexpr int kStages = 3;
+  constexpr int kStages = 2;
   constexpr int L = kStages - 1;                    // steps in flight ahead of the one multiplied
   constexpr int kWI = 16 / NW;                      // wide copies (1 KB each) per wave per step
   constexpr int kNCW = 8 * NUT / NW;                // narrow 16-byte chunks per wave per step
@@ -786,7 +805,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       // step s has landed once at most the later step's copies are outstanding;
       // the barrier shows every wave's copies and frees the slot refilled next
       if (s + 1 < nsteps)
-        wait_vm_lgkm<kOps>();
+        wait_vm_lgkm<(L - 1) * kOps>();
       else
         wait_vm_lgkm<0>();
       __builtin_amdgcn_s_barrier();
