@@ -207,7 +207,7 @@ __device__ __forceinline__ void wait_stages(int n) {
 // MX: the weights are MXFP4 (E2M1 codes, power-of-two scales) instead of RAWINT4.
 template <int KIND, int MT, bool LDMA, bool MX>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt, uint8_t* ring, int32_t* s_src,
-                                          int32_t* s_exp, int32_t* s_slot) {
+                                          int32_t* s_exp, int32_t* s_slot, float* s_rw) {
   constexpr int MB = MT / 16;
   constexpr bool kT = (KIND == kDownBwd || KIND == kGateUpBwd);
   constexpr bool kChunked = (KIND == kDown || KIND == kGateUpBwd);
@@ -256,7 +256,11 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
     }
     s_src[tid] = src;
     s_exp[tid] = ex;
-    s_slot[tid] = tid < mlen ? p.sorted_slot[m] : -1;
+    const int slot = p.sorted_slot[m];
+    s_slot[tid] = tid < mlen ? slot : -1;
+    // the route weights the epilogues of down and down dX scale by, read here
+    // once so that their loads do not wait behind the epilogue's stores
+    if constexpr (KIND == kDown || KIND == kDownBwd) s_rw[tid] = tid < mlen ? p.rw[slot] : 0.f;
   }
   __syncthreads();
 
@@ -1357,7 +1361,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
         const int row = mb * 16 + lg * 4 + i;
         const bool vrow = row < mlen;
         const int slot = vrow ? s_slot[row] : 0;
-        const float wgt = (KIND == kDown && vrow) ? p.rw[slot] : 1.f;
+        const float wgt = (KIND == kDown && vrow) ? s_rw[row] : 1.f;
         float v[4];
         float mx = 0.f;
 #pragma unroll
@@ -1379,13 +1383,14 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
     // times 2^p, p per (row, this wave's 64 columns) for each
     const int half_nch = p.dg_nch / 2;
     const int chunk = (n0 + w * 64) / kDgExp;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      // the saved g, u of this lane's four rows of each column: one 16-byte load each
-      // (quads past the tile's rows are not read: they may lie past the buffer)
+    // the saved g, u of this lane's four rows of each column: one 16-byte load
+    // each (quads past the tile's rows are not read: they may lie past the
+    // buffer).  Row block mb + 1's are requested before row block mb's results
+    // are stored, since the compiler cannot move them above those stores itself.
+    floatx4 gbuf[2][4], ubuf[2][4];
+    auto load_gu = [&](int mb, floatx4 (&gq)[4], floatx4 (&uq)[4]) {
       const int r0 = mb * 16 + lg * 4;
       const int64_t qrow = (qb + r0) >> 2;
-      floatx4 gq[4], uq[4];
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
         const int cc = min(n0 + w * 64 + f * 16 + lr, I - 1);
@@ -1397,12 +1402,19 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
           uq[f] = gq[f];
         }
       }
+    };
+    load_gu(0, gbuf[0], ubuf[0]);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      if (mb + 1 < MB) load_gu(mb + 1, gbuf[(mb + 1) & 1], ubuf[(mb + 1) & 1]);
+      const floatx4(&gq)[4] = gbuf[mb & 1];
+      const floatx4(&uq)[4] = ubuf[mb & 1];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = mb * 16 + lg * 4 + i;
         const bool vrow = row < mlen;
         const size_t m = (size_t)(m0 + min(row, mlen - 1));
-        const float wgt = vrow ? p.rw[s_slot[row]] : 0.f;
+        const float wgt = vrow ? s_rw[row] : 0.f;
         float dg[4], du[4];
         float dr = 0.f, mxg = 0.f, mxu = 0.f;
 #pragma unroll
@@ -1452,6 +1464,7 @@ template <int KIND, bool LDMA, bool MX>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm(GemmParams p) {
   __shared__ __align__(16) uint8_t ring[kRingMax];
   __shared__ int32_t s_src[128], s_exp[128], s_slot[128];
+  __shared__ float s_rw[128];
   // work item: (list position, column tile).  Position p runs on XCD p % 8
   // (blocks reach the XCDs in turn) and each XCD runs its positions' column
   // tiles in order: a tile's activation rows stay in one XCD's L2, and so do
@@ -1465,19 +1478,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int nt = (int)(local % nn);
   switch (p.tile_mt[tile]) {
     case 16:
-      gemm_tile<KIND, 16, LDMA, MX>(p, tile, nt, ring, s_src, s_exp, s_slot);
+      gemm_tile<KIND, 16, LDMA, MX>(p, tile, nt, ring, s_src, s_exp, s_slot, s_rw);
       break;
     case 32:
-      gemm_tile<KIND, 32, LDMA, MX>(p, tile, nt, ring, s_src, s_exp, s_slot);
+      gemm_tile<KIND, 32, LDMA, MX>(p, tile, nt, ring, s_src, s_exp, s_slot, s_rw);
       break;
     case 64:
-      gemm_tile<KIND, 64, LDMA, MX>(p, tile, nt, ring, s_src, s_exp, s_slot);
+      gemm_tile<KIND, 64, LDMA, MX>(p, tile, nt, ring, s_src, s_exp, s_slot, s_rw);
       break;
     case 96:
-      gemm_tile<KIND, 96, LDMA, MX>(p, tile, nt, ring, s_src, s_exp, s_slot);
+      gemm_tile<KIND, 96, LDMA, MX>(p, tile, nt, ring, s_src, s_exp, s_slot, s_rw);
       break;
     default:
-      gemm_tile<KIND, 128, LDMA, MX>(p, tile, nt, ring, s_src, s_exp, s_slot);
+      gemm_tile<KIND, 128, LDMA, MX>(p, tile, nt, ring, s_src, s_exp, s_slot, s_rw);
       break;
   }
 }
