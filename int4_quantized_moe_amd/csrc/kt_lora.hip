@@ -884,7 +884,7 @@ static void launch_grad_family(int nut, unsigned grid, const GradArgs& a, hipStr
       k_lora_grad<64, FAM, 4><<<grid, 256, 0, st>>>(a);
       note_launch();
       break;
-    default:  // 8 waves: the 128-column narrow block and a three-step ring take one CU's LDS
+    default:  // 8 waves: a block of the 128-column narrow width and a two-step ring (64 KB of LDS)
       k_lora_grad<128, FAM, 8><<<grid, 512, 0, st>>>(a);
       note_launch();
       break;
