@@ -233,6 +233,12 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
 
   const int e = p.tile_e[tile], m0 = p.tile_m0[tile];
   const int es = p.expert_slot[e];  // the expert's place in the scale tables
+  // Values the code after the main loop needs, read here with the tile's set-up
+  // (the loop's asm copies keep the compiler from moving these reads above
+  // it): the power-of-two shift of the expert's scale table, and the first
+  // quad-row position of the tile (the expert's tiles start at multiples of 4 rows)
+  const int sshift = p.sshift[2 * e + ((KIND == kGateUp || KIND == kGateUpBwd) ? 0 : 1)];
+  const int64_t qb = (int64_t)p.qoffsets[e] + (m0 - p.offsets[e]);
   const int mlen = min(MT, p.offsets[e + 1] - m0);
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
@@ -914,7 +920,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
   // The scale tables hold scale * 2^-s for an expert whose scales lie outside
   // the exact domain (s = 0 otherwise): the sums get 2^s back before the LoRA terms.
   {
-    const int sh = p.sshift[2 * e + ((KIND == kGateUp || KIND == kGateUpBwd) ? 0 : 1)];
+    const int sh = sshift;
     if (sh != 0) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
@@ -1294,8 +1300,6 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
   // acc holds the plain sums.  One pass: every exponent belongs to one wave's
   // columns of one row, so a 16-lane reduction finds it.
   const float limit = p.limit;
-  // first quad-row position of the tile (the expert's tiles start at multiples of 4 rows)
-  const int64_t qb = (int64_t)p.qoffsets[e] + (m0 - p.offsets[e]);
   if constexpr (KIND == kGateUp) {
     // g, u saved in fp32 (training), a lane's four rows of a column as one 16-byte store
 #pragma unroll
