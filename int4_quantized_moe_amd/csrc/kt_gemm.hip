@@ -86,6 +86,13 @@ struct FTag {
 };
 typedef void __attribute__((address_space(3)))* lds_ptr;
 
+// The ring's wait-and-barrier points are fenced for the compiler as well: the
+// s_waitcnt and s_barrier builtins do not order memory accesses for it, so
+// without these empty asm statements it could move a fragment read of a stage
+// above the barrier that makes the stage visible, or a read of a slot below the
+// barrier after which another wave refills the slot.
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
 struct GemmParams {
   int E, topk, H, I, R;
   float sc, limit;
@@ -600,16 +607,20 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
     Codes C[2];
     issue_acts(0, 0);
     load_codes(0, C[0]);
+    compiler_fence();
     wait_vm_lgkm<0>();
     __builtin_amdgcn_s_barrier();
+    compiler_fence();
     if (nunits > 1) issue_acts(1, 1);
     for (int u0 = 0; u0 < nunits; u0 += 2) {
 #pragma unroll
       for (int d = 0; d < 2; ++d) {
         const int u = u0 + d;
         load_codes(u + 1, C[d ^ 1]);
+        compiler_fence();
         wait_vm_lgkm<kCodeVm>();
         __builtin_amdgcn_s_barrier();
+        compiler_fence();
         if (u + 2 < nunits) issue_acts(u + 2, (u + 2) % kNA);  // (no copy is left in flight at the end)
         __builtin_amdgcn_sched_barrier(0);
         if (u < nunits) compute(C[d], u % kNA);  // (an odd count leaves the loop's last unit empty)
@@ -750,8 +761,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
     // read and its weights decoded.
     auto step = [&](int ss, const u32x4 (&acur)[2][MB], const u32x4 (&bcur)[2][4], u32x4 (&anxt)[2][MB],
                     u32x4 (&bnxt)[2][4]) {
+      compiler_fence();
       if (ss + 1 < nss) wait_stages<kDmaPerStage>(min(kStages - 3, nss - 2 - ss));  // stages issued after ss + 1
       __builtin_amdgcn_s_barrier();
+      compiler_fence();
       if (ss + kStages - 1 < nss) issue(ss + kStages - 1);
       const int sn = min(ss + 1, nss - 1);  // (re-reads the last stage at the end; unused)
       read_a(sn % kStages, anxt);
@@ -772,8 +785,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
       u32x4 afa[2][MB], afb[2][MB], bfa[2][4], bfb[2][4];
       {
         // stage 0 landed: the stages issued after it may still be in flight
+        compiler_fence();
         wait_stages<kDmaPerStage>(min(kStages - 2, nss - 1));
         __builtin_amdgcn_s_barrier();
+        compiler_fence();
         read_a(0, afa);
         decode(0, bfa);
       }
@@ -793,11 +808,13 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
           // this wave's loads of stage ss have landed once at most the later
           // stages' DMAs are outstanding; the barrier makes every wave's loads
           // visible and frees the slot that stage ss + kStages - 1 refills
+          compiler_fence();
           if (ss + 1 < nss)
             wait_vm_lgkm<kDmaPerStage>();
           else
             wait_vm_lgkm<0>();
           __builtin_amdgcn_s_barrier();
+          compiler_fence();
           if (ss + kStages - 1 < nss) issue(ss + kStages - 1);
           if constexpr (kT) {
             // As below for the stored orientation: fragment (j, f) is decoded
@@ -1053,12 +1070,13 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
       for (int sg = 0; sg < nsg; ++sg) {
         const int q0 = sg_q0(sg), half = q0 >= RP ? 1 : 0, qh = q0 - half * RP;
         // sub-group sg has landed once at most sub-group sg + 1's copies are outstanding
+        compiler_fence();
         if (sg + 1 < nsg)
           wait_vm_lgkm<kPI + 4>();
         else
           wait_vm_lgkm<0>();
         __builtin_amdgcn_s_barrier();  // also: every wave is done with the buffers sub-group sg + 2 refills
-        asm volatile("" ::: "memory");
+        compiler_fence();
         if (sg + 2 < nsg) issue_lora(sg + 2);
         const uint8_t* la = ring + (sg % kLBuf) * kLA;
         const uint8_t* lb = ring + kLBuf * kLA + (sg % kLBuf) * kLB;
@@ -1229,8 +1247,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, int nt,
           *reinterpret_cast<u32x4*>(lb + 32 * kLBP + qi * kLBP + 2 * (c32 + 8 * c8)) = lo;
         }
       }
+      compiler_fence();
       wait_vm_lgkm<0>();
       __builtin_amdgcn_s_barrier();
+      compiler_fence();
 
       // plane columns at or past R within the half hold no product: mask them (they may be stale)
       const int nval = min(max(R - (qh + 8 * lg), 0), 8);

@@ -794,6 +794,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     if constexpr (kGather) {
 #pragma unroll
       for (int t = 0; t < L; ++t) issue_idx(t);
+      asm volatile("" ::: "memory");
       wait_vm_lgkm<0>();
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
@@ -804,6 +805,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int s = 0; s < nsteps; ++s) {
       // step s has landed once at most the later step's copies are outstanding;
       // the barrier shows every wave's copies and frees the slot refilled next
+      // (the empty asm statements keep the compiler from moving LDS accesses
+      // across the wait and the barrier, which do not order them for it)
+      asm volatile("" ::: "memory");
       if (s + 1 < nsteps)
         wait_vm_lgkm<(L - 1) * kOps>();
       else
