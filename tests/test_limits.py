@@ -1,7 +1,8 @@
 """GPU parity at the ABI's limits: the largest rank (128, both LoRA halves of
 gate/up 128 wide), the largest expert count (8192, most experts empty, a few
 ids at the top of the range), and top_k = num_experts.  Oracle and bars as in
-test_parity.  Each case prints its name first."""
+test_parity.  Each case prints its name first.  Also more than eight slots
+per token, which the output and dx combine read in rounds of eight."""
 
 import numpy as np
 import pytest
@@ -44,7 +45,8 @@ def _run_and_check(dev, cfg, weights, batch):
               ("dX", dx.float().cpu().numpy(), ref["dx"], 5e-3, 0.9999),
               ("dRoute", dr.cpu().numpy(), ref["droute"], 3e-2, 0.995)]
     g = {n: t.cpu().numpy() for n, t in grads.items()}
-    active = np.unique(batch.expert_ids)
+    ids = batch.expert_ids
+    active = np.unique(ids[(ids >= 0) & (ids < cfg.num_experts)])
     checks += [(n, g[n][active], ref["grads"][n][active], 5e-3, 0.9999) for n in O.LORA_NAMES]
     failures = []
     for name, a, e, rel, cos in checks:
@@ -84,3 +86,18 @@ def test_top_k_equals_experts(dev):
     cfg = W.LayerConfig("topk_all", 6, 6, 96, 128, 8, 16.0, 20, 0.0)
     _say("top_k = num_experts")
     _run_and_check(dev, cfg, W.make_weights(cfg, 137), W.make_batch(cfg, 137))
+
+
+def test_top_k_above_eight_with_dropped_slots(dev):
+    # 12 slots per token: the combine sums them in two rounds (8 + 4); some slots
+    # of both rounds carry dropped ids (-1, or past the last expert), which add nothing
+    cfg = W.LayerConfig("topk12", 20, 12, 96, 128, 8, 16.0, 24, 1.5, x_std=2.0)
+    _say("top_k = 12 with dropped slots")
+    weights = W.make_weights(cfg, 139)
+    batch = W.make_batch(cfg, 139)
+    batch.expert_ids[0, 9] = -1
+    batch.expert_ids[1, 3] = cfg.num_experts
+    batch.expert_ids[2, 11] = -1
+    batch.expert_ids[2, 10] = cfg.num_experts + 5
+    batch.expert_ids[5, 8:] = -1
+    _run_and_check(dev, cfg, weights, batch)
