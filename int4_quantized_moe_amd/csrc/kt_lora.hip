@@ -61,6 +61,7 @@ struct SideArgs {
   int64_t split_ld, split_off, split_off2;
   float split_scale;
   int ksplit;   // contraction ranges (blockIdx.y); above 1 the blocks write partial sums
+  int sub;      // workgroups per tile of the list (each takes MT consecutive rows of it)
   float* part;  // [ksplit][Ms][nq] partial sums, reduced in order by k_side_reduce
   int64_t Ms;
   const int32_t* nrows;  // rows routed to an expert (offsets[E])
@@ -123,13 +124,15 @@ __global__ __launch_bounds__(256) void k_lora_side(SideArgs a) {
   // share an XCD, and so its L2 for the expert's LoRA matrix.  (The grid is a
   // whole number of rounds of 8 blocks, at least the items in use: every XCD
   // has a block for each of its items.)
-  const unsigned nitems = (unsigned)a.counters[kNumTiles] * gridDim.y;
+  const unsigned nitems = (unsigned)a.counters[kNumTiles] * a.sub * gridDim.y;
   const unsigned bid = blockIdx.y * gridDim.x + blockIdx.x, per = (nitems + 7) / 8;
   const unsigned item = (bid % 8) * per + bid / 8;
   if (bid / 8 >= per || item >= nitems) return;
-  const int tile = (int)(item / gridDim.y), ks = (int)(item % gridDim.y);
-  const int e = a.tile_e[tile], m0 = a.tile_m0[tile];
+  const unsigned per_tile = (unsigned)a.sub * gridDim.y;
+  const int tile = (int)(item / per_tile), sb = (int)(item % per_tile / gridDim.y), ks = (int)(item % gridDim.y);
+  const int e = a.tile_e[tile], m0 = a.tile_m0[tile] + MT * sb;
   const int mlen = min(MT, a.offsets[e + 1] - m0);
+  if (mlen <= 0) return;  // (a part of a list tile past its expert's rows)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
   const int R = a.R, kdim = a.kdim;
   if (tid < MT) {
@@ -391,16 +394,23 @@ void launch_lora_rowproj(const Dims& d, const WsMap& w, void* ws, const RowView&
   a.tok_exp = tok_exp;
   const bool half = src.kind == kSrcHalfChunked;
   const int nb = (a.nq + 63) / 64;
+  // Short contractions (the intermediate width) run each 128-row tile of the
+  // list as two 64-row workgroups: fewer padding rows per workgroup for
+  // lightly loaded experts, and twice the workgroups in flight (measured
+  // faster there; the hidden-width contractions are not).
+  a.sub = (w.mt == 128 && kdim <= 2048) ? 2 : 1;
   // few tiles (small token counts) leave most CUs idle through a long
   // contraction: split it over blocks and reduce the partial sums in order
-  a.ksplit = (int)std::min<int64_t>(w.side_ksplit, kdim / (4 * kSK));
+  // (~4096 workgroups in all, at most the split the workspace is planned for)
+  const int64_t items = std::max<int64_t>(w.max_tiles * a.sub, 1);
+  a.ksplit = (int)std::min<int64_t>(std::min<int64_t>(w.side_ksplit, (4096 + items - 1) / items), kdim / (4 * kSK));
   if (a.ksplit < 1) a.ksplit = 1;
   a.part = ws_ptr<float>(ws, w.side_part);
   a.Ms = d.Ms;
   a.nrows = a.offsets + d.E;
   // whole rounds of 8 blocks: every XCD then has a block for each of its items
-  const dim3 grid((unsigned)((w.max_tiles + 7) / 8 * 8), (unsigned)a.ksplit);
-  switch (w.mt) {
+  const dim3 grid((unsigned)((w.max_tiles * a.sub + 7) / 8 * 8), (unsigned)a.ksplit);
+  switch (w.mt / a.sub) {
     case 16:
       launch_side_mt<16>(nb, half, grid, a, st);
       break;
