@@ -401,9 +401,10 @@ void launch_lora_rowproj(const Dims& d, const WsMap& w, void* ws, const RowView&
   a.sub = (w.mt == 128 && kdim <= 2048) ? 2 : 1;
   // few tiles (small token counts) leave most CUs idle through a long
   // contraction: split it over blocks and reduce the partial sums in order
-  // (~4096 workgroups in all, at most the split the workspace is planned for)
+  // (~4096 workgroups in all, at most the split the workspace is planned for;
+  // none once there are 2048 or more workgroups without it)
   const int64_t items = std::max<int64_t>(w.max_tiles * a.sub, 1);
-  a.ksplit = (int)std::min<int64_t>(std::min<int64_t>(w.side_ksplit, (4096 + items - 1) / items), kdim / (4 * kSK));
+  a.ksplit = items >= 2048 ? 1 : (int)std::min<int64_t>(std::min<int64_t>(w.side_ksplit, (4096 + items - 1) / items), kdim / (4 * kSK));
   if (a.ksplit < 1) a.ksplit = 1;
   a.part = ws_ptr<float>(ws, w.side_part);
   a.Ms = d.Ms;
